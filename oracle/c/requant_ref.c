@@ -1,0 +1,180 @@
+/*
+ * Exact reference for the load-time NVFP4 -> sign-symmetric 2-bit
+ * requantisation and for the FP4 delta (oracle; test infrastructure only).
+ *
+ * Sources (public description of vLLM-Moet):
+ *  - README "Frontier MoE on consumer Blackwell (SM120)", section
+ *    "GLM-5.2 (753B) — the headline model": NVFP4 experts (e2m1 values,
+ *    e4m3 scale per 16 weights, fp32 per-tensor scale_2) are requantised at
+ *    load time to sign-symmetric 2-bit planes, exactly in float64.
+ *  - same README, section "How it fits — 2-bit experts at FP4 quality": the
+ *    codebook is {-4,-1,1,4}, chosen at equal L2 error; an FP4 delta restores
+ *    precision for experts held in a delta cache.
+ *  - same README, section "Kimi-K2.7-Code (1T MoE) on 4x RTX PRO 6000": zeros
+ *    exported only as +0 skew the result, so a zero takes its level from its
+ *    own sign bit.
+ *
+ * Readings (the pages leave these open):
+ *  - every NVFP4 value is an integer multiple of u = 2^-10 * scale_2:
+ *    |Y| = (2|e2m1|) * (e4m3 * 2^9), |Y| < 2^22;
+ *  - output per-tensor scale = 2 * scale_2; per-block e4m3 scale over
+ *    B = 32 consecutive weights along K (B is a parameter here so that tiny
+ *    blocks can be brute-forced); the level-1 magnitude of candidate scale code
+ *    t is a = 4 * (e4m3(t) * 2^9) in units of u;
+ *  - the block scale minimises the exact L2 error
+ *        Err(t) = sum_i min((|Y_i| - a)^2, (|Y_i| - 4a)^2)
+ *    over all finite non-negative e4m3 codes t = 0x00..0x7E, ties -> smaller t;
+ *  - element code = (s << 1) | m with s = the NVFP4 sign bit (also for -0) and
+ *    m = 1 iff 2|Y| > 5a (a tie keeps magnitude 1); levels: 0:+1 1:+4 2:-1 3:-4;
+ *  - delta D = Y_nvfp4 - Y_2bit (exact integer in units of u), re-encoded as
+ *    NVFP4 with the source scale_2: block-16 scale = e4m3 nearest (ties to the
+ *    even code, saturating at 448) to max|D| / (6 * 2^10); element = e2m1
+ *    nearest (ties to the even code, saturating at 6) to D / (2 * e4m3*2^9);
+ *    a value rounding to zero keeps the sign of D; D == 0 gives +0.
+ *
+ * All arithmetic is int64 and exact.  OpenMP parallelises over rows only.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+
+/* e4m3fn value * 2^9 for the finite non-negative codes 0x00..0x7E. */
+static int64_t e4m3_x512(int t)
+{
+    int e = (t >> 3) & 15, m = t & 7;
+    if (e == 0)
+        return m;                       /* m/8 * 2^-6 * 2^9 */
+    return (int64_t)(8 + m) << (e - 1); /* (1 + m/8) * 2^(e-7) * 2^9 */
+}
+
+/* 2 * |e2m1| for the magnitude bits of a 4-bit code. */
+static int64_t e2m1_mag2(int c)
+{
+    int e = (c >> 1) & 3, m = c & 1;
+    if (e == 0)
+        return m;                       /* 0 or 0.5, doubled */
+    return (int64_t)(2 + m) << (e - 1); /* (1 + m/2) * 2^(e-1), doubled */
+}
+
+static inline int nib(const uint8_t *row, int64_t k)
+{
+    uint8_t b = row[k >> 1];
+    return (k & 1) ? (b >> 4) : (b & 15);
+}
+
+/* Returns 0 on success, -1 if a block scale byte is negative or NaN. */
+int oracle_requant(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                   int64_t B, uint8_t *codes2, uint8_t *tau, int64_t *err_out)
+{
+    int64_t T9[127];
+    for (int t = 0; t < 127; ++t)
+        T9[t] = e4m3_x512(t);
+    int bad = 0;
+    const int64_t nb = K / B;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *crow = codes + n * (K / 2);
+        const uint8_t *srow = scales + n * (K / 16);
+        int64_t *y = (int64_t *)malloc(sizeof(int64_t) * B);
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int64_t i = 0; i < B; ++i) {
+                int64_t k = b * B + i;
+                int sb = srow[k / 16];
+                if (sb >= 0x7F) { bad = 1; sb = 0; }
+                y[i] = e2m1_mag2(nib(crow, k) & 7) * T9[sb];
+            }
+            int best_t = 0;
+            int64_t best_err = -1;
+            for (int t = 0; t < 127; ++t) {
+                int64_t a = 4 * T9[t];
+                int64_t e = 0;
+                for (int64_t i = 0; i < B; ++i) {
+                    int64_t d1 = y[i] - a, d4 = y[i] - 4 * a;
+                    int64_t q1 = d1 * d1, q4 = d4 * d4;
+                    e += q1 < q4 ? q1 : q4;
+                }
+                if (best_err < 0 || e < best_err) {
+                    best_err = e;
+                    best_t = t;
+                }
+            }
+            tau[n * nb + b] = (uint8_t)best_t;
+            if (err_out)
+                err_out[n * nb + b] = best_err;
+            int64_t a = 4 * T9[best_t];
+            for (int64_t i = 0; i < B; ++i) {
+                int64_t k = b * B + i;
+                int s = (nib(crow, k) >> 3) & 1;
+                int m = (2 * y[i] > 5 * a) ? 1 : 0;
+                codes2[n * K + k] = (uint8_t)((s << 1) | m);
+            }
+        }
+        free(y);
+    }
+    return bad ? -1 : 0;
+}
+
+/* FP4 re-encoding of the exact residual; dcodes gets one 4-bit code per weight. */
+int oracle_delta(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K, int64_t B,
+                 const uint8_t *codes2, const uint8_t *tau, uint8_t *dcodes, uint8_t *dscales)
+{
+    int64_t T9[127];
+    for (int t = 0; t < 127; ++t)
+        T9[t] = e4m3_x512(t);
+    static const int64_t thr2[7] = {1, 3, 5, 7, 10, 14, 20}; /* 2 * e2m1 midpoints, doubled */
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *crow = codes + n * (K / 2);
+        const uint8_t *srow = scales + n * (K / 16);
+        int64_t D[16];
+        for (int64_t g = 0; g < K / 16; ++g) {
+            int64_t M = 0;
+            for (int i = 0; i < 16; ++i) {
+                int64_t k = g * 16 + i;
+                int c = nib(crow, k);
+                int sb = srow[k / 16];
+                if (sb >= 0x7F) { bad = 1; sb = 0; }
+                int64_t y = e2m1_mag2(c & 7) * T9[sb];
+                if (c & 8)
+                    y = -y;
+                int c2 = codes2[n * K + k];
+                int64_t a = 4 * T9[tau[n * (K / B) + k / B]];
+                int64_t lvl = (c2 & 1) ? 4 : 1;
+                if (c2 & 2)
+                    lvl = -lvl;
+                D[i] = y - lvl * a;
+                int64_t ad = D[i] < 0 ? -D[i] : D[i];
+                if (ad > M)
+                    M = ad;
+            }
+            /* nearest e4m3 to M / (6 * 2^10): compare M with 12 * T9 (same units) */
+            int ts = 0;
+            int64_t bd = -1;
+            for (int t = 0; t < 127; ++t) {
+                int64_t d = M - 12 * T9[t];
+                if (d < 0)
+                    d = -d;
+                if (bd < 0 || d < bd || (d == bd && (t & 1) == 0 && (ts & 1) == 1)) {
+                    bd = d;
+                    ts = t;
+                }
+            }
+            dscales[n * (K / 16) + g] = (uint8_t)ts;
+            int64_t T = T9[ts];
+            for (int i = 0; i < 16; ++i) {
+                int64_t k = g * 16 + i;
+                int code = 0;
+                if (T > 0 && D[i] != 0) {
+                    int64_t ad2 = 2 * (D[i] < 0 ? -D[i] : D[i]);
+                    int idx = 0;
+                    for (int j = 0; j < 7; ++j)
+                        if (ad2 > thr2[j] * T || (ad2 == thr2[j] * T && (j & 1)))
+                            idx = j + 1;
+                    code = idx | (D[i] < 0 ? 8 : 0);
+                }
+                dcodes[n * K + k] = (uint8_t)code;
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}

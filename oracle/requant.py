@@ -1,0 +1,115 @@
+"""NVFP4 -> 2-bit requantisation and FP4 delta (oracle; test infrastructure only).
+
+Thin ctypes wrapper around ``oracle/c/requant_ref.c`` (exact int64 search) plus
+float64 dequantisation of its results.  See the C file for the sources and
+the readings taken where the pages leave the method open.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from .formats import e2m1_value, e4m3fn_value
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "c", "requant_ref.c")
+_LIB = os.path.join(_HERE, "c", "liboracle_requant.so")
+_lib = None
+
+#: block length of the 2-bit per-block scale along K (reading: 32, which gives
+#: 2.25 bits per weight)
+BLOCK = 32
+#: 2-bit code -> level of the sign-symmetric codebook
+LEVELS = np.array([1.0, 4.0, -1.0, -4.0])
+
+
+def build_oracle_lib(force: bool = False) -> str:
+    """Compile the C oracle with gcc (OpenMP over rows)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        build_oracle_lib()
+        lib = ctypes.CDLL(_LIB)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_requant.argtypes = [p, p, i64, i64, i64, p, p, p]
+        lib.oracle_requant.restype = ctypes.c_int
+        lib.oracle_delta.argtypes = [p, p, i64, i64, i64, p, p, p, p]
+        lib.oracle_delta.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def requant(codes: np.ndarray, scales: np.ndarray, scale_2: float, block: int = BLOCK,
+            return_err: bool = False):
+    """Requantise one NVFP4 matrix [N, K] (codes uint8 [N, K/2], scales uint8 [N, K/16]).
+
+    Returns (codes2 uint8 [N, K] in 0..3, tau uint8 [N, K/block], scale2_out float32[, err int64]).
+    """
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    N, Kh = codes.shape
+    K = Kh * 2
+    assert scales.shape == (N, K // 16) and K % block == 0
+    codes2 = np.empty((N, K), dtype=np.uint8)
+    tau = np.empty((N, K // block), dtype=np.uint8)
+    err = np.empty((N, K // block), dtype=np.int64) if return_err else None
+    rc = _get().oracle_requant(_ptr(codes), _ptr(scales), N, K, block, _ptr(codes2), _ptr(tau),
+                               _ptr(err) if err is not None else None)
+    if rc != 0:
+        raise ValueError("NVFP4 block scale is negative or NaN")
+    s2 = np.float32(2.0) * np.float32(scale_2)
+    return (codes2, tau, s2, err) if return_err else (codes2, tau, s2)
+
+
+def delta(codes: np.ndarray, scales: np.ndarray, scale_2: float, codes2: np.ndarray,
+          tau: np.ndarray, block: int = BLOCK):
+    """FP4 re-encoding of W_nvfp4 - W_2bit.  Returns (dcodes uint8 [N, K] 4-bit codes,
+    dscales uint8 [N, K/16], dscale2 float32 = scale_2)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    codes2 = np.ascontiguousarray(codes2, dtype=np.uint8)
+    tau = np.ascontiguousarray(tau, dtype=np.uint8)
+    N, Kh = codes.shape
+    K = Kh * 2
+    dcodes = np.empty((N, K), dtype=np.uint8)
+    dscales = np.empty((N, K // 16), dtype=np.uint8)
+    rc = _get().oracle_delta(_ptr(codes), _ptr(scales), N, K, block, _ptr(codes2), _ptr(tau),
+                             _ptr(dcodes), _ptr(dscales))
+    if rc != 0:
+        raise ValueError("NVFP4 block scale is negative or NaN")
+    return dcodes, dscales, np.float32(scale_2)
+
+
+def dequant_2bit(codes2: np.ndarray, tau: np.ndarray, scale2_out: float, block: int = BLOCK) -> np.ndarray:
+    """W_2bit[n,k] = level(code) * e4m3(tau[n, k//block]) * scale2_out, exact in float64."""
+    lv = LEVELS[np.asarray(codes2, dtype=np.int64)]
+    s = np.repeat(e4m3fn_value(np.asarray(tau, dtype=np.uint8)), block, axis=1)
+    return lv * s * np.float64(np.float32(scale2_out))
+
+
+def dequant_fp4_codes(dcodes: np.ndarray, dscales: np.ndarray, dscale2: float) -> np.ndarray:
+    """Decode FP4 codes given one code per element ([N, K] 4-bit) and block-16 scales."""
+    v = e2m1_value(np.asarray(dcodes, dtype=np.int64))
+    s = np.repeat(e4m3fn_value(np.asarray(dscales, dtype=np.uint8)), 16, axis=1)
+    return v * s * np.float64(np.float32(dscale2))
+
+
+def pack_nibbles(dcodes: np.ndarray) -> np.ndarray:
+    """[N, K] 4-bit codes -> uint8 [N, K/2] with the even k in the low nibble."""
+    d = np.asarray(dcodes, dtype=np.uint8)
+    return (d[:, 0::2] & 15) | ((d[:, 1::2] & 15) << 4)

@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark: the routed-expert MoE layer forward at decode on one MI355X.
+
+One step = moet_route + moet_moe_forward (gate/up + SwiGLU kernel, down +
+combine kernel) for one synthetic layer shaped like the pages' decode case:
+3 tokens (1 + 2 MTP drafts), hidden 7168, expert intermediate 2048, 256
+routed experts top-8 (sigmoid, renormalised) plus one shared expert, 2-bit
+planes.  Inputs are resident in HBM before timing.  Steps rotate over a pool
+of layers (so no expert stays in the 256 MB last-level cache between uses)
+and over 8 input sets (so the routed experts change every step).
+
+Printed value: effective HBM GB/s = algorithmic bytes of the step (2-bit
+planes of every distinct expert it routes to, shared expert, activations,
+logits, output; computed per step from that step's routing) / step time.
+The roofline object covers the dominant kernel (gate/up), timed by HIP
+events recorded on its stream around each launch inside the timed region.
+The CPU baseline times the float64 oracle on a bounded sample (one token's
+experts) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published peak
+W2_BYTES_PER_WEIGHT = 2.25 / 8.0
+FP4_BYTES_PER_WEIGHT = 4.5 / 8.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="synthetic layer config (2: MTP decode)")
+    ap.add_argument("--layers", type=int, default=4, help="layers in the rotating pool")
+    ap.add_argument("--inputs", type=int, default=8, help="input sets in the rotation")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--seed", type=int, default=1234)
+    return ap.parse_args()
+
+
+def step_bytes(cfg, ids_np, flags_np, soe_np):
+    """Algorithmic bytes of one decode step and of its gate/up kernel launch."""
+    w13 = 2 * cfg.I * cfg.H * W2_BYTES_PER_WEIGHT
+    w2 = cfg.H * cfg.I * W2_BYTES_PER_WEIGHT
+    d13 = 2 * cfg.I * cfg.H * FP4_BYTES_PER_WEIGHT
+    d2 = cfg.H * cfg.I * FP4_BYTES_PER_WEIGHT
+    experts = set(int(e) for e in ids_np.reshape(-1))
+    n = len(experts) + (1 if cfg.shared else 0)
+    delta_experts = set()
+    if flags_np is not None and soe_np is not None:
+        for t in range(cfg.T):
+            if flags_np[t]:
+                for e in ids_np[t]:
+                    if soe_np[int(e)] >= 0:
+                        delta_experts.add(int(e))
+    nd = len(delta_experts)
+    io = 2 * cfg.T * cfg.H * 2 + 4 * cfg.T * cfg.E
+    total = n * (w13 + w2) + nd * (d13 + d2) + io
+    fc1 = n * w13 + nd * d13 + 2 * cfg.T * cfg.H + 2 * (cfg.T * cfg.k + cfg.T) * cfg.I
+    return total, fc1, n, nd
+
+
+def cpu_baseline(cfg, src, x, lg, seed):
+    """Time the float64 oracle (route + one token's expert FFNs) on the host cores."""
+    import numpy as np
+    from oracle import formats as OF
+    from oracle import requant as OR
+    from oracle import route as ORT
+    from oracle import ffn as OFF
+
+    def npy(t):
+        return t.detach().cpu().numpy()
+
+    lg_np = npy(lg)
+    ids, w, _, _ = ORT.route(lg_np, cfg.k, cfg.score, cfg.renormalize)
+    tok = 0
+    experts = sorted(set(int(e) for e in ids[tok]))
+    # load-time part (not timed): the oracle's own requantisation of the touched experts
+    planes = {}
+
+    def rq(stack, i):
+        c, s, s2 = stack
+        return OR.requant(npy(c[i]), npy(s[i]), float(s2[i]))
+    for e in experts:
+        planes[e] = (rq(src.w13, 2 * e), rq(src.w13, 2 * e + 1), rq(src.w2, e))
+    shared = (rq(src.shared13, 0), rq(src.shared13, 1), rq(src.shared2, 0)) if cfg.shared else None
+    xb = OF.bf16_rne_bits(npy(x.float()).astype(np.float64))
+
+    def dq(p):
+        return OR.dequant_2bit(*p)
+    t0 = time.perf_counter()
+    ids2, w2, _, _ = ORT.route(lg_np, cfg.k, cfg.score, cfg.renormalize)
+    out = OFF.moe_forward(xb, ids2, w2, lambda e: tuple(dq(p) for p in planes[e]),
+                          tuple(dq(p) for p in shared) if shared else None, tokens=[tok])
+    dt = time.perf_counter() - t0
+    n = len(experts) + (1 if cfg.shared else 0)
+    nbytes = n * 3 * cfg.I * cfg.H * W2_BYTES_PER_WEIGHT
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"routing of all {cfg.T} tokens + the layer output of token 0 ({n} experts incl. shared, "
+                      f"{nbytes / 1e6:.1f} MB of 2-bit planes) from the oracle's own requantised planes; "
+                      f"float64 numpy, {dt:.2f} s",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not sharded in this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet, synth
+
+    dev = "cuda"
+    cfg = synth.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    print(f"[bench] building {args.layers} synthetic layers of '{cfg.name}' on the GPU", file=sys.stderr, flush=True)
+    layers, srcs = [], []
+    soe = synth.slot_of_expert(cfg, args.seed) if cfg.n_resident else None
+    rq_ms = []
+    for li in range(args.layers):
+        src = synth.make_layer(cfg, seed=args.seed, device=dev, layer_index=li)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer = moet.layer_from_nvfp4(src, soe)
+        e1.record()
+        torch.cuda.synchronize()
+        rq_ms.append(e0.elapsed_time(e1))
+        layers.append(layer)
+        if li == 0 and not args.no_cpu_baseline:
+            srcs.append(src)
+        else:
+            del src
+        torch.cuda.empty_cache()
+        print(f"[bench] layer {li} ready (requant {rq_ms[-1]:.1f} ms)", file=sys.stderr, flush=True)
+
+    xs = [synth.make_activations(cfg.T, cfg.H, args.seed, tag=f"x{i}", device=dev) for i in range(args.inputs)]
+    lgs = [synth.make_logits(cfg, args.seed, tag=f"logits{i}", device=dev) for i in range(args.inputs)]
+    flags = synth.gate_flags(cfg, args.seed).to(dev) if cfg.n_flagged else None
+    route_out = [(torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
+                  torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
+                  torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev),
+                  torch.empty((cfg.T * cfg.k,), dtype=torch.int32, device=dev)) for _ in range(args.inputs)]
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = moet.alloc_workspace(layers[0], cfg.T, cfg.k, dev)
+
+    def step(i):
+        j = i % args.inputs
+        layer = layers[i % args.layers]
+        ids, w, offs, pairs = moet.route(lgs[j], cfg.k, cfg.score, cfg.renormalize, out=route_out[j])
+        moet.moe_forward(layer, xs[j], ids, w, offs, pairs, flags, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # algorithmic bytes of each input set's routing (deterministic per input set)
+    flags_np = flags.cpu().numpy() if flags is not None else None
+    soe_np = soe.numpy() if soe is not None else None
+    per_input = [step_bytes(cfg, route_out[j][0].cpu().numpy(), flags_np, soe_np) for j in range(args.inputs)]
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:      # create the underlying HIP events before handing them to the library
+        a.record()
+        b.record()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        moet.set_timing_events(*ev[i])
+        step(args.warmup + i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    moet.set_timing_events(None, None)
+
+    # the same steps replayed from HIP graphs (one graph per layer/input combination)
+    graph = None
+    if not args.no_graph:
+        import math
+        combos = args.layers * args.inputs // math.gcd(args.layers, args.inputs)
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        for c in range(combos):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % combos].replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for i in range(K):
+            graphs[(args.warmup + i) % combos].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / K
+        gbytes = sum(per_input[(args.warmup + i) % combos % args.inputs][0] for i in range(K)) / K
+        graph = {"us_per_layer": round(gms * 1e3, 2), "GBps": round(gbytes / (gms / 1e3) / 1e9, 1),
+                 "pct_hbm_peak": round(100.0 * gbytes / (gms / 1e3) / 1e9 / HBM_PEAK_GBS, 1)}
+        # replayed graphs must reproduce the eager output bit for bit
+        ref = out.clone()
+        step(args.warmup + K - 1)
+        eager_last = out.clone()
+        graphs[(args.warmup + K - 1) % combos].replay()
+        torch.cuda.synchronize()
+        graph["replay_matches_eager"] = bool(torch.equal(out, eager_last))
+        del ref
+
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+    fc1_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    tot_bytes = sum(per_input[(args.warmup + i) % args.inputs][0] for i in range(K))
+    fc1_bytes = sum(per_input[(args.warmup + i) % args.inputs][1] for i in range(K))
+    gbs = tot_bytes / (total_ms / 1e3) / 1e9
+    fc1_gbs = fc1_bytes / (sum(fc1_ms) / 1e3) / 1e9
+    n_experts = np.mean([p[2] for p in per_input])
+
+    result = {
+        "metric": "MoE layer decode us + effective weight HBM GB/s (% peak), 1 MI355X",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} top{cfg.k} "
+                               f"{'sigmoid' if cfg.score else 'softmax'}+renorm"
+                               f"{' + shared expert' if cfg.shared else ''}"
+                               f"{f' + FP4 delta ({cfg.n_resident} resident, {cfg.n_flagged} flagged)' if cfg.n_resident else ''}"
+                               f", 2-bit planes, {args.layers}-layer pool, {args.inputs} input sets",
+                   "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.k},
+        "us_per_layer": round(ms_per_step * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "tokens_per_s": round(cfg.T / (ms_per_step / 1e3), 1),
+        "mean_experts_per_step": round(float(n_experts), 2),
+        "algorithmic_bytes_per_step": round(tot_bytes / K),
+        "requant_ms_per_layer": round(float(np.median(rq_ms)), 2),
+        "wall_s_timed_region": round(wall, 4),
+        "graph_replay": graph,
+        "roofline": {
+            "kernel": "fc1_decode_kernel (gate/up GEMV + SwiGLU)",
+            "bound": "hbm",
+            "achieved": round(fc1_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(1e3 * float(np.mean(fc1_ms)), 2),
+            "algorithmic_bytes_per_launch": round(fc1_bytes / K),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
+        cb = cpu_baseline(cfg, srcs[0], xs[0], lgs[0], args.seed)
+        cb.pop("seconds", None)
+        cb["value"] = round(cb["value"], 4)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

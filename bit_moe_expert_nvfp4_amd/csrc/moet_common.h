@@ -1,0 +1,112 @@
+// Shared device helpers and launch utilities of libmoet (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moet.h"
+
+namespace moet {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTile = 64;          // rows per storage tile (one wave, one row per lane)
+constexpr int kGroupK = 128;       // k per scale group (4 two-bit blocks, 8 FP4 blocks)
+
+// ---------------------------------------------------------------------------
+// Scalars
+// ---------------------------------------------------------------------------
+
+// bf16 bits -> float (exact)
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// e4m3fn byte `B` of a packed word -> float.  gfx950's fp8 conversion reads the
+// OCP E4M3 encoding (bias 7, max 448), which is exactly the block-scale format.
+template <int B>
+__device__ __forceinline__ float e4m3_byte(uint32_t word) { return __builtin_amdgcn_cvt_f32_fp8(word, B); }
+
+// e4m3fn value * 2^9 as an exact integer for codes 0x00..0x7E
+__device__ __forceinline__ int e4m3_x512(int t)
+{
+    int e = (t >> 3) & 15, m = t & 7;
+    return e == 0 ? m : ((8 + m) << (e - 1));
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// 2-bit decode.  A word holds 16 codes as 8 (lo, hi) pairs; pair i is turned
+// into two bf16 values equal to level/4 by one rotation and one and-or: after
+// rotating right by (2i - 8) mod 32 the pair's magnitude bits sit at bf16
+// exponent bit 8 / 24 and its sign bits at 15 / 31; or-ing 0.25 (0x3E80) into
+// both halves gives +-0.25 (m = 0) or +-1.0 (m = 1).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t rotr(uint32_t w, int r) { return __builtin_amdgcn_alignbit(w, w, r); }
+
+// v_and_or_b32 with the mask in an SGPR and the or-constant in a VGPR (gfx9 VOP3
+// takes no literal operands, and the compiler would otherwise emit and + or).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t smask, uint32_t vbase)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(smask), "v"(vbase));
+    return r;
+}
+
+template <int I>
+__device__ __forceinline__ uint32_t w2_pair(uint32_t w, uint32_t smask, uint32_t vbase)
+{
+    constexpr int r = (2 * I - 8) & 31;
+    uint32_t v = (r == 0) ? w : rotr(w, r);
+    return and_or(v, smask, vbase);
+}
+
+// Wave-uniform read-only data (activations) is read through the constant
+// address space so that uniform addresses become scalar loads into SGPRs.
+typedef const uint32_t __attribute__((address_space(4))) cu32;
+__device__ __forceinline__ const cu32 *as_const(const void *p) { return (const cu32 *)(uintptr_t)p; }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// FP4 (e2m1) byte `B` of a word -> two bf16 (low nibble first), exact
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+}
+
+// ---------------------------------------------------------------------------
+// Storage layout indices (see include/moet.h)
+// ---------------------------------------------------------------------------
+// uint4 index of the 64-k chunk c of row (tile, r) in a 2-bit matrix with K cols
+__device__ __forceinline__ size_t w2_chunk_idx(int tile, int c, int r, int K) { return ((size_t)tile * (K / 64) + c) * 64 + r; }
+// uint32 index of the scale group g (4 bytes) of row (tile, r)
+__device__ __forceinline__ size_t w2_scale_idx(int tile, int g, int r, int K) { return ((size_t)tile * (K / 128) + g) * 64 + r; }
+// uint4 index of the 32-k chunk c of row (tile, r) in an FP4 matrix
+__device__ __forceinline__ size_t fp4_chunk_idx(int tile, int c, int r, int K) { return ((size_t)tile * (K / 32) + c) * 64 + r; }
+// uint2 index of the scale group g (8 bytes) of row (tile, r) in an FP4 matrix
+__device__ __forceinline__ size_t fp4_scale_idx(int tile, int g, int r, int K) { return ((size_t)tile * (K / 128) + g) * 64 + r; }
+
+}  // namespace moet
+
+// ---------------------------------------------------------------------------
+// Host-side error plumbing shared by the entry points
+// ---------------------------------------------------------------------------
+namespace moet {
+void set_error(const char *fmt, ...);
+int fail(int status, const char *fmt, ...);
+int check_launch(const char *what);
+bool aligned16(const void *p);
+void timing_start(hipStream_t s);  // records the caller's start event, if set
+void timing_stop(hipStream_t s);
+}  // namespace moet

@@ -1,0 +1,299 @@
+"""Python binding of libmoet (ctypes; argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+``include/moet.h``; this module only checks dtypes/shapes of torch tensors,
+allocates outputs with torch, and passes device pointers and the current
+stream.  The library must be built (``bit_moe_expert_nvfp4_amd.build``); there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoet.so")
+
+MOET_OK, MOET_EINVAL, MOET_EUNSUPPORTED, MOET_EWORKSPACE, MOET_EHIP = range(5)
+SOFTMAX, SIGMOID = 0, 1
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class W2(ctypes.Structure):
+    _fields_ = [("codes", _vp), ("scales", _vp), ("scale2", _vp)]
+
+
+class FP4(ctypes.Structure):
+    _fields_ = [("codes", _vp), ("scales", _vp), ("scale2", _vp)]
+
+
+class LayerC(ctypes.Structure):
+    _fields_ = [("H", _i32), ("I", _i32), ("E", _i32), ("w13", W2), ("w2", W2), ("has_shared", _i32),
+                ("shared13", W2), ("shared2", W2), ("n_slots", _i32), ("slot_of_expert", _vp),
+                ("d13", FP4), ("d2", FP4), ("swiglu_limit", ctypes.c_float)]
+
+
+_lib = None
+
+
+class MoetError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib():
+    """Load libmoet.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with bit_moe_expert_nvfp4_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moet_status_str.argtypes = [ctypes.c_int]
+        L.moet_status_str.restype = ctypes.c_char_p
+        L.moet_last_error.argtypes = []
+        L.moet_last_error.restype = ctypes.c_char_p
+        L.moet_abi_version.restype = ctypes.c_int
+        L.moet_requant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp]
+        L.moet_requant.restype = ctypes.c_int
+        L.moet_route.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp]
+        L.moet_route.restype = ctypes.c_int
+        L.moet_moe_workspace_bytes.argtypes = [ctypes.POINTER(LayerC), _i32, _i32]
+        L.moet_moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moet_moe_forward.argtypes = [ctypes.POINTER(LayerC), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_size_t, _vp]
+        L.moet_moe_forward.restype = ctypes.c_int
+        L.moet_delta_forward.argtypes = [ctypes.POINTER(FP4), _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp]
+        L.moet_delta_forward.restype = ctypes.c_int
+        L.moet_set_timing_events.argtypes = [_vp, _vp]
+        L.moet_set_timing_events.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != MOET_OK:
+        L = lib()
+        raise MoetError(rc, f"{L.moet_status_str(rc).decode()}: {L.moet_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous CUDA tensor of dtype {dtype}, got {t.dtype} on {t.device}")
+
+
+# ---------------------------------------------------------------------------
+# moet_requant
+# ---------------------------------------------------------------------------
+@dataclass
+class W2Planes:
+    """2-bit planes of a stack of n_mat matrices [N][K] (library layout)."""
+    codes: torch.Tensor    # uint32 -> stored as int32 [n_mat, N*K/16]
+    scales: torch.Tensor   # uint8 [n_mat, N*K/32]
+    scale2: torch.Tensor   # float32 [n_mat]
+    N: int
+    K: int
+
+    def c(self) -> W2:
+        return W2(self.codes.data_ptr(), self.scales.data_ptr(), self.scale2.data_ptr())
+
+
+@dataclass
+class FP4Planes:
+    """FP4 delta planes of a stack of n matrices [N][K] (library layout)."""
+    codes: torch.Tensor    # uint8 [n, N*K/2]
+    scales: torch.Tensor   # uint8 [n, N*K/16]
+    scale2: torch.Tensor   # float32 [n]
+    N: int
+    K: int
+
+    def c(self) -> FP4:
+        return FP4(self.codes.data_ptr(), self.scales.data_ptr(), self.scale2.data_ptr())
+
+
+def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
+            delta_sel: Optional[torch.Tensor] = None):
+    """NVFP4 stack (codes uint8 [n, N, K/2], scales uint8 [n, N, K/16], scale2 f32 [n]) ->
+    W2Planes (and FP4Planes of the matrices listed in delta_sel, int32)."""
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    _need(scale2, torch.float32, "scale2")
+    n, N, Kh = codes.shape
+    K = 2 * Kh
+    dev = codes.device
+    w = W2Planes(torch.empty((n, N * K // 16), dtype=torch.int32, device=dev),
+                 torch.empty((n, N * K // 32), dtype=torch.uint8, device=dev),
+                 torch.empty((n,), dtype=torch.float32, device=dev), N, K)
+    d = None
+    n_sel = 0
+    if delta_sel is not None:
+        _need(delta_sel, torch.int32, "delta_sel")
+        n_sel = int(delta_sel.numel())
+        d = FP4Planes(torch.empty((n_sel, N * K // 2), dtype=torch.uint8, device=dev),
+                      torch.empty((n_sel, N * K // 16), dtype=torch.uint8, device=dev),
+                      torch.empty((n_sel,), dtype=torch.float32, device=dev), N, K)
+    _check(lib().moet_requant(_ptr(codes), _ptr(scales), _ptr(scale2), n, N, K,
+                              _ptr(w.codes), _ptr(w.scales), _ptr(w.scale2),
+                              _ptr(delta_sel) if n_sel else None, n_sel,
+                              _ptr(d.codes) if d else None, _ptr(d.scales) if d else None,
+                              _ptr(d.scale2) if d else None, _stream()))
+    return (w, d) if delta_sel is not None else w
+
+
+# ---------------------------------------------------------------------------
+# moet_route
+# ---------------------------------------------------------------------------
+def route(logits: torch.Tensor, top_k: int, score_fn: int = SIGMOID, renormalize: bool = True,
+          route_scale: float = 1.0, out=None):
+    """Returns (topk_ids int32 [T,k], topk_w f32 [T,k], expert_offsets int32 [E+1], sorted_pairs int32 [T*k])."""
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = (torch.empty((T, top_k), dtype=torch.int32, device=dev),
+               torch.empty((T, top_k), dtype=torch.float32, device=dev),
+               torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               torch.empty((T * top_k,), dtype=torch.int32, device=dev))
+    ids, w, offs, pairs = out
+    _check(lib().moet_route(_ptr(logits), T, E, top_k, score_fn, int(bool(renormalize)), float(route_scale),
+                            _ptr(ids), _ptr(w), _ptr(offs), _ptr(pairs), _stream()))
+    return ids, w, offs, pairs
+
+
+# ---------------------------------------------------------------------------
+# moet_moe_forward
+# ---------------------------------------------------------------------------
+@dataclass
+class Layer:
+    """A MoE layer in library form: w13 = 2E matrices [I][H] (gate 2e, up 2e+1), w2 = E
+    matrices [H][I]; optional shared expert; optional FP4 delta cache."""
+    H: int
+    I: int
+    E: int
+    w13: W2Planes
+    w2: W2Planes
+    shared13: Optional[W2Planes] = None
+    shared2: Optional[W2Planes] = None
+    slot_of_expert: Optional[torch.Tensor] = None   # int32 [E]
+    d13: Optional[FP4Planes] = None                 # 2*n_slots matrices [I][H]
+    d2: Optional[FP4Planes] = None                  # n_slots matrices [H][I]
+    swiglu_limit: float = 0.0
+
+    def c(self) -> LayerC:
+        z = W2(None, None, None)
+        zf = FP4(None, None, None)
+        n_slots = 0 if self.d2 is None else int(self.d2.scale2.numel())
+        return LayerC(self.H, self.I, self.E, self.w13.c(), self.w2.c(),
+                      1 if self.shared13 is not None else 0,
+                      self.shared13.c() if self.shared13 is not None else z,
+                      self.shared2.c() if self.shared2 is not None else z,
+                      n_slots, self.slot_of_expert.data_ptr() if n_slots else None,
+                      self.d13.c() if n_slots else zf, self.d2.c() if n_slots else zf,
+                      float(self.swiglu_limit))
+
+
+def moe_workspace_bytes(layer: Layer, T: int, top_k: int) -> int:
+    Lc = layer.c()
+    return int(lib().moet_moe_workspace_bytes(ctypes.byref(Lc), T, top_k))
+
+
+def alloc_workspace(layer: Layer, T: int, top_k: int, device="cuda") -> torch.Tensor:
+    n = moe_workspace_bytes(layer, T, top_k)
+    return torch.empty((max(n, 256),), dtype=torch.uint8, device=device)
+
+
+def moe_forward(layer: Layer, x: torch.Tensor, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                gate_flags: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(x, torch.bfloat16, "x")
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(layer, T, k, x.device)
+    if gate_flags is not None:
+        _need(gate_flags, torch.uint8, "gate_flags")
+    Lc = layer.c()
+    _check(lib().moet_moe_forward(ctypes.byref(Lc), _ptr(x), T, k, _ptr(topk_ids), _ptr(topk_w),
+                                  _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(gate_flags), _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# moet_delta_forward
+# ---------------------------------------------------------------------------
+def delta_forward(D: FP4Planes, act: torch.Tensor, row_slot: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
+    """acc[r] += D[row_slot[r]] @ act[r] (in place) for rows with a valid slot."""
+    _need(act, torch.bfloat16, "act")
+    _need(row_slot, torch.int32, "row_slot")
+    _need(acc, torch.float32, "acc")
+    R, K = act.shape
+    Dc = D.c()
+    _check(lib().moet_delta_forward(ctypes.byref(Dc), int(D.scale2.numel()), D.N, K, _ptr(act), _ptr(row_slot), R,
+                                    _ptr(acc), _stream()))
+    return acc
+
+
+def set_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]) -> None:
+    """Time the first expert kernel of the following moe_forward calls with these (recorded
+    at least once, so that torch has created them) torch events; None, None disables."""
+    if start is None:
+        _check(lib().moet_set_timing_events(None, None))
+    else:
+        _check(lib().moet_set_timing_events(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)))
+
+
+# ---------------------------------------------------------------------------
+# Building a layer from NVFP4 sources
+# ---------------------------------------------------------------------------
+def layer_from_nvfp4(src, slot_of_expert: Optional[torch.Tensor] = None, swiglu_limit: float = 0.0,
+                     device="cuda") -> Layer:
+    """Requantise an NVFP4 layer (synth.NVFP4Layer-like: w13/w2/shared13/shared2 tuples of
+    (codes, scales, scale2)) on the GPU and build the library layer; experts with
+    slot_of_expert >= 0 also get their FP4 delta."""
+    cfg = src.cfg
+
+    def dev(t):
+        return t.to(device, non_blocking=True).contiguous()
+
+    w13_src = tuple(dev(t) for t in src.w13)
+    w2_src = tuple(dev(t) for t in src.w2)
+    d13 = d2 = None
+    if slot_of_expert is not None and int((slot_of_expert >= 0).sum()) > 0:
+        soe = slot_of_expert.to(torch.int64)
+        n_slots = int(soe.max()) + 1
+        res = torch.full((n_slots,), -1, dtype=torch.int64)
+        for e in range(cfg.E):
+            if soe[e] >= 0:
+                res[soe[e]] = e
+        sel13 = torch.stack([2 * res, 2 * res + 1], dim=1).reshape(-1).to(torch.int32).to(device)
+        sel2 = res.to(torch.int32).to(device)
+        w13, d13 = requant(*w13_src, delta_sel=sel13)
+        w2, d2 = requant(*w2_src, delta_sel=sel2)
+        slot_dev = slot_of_expert.to(torch.int32).to(device)
+    else:
+        w13 = requant(*w13_src)
+        w2 = requant(*w2_src)
+        slot_dev = None
+    sh13 = sh2 = None
+    if src.shared13 is not None:
+        sh13 = requant(*(dev(t) for t in src.shared13))
+        sh2 = requant(*(dev(t) for t in src.shared2))
+    return Layer(cfg.H, cfg.I, cfg.E, w13, w2, sh13, sh2, slot_dev, d13, d2, swiglu_limit)

@@ -1,0 +1,236 @@
+/*
+ * moet.h - C ABI of libmoet, a 2-bit + FP4-delta MoE expert layer for AMD
+ * MI355X (gfx950).
+ *
+ * The operations follow the public description of the vLLM-Moet project
+ * (README "Frontier MoE on consumer Blackwell (SM120)" as carried by the
+ * pickgithub.com project payload; airanks.app "kacper-daftcode/vLLM-Moet"):
+ *   moet_requant        load-time NVFP4 -> sign-symmetric 2-bit requantisation,
+ *                       plus the FP4 delta of selected matrices
+ *                       (README, "GLM-5.2 (753B) — the headline model" and
+ *                       "How it fits — 2-bit experts at FP4 quality")
+ *   moet_route          router top-k, routing weights and the token->expert
+ *                       permutation the expert GEMMs consume
+ *                       (README, "When the model doesn't fit at all — the GPU
+ *                       as an expert cache": a descriptor step groups the
+ *                       step's routings per expert)
+ *   moet_moe_forward    the expert FFN on the 2-bit planes (gate/up + SwiGLU,
+ *                       down + routing-weighted combine, optional shared
+ *                       expert), with the FP4 delta added for tokens flagged by
+ *                       the confidence gate on experts resident in the delta
+ *                       cache (README, "How it fits")
+ *   moet_delta_forward  the standalone FP4 delta GEMM/GEMV (README, "How it fits")
+ *
+ * Conventions (all entry points):
+ *  - Every array argument is DEVICE memory owned by the caller (e.g. a torch
+ *    tensor); only the moet_layer / moet_w2 / moet_fp4 structs themselves are
+ *    host memory (holding device pointers).  The library never allocates or
+ *    frees: scratch comes from the caller's workspace.
+ *  - Every call enqueues work on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns without synchronising the host.
+ *  - Argument checks run on the host before any launch and return
+ *    MOET_EINVAL / MOET_EUNSUPPORTED / MOET_EWORKSPACE without touching the
+ *    GPU; a failed launch returns MOET_EHIP.  moet_last_error() gives a
+ *    thread-local message for the last failure.  No C++ exception crosses
+ *    the ABI.
+ *  - Pointers must be 16-byte aligned.  Inputs must hold no NaN or Inf
+ *    (undefined results otherwise).
+ *  - Identical inputs give bitwise-identical outputs (no float atomics).
+ *
+ * Storage layouts (the library's own; every matrix is [N rows][K cols], K is
+ * the reduction axis; N % 64 == 0 and K % 128 == 0):
+ *  NVFP4 source (standard modelopt layout): codes uint8 [N][K/2], even k in the
+ *    low nibble; block scales e4m3fn uint8 [N][K/16]; per-tensor scale_2 fp32.
+ *  2-bit planes ("W2"): rows are grouped in tiles of 64;
+ *    codes uint32 word index ((n/64 * K/64 + k/64) * 64 + n%64) * 4 + (k%64)/16;
+ *    inside a word the element e = k%16 belongs to pair i = e/2 (even e = lo,
+ *    odd e = hi) and its code c = (s<<1)|m (levels 0:+1 1:+4 2:-1 3:-4) sits at
+ *    m_lo: bit 2i, s_lo: bit (2i+7)%32, m_hi: bit 2i+16, s_hi: bit (2i+23)%32;
+ *    block scales e4m3fn, one per 32 along k, byte index
+ *    ((n/64 * K/128 + k/128) * 64 + n%64) * 4 + (k%128)/32;
+ *    per-tensor scale2 fp32.  Weight = level * e4m3(scale) * scale2.
+ *    Storage: 2.25 bits per weight.
+ *  FP4 delta planes ("FP4"): NVFP4 values in the same row tiling;
+ *    code byte index ((n/64 * K/32 + k/32) * 64 + n%64) * 16 + (k%32)/2, even k
+ *    in the low nibble; block scales one per 16 along k, byte index
+ *    ((n/64 * K/128 + k/128) * 64 + n%64) * 8 + (k%128)/16; scale2 fp32.
+ *  A stack of matrices is the concatenation of the per-matrix arrays.
+ */
+#ifndef MOET_H
+#define MOET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOET_OK = 0,
+    MOET_EINVAL = 1,       /* bad shape, pointer, alignment or enum value */
+    MOET_EUNSUPPORTED = 2, /* a valid request this build does not implement */
+    MOET_EWORKSPACE = 3,   /* workspace missing or too small */
+    MOET_EHIP = 4          /* a HIP launch or runtime call failed */
+} moet_status;
+
+enum { MOET_SOFTMAX = 0, MOET_SIGMOID = 1 };
+
+/* Static string for a status code. */
+const char *moet_status_str(int status);
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char *moet_last_error(void);
+/* ABI version (bumped on any incompatible change). */
+int moet_abi_version(void);
+
+/*
+ * moet_requant - NVFP4 -> sign-symmetric 2-bit planes for a stack of n_mat
+ * equal-shape matrices [N][K], and optionally the FP4 delta of some of them.
+ * (README "Frontier MoE on consumer Blackwell (SM120)", sections "GLM-5.2
+ * (753B) — the headline model" and "How it fits — 2-bit experts at FP4
+ * quality".)
+ *
+ * Per 32 consecutive weights along K the block scale is the e4m3fn value that
+ * minimises the exact L2 error of the block against the codebook
+ * {-4,-1,1,4} * scale * scale2 (ties -> the smaller scale), scale2 = 2 *
+ * scale_2; each weight takes the nearest level (a tie keeps magnitude 1) and
+ * its sign from the NVFP4 sign bit, zeros included.  The search is exact.
+ *
+ * Inputs: fp4_codes uint8 [n_mat][N][K/2], fp4_scales uint8 [n_mat][N][K/16]
+ *   (finite, non-negative e4m3fn), fp4_scale2 fp32 [n_mat].
+ * Outputs: w2_codes uint32 [n_mat][N*K/16], w2_scales uint8 [n_mat][N*K/32],
+ *   w2_scale2 fp32 [n_mat], all in the 2-bit layout above.
+ * Delta (n_sel > 0): delta_sel int32 [n_sel] (device) lists matrix indices;
+ *   the delta of matrix delta_sel[i] = W_nvfp4 - W_2bit, re-encoded as NVFP4
+ *   with the source scale_2 (block-16 scale nearest to max|D|/6, ties to the
+ *   even code; elements nearest e2m1, ties to even, a value rounding to zero
+ *   keeps D's sign), is written at slot i of d_codes uint8 [n_sel][N*K/2],
+ *   d_scales uint8 [n_sel][N*K/16], d_scale2 fp32 [n_sel] (FP4 layout).
+ *   n_sel == 0: delta_sel and d_* may be NULL.
+ * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
+ *   pointers, n_sel < 0 or n_sel > n_mat.  Out-of-range delta_sel entries are
+ *   skipped by the kernel (their slots are left unwritten).
+ */
+int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2,
+                 int64_t n_mat, int64_t N, int64_t K,
+                 uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2,
+                 const int32_t *delta_sel, int64_t n_sel,
+                 uint8_t *d_codes, uint8_t *d_scales, float *d_scale2,
+                 void *stream);
+
+/*
+ * moet_route - router top-k and token permutation.
+ * (README "Frontier MoE on consumer Blackwell (SM120)", sections "How it fits"
+ * and "When the model doesn't fit at all — the GPU as an expert cache".)
+ *
+ * logits fp32 [T][E].  Per token the top_k largest logits are selected
+ * (equal logits -> lower expert id first) into topk_ids int32 [T][top_k] in
+ * descending order.  topk_w fp32 [T][top_k]: score_fn MOET_SOFTMAX ->
+ * exp(l - l_max) normalised over the selected experts when renormalize != 0,
+ * else over all E; MOET_SIGMOID -> sigmoid(l), divided by the selected sum
+ * when renormalize != 0; then times route_scale.
+ * expert_offsets int32 [E+1]: number of (token, slot) pairs routed to experts
+ * < e; sorted_pairs int32 [T*top_k]: the pair ids p = t*top_k + j ordered by
+ * (expert, p).
+ * Limits: 1 <= T <= 65536, 1 <= E <= 1024, 1 <= top_k <= min(E, 16).
+ * Errors: MOET_EINVAL on any limit, NULL or misaligned pointer, bad score_fn.
+ */
+int moet_route(const float *logits, int32_t T, int32_t E, int32_t top_k, int32_t score_fn,
+               int32_t renormalize, float route_scale,
+               int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *sorted_pairs,
+               void *stream);
+
+/* 2-bit planes of a stack of matrices (device pointers; layout above). */
+typedef struct {
+    const uint32_t *codes;
+    const uint8_t *scales;
+    const float *scale2;
+} moet_w2;
+
+/* FP4 delta planes of a stack of matrices (device pointers; layout above). */
+typedef struct {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *scale2;
+} moet_fp4;
+
+/*
+ * One MoE layer.  w13: stack of 2E matrices [I][H] (expert e: gate = 2e,
+ * up = 2e+1); w2: stack of E matrices [H][I].  has_shared != 0 adds one
+ * always-on shared expert (shared13: 2 matrices [I][H], shared2: 1 matrix
+ * [H][I]) with weight 1 and no delta.  n_slots > 0 enables the delta cache:
+ * slot_of_expert int32 [E] (device; -1 = not resident), d13: stack of
+ * 2*n_slots matrices [I][H] (slot s: gate 2s, up 2s+1), d2: n_slots matrices
+ * [H][I].  swiglu_limit > 0 clamps gate <= L and |up| <= L before SwiGLU.
+ */
+typedef struct {
+    int32_t H, I, E;
+    moet_w2 w13, w2;
+    int32_t has_shared;
+    moet_w2 shared13, shared2;
+    int32_t n_slots;
+    const int32_t *slot_of_expert;
+    moet_fp4 d13, d2;
+    float swiglu_limit;
+} moet_layer;
+
+/* Workspace bytes moet_moe_forward needs for T tokens and top_k. */
+size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
+
+/*
+ * moet_moe_forward - the routed-expert layer forward.
+ * (README "Frontier MoE on consumer Blackwell (SM120)", section "How it fits
+ * — 2-bit experts at FP4 quality".)
+ *
+ * x bf16 [T][H]; topk_ids/topk_w/expert_offsets/sorted_pairs as produced by
+ * moet_route; gate_flags uint8 [T] (device, may be NULL = none flagged).
+ * For every pair (t, e): u = W13_e x_t (+ D13_slot x_t when gate_flags[t] and
+ * slot_of_expert[e] >= 0), h = bf16(silu(u_gate) * u_up), y = W2_e h
+ * (+ D2_slot h); out bf16 [T][H] = bf16(sum_j topk_w[t][j] * y_(t,j) +
+ * y_shared(t)).  Accumulation is fp32; h and out are rounded to nearest-even.
+ * Decode-sized batches (T*top_k <= 1024) run the GEMV kernels; larger
+ * batches run the MFMA grouped-GEMM kernels.
+ * workspace: at least moet_moe_workspace_bytes(L, T, top_k) bytes of device
+ * memory, 256-byte aligned; its contents need no initialisation.
+ * Expert ids outside [0, E) and slots outside [0, n_slots) contribute
+ * nothing (the kernels skip them instead of reading out of bounds).
+ * Errors: MOET_EINVAL on shapes (H, I % 128; 1 <= E <= 1024;
+ * 1 <= top_k <= min(E, 16); 1 <= T <= 65536), NULL or misaligned pointers, a
+ * delta cache with NULL members; MOET_EWORKSPACE if the workspace is short.
+ */
+int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
+                     const int32_t *topk_ids, const float *topk_w,
+                     const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                     const uint8_t *gate_flags, uint16_t *out,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moet_delta_forward - standalone FP4 delta GEMM/GEMV accumulate.
+ * (README "Frontier MoE on consumer Blackwell (SM120)", section "How it fits".)
+ *
+ * D: stack of n_slots FP4 matrices [N][K] (FP4 layout); act bf16 [R][K];
+ * row_slot int32 [R] (device).  For every r with 0 <= row_slot[r] < n_slots:
+ * acc[r][n] += sum_k D_{row_slot[r]}[n][k] * act[r][k] (fp32 accumulation,
+ * one fp32 add into acc per element); other rows are left unchanged.
+ * Errors: MOET_EINVAL for n_slots < 1, N % 64, K % 128, R < 0, NULL or
+ * misaligned pointers.
+ */
+int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
+                       const uint16_t *act, const int32_t *row_slot, int32_t R, float *acc,
+                       void *stream);
+
+/*
+ * moet_set_timing_events - benchmark instrumentation.  While set (per host
+ * thread), every moet_moe_forward call records `start` on its stream right
+ * before it launches its first expert kernel (the gate/up kernel) and `stop`
+ * right after that launch, so the caller can time that one kernel with
+ * hipEventElapsedTime.  `start` / `stop` are caller-owned hipEvent_t handles;
+ * pass NULL, NULL to disable.  Returns MOET_EINVAL if only one is NULL.
+ */
+int moet_set_timing_events(void *start, void *stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOET_H */

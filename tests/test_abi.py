@@ -1,0 +1,109 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/moet.h declares, and rejects bad arguments on the host before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "moet.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moet_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_moe_expert_nvfp4_amd import moet
+    if not os.path.exists(moet.LIB_PATH):
+        from bit_moe_expert_nvfp4_amd import build
+        build.build()
+    return moet.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert {"moet_requant", "moet_route", "moet_moe_forward", "moet_delta_forward"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.moet_status_str(0) == b"MOET_OK"
+    assert L.moet_status_str(3) == b"MOET_EWORKSPACE"
+    assert L.moet_abi_version() >= 1
+
+
+def test_requant_rejects_bad_shapes(L):
+    buf = ctypes.c_void_p(16)      # never dereferenced: checks fail first
+    args = [buf, buf, buf, 1, 64, 128, buf, buf, buf, None, 0, None, None, None, None]
+    for i, bad in [(4, 63), (5, 96), (3, 0), (10, -1), (10, 2)]:
+        a = list(args)
+        a[i] = bad
+        assert L.moet_requant(*a) == 1
+    a = list(args)
+    a[0] = ctypes.c_void_p(8)      # misaligned
+    assert L.moet_requant(*a) == 1
+    assert b"aligned" in L.moet_last_error()
+
+
+def test_route_rejects_bad_args(L):
+    b = ctypes.c_void_p(16)
+    f = ctypes.c_float(1.0)
+    assert L.moet_route(b, 0, 8, 2, 0, 1, f, b, b, b, b, None) == 1
+    assert L.moet_route(b, 4, 2000, 2, 0, 1, f, b, b, b, b, None) == 1
+    assert L.moet_route(b, 4, 8, 9, 0, 1, f, b, b, b, b, None) == 1
+    assert L.moet_route(b, 4, 32, 17, 0, 1, f, b, b, b, b, None) == 1
+    assert L.moet_route(b, 4, 8, 2, 7, 1, f, b, b, b, b, None) == 1
+    assert L.moet_route(None, 4, 8, 2, 0, 1, f, b, b, b, b, None) == 1
+
+
+def _layer(H=256, I=128, E=8):
+    from bit_moe_expert_nvfp4_amd import moet
+    z = moet.W2(16, 16, 16)
+    return moet.LayerC(H, I, E, z, z, 0, moet.W2(None, None, None), moet.W2(None, None, None), 0, None,
+                       moet.FP4(None, None, None), moet.FP4(None, None, None), 0.0)
+
+
+def test_forward_rejects_bad_args_and_short_workspace(L):
+    from bit_moe_expert_nvfp4_amd import moet
+    b = ctypes.c_void_p(256)
+    lay = _layer()
+    need = L.moet_moe_workspace_bytes(ctypes.byref(lay), 4, 2)
+    assert need > 0
+    assert L.moet_moe_workspace_bytes(ctypes.byref(lay), 8, 2) >= need
+    # short workspace
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, b, need - 1, None) == 3
+    # bad shapes
+    for H, I, E in [(200, 128, 8), (256, 64, 8), (256, 128, 0), (256, 128, 2000)]:
+        bad = _layer(H, I, E)
+        assert L.moet_moe_forward(ctypes.byref(bad), b, 4, 2, b, b, b, b, None, b, b, 1 << 30, None) == 1
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 9, b, b, b, b, None, b, b, 1 << 30, None) == 1
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 0, 2, b, b, b, b, None, b, b, 1 << 30, None) == 1
+    # delta cache with missing pointers
+    lay.n_slots = 2
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, b, 1 << 30, None) == 1
+    # shared expert with missing pointers
+    lay2 = _layer()
+    lay2.has_shared = 1
+    assert L.moet_moe_forward(ctypes.byref(lay2), b, 4, 2, b, b, b, b, None, b, b, 1 << 30, None) == 1
+    # unaligned workspace
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, ctypes.c_void_p(272), 1 << 30,
+                              None) == 1
+
+
+def test_delta_forward_rejects_bad_args(L):
+    from bit_moe_expert_nvfp4_amd import moet
+    b = ctypes.c_void_p(16)
+    D = moet.FP4(16, 16, 16)
+    assert L.moet_delta_forward(ctypes.byref(D), 1, 65, 128, b, b, 1, b, None) == 1
+    assert L.moet_delta_forward(ctypes.byref(D), 1, 64, 100, b, b, 1, b, None) == 1
+    assert L.moet_delta_forward(ctypes.byref(D), 0, 64, 128, b, b, 1, b, None) == 1
+    assert L.moet_delta_forward(ctypes.byref(D), 1, 64, 128, b, b, -1, b, None) == 1
+    assert L.moet_delta_forward(None, 1, 64, 128, b, b, 1, b, None) == 1
+    # R == 0 is a no-op that touches nothing
+    assert L.moet_delta_forward(ctypes.byref(D), 1, 64, 128, b, b, 0, b, None) == 0

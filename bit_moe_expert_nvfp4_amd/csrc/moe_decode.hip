@@ -7,23 +7,25 @@
 // and the FP4 delta GEMM adds the residual of delta-cache experts on tokens
 // the confidence gate flags.
 //
-// Kernel shape (MI355X): one 64-lane wavefront owns one 64-row storage tile,
-// one row per lane, so every 16-byte load of a wavefront is one contiguous
-// 1 KiB segment of the tiled planes and every lane works on the same k at the
-// same time.  The activations of the (up to 4) tokens handled together are
-// therefore wave-uniform: they are staged once in LDS and read with broadcast
-// loads (scalar loads would drain on every wait, since they return out of
-// order).  Eight
-// wavefronts split K and are reduced in LDS in a fixed order; each keeps the
-// next 128-k group's loads in flight while it decodes the current one.
+// Kernel shape (MI355X).  Every lane owns one row of one matrix and every
+// lane of a wavefront works on the same k at the same time, so each 16-byte
+// load of a wavefront covers contiguous 512 B / 1 KiB segments of the tiled
+// planes and the activations are wave-uniform: they are read with scalar
+// loads into SGPRs, one 64-k chunk per wait, because scalar loads return out
+// of order and every wait drains all of them.  Weights of the next group are
+// loaded into a second register set while the current group is decoded
+// (ping-pong, no copies).  Decoding costs about 1.5 VALU operations per
+// weight, about as long as streaming the planes from HBM, so work is cut
+// into many small workgroups for load balance.
 //
-//  fc1: grid (I/64 tiles, slots); a slot is the first sorted pair of an
-//       expert (its whole run of tokens) or the shared expert.  Each lane
-//       computes gate row j and up row j of its tile for every token of the
-//       slot, adds the FP4 delta for flagged tokens of resident experts and
-//       writes h = bf16(silu(gate) * up).
-//  fc2: grid (H/64 tiles, slots); y = W2 h (+ D2 h) per pair into an fp32
-//       buffer.
+//  fc1: grid (I/32 half-tiles, slots), 4 wavefronts splitting K.  Lanes 0-31
+//       hold 32 gate rows, lanes 32-63 the same 32 up rows, so SwiGLU pairs
+//       lane j with lane j+32 after the cross-wave reduction in LDS.  A slot
+//       is the first sorted pair of an expert (its whole run of tokens) or
+//       the shared expert.  FP4 delta rows are added for flagged tokens of
+//       resident experts.  Writes h = bf16(silu(gate) * up).
+//  fc2: grid (H/64 tiles, slots), 2 wavefronts splitting K; y = W2 h (+ D2 h)
+//       per pair into an fp32 buffer.
 //  combine: out = bf16(sum_j w_tj * y_(t,j) + y_shared) in slot order:
 //       deterministic, no float atomics.  (A last-workgroup combine inside fc2
 //       needs an agent-scope release per workgroup, which on this chip's
@@ -58,18 +60,31 @@ struct SlotInfo {
     bool shared;
 };
 
+// Slot s is the first sorted pair of expert e iff offsets[e] == s < offsets[e+1];
+// e is the number of experts whose run ends at or before s.  One round of
+// loads over offsets[1..E] (ballot counts), instead of a chain through the
+// permutation and the ids.
 __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotInfo &si)
 {
     const int P = p.T * p.k;
     if (s < P) {
-        const int pair = p.sorted[s];
-        if (pair < 0 || pair >= P) return false;
-        const int e = p.ids[pair];
-        if (e < 0 || e >= p.E) return false;
-        if (p.offsets[e] != s) return false;
+        const int lane = threadIdx.x & 63;
+        int v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = 1 + lane + 64 * i;
+            v[i] = (j <= p.E) ? p.offsets[j] : 0x7FFFFFFF;
+        }
+        int e = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e += __popcll(__ballot(v[i] <= s));
+        e = __builtin_amdgcn_readfirstlane(e);
+        if (e >= p.E) return false;
+        const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
+        if (o0 != s || o1 <= s) return false;
         si.e = e;
         si.pbeg = s;
-        si.pend = min(p.offsets[e + 1], P);
+        si.pend = min(o1, P);
         si.shared = false;
         int ds = -1;
         if (p.n_slots > 0 && p.gate != nullptr) {
@@ -77,7 +92,7 @@ __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotI
             if (ds >= p.n_slots) ds = -1;
         }
         si.dslot = ds;
-        return si.pend > si.pbeg;
+        return true;
     }
     if (p.has_shared && s == P) {
         si.e = -1;
@@ -107,26 +122,8 @@ __device__ __forceinline__ void slot_token(const DecodeParams &p, const SlotInfo
 }
 
 // ---------------------------------------------------------------------------
-// Inner products.  Activations of the tokens handled together are staged in
-// LDS once per pass; every lane of a wavefront reads the same address
-// (broadcast), so each block of 32 k costs 4 ds_read_b128 per token.
+// 2-bit decode constants: the and-mask lives in an SGPR, the or-constant in a VGPR
 // ---------------------------------------------------------------------------
-
-// x pairs [kp, kp + 16) of token row xl (LDS) into 16 dwords
-__device__ __forceinline__ void lds_x16(const uint32_t *xl, int kp, uint32_t xv[16])
-{
-    const uint4 *q = reinterpret_cast<const uint4 *>(xl + kp);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 v = q[i];
-        xv[4 * i + 0] = v.x;
-        xv[4 * i + 1] = v.y;
-        xv[4 * i + 2] = v.z;
-        xv[4 * i + 3] = v.w;
-    }
-}
-
-// decode constants: the and-mask lives in an SGPR, the or-constant in a VGPR
 struct W2Consts {
     uint32_t sm, vb;
 };
@@ -140,117 +137,109 @@ __device__ __forceinline__ W2Consts w2_consts()
     return c;
 }
 
-__device__ __forceinline__ void decode_w2_block(uint32_t w0, uint32_t w1, uint32_t pr[16], W2Consts k)
+// bs[t] += sum over one 16-weight word of (level/4) * x, x pairs x[t][o .. o+7]
+template <int TT>
+__device__ __forceinline__ void w2_word(uint32_t w, const uint32_t (*x)[32], int o, float bs[TT], W2Consts k)
 {
-    const uint32_t sm = k.sm, vb = k.vb;
-    pr[0] = w2_pair<0>(w0, sm, vb);
-    pr[1] = w2_pair<1>(w0, sm, vb);
-    pr[2] = w2_pair<2>(w0, sm, vb);
-    pr[3] = w2_pair<3>(w0, sm, vb);
-    pr[4] = w2_pair<4>(w0, sm, vb);
-    pr[5] = w2_pair<5>(w0, sm, vb);
-    pr[6] = w2_pair<6>(w0, sm, vb);
-    pr[7] = w2_pair<7>(w0, sm, vb);
-    pr[8] = w2_pair<0>(w1, sm, vb);
-    pr[9] = w2_pair<1>(w1, sm, vb);
-    pr[10] = w2_pair<2>(w1, sm, vb);
-    pr[11] = w2_pair<3>(w1, sm, vb);
-    pr[12] = w2_pair<4>(w1, sm, vb);
-    pr[13] = w2_pair<5>(w1, sm, vb);
-    pr[14] = w2_pair<6>(w1, sm, vb);
-    pr[15] = w2_pair<7>(w1, sm, vb);
+    uint32_t pr[8];
+    pr[0] = w2_pair<0>(w, k.sm, k.vb);
+    pr[1] = w2_pair<1>(w, k.sm, k.vb);
+    pr[2] = w2_pair<2>(w, k.sm, k.vb);
+    pr[3] = w2_pair<3>(w, k.sm, k.vb);
+    pr[4] = w2_pair<4>(w, k.sm, k.vb);
+    pr[5] = w2_pair<5>(w, k.sm, k.vb);
+    pr[6] = w2_pair<6>(w, k.sm, k.vb);
+    pr[7] = w2_pair<7>(w, k.sm, k.vb);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bs[t] = dot2_bf16(pr[i], x[t][o + i], bs[t]);
 }
 
-// One 32-k block (2-bit words w0, w1; first bf16 pair index kp) of NM matrices
-// for TT tokens; the activations are read once and shared by all matrices.
-template <int TT, int NM, int BLK>
-__device__ __forceinline__ void w2_block(const uint32_t w0[NM], const uint32_t w1[NM], const uint32_t sc[NM],
-                                         const uint32_t *const xl[TT], int kp, float acc[NM][TT], W2Consts kc)
-{
-    uint32_t xv[TT][16];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) lds_x16(xl[t], kp, xv[t]);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        uint32_t pr[16];
-        decode_w2_block(w0[m], w1[m], pr, kc);
-        const float s = e4m3_byte<BLK>(sc[m]);
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            float bs = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) bs = dot2_bf16(pr[i], xv[t][i], bs);
-            acc[m][t] = fmaf(bs, s, acc[m][t]);
-        }
-    }
-}
-
-template <int NM>
-struct W2Group {
-    uint4 c0[NM], c1[NM];
-    uint32_t sc[NM];
+// per-lane view of the one row this lane computes
+struct LaneRow {
+    const uint4 *c4;      // 2-bit codes of the lane's matrix
+    const uint32_t *s4;   // 2-bit block scales of the lane's matrix
+    const uint4 *dc4;     // FP4 delta codes (or null)
+    const uint2 *ds8;     // FP4 delta scales
+    int tile, rt;         // storage tile and row within it
 };
 
-template <int NM>
-__device__ __forceinline__ void w2_load(W2Group<NM> &G, const uint4 *const c4[NM], const uint32_t *const s4[NM], int tile,
-                                        int lane, int K, int g)
+struct W2Buf {
+    uint4 c0, c1;
+    uint32_t sc;
+};
+
+__device__ __forceinline__ void w2_load(W2Buf &B, const LaneRow &L, int K, int g)
 {
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        G.c0[m] = c4[m][w2_chunk_idx(tile, 2 * g, lane, K)];
-        G.c1[m] = c4[m][w2_chunk_idx(tile, 2 * g + 1, lane, K)];
-        G.sc[m] = s4[m][w2_scale_idx(tile, g, lane, K)];
-    }
+    B.c0 = L.c4[w2_chunk_idx(L.tile, 2 * g, L.rt, K)];
+    B.c1 = L.c4[w2_chunk_idx(L.tile, 2 * g + 1, L.rt, K)];
+    B.sc = L.s4[w2_scale_idx(L.tile, g, L.rt, K)];
 }
 
-template <int TT, int NM>
-__device__ __forceinline__ void w2_group(const W2Group<NM> &G, int g, const uint32_t *const xl[TT], float acc[NM][TT],
-                                         W2Consts kc)
-{
-    const int kp = 64 * g;
-    uint32_t a[NM], b[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) a[m] = G.c0[m].x, b[m] = G.c0[m].y;
-    w2_block<TT, NM, 0>(a, b, G.sc, xl, kp + 0, acc, kc);
-    __builtin_amdgcn_sched_barrier(0);  // keep each block's activations short-lived
-#pragma unroll
-    for (int m = 0; m < NM; ++m) a[m] = G.c0[m].z, b[m] = G.c0[m].w;
-    w2_block<TT, NM, 1>(a, b, G.sc, xl, kp + 16, acc, kc);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) a[m] = G.c1[m].x, b[m] = G.c1[m].y;
-    w2_block<TT, NM, 2>(a, b, G.sc, xl, kp + 32, acc, kc);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) a[m] = G.c1[m].z, b[m] = G.c1[m].w;
-    w2_block<TT, NM, 3>(a, b, G.sc, xl, kp + 48, acc, kc);
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// NM 2-bit matrices of one 64-row tile, groups [g0, g1) of 128 k, TT tokens.
-// acc[m][t] receives sum over k of (level/4) * scale * x.  Two register
-// buffers alternate so that the loads of the next group are in flight while
-// the current one is decoded (no copies between them, so no early drain).
-template <int TT, int NM>
-__device__ __forceinline__ void w2_gemv(const uint4 *const c4[NM], const uint32_t *const s4[NM], int tile, int lane, int K,
-                                        int g0, int g1, const uint32_t *const xl[TT], float acc[NM][TT])
-{
-    const W2Consts kc = w2_consts();
-    if (g0 >= g1) return;
-    W2Group<NM> A, B;
-    w2_load<NM>(A, c4, s4, tile, lane, K, g0);
-    for (int g = g0; g < g1; g += 2) {
-        if (g + 1 < g1) w2_load<NM>(B, c4, s4, tile, lane, K, g + 1);
-        w2_group<TT, NM>(A, g, xl, acc, kc);
-        if (g + 1 >= g1) break;
-        if (g + 2 < g1) w2_load<NM>(A, c4, s4, tile, lane, K, g + 2);
-        w2_group<TT, NM>(B, g + 1, xl, acc, kc);
-    }
-}
-
-// FP4 16-block: words w0, w1 = k .. k+15 (first pair index kp), scale s
+// activations of one 64-k chunk (32 bf16 pairs) of token rows xr[t] (scalar loads)
 template <int TT>
-__device__ __forceinline__ void fp4_block(uint32_t w0, uint32_t w1, float s, const uint32_t *const xl[TT], int kp,
+__device__ __forceinline__ void load_x_chunk(const cu32 *const xr[TT], int kp, uint32_t (*x)[32])
+{
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[t][i] = xr[t][kp + i];
+}
+
+// 64 k of one lane row: words c.x..c.w (two 32-k blocks), block scales B0, B0+1 of sc
+template <int TT, int B0>
+__device__ __forceinline__ void w2_chunk(const uint4 &c, uint32_t sc, const uint32_t (*x)[32], float acc[TT], W2Consts k)
+{
+    float bs[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) bs[t] = 0.f;
+    w2_word<TT>(c.x, x, 0, bs, k);
+    w2_word<TT>(c.y, x, 8, bs, k);
+    const float s0 = e4m3_byte<B0>(sc);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = fmaf(bs[t], s0, acc[t]);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) bs[t] = 0.f;
+    w2_word<TT>(c.z, x, 16, bs, k);
+    w2_word<TT>(c.w, x, 24, bs, k);
+    const float s1 = e4m3_byte<B0 + 1>(sc);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = fmaf(bs[t], s1, acc[t]);
+}
+
+template <int TT>
+__device__ __forceinline__ void w2_group(const W2Buf &B, int g, const cu32 *const xr[TT], float acc[TT], W2Consts k)
+{
+    uint32_t x[TT][32];
+    load_x_chunk<TT>(xr, 64 * g, x);
+    w2_chunk<TT, 0>(B.c0, B.sc, x, acc, k);
+    __builtin_amdgcn_sched_barrier(0);  // the next chunk's activations start here
+    load_x_chunk<TT>(xr, 64 * g + 32, x);
+    w2_chunk<TT, 2>(B.c1, B.sc, x, acc, k);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// acc[t] += sum over groups [g0, g1) of (level/4) * scale * x for this lane's row
+template <int TT>
+__device__ __forceinline__ void w2_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
+{
+    if (g0 >= g1) return;
+    const W2Consts kc = w2_consts();
+    W2Buf A, B;
+    w2_load(A, L, K, g0);
+    for (int g = g0; g < g1; g += 2) {
+        if (g + 1 < g1) w2_load(B, L, K, g + 1);
+        w2_group<TT>(A, g, xr, acc, kc);
+        if (g + 1 >= g1) break;
+        if (g + 2 < g1) w2_load(A, L, K, g + 2);
+        w2_group<TT>(B, g + 1, xr, acc, kc);
+    }
+}
+
+// FP4 delta: 16-k block (words w0, w1) with scale s; x pairs x[t][o .. o+7]
+template <int TT>
+__device__ __forceinline__ void fp4_block(uint32_t w0, uint32_t w1, float s, const uint32_t (*x)[32], int o,
                                           float acc[TT])
 {
     uint32_t pr[8];
@@ -264,199 +253,126 @@ __device__ __forceinline__ void fp4_block(uint32_t w0, uint32_t w1, float s, con
     pr[7] = fp4_pair<3>(w1);
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-        const uint4 *q = reinterpret_cast<const uint4 *>(xl[t] + kp);
-        const uint4 v0 = q[0], v1 = q[1];
-        const uint32_t xv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
         float bs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bs = dot2_bf16(pr[i], xv[i], bs);
+        for (int i = 0; i < 8; ++i) bs = dot2_bf16(pr[i], x[t][o + i], bs);
         acc[t] = fmaf(bs, s, acc[t]);
     }
 }
 
-template <int TT, int NM>
-__device__ __forceinline__ void fp4_gemv(const uint4 *const c4[NM], const uint2 *const s8[NM], int tile, int lane, int K,
-                                         int g0, int g1, const uint32_t *const xl[TT], float acc[NM][TT])
+template <int TT>
+__device__ __forceinline__ void fp4_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
 {
     for (int g = g0; g < g1; ++g) {
-        uint2 sc[NM];
-        uint4 c[NM][4];
+        const uint2 sc = L.ds8[fp4_scale_idx(L.tile, g, L.rt, K)];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            sc[m] = s8[m][fp4_scale_idx(tile, g, lane, K)];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) c[m][j] = c4[m][fp4_chunk_idx(tile, 4 * g + j, lane, K)];
-        }
-        const int kp = 64 * g;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
+        for (int h = 0; h < 2; ++h) {   // 64-k halves of the group: FP4 chunks 4g+2h, 4g+2h+1
+            const uint4 ca = L.dc4[fp4_chunk_idx(L.tile, 4 * g + 2 * h, L.rt, K)];
+            const uint4 cb = L.dc4[fp4_chunk_idx(L.tile, 4 * g + 2 * h + 1, L.rt, K)];
+            uint32_t x[TT][32];
+            load_x_chunk<TT>(xr, 64 * g + 32 * h, x);
+            const uint32_t sw = h ? sc.y : sc.x;
+            fp4_block<TT>(ca.x, ca.y, e4m3_byte<0>(sw), x, 0, acc);
+            fp4_block<TT>(ca.z, ca.w, e4m3_byte<1>(sw), x, 8, acc);
+            fp4_block<TT>(cb.x, cb.y, e4m3_byte<2>(sw), x, 16, acc);
+            fp4_block<TT>(cb.z, cb.w, e4m3_byte<3>(sw), x, 24, acc);
             __builtin_amdgcn_sched_barrier(0);
-            fp4_block<TT>(c[m][0].x, c[m][0].y, e4m3_byte<0>(sc[m].x), xl, kp + 0, acc[m]);
-            fp4_block<TT>(c[m][0].z, c[m][0].w, e4m3_byte<1>(sc[m].x), xl, kp + 8, acc[m]);
-            __builtin_amdgcn_sched_barrier(0);
-            fp4_block<TT>(c[m][1].x, c[m][1].y, e4m3_byte<2>(sc[m].x), xl, kp + 16, acc[m]);
-            fp4_block<TT>(c[m][1].z, c[m][1].w, e4m3_byte<3>(sc[m].x), xl, kp + 24, acc[m]);
-            __builtin_amdgcn_sched_barrier(0);
-            fp4_block<TT>(c[m][2].x, c[m][2].y, e4m3_byte<0>(sc[m].y), xl, kp + 32, acc[m]);
-            fp4_block<TT>(c[m][2].z, c[m][2].w, e4m3_byte<1>(sc[m].y), xl, kp + 40, acc[m]);
-            __builtin_amdgcn_sched_barrier(0);
-            fp4_block<TT>(c[m][3].x, c[m][3].y, e4m3_byte<2>(sc[m].y), xl, kp + 48, acc[m]);
-            fp4_block<TT>(c[m][3].z, c[m][3].w, e4m3_byte<3>(sc[m].y), xl, kp + 56, acc[m]);
         }
     }
 }
 
-// Row pointers and scales of the matrices one slot uses.
-struct Mats {
-    const uint4 *c4[2];
-    const uint32_t *s4[2];
-    float s2[2];
-    const uint4 *dc4[2];
-    const uint2 *ds8[2];
-    float ds2[2];
-};
+constexpr int kTT = 2;     // tokens per pass (more would cost SGPRs / occupancy)
+constexpr int kW1 = 4;     // wavefronts per fc1 workgroup (K split)
+constexpr int kW2 = 2;     // wavefronts per fc2 workgroup (K split)
 
-// One chunk of TT tokens: per-wave partial pre-activations (2-bit + delta) for NM matrices.
-template <int TT, int NM>
-__device__ __forceinline__ void chunk_partials(const Mats &M, int tile, int lane, int K, int g0, int g1,
-                                               const uint32_t *const xl[TT], const bool flag[TT], bool any_flag,
-                                               float out[NM][TT])
+// One pass over up to kTT tokens: this lane's partial pre-activation per token
+// (2-bit part scaled by 4*s2 plus the delta part scaled by ds2 for flagged tokens).
+__device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2, int K, int g0, int g1,
+                                          const cu32 *const xr[kTT], const bool flag[kTT], int n, float part[kTT])
 {
-    float acc[NM][TT];
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[m][t] = 0.f;
-    w2_gemv<TT, NM>(M.c4, M.s4, tile, lane, K, g0, g1, xl, acc);
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int t = 0; t < TT; ++t) out[m][t] = 4.0f * M.s2[m] * acc[m][t];
-    if (any_flag) {
-        float dacc[NM][TT];
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int t = 0; t < TT; ++t) dacc[m][t] = 0.f;
-        fp4_gemv<TT, NM>(M.dc4, M.ds8, tile, lane, K, g0, g1, xl, dacc);
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int t = 0; t < TT; ++t)
-                if (flag[t]) out[m][t] += M.ds2[m] * dacc[m][t];
-    }
-}
-
-constexpr int kTT = 2;   // tokens per pass (more would cost occupancy)
-constexpr int kWaves = 8;
-
-template <int NM>
-__device__ void slot_pass(const Mats &M, int tile, int lane, int wave, int K, const uint32_t *const xl[kTT],
-                          const bool flag[kTT], int n, float part[NM][kTT])
-{
-    const int G = K / 128;
-    const int g0 = wave * G / kWaves, g1 = (wave + 1) * G / kWaves;
     bool any_flag = false;
 #pragma unroll
     for (int t = 0; t < kTT; ++t) any_flag |= (t < n) && flag[t];
+    float acc[kTT] = {0.f, 0.f}, dacc[kTT] = {0.f, 0.f};
     if (n == 1) {
-        float q[NM][1];
-        chunk_partials<1, NM>(M, tile, lane, K, g0, g1, xl, flag, any_flag, q);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) part[m][0] = q[m][0];
+        w2_gemv<1>(L, K, g0, g1, xr, acc);
+        if (any_flag) fp4_gemv<1>(L, K, g0, g1, xr, dacc);
     } else {
-        chunk_partials<2, NM>(M, tile, lane, K, g0, g1, xl, flag, any_flag, part);
+        w2_gemv<2>(L, K, g0, g1, xr, acc);
+        if (any_flag) fp4_gemv<2>(L, K, g0, g1, xr, dacc);
     }
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) part[t] = 4.0f * s2 * acc[t] + ((any_flag && flag[t]) ? ds2 * dacc[t] : 0.f);
 }
 
-// Copy n token rows of K bf16 (16-byte units) from global src rows into LDS dst
-// rows of stride K; all threads of the workgroup take part.
-__device__ __forceinline__ void stage_rows(uint32_t *dst, const uint16_t *const src[kTT], int n, int K)
+__global__ __launch_bounds__(64 * kW1) void fc1_decode_kernel(DecodeParams p)
 {
-    const int per_row = K / 8;  // uint4 per row
-    for (int i = threadIdx.x; i < n * per_row; i += blockDim.x) {
-        const int t = i / per_row, c = i - t * per_row;
-        reinterpret_cast<uint4 *>(dst + (size_t)t * (K / 2))[c] = reinterpret_cast<const uint4 *>(src[t])[c];
-    }
-}
-
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void fc1_decode_kernel(DecodeParams p)
-{
-    extern __shared__ __align__(16) uint32_t smem[];   // x rows [kTT][H/2], reused for the reduction
-    const int tile = blockIdx.x, s = blockIdx.y;
+    __shared__ float red[kW1][kTT][64];
+    const int half = blockIdx.x, s = blockIdx.y;   // rows [32 half, 32 half + 32) of gate and of up
     SlotInfo si;
     if (!resolve_slot(p, s, si)) return;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int I = p.I, H = p.H;
-    const size_t wmat = (size_t)I * H / 16, smat = (size_t)I * H / 32;
+    const int mat = lane >> 5;                      // 0: gate, 1: up
+    const int row = 32 * half + (lane & 31);
     const moet_w2 &W = si.shared ? p.sh13 : p.w13;
     const int m0 = si.shared ? 0 : 2 * si.e;
-    Mats M;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        M.c4[m] = reinterpret_cast<const uint4 *>(W.codes + (m0 + m) * wmat);
-        M.s4[m] = reinterpret_cast<const uint32_t *>(W.scales + (m0 + m) * smat);
-        M.s2[m] = W.scale2[m0 + m];
-        M.dc4[m] = nullptr;
-        M.ds8[m] = nullptr;
-        M.ds2[m] = 0.f;
-    }
+    LaneRow L;
+    L.c4 = reinterpret_cast<const uint4 *>(W.codes + (size_t)(m0 + mat) * I * H / 16);
+    L.s4 = reinterpret_cast<const uint32_t *>(W.scales + (size_t)(m0 + mat) * I * H / 32);
+    L.tile = row >> 6;
+    L.rt = row & 63;
+    const float s2 = W.scale2[m0 + mat];
+    float ds2 = 0.f;
+    L.dc4 = nullptr;
+    L.ds8 = nullptr;
     if (si.dslot >= 0) {
-        const size_t dmat = (size_t)I * H / 2, dsmat = (size_t)I * H / 16;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            M.dc4[m] = reinterpret_cast<const uint4 *>(p.d13.codes + (2 * si.dslot + m) * dmat);
-            M.ds8[m] = reinterpret_cast<const uint2 *>(p.d13.scales + (2 * si.dslot + m) * dsmat);
-            M.ds2[m] = p.d13.scale2[2 * si.dslot + m];
-        }
+        const int dm = 2 * si.dslot + mat;
+        L.dc4 = reinterpret_cast<const uint4 *>(p.d13.codes + (size_t)dm * I * H / 2);
+        L.ds8 = reinterpret_cast<const uint2 *>(p.d13.scales + (size_t)dm * I * H / 16);
+        ds2 = p.d13.scale2[dm];
     }
-    float(*red)[2][kTT][64] = reinterpret_cast<float(*)[2][kTT][64]>(smem);
+    const int G = H / 128;
+    const int g0 = wave * G / kW1, g1 = (wave + 1) * G / kW1;
     for (int i0 = si.pbeg; i0 < si.pend; i0 += kTT) {
         const int n = min(kTT, si.pend - i0);
-        const uint16_t *src[kTT];
-        const uint32_t *xl[kTT];
+        const cu32 *xr[kTT];
         bool flag[kTT];
         int hrow[kTT];
 #pragma unroll
         for (int j = 0; j < kTT; ++j) {
             int t;
             slot_token(p, si, i0 + (j < n ? j : 0), t, hrow[j], flag[j]);
-            src[j] = p.x + (size_t)t * H;
-            xl[j] = smem + (size_t)(j < n ? j : 0) * (H / 2);
+            xr[j] = as_const(p.x + (size_t)t * H);
         }
-        stage_rows(smem, src, n, H);
-        __syncthreads();
-        float part[2][kTT];
-        slot_pass<2>(M, tile, lane, wave, H, xl, flag, n, part);
-        __syncthreads();
+        float part[kTT];
+        lane_pass(L, s2, ds2, H, g0, g1, xr, flag, n, part);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int t = 0; t < kTT; ++t)
-                if (t < n) red[wave][m][t][lane] = part[m][t];
+        for (int t = 0; t < kTT; ++t)
+            if (t < n) red[wave][t][lane] = part[t];
         __syncthreads();
-        if (wave < n) {
+        if (wave < n && lane < 32) {
             const int j = wave;
             float ug = 0.f, uu = 0.f;
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v) {
-                ug += red[v][0][j][lane];
-                uu += red[v][1][j][lane];
+            for (int v = 0; v < kW1; ++v) {
+                ug += red[v][j][lane];
+                uu += red[v][j][lane + 32];
             }
             if (p.swiglu_limit > 0.f) {
                 ug = fminf(ug, p.swiglu_limit);
                 uu = fminf(fmaxf(uu, -p.swiglu_limit), p.swiglu_limit);
             }
             const float hv = silu_f32(ug) * uu;
-            p.h[(size_t)hrow[j] * I + tile * 64 + lane] = (uint16_t)f32_to_bf16_rne(hv);
+            p.h[(size_t)hrow[j] * I + row] = (uint16_t)f32_to_bf16_rne(hv);
         }
         __syncthreads();
     }
 }
 
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void fc2_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * kW2) void fc2_decode_kernel(DecodeParams p)
 {
-    extern __shared__ __align__(16) uint32_t smem[];   // h rows [kTT][I/2], reused for the reduction
+    __shared__ float red[kW2][kTT][64];
     const int tile = blockIdx.x, s = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int I = p.I, H = p.H;
@@ -464,48 +380,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void f
     if (!resolve_slot(p, s, si)) return;
     const moet_w2 &W = si.shared ? p.sh2 : p.w2;
     const int m0 = si.shared ? 0 : si.e;
-    const size_t wmat = (size_t)H * I / 16, smat = (size_t)H * I / 32;
-    Mats M;
-    M.c4[0] = reinterpret_cast<const uint4 *>(W.codes + m0 * wmat);
-    M.s4[0] = reinterpret_cast<const uint32_t *>(W.scales + m0 * smat);
-    M.s2[0] = W.scale2[m0];
-    M.dc4[0] = nullptr;
-    M.ds8[0] = nullptr;
-    M.ds2[0] = 0.f;
+    LaneRow L;
+    L.c4 = reinterpret_cast<const uint4 *>(W.codes + (size_t)m0 * H * I / 16);
+    L.s4 = reinterpret_cast<const uint32_t *>(W.scales + (size_t)m0 * H * I / 32);
+    L.tile = tile;
+    L.rt = lane;
+    const float s2 = W.scale2[m0];
+    float ds2 = 0.f;
+    L.dc4 = nullptr;
+    L.ds8 = nullptr;
     if (si.dslot >= 0) {
-        const size_t dmat = (size_t)H * I / 2, dsmat = (size_t)H * I / 16;
-        M.dc4[0] = reinterpret_cast<const uint4 *>(p.d2.codes + si.dslot * dmat);
-        M.ds8[0] = reinterpret_cast<const uint2 *>(p.d2.scales + si.dslot * dsmat);
-        M.ds2[0] = p.d2.scale2[si.dslot];
+        L.dc4 = reinterpret_cast<const uint4 *>(p.d2.codes + (size_t)si.dslot * H * I / 2);
+        L.ds8 = reinterpret_cast<const uint2 *>(p.d2.scales + (size_t)si.dslot * H * I / 16);
+        ds2 = p.d2.scale2[si.dslot];
     }
-    float(*red)[1][kTT][64] = reinterpret_cast<float(*)[1][kTT][64]>(smem);
+    const int G = I / 128;
+    const int g0 = wave * G / kW2, g1 = (wave + 1) * G / kW2;
     for (int i0 = si.pbeg; i0 < si.pend; i0 += kTT) {
         const int n = min(kTT, si.pend - i0);
-        const uint16_t *src[kTT];
-        const uint32_t *xl[kTT];
+        const cu32 *xr[kTT];
         bool flag[kTT];
         int hrow[kTT];
 #pragma unroll
         for (int j = 0; j < kTT; ++j) {
             int t;
             slot_token(p, si, i0 + (j < n ? j : 0), t, hrow[j], flag[j]);
-            src[j] = p.h + (size_t)hrow[j] * I;
-            xl[j] = smem + (size_t)(j < n ? j : 0) * (I / 2);
+            xr[j] = as_const(p.h + (size_t)hrow[j] * I);
         }
-        stage_rows(smem, src, n, I);
-        __syncthreads();
-        float part[1][kTT];
-        slot_pass<1>(M, tile, lane, wave, I, xl, flag, n, part);
-        __syncthreads();
+        float part[kTT];
+        lane_pass(L, s2, ds2, I, g0, g1, xr, flag, n, part);
 #pragma unroll
         for (int t = 0; t < kTT; ++t)
-            if (t < n) red[wave][0][t][lane] = part[0][t];
+            if (t < n) red[wave][t][lane] = part[t];
         __syncthreads();
         if (wave < n) {
             const int j = wave;
             float y = 0.f;
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v) y += red[v][0][j][lane];
+            for (int v = 0; v < kW2; ++v) y += red[v][j][lane];
             p.ypart[(size_t)hrow[j] * H + tile * 64 + lane] = y;
         }
         __syncthreads();
@@ -532,34 +444,36 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p)
 // ---------------------------------------------------------------------------
 // Standalone FP4 delta GEMV: acc[r][n] += D_slot[n][:] . act[r][:]
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void delta_gemv_kernel(moet_fp4 D, int n_slots, int N, int K,
-                                                         const uint16_t *__restrict__ act,
-                                                         const int32_t *__restrict__ row_slot,
-                                                         float *__restrict__ acc)
+constexpr int kWd = 4;
+
+__global__ __launch_bounds__(64 * kWd) void delta_gemv_kernel(moet_fp4 D, int n_slots, int N, int K,
+                                                              const uint16_t *__restrict__ act,
+                                                              const int32_t *__restrict__ row_slot,
+                                                              float *__restrict__ acc)
 {
-    extern __shared__ __align__(16) uint32_t smem[];   // act row [K/2], then the reduction
+    __shared__ float red[kWd][64];
     const int tile = blockIdx.x, r = blockIdx.y;
     const int slot = row_slot[r];
     if (slot < 0 || slot >= n_slots) return;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = K / 128;
-    const int g0 = wave * G / kWaves, g1 = (wave + 1) * G / kWaves;
-    const uint16_t *src[kTT] = {act + (size_t)r * K, nullptr};
-    stage_rows(smem, src, 1, K);
-    __syncthreads();
-    const uint4 *c4[1] = {reinterpret_cast<const uint4 *>(D.codes + (size_t)slot * N * K / 2)};
-    const uint2 *s8[1] = {reinterpret_cast<const uint2 *>(D.scales + (size_t)slot * N * K / 16)};
-    const uint32_t *xl[1] = {smem};
-    float a[1][1] = {{0.f}};
-    fp4_gemv<1, 1>(c4, s8, tile, lane, K, g0, g1, xl, a);
-    __syncthreads();
-    float *red = reinterpret_cast<float *>(smem);
-    red[wave * 64 + lane] = a[0][0];
+    const int g0 = wave * G / kWd, g1 = (wave + 1) * G / kWd;
+    LaneRow L;
+    L.c4 = nullptr;
+    L.s4 = nullptr;
+    L.dc4 = reinterpret_cast<const uint4 *>(D.codes + (size_t)slot * N * K / 2);
+    L.ds8 = reinterpret_cast<const uint2 *>(D.scales + (size_t)slot * N * K / 16);
+    L.tile = tile;
+    L.rt = lane;
+    const cu32 *xr[1] = {as_const(act + (size_t)r * K)};
+    float a[1] = {0.f};
+    fp4_gemv<1>(L, K, g0, g1, xr, a);
+    red[wave][lane] = a[0];
     __syncthreads();
     if (wave == 0) {
         float v = 0.f;
 #pragma unroll
-        for (int u = 0; u < kWaves; ++u) v += red[u * 64 + lane];
+        for (int u = 0; u < kWd; ++u) v += red[u][lane];
         v *= D.scale2[slot];
         float *dst = acc + (size_t)r * N + tile * 64 + lane;
         *dst = *dst + v;
@@ -610,14 +524,11 @@ int launch_decode(const moet_layer *L, const uint16_t *x, int T, int k, const in
     p.out = out;
     const int slots = T * k + p.has_shared;
     timing_start(stream);
-    const int tt = T < kTT ? T : kTT;
-    const size_t red1 = (size_t)kWaves * 2 * kTT * 64 * 4, red2 = (size_t)kWaves * kTT * 64 * 4;
-    const size_t lds1 = std::max((size_t)tt * L->H * 2, red1), lds2 = std::max((size_t)tt * L->I * 2, red2);
-    hipLaunchKernelGGL(fc1_decode_kernel, dim3(L->I / 64, slots), dim3(64 * kWaves), lds1, stream, p);
+    hipLaunchKernelGGL(fc1_decode_kernel, dim3(L->I / 32, slots), dim3(64 * kW1), 0, stream, p);
     timing_stop(stream);
     int rc = check_launch("fc1_decode_kernel");
     if (rc != MOET_OK) return rc;
-    hipLaunchKernelGGL(fc2_decode_kernel, dim3(L->H / 64, slots), dim3(64 * kWaves), lds2, stream, p);
+    hipLaunchKernelGGL(fc2_decode_kernel, dim3(L->H / 64, slots), dim3(64 * kW2), 0, stream, p);
     rc = check_launch("fc2_decode_kernel");
     if (rc != MOET_OK) return rc;
     hipLaunchKernelGGL(combine_kernel, dim3((L->H + 255) / 256, T), dim3(256), 0, stream, p);
@@ -628,8 +539,8 @@ int launch_delta(const moet_fp4 *D, int n_slots, int N, int K, const uint16_t *a
                  float *acc, hipStream_t stream)
 {
     if (R == 0) return MOET_OK;
-    const size_t lds = std::max((size_t)K * 2, (size_t)kWaves * 64 * 4);
-    hipLaunchKernelGGL(delta_gemv_kernel, dim3(N / 64, R), dim3(64 * kWaves), lds, stream, *D, n_slots, N, K, act, row_slot, acc);
+    hipLaunchKernelGGL(delta_gemv_kernel, dim3(N / 64, R), dim3(64 * kWd), 0, stream, *D, n_slots, N, K, act, row_slot,
+                       acc);
     return check_launch("delta_gemv_kernel");
 }
 

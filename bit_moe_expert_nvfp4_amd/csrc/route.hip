@@ -7,10 +7,13 @@
 //
 // Selection uses the raw fp32 logits (largest first, equal logits -> lower id;
 // softmax and sigmoid are monotonic).  One 64-lane wavefront owns one token:
-// each lane holds up to 16 logits (e = lane + 64 i) and top_k rounds of
-// shuffle reductions pick the winners.  The permutation is stable by pair id:
-//  - small batches (T*top_k <= 1024): one workgroup does top-k, counts,
-//    scan and ranks in LDS (one launch);
+// each lane holds up to 16 logits (e = lane + 64 i); the k-th largest is found
+// by a 32-step bisection over order-preserving integer keys with ballot
+// counts, so no cross-lane shuffles sit on the critical path.  The
+// permutation is stable by pair id:
+//  - small batches (T*top_k <= 1024): one workgroup does top-k, then every
+//    thread counts the offset of one expert and the rank of one pair in LDS
+//    (one launch);
 //  - large batches: a top-k kernel, then one workgroup per expert that scans
 //    all pair ids twice (count of smaller ids -> offset, then a ballot-ordered
 //    compaction of its own pairs).
@@ -21,71 +24,96 @@
 namespace moet {
 
 constexpr int kMaxE = 1024;
-constexpr int kMaxPerLane = kMaxE / 64;
 constexpr int kSmallPairs = 1024;
 
-__device__ __forceinline__ bool better(float v, int id, float bv, int bid)
+// monotonic map float -> uint32 (larger float -> larger key); inputs are finite
+__device__ __forceinline__ uint32_t fkey(float f)
 {
-    return v > bv || (v == bv && id < bid);
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Top-k of one token by one wavefront; writes ids / weights of token t.
+// The k-th largest key is found by bisection on its 32 bits, counting with
+// ballots (no cross-lane shuffles); ties at the threshold are filled in
+// increasing expert id; the k winners are then ordered by (key desc, id asc).
+template <int NPL>
 __device__ void topk_token(const float *__restrict__ logits, int t, int E, int k, int fn, int renorm, float rscale,
-                           int32_t *__restrict__ ids, float *__restrict__ w, int32_t *lds_ids)
+                           int32_t *__restrict__ ids, float *__restrict__ w, int32_t *lds_ids, uint32_t *scratch)
 {
     const int lane = threadIdx.x & 63;
-    float v[kMaxPerLane];
+    uint32_t key[NPL];
+    float v[NPL];
     const float *row = logits + (size_t)t * E;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
-        v[i] = (e < E) ? row[e] : -FLT_MAX;
+        v[i] = (e < E) ? row[e] : 0.f;
+        key[i] = (e < E) ? fkey(v[i]) : 0u;   // key 0 is below every finite value
     }
-    uint32_t used = 0;
-    float my_val = 0.f;
-    int my_id = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -FLT_MAX;
-        int bid = 0x7FFFFFFF;
+    uint32_t thr = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = thr | (1u << b);
+        int c = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((used >> i) & 1u) && better(v[i], e, bv, bid)) {
-                bv = v[i];
-                bid = e;
-            }
-        }
+        for (int i = 0; i < NPL; ++i) c += __popcll(__ballot(key[i] >= cand));
+        if (c >= k) thr = cand;
+    }
+    int c_gt = 0;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oid = __shfl_xor(bid, off, 64);
-            if (better(ov, oid, bv, bid)) {
-                bv = ov;
-                bid = oid;
-            }
+    for (int i = 0; i < NPL; ++i) c_gt += __popcll(__ballot(key[i] > thr));
+    const int need_eq = k - c_gt;   // >= 1
+    // selected flags: key > thr, or key == thr among the first need_eq in id order
+    bool sel[NPL];
+    int eq_before = 0;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const bool eq = (lane + 64 * i < E) && key[i] == thr;
+        const uint64_t be = __ballot(eq);
+        const int rank_eq = eq_before + __popcll(be & lt_mask);
+        sel[i] = key[i] > thr || (eq && rank_eq < need_eq);
+        eq_before += __popcll(be);
+    }
+    // compact the k winners (key, id) into scratch[0..k) in (i, lane) order
+    int before = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const uint64_t bs = __ballot(sel[i]);
+        if (sel[i]) {
+            const int pos = before + __popcll(bs & lt_mask);
+            scratch[2 * pos] = key[i];
+            scratch[2 * pos + 1] = (uint32_t)(lane + 64 * i);
         }
-        if ((bid & 63) == lane) used |= 1u << (bid >> 6);
-        if (lane == j) {
-            my_val = bv;
-            my_id = bid;
+        before += __popcll(bs);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // LDS writes done before other lanes read them
+    __builtin_amdgcn_wave_barrier();
+    uint32_t my_key = 0, my_id = 0;
+    int rank = 0;
+    if (lane < k) {
+        my_key = scratch[2 * lane];
+        my_id = scratch[2 * lane + 1];
+        for (int j = 0; j < k; ++j) {
+            const uint32_t kj = scratch[2 * j], ij = scratch[2 * j + 1];
+            rank += (kj > my_key || (kj == my_key && ij < my_id)) ? 1 : 0;
         }
     }
-    // weights: lane j < k holds selected logit j (descending)
-    const float lmax = __shfl(my_val, 0, 64);
+    const float my_val = (lane < k) ? row[my_id] : 0.f;
+    // largest selected logit (rank 0)
+    const uint64_t r0 = __ballot(lane < k && rank == 0);
+    const float lmax = __shfl(my_val, (int)__builtin_ctzll(r0), 64);
     float s;
     if (fn == MOET_SOFTMAX) s = expf(my_val - lmax);
     else s = 1.0f / (1.0f + expf(-my_val));
-    float part = (lane < k) ? s : 0.f;
     float denom;
     if (renorm) {
-        denom = part;
+        denom = (lane < k) ? s : 0.f;
     } else if (fn == MOET_SOFTMAX) {
         denom = 0.f;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E) denom += expf(v[i] - lmax);
-        }
+        for (int i = 0; i < NPL; ++i)
+            if (lane + 64 * i < E) denom += expf(v[i] - lmax);
     } else {
         denom = 0.f;
     }
@@ -94,10 +122,27 @@ __device__ void topk_token(const float *__restrict__ logits, int t, int E, int k
     float wt = (fn == MOET_SIGMOID && !renorm) ? s : s / denom;
     wt *= rscale;
     if (lane < k) {
-        ids[(size_t)t * k + lane] = my_id;
-        w[(size_t)t * k + lane] = wt;
-        if (lds_ids) lds_ids[t * k + lane] = my_id;
+        ids[(size_t)t * k + rank] = (int32_t)my_id;
+        w[(size_t)t * k + rank] = wt;
+        if (lds_ids) lds_ids[t * k + rank] = (int32_t)my_id;
     }
+}
+
+template <int NPL>
+__device__ void topk_dispatch_token(const float *logits, int t, int E, int k, int fn, int renorm, float rscale, int32_t *ids,
+                                    float *w, int32_t *lds_ids, uint32_t *scratch)
+{
+    topk_token<NPL>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
+}
+
+__device__ void topk_any(const float *logits, int t, int E, int k, int fn, int renorm, float rscale, int32_t *ids, float *w,
+                         int32_t *lds_ids, uint32_t *scratch)
+{
+    if (E <= 64) topk_token<1>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
+    else if (E <= 128) topk_token<2>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
+    else if (E <= 256) topk_token<4>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
+    else if (E <= 512) topk_token<8>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
+    else topk_token<16>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
 }
 
 __global__ __launch_bounds__(1024) void route_small_kernel(const float *__restrict__ logits, int T, int E, int k, int fn,
@@ -106,40 +151,26 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float *__restri
                                                            int32_t *__restrict__ sorted)
 {
     __shared__ int32_t s_ids[kSmallPairs];
-    __shared__ int32_t s_cnt[kMaxE + 1];
+    __shared__ int32_t s_off[kMaxE + 1];
+    __shared__ uint32_t s_scr[16][32];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int wave = tid >> 6, nwaves = nthr >> 6;
-    for (int e = tid; e <= E; e += nthr) s_cnt[e] = 0;
-    for (int t = wave; t < T; t += nwaves) topk_token(logits, t, E, k, fn, renorm, rscale, ids, w, s_ids);
+    for (int t = wave; t < T; t += nwaves) topk_any(logits, t, E, k, fn, renorm, rscale, ids, w, s_ids, s_scr[wave]);
     __syncthreads();
     const int P = T * k;
-    for (int p = tid; p < P; p += nthr) atomicAdd(&s_cnt[s_ids[p]], 1);
-    __syncthreads();
-    // exclusive scan of s_cnt[0..E) by wave 0, 64 entries per step
-    if (wave == 0) {
-        const int lane = tid & 63;
-        int carry = 0;
-        for (int base = 0; base < E; base += 64) {
-            const int e = base + lane;
-            const int c = (e < E) ? s_cnt[e] : 0;
-            int incl = c;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
-            if (e < E) s_cnt[e] = carry + incl - c;
-            carry += __shfl(incl, 63, 64);
-        }
-        if (lane == 0) s_cnt[E] = carry;
+    // offsets[e] = number of pairs routed to experts < e
+    for (int e = tid; e <= E; e += nthr) {
+        int c = 0;
+        for (int p = 0; p < P; ++p) c += (s_ids[p] < e) ? 1 : 0;
+        s_off[e] = c;
+        offsets[e] = c;
     }
     __syncthreads();
-    for (int e = tid; e <= E; e += nthr) offsets[e] = s_cnt[e];
     for (int p = tid; p < P; p += nthr) {
         const int e = s_ids[p];
         int rank = 0;
         for (int q = 0; q < p; ++q) rank += (s_ids[q] == e) ? 1 : 0;
-        sorted[s_cnt[e] + rank] = p;
+        sorted[s_off[e] + rank] = p;
     }
 }
 
@@ -147,8 +178,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
                                                          int renorm, float rscale, int32_t *__restrict__ ids,
                                                          float *__restrict__ w)
 {
+    __shared__ uint32_t s_scr[4][32];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t < T) topk_token(logits, t, E, k, fn, renorm, rscale, ids, w, nullptr);
+    if (t < T) topk_any(logits, t, E, k, fn, renorm, rscale, ids, w, nullptr, s_scr[threadIdx.x >> 6]);
 }
 
 // One workgroup per expert e: offset = #pairs with id < e, then its pairs in order.

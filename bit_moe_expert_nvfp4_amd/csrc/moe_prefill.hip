@@ -1,20 +1,466 @@
-// Prefill-sized MoE layer forward (placeholder: runs the GEMV kernels).
+// Prefill-sized MoE layer forward: grouped GEMM on the matrix cores.
+//
+// Method: README "Frontier MoE on consumer Blackwell (SM120)", section
+// "How it fits — 2-bit experts at FP4 quality": prefill runs the same 2-bit
+// expert GEMM as decode on many tokens per expert; the page notes that the
+// prefill GEMM is limited by how fast operands are fed to the matrix units
+// (one wide load per operand fragment), not by DRAM.
+//
+// MI355X design (bf16 v_mfma_f32_32x32x16, fp32 accumulation):
+//  * Work item = (M-tile of up to 128 consecutive sorted pairs of one expert,
+//    N-tile).  M-tiles are numbered per expert from expert_offsets, so the
+//    routing never round-trips to the host.  Linear workgroup ids are mapped
+//    so that every N-tile of one M-tile lands on the same XCD (workgroups are
+//    dispatched round-robin over the 8 XCDs): the gathered activation rows
+//    are then read from that XCD's L2 by all of them.
+//  * A (activations): 128 rows x 64 k bf16 per step, gathered by token
+//    (gate/up) or read from h in sorted order (down), staged in LDS with an
+//    XOR swizzle of the 16-byte columns so each MFMA A fragment is one
+//    conflict-free ds_read_b128.  A, B codes and B scales of each 64-k step
+//    travel by LDS-DMA into a 3-stage ring, so two steps are in flight while
+//    one is computed and no registers are spent on prefetching.
+//  * B (weights): each lane dequantises the 8 k-values its MFMA B fragment
+//    needs from the staged 2-bit words into registers: bf16(level * e4m3
+//    block scale) is exact (4 significant bits), built from the bf16 scale by
+//    adding 2 to the exponent for magnitude 4 and setting the sign bit.
+//    The per-tensor scale2 is applied in the epilogue.
+//  * gate/up kernel: wave w owns 32 gate columns and the same 32 up columns,
+//    so SwiGLU is computed in registers and h = bf16(silu(g) * u) is written
+//    in sorted-pair order (the down kernel reads it contiguously).
+//  * down kernel: 256 output features per workgroup, y (fp32) scattered to
+//    the pair's row for the shared combine kernel.
+#include <algorithm>
+
 #include "moet_common.h"
 
 namespace moet {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPM = 128;    // rows per M-tile
+constexpr int kPMB = 4;     // 32-row MFMA blocks per M-tile
+constexpr int kPK = 64;     // k per pipeline step
+constexpr int kPW = 4;      // wavefronts per workgroup
+
+struct PrefillParams {
+    const uint16_t *x;
+    int T, k, H, I, E;
+    const int32_t *ids;
+    const float *w;
+    const int32_t *offsets;
+    const int32_t *sorted;
+    moet_w2 w13, w2, sh13, sh2;
+    int has_shared;
+    float swiglu_limit;
+    uint16_t *h;        // [P + T][I] bf16, rows in sorted-pair order (shared expert: P + t)
+    float *ypart;       // [P + T][H] fp32, rows by pair id (shared expert: P + t)
+    uint16_t *out;
+    int n_mslots;       // upper bound on M-tiles (grid)
+    int n_ntiles;
+};
+
+struct MTile {
+    int e;        // expert, or -1 for the shared expert
+    int row0;     // first row in sorted order (shared: first token)
+    int rows;     // valid rows (<= kPM)
+};
+
+// M-tile number ms -> (expert, rows).  Tiles are enumerated expert by expert
+// (ceil(count / kPM) each), then the shared expert's tiles.  One wavefront
+// computes it: per-lane tile counts, inclusive scan, ballot search.
+__device__ bool locate_mtile(const PrefillParams &p, int ms, MTile &mt)
+{
+    const int lane = threadIdx.x & 63;
+    int base = 0;   // tiles before the current 64-expert chunk
+    for (int c = 0; c < p.E; c += 64) {
+        const int e = c + lane;
+        int cnt = 0, o0 = 0;
+        if (e < p.E) {
+            o0 = p.offsets[e];
+            cnt = p.offsets[e + 1] - o0;
+        }
+        const int tiles = (cnt + kPM - 1) / kPM;
+        int incl = tiles;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
+        }
+        const int excl = base + incl - tiles;
+        const bool mine = (e < p.E) && ms >= excl && ms < excl + tiles;
+        const uint64_t b = __ballot(mine);
+        if (b) {
+            const int src = __builtin_ctzll(b);
+            const int ee = __shfl(e, src, 64), oo = __shfl(o0, src, 64), cc = __shfl(cnt, src, 64),
+                      ex = __shfl(excl, src, 64);
+            const int t = ms - ex;
+            mt.e = ee;
+            mt.row0 = oo + t * kPM;
+            mt.rows = min(kPM, cc - t * kPM);
+            return true;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    if (p.has_shared) {
+        const int t = ms - base;
+        if (t >= 0 && t * kPM < p.T) {
+            mt.e = -1;
+            mt.row0 = t * kPM;
+            mt.rows = min(kPM, p.T - t * kPM);
+            return true;
+        }
+    }
+    return false;
+}
+
+// XCD-aware decode of the linear workgroup id into (M-tile slot, N-tile)
+__device__ __forceinline__ void decode_wg(int id, int n_ntiles, int &ms, int &nt)
+{
+    const int xcd = id & 7, local = id >> 3;
+    nt = local % n_ntiles;
+    ms = (local / n_ntiles) * 8 + xcd;
+}
+
+// bf16 pair of (level * scale) for pair bits already rotated to 8/15/24/31
+__device__ __forceinline__ uint32_t deq_pair(uint32_t rotated, uint32_t mask, uint32_t spair)
+{
+    return (rotated & mask) + spair;
+}
+
+// per (row, 32-k block) dequant constants from a scale byte
+__device__ __forceinline__ void block_consts(uint32_t scale_word, int byte, uint32_t &mask, uint32_t &spair)
+{
+    const uint32_t b = (scale_word >> (8 * byte)) & 0xFFu;
+    const float f = __builtin_amdgcn_cvt_f32_fp8(b, 0);
+    const uint32_t hb = __float_as_uint(f) >> 16;   // exact bf16 of the e4m3 scale
+    spair = hb | (hb << 16);
+    mask = b ? 0x81008100u : 0u;
+}
+
+// 8 bf16 of one row for one MFMA k-step: word w (16 k), this lane's half h (k 8h .. 8h+7)
+__device__ __forceinline__ bf16x8 deq_frag(uint32_t w, int rbase, uint32_t mask, uint32_t spair)
+{
+    uint32_t q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = deq_pair(__builtin_amdgcn_alignbit(w, w, rbase + 2 * j), mask, spair);
+    return __builtin_bit_cast(bf16x8, make_uint4(q[0], q[1], q[2], q[3]));
+}
+
+// ---------------------------------------------------------------------------
+// Pipeline: kPS-stage LDS ring filled by LDS-DMA (global_load_lds) so no
+// registers are held for prefetch.  Per stage and wavefront: 4 A segments
+// (1 KiB each), 1 B chunk (1 KiB = 64 rows x 16 B), 1 scale dword per row of
+// the B chunk (256 B).  The DMA is issued from inline asm, invisible to the
+// compiler's wait-count pass, and waited explicitly (6 per stage).
+// ---------------------------------------------------------------------------
+constexpr int kPS = 3;                         // stages
+constexpr int kStageA = kPM * 128;             // 16 KiB: 128 rows x 64 k bf16
+constexpr int kStageB = 4 * 1024;              // 256 B-rows x 16 B
+constexpr int kStageS = 4 * 256;               // 256 rows x one scale dword
+constexpr int kStage = kStageA + kStageB + kStageS;
+constexpr int kDmaPerStage = 6;
+
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
+}
+
+// wait until at most n of this wave's LDS-DMA instructions are outstanding, then
+// barrier (every wave's part of the stage has landed; the oldest buffer is free)
+template <int N>
+__device__ __forceinline__ void wait_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ bf16x8 a_frag(const uint8_t *a, int r, int c)
+{
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(a + r * 128 + ((c ^ (r & 7)) << 4)));
+}
+
+struct PipeSrc {
+    const uint8_t *arow[4];     // this lane's A source rows, one per A segment it fetches
+    const uint8_t *bsrc;        // this wave's B storage tile (codes), row = lane
+    const uint8_t *ssrc;        // this wave's B storage tile (scales), row = lane
+    int K;
+};
+
+// issue the DMA of pipeline step s into stage buffer `stage`
+__device__ __forceinline__ void issue_stage(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage);
+    const int c = (lane & 7) ^ ((lane >> 3) & 7);   // logical 16-B column for this lane's LDS slot
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((4 * wave + i) * 1024));
+    dma16(src.bsrc + ((size_t)s * 64 + lane) * 16, base + kStageA + wave * 1024);
+    dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 4, base + kStageA + kStageB + wave * 256);
+}
+
+// Main loop shared by both kernels.  acc[mb][nb] += A(tile rows) x dequant(B row brow[nb]);
+// brow[nb] = index (0..255) of this lane's B row within the workgroup's 256 B-rows.
+template <int NMB>
+__device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2])
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;                 // k half of the MFMA fragment
+    const int rbase = h ? 0 : 24;            // rotation of pair 4h
+    const int nsteps = src.K / kPK;
+#pragma unroll
+    for (int st = 0; st < kPS - 1; ++st)
+        if (st < nsteps) issue_stage(src, smem, st, st, wave, lane);
+    for (int s = 0; s < nsteps; ++s) {
+        // stages issued after s: min(kPS - 2, nsteps - 1 - s)
+        if (s + 1 < nsteps) wait_barrier<kDmaPerStage * (kPS - 2)>();
+        else wait_barrier<0>();
+        if (s + kPS - 1 < nsteps) issue_stage(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
+        const uint8_t *stg = smem + (s % kPS) * kStage;
+        const uint8_t *aT = stg;
+        const uint8_t *bT = stg + kStageA;
+        const uint8_t *sT = stg + kStageA + kStageB;
+        uint4 bw[2];
+        uint32_t mask[2][2], spair[2][2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            bw[nb] = *reinterpret_cast<const uint4 *>(bT + brow[nb] * 16);
+            const uint32_t sw = *reinterpret_cast<const uint32_t *>(sT + brow[nb] * 4);
+            block_consts(sw, 2 * (s & 1) + 0, mask[nb][0], spair[nb][0]);
+            block_consts(sw, 2 * (s & 1) + 1, mask[nb][1], spair[nb][1]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {   // MFMA k-steps of 16
+            bf16x8 bfr[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const uint32_t wv = (q == 0) ? bw[nb].x : (q == 1) ? bw[nb].y : (q == 2) ? bw[nb].z : bw[nb].w;
+                bfr[nb] = deq_frag(wv, rbase, mask[nb][q >> 1], spair[nb][q >> 1]);
+            }
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                const bf16x8 afr = a_frag(aT, 32 * mb + (lane & 31), 2 * q + h);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[nb], acc[mb][nb], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// one instantiation per number of valid 32-row blocks, chosen once per workgroup
+__device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2],
+                                          int nmb)
+{
+    switch (nmb) {
+    case 1: gemm_pipe_n<1>(src, smem, brow, acc); break;
+    case 2: gemm_pipe_n<2>(src, smem, brow, acc); break;
+    case 3: gemm_pipe_n<3>(src, smem, brow, acc); break;
+    default: gemm_pipe_n<4>(src, smem, brow, acc); break;
+    }
+}
+
+// gate/up + SwiGLU.  N-tile nt covers h columns [128 nt, 128 nt + 128); wave w
+// owns gate rows and up rows [128 nt + 32 w, + 32).
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc1_prefill_kernel(PrefillParams p)
+{
+    __shared__ __align__(1024) uint8_t smem[kPS * kStage];
+    int ms, nt;
+    decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
+    if (ms >= p.n_mslots) return;
+    MTile mt;
+    if (!locate_mtile(p, ms, mt)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = p.H, I = p.I, P = p.T * p.k;
+    // A rows fetched by this lane: segment i of wave w holds rows 8(4w+i) .. +7; lane -> row + lane/8
+    PipeSrc src;
+    src.K = H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = min(8 * (4 * wave + i) + (lane >> 3), mt.rows - 1);
+        int tok;
+        if (mt.e >= 0) tok = min(max(p.sorted[mt.row0 + r], 0), P - 1) / p.k;
+        else tok = mt.row0 + r;
+        src.arow[i] = reinterpret_cast<const uint8_t *>(p.x + (size_t)tok * H);
+    }
+    // B: 256 rows = gate rows [128 nt, +128) then up rows [128 nt, +128); wave w fetches storage tile w
+    const moet_w2 &W = (mt.e >= 0) ? p.w13 : p.sh13;
+    const int m0 = (mt.e >= 0) ? 2 * mt.e : 0;
+    {
+        const int mat = m0 + (wave >> 1);
+        const int tile = 2 * nt + (wave & 1);
+        src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)mat * I * H / 16) + (size_t)tile * (H / 64) * 1024;
+        src.ssrc = W.scales + (size_t)mat * I * H / 32 + (size_t)tile * (H / 128) * 256;
+    }
+    const int jl = 32 * wave + (lane & 31);          // h column within the tile
+    const int j = 128 * nt + jl;
+    const int brow[2] = {jl, 128 + jl};               // gate row, up row in the stage
+    f32x16 acc[kPMB][2];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+    const int nmb = (mt.rows + 31) / 32;
+    gemm_pipe(src, smem, brow, acc, nmb);
+    const float sg = W.scale2[m0], su = W.scale2[m0 + 1];
+    const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb) {
+        if (mb >= nmb) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (r < mt.rows) {
+                float g = acc[mb][0][v] * sg, u = acc[mb][1][v] * su;
+                if (p.swiglu_limit > 0.f) {
+                    g = fminf(g, p.swiglu_limit);
+                    u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+                }
+                p.h[(size_t)(rowbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
+            }
+        }
+    }
+}
+
+// down: N-tile nt covers output features [256 nt, 256 nt + 256); wave w owns 64 of them.
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc2_prefill_kernel(PrefillParams p)
+{
+    __shared__ __align__(1024) uint8_t smem[kPS * kStage];
+    int ms, nt;
+    decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
+    if (ms >= p.n_mslots) return;
+    MTile mt;
+    if (!locate_mtile(p, ms, mt)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = p.H, I = p.I, P = p.T * p.k;
+    const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;
+    PipeSrc src;
+    src.K = I;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = min(8 * (4 * wave + i) + (lane >> 3), mt.rows - 1);
+        src.arow[i] = reinterpret_cast<const uint8_t *>(p.h + (size_t)(rowbase + r) * I);
+    }
+    const moet_w2 &W = (mt.e >= 0) ? p.w2 : p.sh2;
+    const int m0 = (mt.e >= 0) ? mt.e : 0;
+    {
+        const int tile = 4 * nt + wave;
+        src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
+        src.ssrc = W.scales + (size_t)m0 * H * I / 32 + (size_t)tile * (I / 128) * 256;
+    }
+    const int brow[2] = {64 * wave + (lane & 31), 64 * wave + 32 + (lane & 31)};
+    int ncol[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) ncol[nb] = 256 * nt + brow[nb];
+    f32x16 acc[kPMB][2];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+    const int nmb = (mt.rows + 31) / 32;
+    gemm_pipe(src, smem, brow, acc, nmb);
+    const float s2 = W.scale2[m0];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb) {
+        if (mb >= nmb) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (r < mt.rows) {
+                const int prow = (mt.e >= 0) ? min(max(p.sorted[mt.row0 + r], 0), P - 1) : P + mt.row0 + r;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) p.ypart[(size_t)prow * H + ncol[nb]] = acc[mb][nb][v] * s2;
+            }
+        }
+    }
+}
+
+// out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order
+__global__ __launch_bounds__(256) void combine_prefill_kernel(PrefillParams p)
+{
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    const int t = blockIdx.y;
+    if (n >= p.H) return;
+    const int P = p.T * p.k;
+    float acc = 0.f;
+    for (int j = 0; j < p.k; ++j) {
+        const int pair = t * p.k + j;
+        const int e = p.ids[pair];
+        if (e >= 0 && e < p.E) acc = fmaf(p.w[pair], p.ypart[(size_t)pair * p.H + n], acc);
+    }
+    if (p.has_shared) acc += p.ypart[(size_t)(P + t) * p.H + n];
+    p.out[(size_t)t * p.H + n] = (uint16_t)f32_to_bf16_rne(acc);
+}
 
 size_t decode_workspace_bytes(int T, int k, int H, int I);
 int launch_decode(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
                   const int32_t *, const uint8_t *, uint16_t *, void *, hipStream_t);
 
-size_t prefill_workspace_bytes(int T, int k, int H, int I, int E) { (void)E; return decode_workspace_bytes(T, k, H, I); }
+size_t prefill_workspace_bytes(int T, int k, int H, int I, int E)
+{
+    (void)E;
+    const size_t rows = (size_t)T * k + T;
+    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    return al(rows * I * 2) + al(rows * H * 4);
+}
 
 int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const int32_t *ids, const float *w,
                    const int32_t *offsets, const int32_t *sorted, const uint8_t *gate, uint16_t *out, void *ws,
                    hipStream_t stream)
 {
-    if ((int64_t)T * k + 1 > 65535) return fail(MOET_EUNSUPPORTED, "T*top_k too large for this build");
-    return launch_decode(L, x, T, k, ids, w, offsets, sorted, gate, out, ws, stream);
+    if (L->n_slots > 0 && gate != nullptr) {
+        // the FP4 delta on gated tokens is fused only into the GEMV kernels
+        if ((int64_t)T * k + 1 > 65535) return fail(MOET_EUNSUPPORTED, "delta cache with T*top_k > 65534 is not supported");
+        return launch_decode(L, x, T, k, ids, w, offsets, sorted, gate, out, ws, stream);
+    }
+    PrefillParams p;
+    p.x = x;
+    p.T = T;
+    p.k = k;
+    p.H = L->H;
+    p.I = L->I;
+    p.E = L->E;
+    p.ids = ids;
+    p.w = w;
+    p.offsets = offsets;
+    p.sorted = sorted;
+    p.w13 = L->w13;
+    p.w2 = L->w2;
+    p.has_shared = L->has_shared ? 1 : 0;
+    p.sh13 = L->shared13;
+    p.sh2 = L->shared2;
+    p.swiglu_limit = L->swiglu_limit;
+    const size_t rows = (size_t)T * k + T;
+    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    char *base = static_cast<char *>(ws);
+    p.h = reinterpret_cast<uint16_t *>(base);
+    p.ypart = reinterpret_cast<float *>(base + al(rows * L->I * 2));
+    p.out = out;
+    const int P = T * k;
+    const int mslots = (P + kPM - 1) / kPM + L->E + (p.has_shared ? (T + kPM - 1) / kPM : 0);
+    p.n_mslots = mslots;
+    const int ms8 = (mslots + 7) / 8 * 8;
+    if (L->I % 128 || L->H % 256) return fail(MOET_EUNSUPPORTED, "prefill needs I %% 128 == 0 and H %% 256 == 0");
+    p.n_ntiles = L->I / 128;
+    timing_start(stream);
+    hipLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
+    timing_stop(stream);
+    int rc = check_launch("fc1_prefill_kernel");
+    if (rc != MOET_OK) return rc;
+    p.n_ntiles = L->H / 256;
+    hipLaunchKernelGGL(fc2_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
+    rc = check_launch("fc2_prefill_kernel");
+    if (rc != MOET_OK) return rc;
+    hipLaunchKernelGGL(combine_prefill_kernel, dim3((L->H + 255) / 256, T), dim3(256), 0, stream, p);
+    return check_launch("combine_prefill_kernel");
 }
 
 }  // namespace moet

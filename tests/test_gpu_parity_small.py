@@ -167,6 +167,11 @@ def _run_forward_case(cfg, seed=0, check_determinism=False):
     dict(swiglu_limit=0.004, T=6),
     dict(H=384, I=256, E=16, k=4, T=9, n_resident=5, n_flagged=4),
     dict(T=700, k=2, E=8, n_resident=2, n_flagged=300),
+    # batches above 1024 (token, expert) pairs without a delta run the MFMA grouped GEMM
+    dict(T=300, E=16, k=8, score=synth.SIGMOID),
+    dict(T=700, E=8, k=2, shared=True),
+    dict(T=200, E=64, k=8, H=512, I=256, score=synth.SIGMOID, swiglu_limit=0.01),
+    dict(T=1500, E=4, k=1),
 ])
 def test_forward_small(case):
     cfg = _small_cfg(**case)

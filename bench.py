@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published peak
 W2_BYTES_PER_WEIGHT = 2.25 / 8.0
 FP4_BYTES_PER_WEIGHT = 4.5 / 8.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, AMD published
 
 
 def parse():
@@ -43,8 +44,67 @@ def parse():
     ap.add_argument("--inputs", type=int, default=8, help="input sets in the rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk (T=4096) measurement")
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (HBM counter calibration)")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="print per-kernel means of a rocprofv3 counter_collection.csv and exit (no GPU use)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy(reps=10):
+    """A plain elementwise kernel of known traffic: reads COPY_BYTES, writes COPY_BYTES per launch."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "torch.mul fp32", "read_bytes": COPY_BYTES, "write_bytes": COPY_BYTES,
+                      "launches": reps}), flush=True)
+
+
+def summarize_counters(path):
+    """Mean counter value per dispatch, per kernel name, of a rocprofv3 --pmc CSV."""
+    import csv
+    acc = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            key = (row["Kernel_Name"], row["Counter_Name"])
+            a = acc.setdefault(key, [0, 0.0])
+            a[0] += 1
+            a[1] += float(row["Counter_Value"])
+    for (name, ctr), (n, tot) in sorted(acc.items(), key=lambda kv: -kv[1][1]):
+        print(f"{ctr:12s} dispatches {n:6d} mean {tot / n:14.1f}  {name[:110]}")
+
+
+def counted_traffic():
+    """HBM bytes per launch of the gate/up decode kernel from the committed counter summary, if that summary
+    was taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "fc1_decode_kernel_hbm_counters_T3_H7168_I2048_E256.md")
+    src = os.path.join(ROOT, "bit_moe_expert_nvfp4_amd", "csrc")
+    try:
+        h = hashlib.sha256()
+        for name in ("moe_decode.hip", "moet_common.h"):
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(f.read())
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and line.startswith("- "):
+                    k, v = line[2:].split(":", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("kernel source sha256") != h.hexdigest():
+            return None
+        return float(fields["HBM bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def step_bytes(cfg, ids_np, flags_np, soe_np):
@@ -70,7 +130,7 @@ def step_bytes(cfg, ids_np, flags_np, soe_np):
 
 
 def cpu_baseline(cfg, src, x, lg, seed):
-    """Time the float64 oracle (route + one token's expert FFNs) on the host cores."""
+    """Time the float64 oracle (route + the layer output of every token) on the host cores."""
     import numpy as np
     from oracle import formats as OF
     from oracle import requant as OR
@@ -82,8 +142,7 @@ def cpu_baseline(cfg, src, x, lg, seed):
 
     lg_np = npy(lg)
     ids, w, _, _ = ORT.route(lg_np, cfg.k, cfg.score, cfg.renormalize)
-    tok = 0
-    experts = sorted(set(int(e) for e in ids[tok]))
+    experts = sorted(set(int(e) for e in ids.reshape(-1)))
     # load-time part (not timed): the oracle's own requantisation of the touched experts
     planes = {}
 
@@ -99,20 +158,92 @@ def cpu_baseline(cfg, src, x, lg, seed):
         return OR.dequant_2bit(*p)
     t0 = time.perf_counter()
     ids2, w2, _, _ = ORT.route(lg_np, cfg.k, cfg.score, cfg.renormalize)
-    out = OFF.moe_forward(xb, ids2, w2, lambda e: tuple(dq(p) for p in planes[e]),
-                          tuple(dq(p) for p in shared) if shared else None, tokens=[tok])
+    OFF.moe_forward(xb, ids2, w2, lambda e: tuple(dq(p) for p in planes[e]),
+                    tuple(dq(p) for p in shared) if shared else None)
     dt = time.perf_counter() - t0
     n = len(experts) + (1 if cfg.shared else 0)
-    nbytes = n * 3 * cfg.I * cfg.H * W2_BYTES_PER_WEIGHT
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"routing of all {cfg.T} tokens + the layer output of token 0 ({n} experts incl. shared, "
-                      f"{nbytes / 1e6:.1f} MB of 2-bit planes) from the oracle's own requantised planes; "
-                      f"float64 numpy, {dt:.2f} s",
+    nbytes = n * 3 * cfg.I * cfg.H * W2_BYTES_PER_WEIGHT + 2 * cfg.T * cfg.H * 2 + 4 * cfg.T * cfg.E
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"one full step of input set 0: routing and the layer output of all {cfg.T} tokens "
+                      f"({n} distinct experts incl. shared, {nbytes / 1e6:.1f} MB of 2-bit planes, dequantised "
+                      f"and applied in float64 numpy from the oracle's own requantised planes), {dt:.2f} s",
             "seconds": dt}
+
+
+def _blas_threads():
+    """Threads the oracle's numpy BLAS uses on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def prefill_leg(layer, cfg5, steps, seed, dev):
+    """Time route + forward of a prefill chunk (MFMA grouped GEMM path) on one pool layer."""
+    import numpy as np
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet, synth
+
+    T, k = cfg5.T, cfg5.k
+    x = synth.make_activations(T, cfg5.H, seed, tag="prefill_x", device=dev)
+    lg = synth.make_logits(cfg5, seed, tag="prefill_logits", device=dev)
+    ws = moet.alloc_workspace(layer, T, k, dev)
+    out = torch.empty((T, cfg5.H), dtype=torch.bfloat16, device=dev)
+    ro = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+          torch.empty((cfg5.E + 1,), dtype=torch.int32, device=dev), torch.empty((T * k,), dtype=torch.int32, device=dev))
+
+    def step():
+        ids, w, offs, pairs = moet.route(lg, k, cfg5.score, cfg5.renormalize, out=ro)
+        moet.moe_forward(layer, x, ids, w, offs, pairs, None, out=out, workspace=ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        moet.set_timing_events(*ev[i])
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    moet.set_timing_events(None, None)
+    ms = t0.elapsed_time(t1) / steps
+    fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    P = T * k
+    fl_fc1 = 2.0 * P * 2 * cfg5.I * cfg5.H
+    fl = fl_fc1 + 2.0 * P * cfg5.H * cfg5.I
+    peak = MFMA_BF16_PEAK_TFLOPS
+    return {
+        "workload": f"prefill chunk: T={T} H={cfg5.H} I={cfg5.I} E={cfg5.E} top{k} sigmoid+renorm, "
+                    f"N(0,1) logits, no shared expert, 2-bit planes -> bf16 MFMA grouped GEMM",
+        "us_per_layer": round(ms * 1e3, 1),
+        "tokens_per_s": round(T / (ms / 1e3), 1),
+        "useful_tflops": round(fl / (ms / 1e3) / 1e12, 1),
+        "mfma_frac": round(fl / (ms / 1e3) / 1e12 / peak, 4),
+        "roofline": {"kernel": "fc1_prefill_kernel (gate/up grouped GEMM + SwiGLU)", "bound": "mfma",
+                     "achieved": round(fl_fc1 / (fc1_ms / 1e3) / 1e12, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(fl_fc1 / (fc1_ms / 1e3) / 1e12 / peak, 4), "traffic": None,
+                     "avg_launch_us": round(fc1_ms * 1e3, 1), "algorithmic_flop_per_launch": fl_fc1},
+    }
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not sharded in this build.",
               file=sys.stderr)
@@ -265,11 +396,16 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(),
             "avg_launch_us": round(1e3 * float(np.mean(fc1_ms)), 2),
             "algorithmic_bytes_per_launch": round(fc1_bytes / K),
         },
     }
+    if not args.no_prefill:
+        print("[bench] timing the prefill chunk", file=sys.stderr, flush=True)
+        import dataclasses
+        pl = dataclasses.replace(layers[0], shared13=None, shared2=None)
+        result["prefill"] = prefill_leg(pl, synth.CONFIGS[5], args.prefill_steps, args.seed, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
         cb = cpu_baseline(cfg, srcs[0], xs[0], lgs[0], args.seed)

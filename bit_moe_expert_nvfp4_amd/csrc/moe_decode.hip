@@ -14,8 +14,10 @@
 // loads into SGPRs, one 64-k chunk per wait, because scalar loads return out
 // of order and every wait drains all of them.  Weights of the next group are
 // loaded into a second register set while the current group is decoded
-// (ping-pong, no copies).  Decoding costs about 1.5 VALU operations per
-// weight, about as long as streaming the planes from HBM, so work is cut
+// (ping-pong, no copies).  A code word of 16 weights becomes 8 bf16 pairs
+// with 3 and-or/shift operations and 8 FP4 -> bf16 conversions, so a weight
+// costs about 0.7 VALU operations to decode plus one dot2 per pair and token;
+// that is about as long as streaming the planes from HBM, so work is cut
 // into many small workgroups for load balance.
 //
 //  fc1: grid (I/32 half-tiles, slots), 4 wavefronts splitting K.  Lanes 0-31
@@ -123,7 +125,6 @@ __device__ __forceinline__ void slot_token(const DecodeParams &p, const SlotInfo
 
 // ---------------------------------------------------------------------------
 // 2-bit decode constants: the and-mask lives in an SGPR, the or-constant in a VGPR
-// ---------------------------------------------------------------------------
 struct W2Consts {
     uint32_t sm, vb;
 };
@@ -131,25 +132,26 @@ struct W2Consts {
 __device__ __forceinline__ W2Consts w2_consts()
 {
     W2Consts c;
-    c.sm = __builtin_amdgcn_readfirstlane(0x81008100u);
-    c.vb = 0x3E803E80u;
+    c.sm = __builtin_amdgcn_readfirstlane(kW2Mask);
+    c.vb = kW2Or;
     asm volatile("" : "+v"(c.vb));
     return c;
 }
 
-// bs[t] += sum over one 16-weight word of (level/4) * x, x pairs x[t][o .. o+7]
+// bs[t] += sum over one 16-weight word of level * x, x pairs x[t][o .. o+7]
 template <int TT>
 __device__ __forceinline__ void w2_word(uint32_t w, const uint32_t (*x)[32], int o, float bs[TT], W2Consts k)
 {
+    const uint32_t fa = w2_fp4_lo(w, k.sm, k.vb), fb = w2_fp4_hi(w, k.sm, k.vb);
     uint32_t pr[8];
-    pr[0] = w2_pair<0>(w, k.sm, k.vb);
-    pr[1] = w2_pair<1>(w, k.sm, k.vb);
-    pr[2] = w2_pair<2>(w, k.sm, k.vb);
-    pr[3] = w2_pair<3>(w, k.sm, k.vb);
-    pr[4] = w2_pair<4>(w, k.sm, k.vb);
-    pr[5] = w2_pair<5>(w, k.sm, k.vb);
-    pr[6] = w2_pair<6>(w, k.sm, k.vb);
-    pr[7] = w2_pair<7>(w, k.sm, k.vb);
+    pr[0] = fp4_pair<0>(fa);
+    pr[1] = fp4_pair<1>(fa);
+    pr[2] = fp4_pair<2>(fa);
+    pr[3] = fp4_pair<3>(fa);
+    pr[4] = fp4_pair<0>(fb);
+    pr[5] = fp4_pair<1>(fb);
+    pr[6] = fp4_pair<2>(fb);
+    pr[7] = fp4_pair<3>(fb);
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -220,7 +222,7 @@ __device__ __forceinline__ void w2_group(const W2Buf &B, int g, const cu32 *cons
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// acc[t] += sum over groups [g0, g1) of (level/4) * scale * x for this lane's row
+// acc[t] += sum over groups [g0, g1) of level * scale * x for this lane's row
 template <int TT>
 __device__ __forceinline__ void w2_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
 {
@@ -286,7 +288,7 @@ constexpr int kW1 = 4;     // wavefronts per fc1 workgroup (K split)
 constexpr int kW2 = 2;     // wavefronts per fc2 workgroup (K split)
 
 // One pass over up to kTT tokens: this lane's partial pre-activation per token
-// (2-bit part scaled by 4*s2 plus the delta part scaled by ds2 for flagged tokens).
+// (2-bit part scaled by s2 plus the delta part scaled by ds2 for flagged tokens).
 __device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2, int K, int g0, int g1,
                                           const cu32 *const xr[kTT], const bool flag[kTT], int n, float part[kTT])
 {
@@ -302,7 +304,7 @@ __device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2,
         if (any_flag) fp4_gemv<2>(L, K, g0, g1, xr, dacc);
     }
 #pragma unroll
-    for (int t = 0; t < kTT; ++t) part[t] = 4.0f * s2 * acc[t] + ((any_flag && flag[t]) ? ds2 * dacc[t] : 0.f);
+    for (int t = 0; t < kTT; ++t) part[t] = s2 * acc[t] + ((any_flag && flag[t]) ? ds2 * dacc[t] : 0.f);
 }
 
 __global__ __launch_bounds__(64 * kW1) void fc1_decode_kernel(DecodeParams p)

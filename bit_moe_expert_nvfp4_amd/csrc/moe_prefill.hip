@@ -20,9 +20,10 @@
 //    travel by LDS-DMA into a 3-stage ring, so two steps are in flight while
 //    one is computed and no registers are spent on prefetching.
 //  * B (weights): each lane dequantises the 8 k-values its MFMA B fragment
-//    needs from the staged 2-bit words into registers: bf16(level * e4m3
-//    block scale) is exact (4 significant bits), built from the bf16 scale by
-//    adding 2 to the exponent for magnitude 4 and setting the sign bit.
+//    needs from the staged 2-bit words into registers: one and-or makes their
+//    e2m1 image, four FP4 -> bf16 conversions give the levels, and a packed
+//    16-bit add of the scale's bf16 bits (less those of 1.0) multiplies by
+//    the e4m3 block scale; bf16(level * scale) is exact (4 significant bits).
 //    The per-tensor scale2 is applied in the epilogue.
 //  * gate/up kernel: wave w owns 32 gate columns and the same 32 up columns,
 //    so SwiGLU is computed in registers and h = bf16(silu(g) * u) is written
@@ -122,28 +123,36 @@ __device__ __forceinline__ void decode_wg(int id, int n_ntiles, int &ms, int &nt
     ms = (local / n_ntiles) * 8 + xcd;
 }
 
-// bf16 pair of (level * scale) for pair bits already rotated to 8/15/24/31
-__device__ __forceinline__ uint32_t deq_pair(uint32_t rotated, uint32_t mask, uint32_t spair)
-{
-    return (rotated & mask) + spair;
-}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// per (row, 32-k block) dequant constants from a scale byte
-__device__ __forceinline__ void block_consts(uint32_t scale_word, int byte, uint32_t &mask, uint32_t &spair)
+// per (row, 32-k block) dequant constants from a scale byte: the and-mask and
+// or-constant that turn a code word into e2m1 values (both 0 for a zero scale,
+// which then yields +0), and the per-half bf16 bit offset that multiplies a
+// level +-1 / +-4 by the scale: level and scale are exact bf16 with the level's
+// mantissa 0, so adding bits(scale) - bits(1.0) to the level's bits adds the
+// exponents and copies the scale's mantissa.
+__device__ __forceinline__ void block_consts(uint32_t scale_word, int byte, uint32_t &mask, uint32_t &orc,
+                                             uint32_t &sadd)
 {
     const uint32_t b = (scale_word >> (8 * byte)) & 0xFFu;
     const float f = __builtin_amdgcn_cvt_f32_fp8(b, 0);
-    const uint32_t hb = __float_as_uint(f) >> 16;   // exact bf16 of the e4m3 scale
-    spair = hb | (hb << 16);
-    mask = b ? 0x81008100u : 0u;
+    const uint32_t d = ((__float_as_uint(f) >> 16) - 0x3F80u) & 0xFFFFu;
+    sadd = b ? (d | (d << 16)) : 0u;
+    mask = b ? kW2Mask : 0u;
+    orc = b ? kW2Or : 0u;
 }
 
-// 8 bf16 of one row for one MFMA k-step: word w (16 k), this lane's half h (k 8h .. 8h+7)
-__device__ __forceinline__ bf16x8 deq_frag(uint32_t w, int rbase, uint32_t mask, uint32_t spair)
+// 8 bf16 of one row for one MFMA k-step: elements 8h .. 8h+7 of code word w
+// (sh = 2h selects the bit pair of each nibble), times the block scale
+__device__ __forceinline__ bf16x8 deq_frag(uint32_t w, uint32_t sh, uint32_t mask, uint32_t orc, uint32_t sadd)
 {
+    const uint32_t f = and_or_v(w << sh, mask, orc);
+    const u16x2 a = __builtin_bit_cast(u16x2, sadd);
     uint32_t q[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) q[j] = deq_pair(__builtin_amdgcn_alignbit(w, w, rbase + 2 * j), mask, spair);
+    q[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, fp4_pair<0>(f)) + a);
+    q[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, fp4_pair<1>(f)) + a);
+    q[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, fp4_pair<2>(f)) + a);
+    q[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, fp4_pair<3>(f)) + a);
     return __builtin_bit_cast(bf16x8, make_uint4(q[0], q[1], q[2], q[3]));
 }
 
@@ -210,7 +219,7 @@ __device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, c
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;                 // k half of the MFMA fragment
-    const int rbase = h ? 0 : 24;            // rotation of pair 4h
+    const uint32_t sh = 2 * h;               // selects elements 8h .. 8h+7 of a code word
     const int nsteps = src.K / kPK;
 #pragma unroll
     for (int st = 0; st < kPS - 1; ++st)
@@ -225,13 +234,13 @@ __device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, c
         const uint8_t *bT = stg + kStageA;
         const uint8_t *sT = stg + kStageA + kStageB;
         uint4 bw[2];
-        uint32_t mask[2][2], spair[2][2];
+        uint32_t mask[2][2], orc[2][2], sadd[2][2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             bw[nb] = *reinterpret_cast<const uint4 *>(bT + brow[nb] * 16);
             const uint32_t sw = *reinterpret_cast<const uint32_t *>(sT + brow[nb] * 4);
-            block_consts(sw, 2 * (s & 1) + 0, mask[nb][0], spair[nb][0]);
-            block_consts(sw, 2 * (s & 1) + 1, mask[nb][1], spair[nb][1]);
+            block_consts(sw, 2 * (s & 1) + 0, mask[nb][0], orc[nb][0], sadd[nb][0]);
+            block_consts(sw, 2 * (s & 1) + 1, mask[nb][1], orc[nb][1], sadd[nb][1]);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {   // MFMA k-steps of 16
@@ -239,7 +248,7 @@ __device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, c
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
                 const uint32_t wv = (q == 0) ? bw[nb].x : (q == 1) ? bw[nb].y : (q == 2) ? bw[nb].z : bw[nb].w;
-                bfr[nb] = deq_frag(wv, rbase, mask[nb][q >> 1], spair[nb][q >> 1]);
+                bfr[nb] = deq_frag(wv, sh, mask[nb][q >> 1], orc[nb][q >> 1], sadd[nb][q >> 1]);
             }
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {

@@ -43,13 +43,15 @@ __device__ __forceinline__ int e4m3_x512(int t)
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------------------
-// 2-bit decode.  A word holds 16 codes as 8 (lo, hi) pairs; pair i is turned
-// into two bf16 values equal to level/4 by one rotation and one and-or: after
-// rotating right by (2i - 8) mod 32 the pair's magnitude bits sit at bf16
-// exponent bit 8 / 24 and its sign bits at 15 / 31; or-ing 0.25 (0x3E80) into
-// both halves gives +-0.25 (m = 0) or +-1.0 (m = 1).
+// 2-bit decode.  Nibble j of a code word holds element j in bits 2-3 and
+// element j + 8 in bits 0-1, each as (s, m) with m the lower bit.  Masking
+// one bit pair per nibble and or-ing 0b0010 into the rest gives an FP4 (e2m1)
+// nibble s|m|1|0 = +-1 (m = 0) or +-4 (m = 1), so one and-or turns eight
+// codes into eight e2m1 values, and the hardware FP4 -> bf16 conversion then
+// makes one bf16 pair per instruction.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t rotr(uint32_t w, int r) { return __builtin_amdgcn_alignbit(w, w, r); }
+constexpr uint32_t kW2Mask = 0xCCCCCCCCu;   // bits 2-3 of every nibble
+constexpr uint32_t kW2Or = 0x22222222u;     // e2m1 exponent low bit
 
 // v_and_or_b32 with the mask in an SGPR and the or-constant in a VGPR (gfx9 VOP3
 // takes no literal operands, and the compiler would otherwise emit and + or).
@@ -60,13 +62,24 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t smask, uint32_t 
     return r;
 }
 
-template <int I>
-__device__ __forceinline__ uint32_t w2_pair(uint32_t w, uint32_t smask, uint32_t vbase)
+// the same with a per-lane mask
+__device__ __forceinline__ uint32_t and_or_v(uint32_t x, uint32_t vmask, uint32_t vbase)
 {
-    constexpr int r = (2 * I - 8) & 31;
-    uint32_t v = (r == 0) ? w : rotr(w, r);
-    return and_or(v, smask, vbase);
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(vmask), "v"(vbase));
+    return r;
 }
+
+// FP4 (e2m1) byte `B` of a word -> two bf16 (low nibble first), exact
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+}
+
+// e2m1 image of elements 0..7 (lo) or 8..15 (hi) of a 2-bit code word
+__device__ __forceinline__ uint32_t w2_fp4_lo(uint32_t w, uint32_t smask, uint32_t vbase) { return and_or(w, smask, vbase); }
+__device__ __forceinline__ uint32_t w2_fp4_hi(uint32_t w, uint32_t smask, uint32_t vbase) { return and_or(w << 2, smask, vbase); }
 
 // Wave-uniform read-only data (activations) is read through the constant
 // address space so that uniform addresses become scalar loads into SGPRs.
@@ -76,13 +89,6 @@ __device__ __forceinline__ const cu32 *as_const(const void *p) { return (const c
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
 {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-// FP4 (e2m1) byte `B` of a word -> two bf16 (low nibble first), exact
-template <int B>
-__device__ __forceinline__ uint32_t fp4_pair(uint32_t w)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
 }
 
 // ---------------------------------------------------------------------------

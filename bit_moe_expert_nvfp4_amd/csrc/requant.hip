@@ -55,9 +55,10 @@ __device__ __forceinline__ int mag2_of(int L)  // 2*|e2m1| for magnitude code L 
     return L < 2 ? L : ((2 + (L & 1)) << ((L >> 1) - 1));
 }
 
-// bit positions of element e (0..15) of a 2-bit word
-__device__ __forceinline__ int mbit(int e) { return 2 * (e >> 1) + ((e & 1) ? 16 : 0); }
-__device__ __forceinline__ int sbit(int e) { return (2 * (e >> 1) + ((e & 1) ? 23 : 7)) & 31; }
+// bit positions of element e (0..15) of a 2-bit word: nibble e%8, upper bit
+// pair for e < 8, lower pair for e >= 8 (m below s)
+__device__ __forceinline__ int mbit(int e) { return 4 * (e & 7) + ((e & 8) ? 0 : 2); }
+__device__ __forceinline__ int sbit(int e) { return mbit(e) + 1; }
 
 __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales,

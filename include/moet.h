@@ -43,9 +43,10 @@
  *    low nibble; block scales e4m3fn uint8 [N][K/16]; per-tensor scale_2 fp32.
  *  2-bit planes ("W2"): rows are grouped in tiles of 64;
  *    codes uint32 word index ((n/64 * K/64 + k/64) * 64 + n%64) * 4 + (k%64)/16;
- *    inside a word the element e = k%16 belongs to pair i = e/2 (even e = lo,
- *    odd e = hi) and its code c = (s<<1)|m (levels 0:+1 1:+4 2:-1 3:-4) sits at
- *    m_lo: bit 2i, s_lo: bit (2i+7)%32, m_hi: bit 2i+16, s_hi: bit (2i+23)%32;
+ *    inside a word, element e = k%16 has code c = (s<<1)|m (levels 0:+1 1:+4
+ *    2:-1 3:-4) with m at bit 4e+2 and s at bit 4e+3 for e < 8, and m at bit
+ *    4(e-8), s at bit 4(e-8)+1 for e >= 8 (nibble j: element j in bits 2-3,
+ *    element j+8 in bits 0-1);
  *    block scales e4m3fn, one per 32 along k, byte index
  *    ((n/64 * K/128 + k/128) * 64 + n%64) * 4 + (k%128)/32;
  *    per-tensor scale2 fp32.  Weight = level * e4m3(scale) * scale2.

@@ -8,10 +8,11 @@ stored in row tiles of 64 rows:
 
 2-bit codes, uint32 words:
     word((n, k)) = ((n//64 * K/64 + k//64) * 64 + n%64) * 4 + (k%64)//16
-  inside a word the 16 elements e = k%16 form pairs i = e//2 (lo = even e,
-  hi = odd e); code c = (s<<1)|m is stored as
-    m_lo at bit 2i,  s_lo at bit (2i+7) mod 32,
-    m_hi at bit 2i+16, s_hi at bit (2i+23) mod 32.
+  inside a word, element e = k%16 with code c = (s<<1)|m is stored as
+    e < 8:  m at bit 4e + 2,      s at bit 4e + 3
+    e >= 8: m at bit 4(e-8),      s at bit 4(e-8) + 1
+  i.e. the word's nibble j holds element j in its upper two bits and element
+  j + 8 in its lower two bits.
 2-bit block scales (one e4m3 byte per 32 along K):
     byte((n, b)) = ((n//64 * K/128 + b//4) * 64 + n%64) * 4 + b%4
 FP4 delta codes (two per byte, even k in the low nibble):
@@ -35,9 +36,10 @@ def _bit_positions():
     pm = np.zeros(16, dtype=np.int64)
     ps = np.zeros(16, dtype=np.int64)
     for e in range(16):
-        i, hi = divmod(e, 2)
-        pm[e] = 2 * i + (16 if hi else 0)
-        ps[e] = (2 * i + (23 if hi else 7)) % 32
+        nibble = e % 8
+        low_half = e >= 8
+        pm[e] = 4 * nibble + (0 if low_half else 2)
+        ps[e] = pm[e] + 1
     return pm, ps
 
 

@@ -291,21 +291,31 @@ def test_layout_roundtrip_and_density():
 
 
 def test_layout_bit_positions_hand_example():
-    # a single code 1 (m=1, s=0) at k=0 of row 0 sets bit 0 of word 0; code 2 (s=1)
-    # at k=1 sets bit 23; code 3 at k=10 (pair 5, lo) sets bits 10 and 17
+    # nibble j of a word holds element j in bits 2..3 and element j + 8 in bits 0..1
+    # (m in the lower bit of each pair).  A code 1 (m=1, s=0) at k=0 of row 0 sets
+    # bit 2 of word 0; code 2 (s=1) at k=1 sets bit 7; code 3 at k=10 (nibble 2,
+    # lower pair) sets bits 8 and 9; code 1 at k=15 sets bit 28.
     N, K = 64, 128
     c2 = np.zeros((N, K), dtype=np.uint8)
     c2[0, 0] = 1
     w = L.pack_2bit_codes(c2)
-    assert w[0] == 1 and (w[1:] == 0).all()
+    assert w[0] == 1 << 2 and (w[1:] == 0).all()
     c2[0, 0] = 0
     c2[0, 1] = 2
-    assert L.pack_2bit_codes(c2)[0] == 1 << 23
+    assert L.pack_2bit_codes(c2)[0] == 1 << 7
     c2[0, 1] = 0
     c2[0, 10] = 3
-    assert L.pack_2bit_codes(c2)[0] == (1 << 10) | (1 << 17)
-    # row 1, k = 64 lives in chunk 1: word index (1*64 + 1)*4
+    assert L.pack_2bit_codes(c2)[0] == (1 << 8) | (1 << 9)
     c2[0, 10] = 0
+    c2[0, 15] = 1
+    assert L.pack_2bit_codes(c2)[0] == 1 << 28
+    # k = 16 starts the next word of the same 64-k chunk
+    c2[0, 15] = 0
+    c2[0, 16] = 2
+    w = L.pack_2bit_codes(c2)
+    assert w[1] == 1 << 3 and np.count_nonzero(w) == 1
+    # row 1, k = 64 lives in chunk 1: word index (1*64 + 1)*4
+    c2[0, 16] = 0
     c2[1, 64] = 1
     w = L.pack_2bit_codes(c2)
-    assert w[(1 * 64 + 1) * 4] == 1 and np.count_nonzero(w) == 1
+    assert w[(1 * 64 + 1) * 4] == 1 << 2 and np.count_nonzero(w) == 1

@@ -20,14 +20,19 @@
 // that is about as long as streaming the planes from HBM, so work is cut
 // into many small workgroups for load balance.
 //
-//  fc1: grid (I/32 half-tiles, slots), 4 wavefronts splitting K.  Lanes 0-31
-//       hold 32 gate rows, lanes 32-63 the same 32 up rows, so SwiGLU pairs
-//       lane j with lane j+32 after the cross-wave reduction in LDS.  A slot
-//       is the first sorted pair of an expert (its whole run of tokens) or
-//       the shared expert.  FP4 delta rows are added for flagged tokens of
-//       resident experts.  Writes h = bf16(silu(gate) * up).
-//  fc2: grid (H/64 tiles, slots), 2 wavefronts splitting K; y = W2 h (+ D2 h)
-//       per pair into an fp32 buffer.
+//  fc1: grid (I/32 half-tiles, entries), 4 wavefronts splitting K.  Lanes
+//       0-31 hold 32 gate rows, lanes 32-63 the same 32 up rows, so SwiGLU
+//       pairs lane j with lane j+32 after the cross-wave reduction in LDS.  An
+//       entry is one pass over up to two tokens of one expert (two
+//       consecutive sorted pairs of its run, or two shared-expert tokens), so
+//       every workgroup does the same work; the shared expert's entries come
+//       first in the grid so the hardware dispatches them first.  FP4 delta
+//       rows are added for flagged tokens of resident experts.  Writes
+//       h = bf16(silu(gate) * up).
+//  fc2: grid (H/64 tiles, entries), 2 wavefronts splitting K; y = W2 h
+//       (+ D2 h) per pair into an fp32 buffer.
+//  Both run at 8 wavefronts per SIMD (<= 64 VGPRs) so the whole grid of a
+//  decode step is resident at once.
 //  combine: out = bf16(sum_j w_tj * y_(t,j) + y_shared) in slot order:
 //       deterministic, no float atomics.  (A last-workgroup combine inside fc2
 //       needs an agent-scope release per workgroup, which on this chip's
@@ -62,49 +67,62 @@ struct SlotInfo {
     bool shared;
 };
 
-// Slot s is the first sorted pair of expert e iff offsets[e] == s < offsets[e+1];
-// e is the number of experts whose run ends at or before s.  One round of
-// loads over offsets[1..E] (ballot counts), instead of a chain through the
-// permutation and the ids.
+constexpr int kTT = 2;     // tokens per pass (more would cost SGPRs / occupancy)
+
+// Number of grid entries (blockIdx.y) of the GEMV kernels: the shared
+// expert's token groups come first, so that their workgroups are dispatched
+// first, then one entry per sorted pair position.
+__host__ __device__ __forceinline__ int decode_entries(int T, int k, int has_shared)
+{
+    return (has_shared ? (T + kTT - 1) / kTT : 0) + T * k;
+}
+
+// Entry s -> one pass over at most kTT tokens of one expert.  Entries below
+// nsh cover shared-expert tokens [kTT s, kTT s + kTT).  Entry nsh + q covers
+// sorted positions [q, q + kTT) of expert e when q starts a group of kTT
+// inside e's run [offsets[e], offsets[e+1]); e is the number of experts whose
+// run ends at or before q.  One round of loads over offsets[1..E] (ballot
+// counts) finds it, instead of a chain through the permutation and the ids.
+// Every workgroup therefore does exactly one pass of equal length.
 __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotInfo &si)
 {
     const int P = p.T * p.k;
-    if (s < P) {
-        const int lane = threadIdx.x & 63;
-        int v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int j = 1 + lane + 64 * i;
-            v[i] = (j <= p.E) ? p.offsets[j] : 0x7FFFFFFF;
-        }
-        int e = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) e += __popcll(__ballot(v[i] <= s));
-        e = __builtin_amdgcn_readfirstlane(e);
-        if (e >= p.E) return false;
-        const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
-        if (o0 != s || o1 <= s) return false;
-        si.e = e;
-        si.pbeg = s;
-        si.pend = min(o1, P);
-        si.shared = false;
-        int ds = -1;
-        if (p.n_slots > 0 && p.gate != nullptr) {
-            ds = p.slot_of_expert[e];
-            if (ds >= p.n_slots) ds = -1;
-        }
-        si.dslot = ds;
-        return true;
-    }
-    if (p.has_shared && s == P) {
+    const int nsh = p.has_shared ? (p.T + kTT - 1) / kTT : 0;
+    if (s < nsh) {
         si.e = -1;
-        si.pbeg = 0;
-        si.pend = p.T;
+        si.pbeg = kTT * s;
+        si.pend = min(kTT * s + kTT, p.T);
         si.shared = true;
         si.dslot = -1;
         return true;
     }
-    return false;
+    const int q = s - nsh;
+    if (q >= P) return false;
+    const int lane = threadIdx.x & 63;
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int j = 1 + lane + 64 * i;
+        v[i] = (j <= p.E) ? p.offsets[j] : 0x7FFFFFFF;
+    }
+    int e = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e += __popcll(__ballot(v[i] <= q));
+    e = __builtin_amdgcn_readfirstlane(e);
+    if (e >= p.E) return false;
+    const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
+    if (q < o0 || q >= o1 || (q - o0) % kTT != 0) return false;
+    si.e = e;
+    si.pbeg = q;
+    si.pend = min(min(q + kTT, o1), P);
+    si.shared = false;
+    int ds = -1;
+    if (p.n_slots > 0 && p.gate != nullptr) {
+        ds = p.slot_of_expert[e];
+        if (ds >= p.n_slots) ds = -1;
+    }
+    si.dslot = ds;
+    return true;
 }
 
 // token / h-row / delta flag of entry i of a slot's run
@@ -139,8 +157,8 @@ __device__ __forceinline__ W2Consts w2_consts()
 }
 
 // bs[t] += sum over one 16-weight word of level * x, x pairs x[t][o .. o+7]
-template <int TT>
-__device__ __forceinline__ void w2_word(uint32_t w, const uint32_t (*x)[32], int o, float bs[TT], W2Consts k)
+template <int TT, typename XT>
+__device__ __forceinline__ void w2_word(uint32_t w, const XT *x, int o, float bs[TT], W2Consts k)
 {
     const uint32_t fa = w2_fp4_lo(w, k.sm, k.vb), fb = w2_fp4_hi(w, k.sm, k.vb);
     uint32_t pr[8];
@@ -189,54 +207,106 @@ __device__ __forceinline__ void load_x_chunk(const cu32 *const xr[TT], int kp, u
         for (int i = 0; i < 32; ++i) x[t][i] = xr[t][kp + i];
 }
 
-// 64 k of one lane row: words c.x..c.w (two 32-k blocks), block scales B0, B0+1 of sc
-template <int TT, int B0>
-__device__ __forceinline__ void w2_chunk(const uint4 &c, uint32_t sc, const uint32_t (*x)[32], float acc[TT], W2Consts k)
+// Activations of one code word (16 k = 8 bf16 pairs) of one token travel by
+// one scalar load into SGPRs.  The loads are issued from inline asm one word
+// ahead and waited explicitly (the wait names the buffer, so no use of it can
+// move above the wait): scalar loads return out of order and every wait
+// drains all of them, so the compiler would otherwise wait for the
+// prefetched word together with the current one.  Every prefetch issued is
+// waited before the loop ends.
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// `sum` is tied to the load so that the arithmetic that follows in program
+// order (which updates it) cannot be hoisted above the load's issue
+__device__ __forceinline__ void xload(u32x8 &v, const cu32 *p, float &sum)
 {
-    float bs[TT];
+    asm volatile("s_load_dwordx8 %0, %2, 0x0" : "=s"(v), "+v"(sum) : "s"(p));
+}
+
+// The wait also names the running sums, so the previous word's arithmetic
+// stays above it and the prefetch it follows has that long to land.
+template <int TT>
+__device__ __forceinline__ void xwait(u32x8 (&v)[TT], float bs[TT], float acc[TT])
+{
+    if constexpr (TT == 1)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v[0]), "+v"(bs[0]), "+v"(acc[0]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v[0]), "+s"(v[1]), "+v"(bs[0]), "+v"(bs[1]), "+v"(acc[0]),
+                     "+v"(acc[1]));
+}
+
+// word j (0..7) of group g: wait for its activations (in `cur`), prefetch word
+// j + 1 (clamped to the wave's last word `wl`) into `nxt`, then decode and dot
+template <int TT>
+__device__ __forceinline__ void w2_step(uint32_t w, int word, const cu32 *const xr[TT], int wl, u32x8 (&cur)[TT],
+                                        u32x8 (&nxt)[TT], float bs[TT], float acc[TT], W2Consts k)
+{
+    xwait<TT>(cur, bs, acc);
 #pragma unroll
-    for (int t = 0; t < TT; ++t) bs[t] = 0.f;
-    w2_word<TT>(c.x, x, 0, bs, k);
-    w2_word<TT>(c.y, x, 8, bs, k);
-    const float s0 = e4m3_byte<B0>(sc);
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = fmaf(bs[t], s0, acc[t]);
-#pragma unroll
-    for (int t = 0; t < TT; ++t) bs[t] = 0.f;
-    w2_word<TT>(c.z, x, 16, bs, k);
-    w2_word<TT>(c.w, x, 24, bs, k);
-    const float s1 = e4m3_byte<B0 + 1>(sc);
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = fmaf(bs[t], s1, acc[t]);
+    for (int t = 0; t < TT; ++t) xload(nxt[t], xr[t] + 8 * min(word + 1, wl), bs[t]);
+    w2_word<TT>(w, cur, 0, bs, k);
 }
 
 template <int TT>
-__device__ __forceinline__ void w2_group(const W2Buf &B, int g, const cu32 *const xr[TT], float acc[TT], W2Consts k)
+__device__ __forceinline__ void block_done(float bs[TT], float s, float acc[TT])
 {
-    uint32_t x[TT][32];
-    load_x_chunk<TT>(xr, 64 * g, x);
-    w2_chunk<TT, 0>(B.c0, B.sc, x, acc, k);
-    __builtin_amdgcn_sched_barrier(0);  // the next chunk's activations start here
-    load_x_chunk<TT>(xr, 64 * g + 32, x);
-    w2_chunk<TT, 2>(B.c1, B.sc, x, acc, k);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        acc[t] = fmaf(bs[t], s, acc[t]);
+        bs[t] = 0.f;
+    }
 }
 
-// acc[t] += sum over groups [g0, g1) of level * scale * x for this lane's row
+// the 8 code words of group g; word buffers alternate xa (even words), xb (odd)
+template <int TT>
+__device__ __forceinline__ void w2_group(const W2Buf &B, int g, const cu32 *const xr[TT], int wl, u32x8 (&xa)[TT],
+                                         u32x8 (&xb)[TT], float acc[TT], W2Consts k)
+{
+    const int w0 = 8 * g;
+    float bs[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) bs[t] = 0.f;
+    w2_step<TT>(B.c0.x, w0 + 0, xr, wl, xa, xb, bs, acc, k);
+    w2_step<TT>(B.c0.y, w0 + 1, xr, wl, xb, xa, bs, acc, k);
+    block_done<TT>(bs, e4m3_byte<0>(B.sc), acc);
+    w2_step<TT>(B.c0.z, w0 + 2, xr, wl, xa, xb, bs, acc, k);
+    w2_step<TT>(B.c0.w, w0 + 3, xr, wl, xb, xa, bs, acc, k);
+    block_done<TT>(bs, e4m3_byte<1>(B.sc), acc);
+    w2_step<TT>(B.c1.x, w0 + 4, xr, wl, xa, xb, bs, acc, k);
+    w2_step<TT>(B.c1.y, w0 + 5, xr, wl, xb, xa, bs, acc, k);
+    block_done<TT>(bs, e4m3_byte<2>(B.sc), acc);
+    w2_step<TT>(B.c1.z, w0 + 6, xr, wl, xa, xb, bs, acc, k);
+    w2_step<TT>(B.c1.w, w0 + 7, xr, wl, xb, xa, bs, acc, k);
+    block_done<TT>(bs, e4m3_byte<3>(B.sc), acc);
+}
+
+// acc[t] += sum over groups [g0, g1) of level * scale * x for this lane's row.
+// Weights of the next group are loaded while the current one is computed; the
+// load is issued on every iteration (the last one re-loads the final group) so
+// that the outstanding-load count, and with it the compiler's wait, is the
+// same on every path.  xr[] must be wave-uniform.
 template <int TT>
 __device__ __forceinline__ void w2_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
 {
     if (g0 >= g1) return;
     const W2Consts kc = w2_consts();
+    const int wl = 8 * g1 - 1;
     W2Buf A, B;
+    u32x8 xa[TT], xb[TT];
     w2_load(A, L, K, g0);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) xload(xa[t], xr[t] + 8 * (8 * g0), acc[t]);
     for (int g = g0; g < g1; g += 2) {
-        if (g + 1 < g1) w2_load(B, L, K, g + 1);
-        w2_group<TT>(A, g, xr, acc, kc);
+        w2_load(B, L, K, min(g + 1, g1 - 1));
+        w2_group<TT>(A, g, xr, wl, xa, xb, acc, kc);
         if (g + 1 >= g1) break;
-        if (g + 2 < g1) w2_load(A, L, K, g + 2);
-        w2_group<TT>(B, g + 1, xr, acc, kc);
+        w2_load(A, L, K, min(g + 2, g1 - 1));
+        w2_group<TT>(B, g + 1, xr, wl, xa, xb, acc, kc);
     }
+    float bs[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) bs[t] = 0.f;
+    xwait<TT>(xa, bs, acc);   // drain the last prefetch
 }
 
 // FP4 delta: 16-k block (words w0, w1) with scale s; x pairs x[t][o .. o+7]
@@ -283,7 +353,6 @@ __device__ __forceinline__ void fp4_gemv(const LaneRow &L, int K, int g0, int g1
     }
 }
 
-constexpr int kTT = 2;     // tokens per pass (more would cost SGPRs / occupancy)
 constexpr int kW1 = 4;     // wavefronts per fc1 workgroup (K split)
 constexpr int kW2 = 2;     // wavefronts per fc2 workgroup (K split)
 
@@ -307,7 +376,7 @@ __device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2,
     for (int t = 0; t < kTT; ++t) part[t] = s2 * acc[t] + ((any_flag && flag[t]) ? ds2 * dacc[t] : 0.f);
 }
 
-__global__ __launch_bounds__(64 * kW1) void fc1_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(8))) void fc1_decode_kernel(DecodeParams p)
 {
     __shared__ float red[kW1][kTT][64];
     const int half = blockIdx.x, s = blockIdx.y;   // rows [32 half, 32 half + 32) of gate and of up
@@ -345,6 +414,7 @@ __global__ __launch_bounds__(64 * kW1) void fc1_decode_kernel(DecodeParams p)
         for (int j = 0; j < kTT; ++j) {
             int t;
             slot_token(p, si, i0 + (j < n ? j : 0), t, hrow[j], flag[j]);
+            t = __builtin_amdgcn_readfirstlane(t);
             xr[j] = as_const(p.x + (size_t)t * H);
         }
         float part[kTT];
@@ -372,7 +442,7 @@ __global__ __launch_bounds__(64 * kW1) void fc1_decode_kernel(DecodeParams p)
     }
 }
 
-__global__ __launch_bounds__(64 * kW2) void fc2_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(8))) void fc2_decode_kernel(DecodeParams p)
 {
     __shared__ float red[kW2][kTT][64];
     const int tile = blockIdx.x, s = blockIdx.y;
@@ -407,6 +477,7 @@ __global__ __launch_bounds__(64 * kW2) void fc2_decode_kernel(DecodeParams p)
         for (int j = 0; j < kTT; ++j) {
             int t;
             slot_token(p, si, i0 + (j < n ? j : 0), t, hrow[j], flag[j]);
+            hrow[j] = __builtin_amdgcn_readfirstlane(hrow[j]);
             xr[j] = as_const(p.h + (size_t)hrow[j] * I);
         }
         float part[kTT];
@@ -524,7 +595,7 @@ int launch_decode(const moet_layer *L, const uint16_t *x, int T, int k, const in
     p.h = reinterpret_cast<uint16_t *>(base);
     p.ypart = reinterpret_cast<float *>(base + al(rows * L->I * 2));
     p.out = out;
-    const int slots = T * k + p.has_shared;
+    const int slots = decode_entries(T, k, p.has_shared);
     timing_start(stream);
     hipLaunchKernelGGL(fc1_decode_kernel, dim3(L->I / 32, slots), dim3(64 * kW1), 0, stream, p);
     timing_stop(stream);

@@ -427,7 +427,8 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
 {
     if (L->n_slots > 0 && gate != nullptr) {
         // the FP4 delta on gated tokens is fused only into the GEMV kernels
-        if ((int64_t)T * k + 1 > 65535) return fail(MOET_EUNSUPPORTED, "delta cache with T*top_k > 65534 is not supported");
+        if ((int64_t)T * k + (T + 1) / 2 > 65535)
+            return fail(MOET_EUNSUPPORTED, "delta cache with T*top_k + T/2 > 65535 is not supported");
         return launch_decode(L, x, T, k, ids, w, offsets, sorted, gate, out, ws, stream);
     }
     PrefillParams p;

@@ -99,15 +99,26 @@ __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotI
     const int q = s - nsh;
     if (q >= P) return false;
     const int lane = threadIdx.x & 63;
-    int v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int j = 1 + lane + 64 * i;
-        v[i] = (j <= p.E) ? p.offsets[j] : 0x7FFFFFFF;
-    }
     int e = 0;
+    if (p.E <= 256) {   // the common sizes: one round of at most 4 loads
+        int v[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) e += __popcll(__ballot(v[i] <= q));
+        for (int i = 0; i < 4; ++i) {
+            const int j = 1 + lane + 64 * i;
+            v[i] = (j <= p.E) ? p.offsets[j] : 0x7FFFFFFF;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e += __popcll(__ballot(v[i] <= q));
+    } else {
+        int v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = 1 + lane + 64 * i;
+            v[i] = (j <= p.E) ? p.offsets[j] : 0x7FFFFFFF;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e += __popcll(__ballot(v[i] <= q));
+    }
     e = __builtin_amdgcn_readfirstlane(e);
     if (e >= p.E) return false;
     const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
@@ -157,7 +168,17 @@ __device__ __forceinline__ W2Consts w2_consts()
 }
 
 // bs[t] += sum over one 16-weight word of level * x, x pairs x[t][o .. o+7]
-template <int TT, typename XT>
+// dot2 that starts a new sum (the zero is an inline constant, so no register
+// has to be cleared first)
+__device__ __forceinline__ float dot2_bf16_new(uint32_t a, uint32_t b)
+{
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "s"(b));
+    return r;
+}
+
+// FIRST: bs[] holds no sum yet (the word opens a 32-k block)
+template <int TT, bool FIRST, typename XT>
 __device__ __forceinline__ void w2_word(uint32_t w, const XT *x, int o, float bs[TT], W2Consts k)
 {
     const uint32_t fa = w2_fp4_lo(w, k.sm, k.vb), fb = w2_fp4_hi(w, k.sm, k.vb);
@@ -171,19 +192,37 @@ __device__ __forceinline__ void w2_word(uint32_t w, const XT *x, int o, float bs
     pr[6] = fp4_pair<2>(fb);
     pr[7] = fp4_pair<3>(fb);
 #pragma unroll
-    for (int t = 0; t < TT; ++t)
+    for (int t = 0; t < TT; ++t) {
+        if constexpr (FIRST)
+            bs[t] = dot2_bf16_new(pr[0], x[t][o]);
+        else
+            bs[t] = dot2_bf16(pr[0], x[t][o], bs[t]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bs[t] = dot2_bf16(pr[i], x[t][o + i], bs[t]);
+        for (int i = 1; i < 8; ++i) bs[t] = dot2_bf16(pr[i], x[t][o + i], bs[t]);
+    }
 }
 
 // per-lane view of the one row this lane computes
+// The 2-bit planes are addressed as a wave-uniform base plus a 32-bit per-lane
+// offset, so the loads use scalar base registers and the per-group advance
+// is scalar arithmetic.
 struct LaneRow {
-    const uint4 *c4;      // 2-bit codes of the lane's matrix
-    const uint32_t *s4;   // 2-bit block scales of the lane's matrix
+    const uint8_t *cb;    // wave-uniform: 2-bit codes of the wave's first matrix
+    const uint8_t *sb;    // wave-uniform: its block scales
+    uint32_t co, so;      // this lane's byte offsets (codes of 64-k chunk 0, scale dword of group 0)
     const uint4 *dc4;     // FP4 delta codes (or null)
     const uint2 *ds8;     // FP4 delta scales
     int tile, rt;         // storage tile and row within it
 };
+
+// per-lane offsets of row (tile, rt) of matrix `mat` (relative to the wave's first matrix)
+__device__ __forceinline__ void lane_offsets(LaneRow &L, int mat, int tile, int rt, int N, int K)
+{
+    L.co = (uint32_t)mat * (uint32_t)(N * (K / 4)) + (uint32_t)(tile * (K / 64) + 0) * 1024u + (uint32_t)rt * 16u;
+    L.so = (uint32_t)mat * (uint32_t)(N * (K / 32)) + (uint32_t)(tile * (K / 128)) * 256u + (uint32_t)rt * 4u;
+    L.tile = tile;
+    L.rt = rt;
+}
 
 struct W2Buf {
     uint4 c0, c1;
@@ -192,9 +231,20 @@ struct W2Buf {
 
 __device__ __forceinline__ void w2_load(W2Buf &B, const LaneRow &L, int K, int g)
 {
-    B.c0 = L.c4[w2_chunk_idx(L.tile, 2 * g, L.rt, K)];
-    B.c1 = L.c4[w2_chunk_idx(L.tile, 2 * g + 1, L.rt, K)];
-    B.sc = L.s4[w2_scale_idx(L.tile, g, L.rt, K)];
+    (void)K;
+    // the opaque copies keep the group advance in the scalar base (scalar base +
+    // 32-bit lane offset addressing) instead of being folded into lane pointers
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    typedef const uint8_t __attribute__((address_space(1))) gu8;
+    typedef const v4u __attribute__((address_space(1))) gv4;
+    typedef const uint32_t __attribute__((address_space(1))) gu32;
+    gu8 *c = (gu8 *)(uintptr_t)(L.cb + (size_t)g * 2048);   // 64-k chunks 2g, 2g+1 of the row: 1 KiB apart
+    gu8 *sc = (gu8 *)(uintptr_t)(L.sb + (size_t)g * 256);
+    asm volatile("" : "+s"(c), "+s"(sc));
+    const v4u a = *(gv4 *)(c + L.co), b = *(gv4 *)(c + (L.co + 1024u));
+    B.c0 = make_uint4(a.x, a.y, a.z, a.w);
+    B.c1 = make_uint4(b.x, b.y, b.z, b.w);
+    B.sc = *(gu32 *)(sc + L.so);
 }
 
 // activations of one 64-k chunk (32 bf16 pairs) of token rows xr[t] (scalar loads)
@@ -238,13 +288,30 @@ __device__ __forceinline__ void xwait(u32x8 (&v)[TT], float bs[TT], float acc[TT
 // word j (0..7) of group g: wait for its activations (in `cur`), prefetch word
 // j + 1 (clamped to the wave's last word `wl`) into `nxt`, then decode and dot
 template <int TT>
+__device__ __forceinline__ void xwait_acc(u32x8 (&v)[TT], float acc[TT])
+{
+    if constexpr (TT == 1)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v[0]), "+v"(acc[0]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v[0]), "+s"(v[1]), "+v"(acc[0]), "+v"(acc[1]));
+}
+
+// FIRST: the word opens a 32-k block (its running sums are still zero, so the
+// wait orders it after the previous block's accumulation instead)
+template <int TT, bool FIRST>
 __device__ __forceinline__ void w2_step(uint32_t w, int word, const cu32 *const xr[TT], int wl, u32x8 (&cur)[TT],
                                         u32x8 (&nxt)[TT], float bs[TT], float acc[TT], W2Consts k)
 {
-    xwait<TT>(cur, bs, acc);
+    if constexpr (FIRST) {
+        xwait_acc<TT>(cur, acc);
 #pragma unroll
-    for (int t = 0; t < TT; ++t) xload(nxt[t], xr[t] + 8 * min(word + 1, wl), bs[t]);
-    w2_word<TT>(w, cur, 0, bs, k);
+        for (int t = 0; t < TT; ++t) xload(nxt[t], xr[t] + 8 * min(word + 1, wl), acc[t]);
+    } else {
+        xwait<TT>(cur, bs, acc);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) xload(nxt[t], xr[t] + 8 * min(word + 1, wl), bs[t]);
+    }
+    w2_word<TT, FIRST>(w, cur, 0, bs, k);
 }
 
 template <int TT>
@@ -266,42 +333,54 @@ __device__ __forceinline__ void w2_group(const W2Buf &B, int g, const cu32 *cons
     float bs[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) bs[t] = 0.f;
-    w2_step<TT>(B.c0.x, w0 + 0, xr, wl, xa, xb, bs, acc, k);
-    w2_step<TT>(B.c0.y, w0 + 1, xr, wl, xb, xa, bs, acc, k);
+    w2_step<TT, true>(B.c0.x, w0 + 0, xr, wl, xa, xb, bs, acc, k);
+    w2_step<TT, false>(B.c0.y, w0 + 1, xr, wl, xb, xa, bs, acc, k);
     block_done<TT>(bs, e4m3_byte<0>(B.sc), acc);
-    w2_step<TT>(B.c0.z, w0 + 2, xr, wl, xa, xb, bs, acc, k);
-    w2_step<TT>(B.c0.w, w0 + 3, xr, wl, xb, xa, bs, acc, k);
+    w2_step<TT, true>(B.c0.z, w0 + 2, xr, wl, xa, xb, bs, acc, k);
+    w2_step<TT, false>(B.c0.w, w0 + 3, xr, wl, xb, xa, bs, acc, k);
     block_done<TT>(bs, e4m3_byte<1>(B.sc), acc);
-    w2_step<TT>(B.c1.x, w0 + 4, xr, wl, xa, xb, bs, acc, k);
-    w2_step<TT>(B.c1.y, w0 + 5, xr, wl, xb, xa, bs, acc, k);
+    w2_step<TT, true>(B.c1.x, w0 + 4, xr, wl, xa, xb, bs, acc, k);
+    w2_step<TT, false>(B.c1.y, w0 + 5, xr, wl, xb, xa, bs, acc, k);
     block_done<TT>(bs, e4m3_byte<2>(B.sc), acc);
-    w2_step<TT>(B.c1.z, w0 + 6, xr, wl, xa, xb, bs, acc, k);
-    w2_step<TT>(B.c1.w, w0 + 7, xr, wl, xb, xa, bs, acc, k);
+    w2_step<TT, true>(B.c1.z, w0 + 6, xr, wl, xa, xb, bs, acc, k);
+    w2_step<TT, false>(B.c1.w, w0 + 7, xr, wl, xb, xa, bs, acc, k);
     block_done<TT>(bs, e4m3_byte<3>(B.sc), acc);
 }
 
+#ifndef MOET_DECODE_WAVES
+#define MOET_DECODE_WAVES 8
+#endif
+#ifndef MOET_DECODE_PF
+#define MOET_DECODE_PF 1
+#endif
+constexpr int kPF = MOET_DECODE_PF;   // weight groups loaded ahead of the one being computed
+
 // acc[t] += sum over groups [g0, g1) of level * scale * x for this lane's row.
-// Weights of the next group are loaded while the current one is computed; the
-// load is issued on every iteration (the last one re-loads the final group) so
-// that the outstanding-load count, and with it the compiler's wait, is the
-// same on every path.  xr[] must be wave-uniform.
+// Weights run kPF groups ahead of the group being computed, in a ring of
+// kPF + 1 register sets; a load is issued for every group computed (past the
+// end it re-loads the final group) so that the outstanding-load count, and
+// with it the compiler's wait, is the same on every path.  xr[] must be
+// wave-uniform.
 template <int TT>
 __device__ __forceinline__ void w2_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
 {
     if (g0 >= g1) return;
     const W2Consts kc = w2_consts();
     const int wl = 8 * g1 - 1;
-    W2Buf A, B;
+    W2Buf buf[kPF + 1];
     u32x8 xa[TT], xb[TT];
-    w2_load(A, L, K, g0);
+#pragma unroll
+    for (int d = 0; d < kPF; ++d) w2_load(buf[d], L, K, min(g0 + d, g1 - 1));
 #pragma unroll
     for (int t = 0; t < TT; ++t) xload(xa[t], xr[t] + 8 * (8 * g0), acc[t]);
-    for (int g = g0; g < g1; g += 2) {
-        w2_load(B, L, K, min(g + 1, g1 - 1));
-        w2_group<TT>(A, g, xr, wl, xa, xb, acc, kc);
-        if (g + 1 >= g1) break;
-        w2_load(A, L, K, min(g + 2, g1 - 1));
-        w2_group<TT>(B, g + 1, xr, wl, xa, xb, acc, kc);
+    for (int g = g0; g < g1; g += kPF + 1) {
+#pragma unroll
+        for (int u = 0; u <= kPF; ++u) {
+            if (g + u < g1) {
+                w2_load(buf[(u + kPF) % (kPF + 1)], L, K, min(g + u + kPF, g1 - 1));
+                w2_group<TT>(buf[u], g + u, xr, wl, xa, xb, acc, kc);
+            }
+        }
     }
     float bs[TT];
 #pragma unroll
@@ -376,7 +455,7 @@ __device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2,
     for (int t = 0; t < kTT; ++t) part[t] = s2 * acc[t] + ((any_flag && flag[t]) ? ds2 * dacc[t] : 0.f);
 }
 
-__global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(8))) void fc1_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_DECODE_WAVES))) void fc1_decode_kernel(DecodeParams p)
 {
     __shared__ float red[kW1][kTT][64];
     const int half = blockIdx.x, s = blockIdx.y;   // rows [32 half, 32 half + 32) of gate and of up
@@ -389,10 +468,9 @@ __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(8))) v
     const moet_w2 &W = si.shared ? p.sh13 : p.w13;
     const int m0 = si.shared ? 0 : 2 * si.e;
     LaneRow L;
-    L.c4 = reinterpret_cast<const uint4 *>(W.codes + (size_t)(m0 + mat) * I * H / 16);
-    L.s4 = reinterpret_cast<const uint32_t *>(W.scales + (size_t)(m0 + mat) * I * H / 32);
-    L.tile = row >> 6;
-    L.rt = row & 63;
+    L.cb = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * I * H / 16);
+    L.sb = W.scales + (size_t)m0 * I * H / 32;
+    lane_offsets(L, mat, row >> 6, row & 63, I, H);
     const float s2 = W.scale2[m0 + mat];
     float ds2 = 0.f;
     L.dc4 = nullptr;
@@ -442,7 +520,7 @@ __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(8))) v
     }
 }
 
-__global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(8))) void fc2_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_DECODE_WAVES))) void fc2_decode_kernel(DecodeParams p)
 {
     __shared__ float red[kW2][kTT][64];
     const int tile = blockIdx.x, s = blockIdx.y;
@@ -453,10 +531,9 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(8))) v
     const moet_w2 &W = si.shared ? p.sh2 : p.w2;
     const int m0 = si.shared ? 0 : si.e;
     LaneRow L;
-    L.c4 = reinterpret_cast<const uint4 *>(W.codes + (size_t)m0 * H * I / 16);
-    L.s4 = reinterpret_cast<const uint32_t *>(W.scales + (size_t)m0 * H * I / 32);
-    L.tile = tile;
-    L.rt = lane;
+    L.cb = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16);
+    L.sb = W.scales + (size_t)m0 * H * I / 32;
+    lane_offsets(L, 0, tile, lane, H, I);
     const float s2 = W.scale2[m0];
     float ds2 = 0.f;
     L.dc4 = nullptr;
@@ -532,8 +609,9 @@ __global__ __launch_bounds__(64 * kWd) void delta_gemv_kernel(moet_fp4 D, int n_
     const int G = K / 128;
     const int g0 = wave * G / kWd, g1 = (wave + 1) * G / kWd;
     LaneRow L;
-    L.c4 = nullptr;
-    L.s4 = nullptr;
+    L.cb = nullptr;
+    L.sb = nullptr;
+    L.co = L.so = 0;
     L.dc4 = reinterpret_cast<const uint4 *>(D.codes + (size_t)slot * N * K / 2);
     L.ds8 = reinterpret_cast<const uint2 *>(D.scales + (size_t)slot * N * K / 16);
     L.tile = tile;

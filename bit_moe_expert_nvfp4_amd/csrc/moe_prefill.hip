@@ -425,10 +425,12 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
                    const int32_t *offsets, const int32_t *sorted, const uint8_t *gate, uint16_t *out, void *ws,
                    hipStream_t stream)
 {
-    if (L->n_slots > 0 && gate != nullptr) {
-        // the FP4 delta on gated tokens is fused only into the GEMV kernels
+    if ((L->n_slots > 0 && gate != nullptr) || L->I % 128 || L->H % 256) {
+        // the FP4 delta on gated tokens is fused only into the GEMV kernels, and
+        // the grouped GEMM tiles need I % 128 == 0 and H % 256 == 0
         if ((int64_t)T * k + (T + 1) / 2 > 65535)
-            return fail(MOET_EUNSUPPORTED, "delta cache with T*top_k + T/2 > 65535 is not supported");
+            return fail(MOET_EUNSUPPORTED, "this batch needs the GEMV kernels (delta cache, or I %% 128 / H %% 256 "
+                                            "not 0), which take at most T*top_k + T/2 = 65535 entries");
         return launch_decode(L, x, T, k, ids, w, offsets, sorted, gate, out, ws, stream);
     }
     PrefillParams p;
@@ -458,7 +460,6 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     const int mslots = (P + kPM - 1) / kPM + L->E + (p.has_shared ? (T + kPM - 1) / kPM : 0);
     p.n_mslots = mslots;
     const int ms8 = (mslots + 7) / 8 * 8;
-    if (L->I % 128 || L->H % 256) return fail(MOET_EUNSUPPORTED, "prefill needs I %% 128 == 0 and H %% 256 == 0");
     p.n_ntiles = L->I / 128;
     timing_start(stream);
     hipLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);

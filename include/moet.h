@@ -190,7 +190,10 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
  * (+ D2_slot h); out bf16 [T][H] = bf16(sum_j topk_w[t][j] * y_(t,j) +
  * y_shared(t)).  Accumulation is fp32; h and out are rounded to nearest-even.
  * Decode-sized batches (T*top_k <= 1024) run the GEMV kernels; larger
- * batches run the MFMA grouped-GEMM kernels.
+ * batches run the MFMA grouped-GEMM kernels when I % 128 == 0, H % 256 == 0
+ * and no token is gated onto the delta cache, else the GEMV kernels, which
+ * take at most T*top_k + ceil(T/2) = 65535 work entries (MOET_EUNSUPPORTED
+ * beyond).
  * workspace: at least moet_moe_workspace_bytes(L, T, top_k) bytes of device
  * memory, 256-byte aligned; its contents need no initialisation.
  * Expert ids outside [0, E) and slots outside [0, n_slots) contribute

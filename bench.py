@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk (T=4096) measurement")
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="skip the delta-cache and batched decode legs")
+    ap.add_argument("--extra-steps", type=int, default=100)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (HBM counter calibration)")
@@ -180,6 +182,81 @@ def _blas_threads():
     except Exception:
         pass
     return len(os.sched_getaffinity(0))
+
+
+def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8):
+    """Route + forward of another decode configuration (FP4 delta cache, batched streams), timed like the
+    main step over its own pool of layers and input sets."""
+    import numpy as np
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet, synth
+
+    cfg = synth.CONFIGS[cfg_no]
+    soe = synth.slot_of_expert(cfg, seed) if cfg.n_resident else None
+    layers = []
+    for li in range(n_layers):
+        src = synth.make_layer(cfg, seed=seed, device=dev, layer_index=li)
+        layers.append(moet.layer_from_nvfp4(src, soe))
+        del src
+        torch.cuda.empty_cache()
+    xs = [synth.make_activations(cfg.T, cfg.H, seed, tag=f"x{i}", device=dev) for i in range(n_inputs)]
+    lgs = [synth.make_logits(cfg, seed, tag=f"logits{i}", device=dev) for i in range(n_inputs)]
+    flags = synth.gate_flags(cfg, seed).to(dev) if cfg.n_flagged else None
+    ro = [(torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
+           torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
+           torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev),
+           torch.empty((cfg.T * cfg.k,), dtype=torch.int32, device=dev)) for _ in range(n_inputs)]
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = moet.alloc_workspace(layers[0], cfg.T, cfg.k, dev)
+
+    def step(i):
+        j = i % n_inputs
+        ids, w, offs, pairs = moet.route(lgs[j], cfg.k, cfg.score, cfg.renormalize, out=ro[j])
+        moet.moe_forward(layers[i % n_layers], xs[j], ids, w, offs, pairs, flags, out=out, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    flags_np = flags.cpu().numpy() if flags is not None else None
+    soe_np = soe.numpy() if soe is not None else None
+    per_input = [step_bytes(cfg, ro[j][0].cpu().numpy(), flags_np, soe_np) for j in range(n_inputs)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        moet.set_timing_events(*ev[i])
+        step(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    moet.set_timing_events(None, None)
+    ms = t0.elapsed_time(t1) / steps
+    sel = [per_input[(warmup + i) % n_inputs] for i in range(steps)]
+    nbytes = float(np.mean([b[0] for b in sel]))
+    fc1_bytes = float(np.mean([b[1] for b in sel]))
+    fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    res = {
+        "workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} top{cfg.k} sigmoid+renorm"
+                    f"{' (Zipf-skewed logits)' if cfg.logits == 'zipf' else ''}"
+                    f"{' + shared expert' if cfg.shared else ''}"
+                    f"{f' + FP4 delta ({cfg.n_resident} resident, {cfg.n_flagged} of {cfg.T} tokens flagged)' if cfg.n_resident else ''}"
+                    f", {n_layers}-layer pool, {n_inputs} input sets",
+        "us_per_layer": round(ms * 1e3, 2),
+        "GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 1),
+        "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
+        "algorithmic_bytes_per_step": round(nbytes),
+        "mean_experts_per_step": round(float(np.mean([b[2] for b in sel])), 2),
+        "mean_delta_experts_per_step": round(float(np.mean([b[3] for b in sel])), 2),
+        "fc1_avg_launch_us": round(fc1_ms * 1e3, 2),
+        "fc1_GBps": round(fc1_bytes / (fc1_ms / 1e3) / 1e9, 1),
+    }
+    del layers, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def prefill_leg(layer, cfg5, steps, seed, dev):
@@ -406,6 +483,13 @@ def main():
         import dataclasses
         pl = dataclasses.replace(layers[0], shared13=None, shared2=None)
         result["prefill"] = prefill_leg(pl, synth.CONFIGS[5], args.prefill_steps, args.seed, dev)
+    if not args.no_extra:
+        del layers
+        torch.cuda.empty_cache()
+        result["other_decode"] = {}
+        for cno, key in ((3, "delta_cache"), (4, "batched")):
+            print(f"[bench] timing decode config {key}", file=sys.stderr, flush=True)
+            result["other_decode"][key] = decode_leg(cno, args.extra_steps, 10, args.seed, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
         cb = cpu_baseline(cfg, srcs[0], xs[0], lgs[0], args.seed)

@@ -388,11 +388,28 @@ __device__ __forceinline__ void w2_gemv(const LaneRow &L, int K, int g0, int g1,
     xwait<TT>(xa, bs, acc);   // drain the last prefetch
 }
 
-// FP4 delta: 16-k block (words w0, w1) with scale s; x pairs x[t][o .. o+7]
-template <int TT>
-__device__ __forceinline__ void fp4_block(uint32_t w0, uint32_t w1, float s, const uint32_t (*x)[32], int o,
-                                          float acc[TT])
+// FP4 delta planes: a 64-k half group of a row is two 32-k chunks (16 B each,
+// 8 e2m1 codes per word) and four e4m3 block scales (one per 16 k, one dword).
+struct FP4Buf {
+    uint4 c0, c1;
+    uint32_t sc;
+};
+
+// half group hg = 64-k chunk pair hg of the row
+__device__ __forceinline__ void fp4_load(FP4Buf &B, const LaneRow &L, int K, int hg)
 {
+    B.c0 = L.dc4[fp4_chunk_idx(L.tile, 2 * hg, L.rt, K)];
+    B.c1 = L.dc4[fp4_chunk_idx(L.tile, 2 * hg + 1, L.rt, K)];
+    B.sc = reinterpret_cast<const uint32_t *>(L.ds8)[2 * fp4_scale_idx(L.tile, hg >> 1, L.rt, K) + (hg & 1)];
+}
+
+template <int TT>
+__device__ __forceinline__ void fp4_step(uint32_t w0, uint32_t w1, float s, int word, const cu32 *const xr[TT], int wl,
+                                         u32x8 (&cur)[TT], u32x8 (&nxt)[TT], float acc[TT])
+{
+    xwait_acc<TT>(cur, acc);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) xload(nxt[t], xr[t] + 8 * min(word + 1, wl), acc[t]);
     uint32_t pr[8];
     pr[0] = fp4_pair<0>(w0);
     pr[1] = fp4_pair<1>(w0);
@@ -404,32 +421,45 @@ __device__ __forceinline__ void fp4_block(uint32_t w0, uint32_t w1, float s, con
     pr[7] = fp4_pair<3>(w1);
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-        float bs = 0.f;
+        float bs = dot2_bf16_new(pr[0], cur[t][0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bs = dot2_bf16(pr[i], x[t][o + i], bs);
+        for (int i = 1; i < 8; ++i) bs = dot2_bf16(pr[i], cur[t][i], bs);
         acc[t] = fmaf(bs, s, acc[t]);
     }
 }
 
 template <int TT>
+__device__ __forceinline__ void fp4_half(const FP4Buf &B, int hg, const cu32 *const xr[TT], int wl, u32x8 (&xa)[TT],
+                                         u32x8 (&xb)[TT], float acc[TT])
+{
+    const int w0 = 4 * hg;   // 16-k words of this half group
+    fp4_step<TT>(B.c0.x, B.c0.y, e4m3_byte<0>(B.sc), w0 + 0, xr, wl, xa, xb, acc);
+    fp4_step<TT>(B.c0.z, B.c0.w, e4m3_byte<1>(B.sc), w0 + 1, xr, wl, xb, xa, acc);
+    fp4_step<TT>(B.c1.x, B.c1.y, e4m3_byte<2>(B.sc), w0 + 2, xr, wl, xa, xb, acc);
+    fp4_step<TT>(B.c1.z, B.c1.w, e4m3_byte<3>(B.sc), w0 + 3, xr, wl, xb, xa, acc);
+}
+
+// acc[t] += sum over groups [g0, g1) of e2m1 * scale * x for this lane's FP4 row
+// (same prefetching as the 2-bit GEMV: weights one 64-k half group ahead,
+// activations one 16-k block ahead; xr[] wave-uniform)
+template <int TT>
 __device__ __forceinline__ void fp4_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
 {
-    for (int g = g0; g < g1; ++g) {
-        const uint2 sc = L.ds8[fp4_scale_idx(L.tile, g, L.rt, K)];
+    if (g0 >= g1) return;
+    const int h0 = 2 * g0, h1 = 2 * g1;
+    const int wl = 8 * g1 - 1;
+    FP4Buf A, B;
+    u32x8 xa[TT], xb[TT];
+    fp4_load(A, L, K, h0);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {   // 64-k halves of the group: FP4 chunks 4g+2h, 4g+2h+1
-            const uint4 ca = L.dc4[fp4_chunk_idx(L.tile, 4 * g + 2 * h, L.rt, K)];
-            const uint4 cb = L.dc4[fp4_chunk_idx(L.tile, 4 * g + 2 * h + 1, L.rt, K)];
-            uint32_t x[TT][32];
-            load_x_chunk<TT>(xr, 64 * g + 32 * h, x);
-            const uint32_t sw = h ? sc.y : sc.x;
-            fp4_block<TT>(ca.x, ca.y, e4m3_byte<0>(sw), x, 0, acc);
-            fp4_block<TT>(ca.z, ca.w, e4m3_byte<1>(sw), x, 8, acc);
-            fp4_block<TT>(cb.x, cb.y, e4m3_byte<2>(sw), x, 16, acc);
-            fp4_block<TT>(cb.z, cb.w, e4m3_byte<3>(sw), x, 24, acc);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    for (int t = 0; t < TT; ++t) xload(xa[t], xr[t] + 8 * (8 * g0), acc[t]);
+    for (int hg = h0; hg < h1; hg += 2) {   // h1 - h0 is even
+        fp4_load(B, L, K, hg + 1);
+        fp4_half<TT>(A, hg, xr, wl, xa, xb, acc);
+        fp4_load(A, L, K, min(hg + 2, h1 - 1));
+        fp4_half<TT>(B, hg + 1, xr, wl, xa, xb, acc);
     }
+    xwait_acc<TT>(xa, acc);   // drain the last prefetch
 }
 
 constexpr int kW1 = 4;     // wavefronts per fc1 workgroup (K split)

@@ -16,6 +16,12 @@ compared tightly):
   out_t = bf16_rne(sum_j w_tj * y_(t,j) + y_shared(t)); the shared expert uses
   the same FFN with weight 1 and no delta.
 All real arithmetic is float64 on exactly dequantised weights.
+
+Expert cache (README, section "When the model doesn't fit at all — the GPU
+as an expert cache"): when only some experts' base weights are on the GPU, a
+routing to a missing expert contributes nothing to its token's output (its
+weight is not redistributed) and is counted; once the missing experts are
+fetched, the same step reproduces the fully resident output exactly.
 """
 from __future__ import annotations
 
@@ -61,14 +67,16 @@ def moe_forward(x_bits: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
                 expert_weights: WeightFn, shared_weights: Optional[Sequence[np.ndarray]] = None,
                 gate_flags: Optional[np.ndarray] = None, slot_of_expert: Optional[np.ndarray] = None,
                 delta_weights: Optional[WeightFn] = None, swiglu_limit: float = 0.0,
-                tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+                tokens: Optional[Sequence[int]] = None,
+                resident: Optional[np.ndarray] = None) -> np.ndarray:
     """Layer output as bf16 bit patterns [len(tokens), H].
 
     x_bits: bf16 bits [T, H]; expert_weights(e) -> (Wg, Wu, Wd) float64;
     delta_weights(slot) -> (Dg, Du, Dd) float64; a pair (t, e) takes the delta
     iff gate_flags[t] != 0 and slot_of_expert[e] >= 0.  ``tokens`` restricts
     the computation to a subset of rows (each output row depends only on its
-    own token).
+    own token).  ``resident`` (bool [E], None = all): pairs whose expert is not
+    resident contribute nothing.
     """
     x = bf16_bits_to_f64(x_bits)
     T, H = x.shape
@@ -84,6 +92,8 @@ def moe_forward(x_bits: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
         for j in range(ids.shape[1]):
             by_expert.setdefault(int(ids[t, j]), []).append((ti, t, j))
     for e, lst in sorted(by_expert.items()):
+        if resident is not None and not resident[e]:
+            continue
         Wg, Wu, Wd = expert_weights(e)
         for ti, t, j in lst:
             use_delta = (gate_flags is not None and slot_of_expert is not None and delta_weights is not None
@@ -100,6 +110,12 @@ def moe_forward(x_bits: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
         h = expert_hidden(x[tokens], Wg, Wu, swiglu_limit)
         acc += expert_out(h, Wd)
     return bf16_rne_bits(acc)
+
+
+def miss_count(topk_ids: np.ndarray, resident: np.ndarray) -> int:
+    """Number of (token, expert) routings whose expert is not resident."""
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    return int(np.count_nonzero(~np.asarray(resident, dtype=bool)[ids]))
 
 
 def fp4_gemm_accumulate(acc: np.ndarray, act_bits: np.ndarray, row_slot: np.ndarray,

@@ -189,3 +189,38 @@ def test_swiglu_clamp():
     assert (h == F.bf16_bits_to_f64(F.bf16_rne_bits(ug / (1 + np.exp(-ug)) * uu))).all()
     # silu on (-inf, L] is bounded by max(0.2785, silu(L)) in magnitude
     assert np.abs(h).max() <= max(0.2785, L / (1 + np.exp(-L))) * L * 1.01
+
+
+def test_moe_forward_expert_cache_mask():
+    """Missing experts contribute nothing and are counted (README, "When the model doesn't fit at all
+    — the GPU as an expert cache"): checked against the dense form with the missing experts' combine
+    weights set to zero, against a loop count of missed routings, and at the two ends (all resident ==
+    no mask bit for bit; nothing resident == only the shared expert)."""
+    rng = np.random.default_rng(11)
+    E, H, I, T, k = 6, 128, 64, 7, 3
+    ex = _tiny_layer(rng, E, H, I)
+    sh = _tiny_layer(rng, 1, H, I)[0]
+    xb = F.bf16_rne_bits(rng.standard_normal((T, H)))
+    x = F.bf16_bits_to_f64(xb)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w, _, _ = RT.route(lg, k, RT.SOFTMAX)
+    resident = np.array([True, False, True, True, False, True])
+    out = FF.moe_forward(xb, ids, w, lambda e: ex[e], shared_weights=sh, resident=resident)
+    Wt = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            if resident[ids[t, j]]:
+                Wt[t, ids[t, j]] = w[t, j]
+    dense = np.zeros((T, H))
+    for e in range(E):
+        dense += Wt[:, e:e + 1] * FF.expert_out(FF.expert_hidden(x, ex[e][0], ex[e][1]), ex[e][2])
+    dense += FF.expert_out(FF.expert_hidden(x, sh[0], sh[1]), sh[2])
+    assert (out == F.bf16_rne_bits(dense)).all()
+    misses = sum(1 for t in range(T) for j in range(k) if not resident[ids[t, j]])
+    assert FF.miss_count(ids, resident) == misses > 0
+    full = FF.moe_forward(xb, ids, w, lambda e: ex[e], shared_weights=sh)
+    assert (FF.moe_forward(xb, ids, w, lambda e: ex[e], shared_weights=sh, resident=np.ones(E, bool)) == full).all()
+    none = FF.moe_forward(xb, ids, w, lambda e: ex[e], shared_weights=sh, resident=np.zeros(E, bool))
+    shared_only = F.bf16_rne_bits(FF.expert_out(FF.expert_hidden(x, sh[0], sh[1]), sh[2]))
+    assert (none == shared_only).all()
+    assert FF.miss_count(ids, np.zeros(E, bool)) == T * k

@@ -109,20 +109,21 @@ def counted_traffic():
         return None
 
 
-def step_bytes(cfg, ids_np, flags_np, soe_np):
-    """Algorithmic bytes of one decode step and of its gate/up kernel launch."""
+def step_bytes(cfg, ids_np, flags_np, soe_np, resident=None):
+    """Algorithmic bytes of one decode step and of its gate/up kernel launch (with an expert cache, only
+    the resident experts' planes are read)."""
     w13 = 2 * cfg.I * cfg.H * W2_BYTES_PER_WEIGHT
     w2 = cfg.H * cfg.I * W2_BYTES_PER_WEIGHT
     d13 = 2 * cfg.I * cfg.H * FP4_BYTES_PER_WEIGHT
     d2 = cfg.H * cfg.I * FP4_BYTES_PER_WEIGHT
-    experts = set(int(e) for e in ids_np.reshape(-1))
+    experts = set(int(e) for e in ids_np.reshape(-1) if resident is None or resident[int(e)])
     n = len(experts) + (1 if cfg.shared else 0)
     delta_experts = set()
     if flags_np is not None and soe_np is not None:
         for t in range(cfg.T):
             if flags_np[t]:
                 for e in ids_np[t]:
-                    if soe_np[int(e)] >= 0:
+                    if soe_np[int(e)] >= 0 and (resident is None or resident[int(e)]):
                         delta_experts.add(int(e))
     nd = len(delta_experts)
     io = 2 * cfg.T * cfg.H * 2 + 4 * cfg.T * cfg.E
@@ -184,7 +185,7 @@ def _blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8):
+def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_fraction=None):
     """Route + forward of another decode configuration (FP4 delta cache, batched streams), timed like the
     main step over its own pool of layers and input sets."""
     import numpy as np
@@ -194,11 +195,23 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8):
     cfg = synth.CONFIGS[cfg_no]
     soe = synth.slot_of_expert(cfg, seed) if cfg.n_resident else None
     layers = []
+    resident = None
+    if cache_fraction is not None:     # expert cache holding a seeded fraction of the experts
+        g = torch.Generator().manual_seed(seed)
+        perm = torch.randperm(cfg.E, generator=g)
+        n_res = int(round(cache_fraction * cfg.E))
+        base_soe = torch.full((cfg.E,), -1, dtype=torch.int64)
+        base_soe[perm[:n_res]] = torch.arange(n_res)
+        resident = (base_soe >= 0).numpy()
     for li in range(n_layers):
         src = synth.make_layer(cfg, seed=seed, device=dev, layer_index=li)
-        layers.append(moet.layer_from_nvfp4(src, soe))
+        lay = moet.layer_from_nvfp4(src, soe)
         del src
+        if resident is not None:
+            lay = moet.expert_cache(lay, base_soe)
+        layers.append(lay)
         torch.cuda.empty_cache()
+    miss = torch.zeros((1,), dtype=torch.int32, device=dev)
     xs = [synth.make_activations(cfg.T, cfg.H, seed, tag=f"x{i}", device=dev) for i in range(n_inputs)]
     lgs = [synth.make_logits(cfg, seed, tag=f"logits{i}", device=dev) for i in range(n_inputs)]
     flags = synth.gate_flags(cfg, seed).to(dev) if cfg.n_flagged else None
@@ -212,14 +225,19 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8):
     def step(i):
         j = i % n_inputs
         ids, w, offs, pairs = moet.route(lgs[j], cfg.k, cfg.score, cfg.renormalize, out=ro[j])
-        moet.moe_forward(layers[i % n_layers], xs[j], ids, w, offs, pairs, flags, out=out, workspace=ws)
+        moet.moe_forward(layers[i % n_layers], xs[j], ids, w, offs, pairs, flags, out=out, workspace=ws,
+                         miss_count=miss if resident is not None else None)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     flags_np = flags.cpu().numpy() if flags is not None else None
     soe_np = soe.numpy() if soe is not None else None
-    per_input = [step_bytes(cfg, ro[j][0].cpu().numpy(), flags_np, soe_np) for j in range(n_inputs)]
+    per_input = [step_bytes(cfg, ro[j][0].cpu().numpy(), flags_np, soe_np, resident) for j in range(n_inputs)]
+    misses = [int((~resident[ro[j][0].cpu().numpy().reshape(-1)]).sum()) if resident is not None else 0
+              for j in range(n_inputs)]
+    if resident is not None:          # the on-device counter of the last warm-up step
+        assert int(miss.item()) == misses[(warmup - 1) % n_inputs], "miss counter disagrees with the routing"
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in ev:
         a.record()
@@ -238,12 +256,14 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8):
     nbytes = float(np.mean([b[0] for b in sel]))
     fc1_bytes = float(np.mean([b[1] for b in sel]))
     fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    cache_txt = (f", expert cache holding {int(resident.sum())} of {cfg.E} experts (seeded choice)"
+                 if resident is not None else "")
     res = {
         "workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} top{cfg.k} sigmoid+renorm"
                     f"{' (Zipf-skewed logits)' if cfg.logits == 'zipf' else ''}"
                     f"{' + shared expert' if cfg.shared else ''}"
                     f"{f' + FP4 delta ({cfg.n_resident} resident, {cfg.n_flagged} of {cfg.T} tokens flagged)' if cfg.n_resident else ''}"
-                    f", {n_layers}-layer pool, {n_inputs} input sets",
+                    f"{cache_txt}, {n_layers}-layer pool, {n_inputs} input sets",
         "us_per_layer": round(ms * 1e3, 2),
         "GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
         "pct_hbm_peak": round(100.0 * nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 1),
@@ -254,6 +274,9 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8):
         "fc1_avg_launch_us": round(fc1_ms * 1e3, 2),
         "fc1_GBps": round(fc1_bytes / (fc1_ms / 1e3) / 1e9, 1),
     }
+    if resident is not None:
+        res["mean_missed_routings_per_step"] = round(float(np.mean([misses[(warmup + i) % n_inputs]
+                                                                    for i in range(steps)])), 2)
     del layers, ws
     torch.cuda.empty_cache()
     return res
@@ -487,9 +510,9 @@ def main():
         del layers
         torch.cuda.empty_cache()
         result["other_decode"] = {}
-        for cno, key in ((3, "delta_cache"), (4, "batched")):
+        for cno, key, frac in ((3, "delta_cache", None), (4, "batched", None), (2, "expert_cache_half", 0.5)):
             print(f"[bench] timing decode config {key}", file=sys.stderr, flush=True)
-            result["other_decode"][key] = decode_leg(cno, args.extra_steps, 10, args.seed, dev)
+            result["other_decode"][key] = decode_leg(cno, args.extra_steps, 10, args.seed, dev, cache_fraction=frac)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
         cb = cpu_baseline(cfg, srcs[0], xs[0], lgs[0], args.seed)

@@ -57,15 +57,26 @@ struct DecodeParams {
     const int32_t *slot_of_expert;
     moet_fp4 d13, d2;
     float swiglu_limit;
+    const int32_t *base_slot;   // expert -> cache slot of w13/w2 (null: expert e at e)
+    int n_base_slots;
+    int32_t *miss_count;        // routings to missing experts (null: not counted)
     uint16_t *h;        // [P + T][I] bf16
     float *ypart;       // [P + T][H] fp32
     uint16_t *out;      // [T][H] bf16
 };
 
 struct SlotInfo {
-    int e, pbeg, pend, dslot;
+    int e, ws, pbeg, pend, dslot;   // expert, its slot in w13/w2, sorted pairs [pbeg, pend), delta slot
     bool shared;
 };
+
+// cache slot of expert e's 2-bit planes, or -1 when it is missing from the expert cache
+__device__ __forceinline__ int weight_slot(const DecodeParams &p, int e)
+{
+    if (!p.base_slot) return e;
+    const int ws = p.base_slot[e];
+    return (ws >= 0 && ws < p.n_base_slots) ? ws : -1;
+}
 
 constexpr int kTT = 2;     // tokens per pass (more would cost SGPRs / occupancy)
 
@@ -90,6 +101,7 @@ __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotI
     const int nsh = p.has_shared ? (p.T + kTT - 1) / kTT : 0;
     if (s < nsh) {
         si.e = -1;
+        si.ws = 0;
         si.pbeg = kTT * s;
         si.pend = min(kTT * s + kTT, p.T);
         si.shared = true;
@@ -123,7 +135,10 @@ __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotI
     if (e >= p.E) return false;
     const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
     if (q < o0 || q >= o1 || (q - o0) % kTT != 0) return false;
+    const int ws = weight_slot(p, e);
+    if (ws < 0) return false;   // missing expert: no work, the combine skips its routings
     si.e = e;
+    si.ws = ws;
     si.pbeg = q;
     si.pend = min(min(q + kTT, o1), P);
     si.shared = false;
@@ -487,6 +502,7 @@ __device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2,
 
 __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_DECODE_WAVES))) void fc1_decode_kernel(DecodeParams p)
 {
+    if (p.miss_count && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.miss_count = 0;   // counted by the combine
     __shared__ float red[kW1][kTT][64];
     const int half = blockIdx.x, s = blockIdx.y;   // rows [32 half, 32 half + 32) of gate and of up
     SlotInfo si;
@@ -496,7 +512,7 @@ __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_D
     const int mat = lane >> 5;                      // 0: gate, 1: up
     const int row = 32 * half + (lane & 31);
     const moet_w2 &W = si.shared ? p.sh13 : p.w13;
-    const int m0 = si.shared ? 0 : 2 * si.e;
+    const int m0 = si.shared ? 0 : 2 * si.ws;
     LaneRow L;
     L.cb = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * I * H / 16);
     L.sb = W.scales + (size_t)m0 * I * H / 32;
@@ -559,7 +575,7 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_D
     SlotInfo si;
     if (!resolve_slot(p, s, si)) return;
     const moet_w2 &W = si.shared ? p.sh2 : p.w2;
-    const int m0 = si.shared ? 0 : si.e;
+    const int m0 = si.shared ? 0 : si.ws;
     LaneRow L;
     L.cb = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16);
     L.sb = W.scales + (size_t)m0 * H * I / 32;
@@ -604,18 +620,28 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_D
     }
 }
 
-// out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order
+// out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order;
+// routings to experts missing from the expert cache contribute nothing and are
+// counted once per token (by the first column block)
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p)
 {
     const int n = blockIdx.x * 256 + threadIdx.x;
     const int t = blockIdx.y;
-    if (n >= p.H) return;
     const int P = p.T * p.k;
+    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0) {
+        int miss = 0;
+        for (int j = 0; j < p.k; ++j) {
+            const int e = p.ids[t * p.k + j];
+            if (e >= 0 && e < p.E && weight_slot(p, e) < 0) ++miss;
+        }
+        if (miss) atomicAdd(p.miss_count, miss);
+    }
+    if (n >= p.H) return;
     float acc = 0.f;
     for (int j = 0; j < p.k; ++j) {
         const int pair = t * p.k + j;
         const int e = p.ids[pair];
-        if (e >= 0 && e < p.E) acc = fmaf(p.w[pair], p.ypart[(size_t)pair * p.H + n], acc);
+        if (e >= 0 && e < p.E && weight_slot(p, e) >= 0) acc = fmaf(p.w[pair], p.ypart[(size_t)pair * p.H + n], acc);
     }
     if (p.has_shared) acc += p.ypart[(size_t)(P + t) * p.H + n];
     p.out[(size_t)t * p.H + n] = (uint16_t)f32_to_bf16_rne(acc);
@@ -672,8 +698,8 @@ size_t decode_workspace_bytes(int T, int k, int H, int I)
 }
 
 int launch_decode(const moet_layer *L, const uint16_t *x, int T, int k, const int32_t *ids, const float *w,
-                  const int32_t *offsets, const int32_t *sorted, const uint8_t *gate, uint16_t *out, void *ws,
-                  hipStream_t stream)
+                  const int32_t *offsets, const int32_t *sorted, const uint8_t *gate, uint16_t *out, int32_t *miss_count,
+                  void *ws, hipStream_t stream)
 {
     DecodeParams p;
     p.x = x;
@@ -697,6 +723,9 @@ int launch_decode(const moet_layer *L, const uint16_t *x, int T, int k, const in
     p.d13 = L->d13;
     p.d2 = L->d2;
     p.swiglu_limit = L->swiglu_limit;
+    p.base_slot = L->base_slot_of_expert;
+    p.n_base_slots = L->n_base_slots;
+    p.miss_count = miss_count;
     const size_t rows = (size_t)T * k + T;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     char *base = static_cast<char *>(ws);

@@ -59,7 +59,18 @@ struct PrefillParams {
     uint16_t *out;
     int n_mslots;       // upper bound on M-tiles (grid)
     int n_ntiles;
+    const int32_t *base_slot;   // expert -> cache slot of w13/w2 (null: expert e at e)
+    int n_base_slots;
+    int32_t *miss_count;        // routings to missing experts (null: not counted)
 };
+
+// cache slot of expert e's 2-bit planes, or -1 when it is missing from the expert cache
+__device__ __forceinline__ int weight_slot(const PrefillParams &p, int e)
+{
+    if (!p.base_slot) return e;
+    const int ws = p.base_slot[e];
+    return (ws >= 0 && ws < p.n_base_slots) ? ws : -1;
+}
 
 struct MTile {
     int e;        // expert, or -1 for the shared expert
@@ -278,6 +289,7 @@ __device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, con
 __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc1_prefill_kernel(PrefillParams p)
 {
     __shared__ __align__(1024) uint8_t smem[kPS * kStage];
+    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0) *p.miss_count = 0;   // counted by the combine
     int ms, nt;
     decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
     if (ms >= p.n_mslots) return;
@@ -297,8 +309,10 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
         src.arow[i] = reinterpret_cast<const uint8_t *>(p.x + (size_t)tok * H);
     }
     // B: 256 rows = gate rows [128 nt, +128) then up rows [128 nt, +128); wave w fetches storage tile w
+    const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
+    if (ws < 0) return;   // missing expert: no work, the combine skips its routings
     const moet_w2 &W = (mt.e >= 0) ? p.w13 : p.sh13;
-    const int m0 = (mt.e >= 0) ? 2 * mt.e : 0;
+    const int m0 = (mt.e >= 0) ? 2 * ws : 0;
     {
         const int mat = m0 + (wave >> 1);
         const int tile = 2 * nt + (wave & 1);
@@ -356,8 +370,10 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
         const int r = min(8 * (4 * wave + i) + (lane >> 3), mt.rows - 1);
         src.arow[i] = reinterpret_cast<const uint8_t *>(p.h + (size_t)(rowbase + r) * I);
     }
+    const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
+    if (ws < 0) return;
     const moet_w2 &W = (mt.e >= 0) ? p.w2 : p.sh2;
-    const int m0 = (mt.e >= 0) ? mt.e : 0;
+    const int m0 = (mt.e >= 0) ? ws : 0;
     {
         const int tile = 4 * nt + wave;
         src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
@@ -392,18 +408,28 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 }
 
-// out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order
+// out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order;
+// routings to experts missing from the expert cache contribute nothing and are
+// counted once per token (by the first column block)
 __global__ __launch_bounds__(256) void combine_prefill_kernel(PrefillParams p)
 {
     const int n = blockIdx.x * 256 + threadIdx.x;
     const int t = blockIdx.y;
-    if (n >= p.H) return;
     const int P = p.T * p.k;
+    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0) {
+        int miss = 0;
+        for (int j = 0; j < p.k; ++j) {
+            const int e = p.ids[t * p.k + j];
+            if (e >= 0 && e < p.E && weight_slot(p, e) < 0) ++miss;
+        }
+        if (miss) atomicAdd(p.miss_count, miss);
+    }
+    if (n >= p.H) return;
     float acc = 0.f;
     for (int j = 0; j < p.k; ++j) {
         const int pair = t * p.k + j;
         const int e = p.ids[pair];
-        if (e >= 0 && e < p.E) acc = fmaf(p.w[pair], p.ypart[(size_t)pair * p.H + n], acc);
+        if (e >= 0 && e < p.E && weight_slot(p, e) >= 0) acc = fmaf(p.w[pair], p.ypart[(size_t)pair * p.H + n], acc);
     }
     if (p.has_shared) acc += p.ypart[(size_t)(P + t) * p.H + n];
     p.out[(size_t)t * p.H + n] = (uint16_t)f32_to_bf16_rne(acc);
@@ -411,7 +437,7 @@ __global__ __launch_bounds__(256) void combine_prefill_kernel(PrefillParams p)
 
 size_t decode_workspace_bytes(int T, int k, int H, int I);
 int launch_decode(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
-                  const int32_t *, const uint8_t *, uint16_t *, void *, hipStream_t);
+                  const int32_t *, const uint8_t *, uint16_t *, int32_t *, void *, hipStream_t);
 
 size_t prefill_workspace_bytes(int T, int k, int H, int I, int E)
 {
@@ -422,8 +448,8 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I, int E)
 }
 
 int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const int32_t *ids, const float *w,
-                   const int32_t *offsets, const int32_t *sorted, const uint8_t *gate, uint16_t *out, void *ws,
-                   hipStream_t stream)
+                   const int32_t *offsets, const int32_t *sorted, const uint8_t *gate, uint16_t *out, int32_t *miss_count,
+                   void *ws, hipStream_t stream)
 {
     if ((L->n_slots > 0 && gate != nullptr) || L->I % 128 || L->H % 256) {
         // the FP4 delta on gated tokens is fused only into the GEMV kernels, and
@@ -431,7 +457,7 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
         if ((int64_t)T * k + (T + 1) / 2 > 65535)
             return fail(MOET_EUNSUPPORTED, "this batch needs the GEMV kernels (delta cache, or I %% 128 / H %% 256 "
                                             "not 0), which take at most T*top_k + T/2 = 65535 entries");
-        return launch_decode(L, x, T, k, ids, w, offsets, sorted, gate, out, ws, stream);
+        return launch_decode(L, x, T, k, ids, w, offsets, sorted, gate, out, miss_count, ws, stream);
     }
     PrefillParams p;
     p.x = x;
@@ -450,6 +476,9 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     p.sh13 = L->shared13;
     p.sh2 = L->shared2;
     p.swiglu_limit = L->swiglu_limit;
+    p.base_slot = L->base_slot_of_expert;
+    p.n_base_slots = L->n_base_slots;
+    p.miss_count = miss_count;
     const size_t rows = (size_t)T * k + T;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     char *base = static_cast<char *>(ws);

@@ -53,11 +53,11 @@ int launch_requant(const uint8_t *, const uint8_t *, const float *, int64_t, int
 int launch_route(const float *, int, int, int, int, int, float, int32_t *, float *, int32_t *, int32_t *, hipStream_t);
 size_t decode_workspace_bytes(int T, int k, int H, int I);
 int launch_decode(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
-                  const int32_t *, const uint8_t *, uint16_t *, void *, hipStream_t);
+                  const int32_t *, const uint8_t *, uint16_t *, int32_t *, void *, hipStream_t);
 int launch_delta(const moet_fp4 *, int, int, int, const uint16_t *, const int32_t *, int, float *, hipStream_t);
 size_t prefill_workspace_bytes(int T, int k, int H, int I, int E);
 int launch_prefill(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
-                   const int32_t *, const uint8_t *, uint16_t *, void *, hipStream_t);
+                   const int32_t *, const uint8_t *, uint16_t *, int32_t *, void *, hipStream_t);
 
 static bool w2_ok(const moet_w2 &w) { return aligned16(w.codes) && aligned16(w.scales) && aligned16(w.scale2); }
 static bool fp4_ok(const moet_fp4 &w) { return aligned16(w.codes) && aligned16(w.scales) && aligned16(w.scale2); }
@@ -68,10 +68,13 @@ static int check_layer(const moet_layer *L)
     if (L->H <= 0 || L->I <= 0 || L->H % 128 || L->I % 128)
         return fail(MOET_EINVAL, "H (%d) and I (%d) must be positive multiples of 128", L->H, L->I);
     if (L->E < 1 || L->E > 1024) return fail(MOET_EINVAL, "E (%d) must be in [1, 1024]", L->E);
-    if (!w2_ok(L->w13) || !w2_ok(L->w2)) return fail(MOET_EINVAL, "w13 / w2 pointers must be non-NULL and 16-byte aligned");
+    if ((!L->base_slot_of_expert || L->n_base_slots > 0) && (!w2_ok(L->w13) || !w2_ok(L->w2)))
+        return fail(MOET_EINVAL, "w13 / w2 pointers must be non-NULL and 16-byte aligned");
     if (L->has_shared && (!w2_ok(L->shared13) || !w2_ok(L->shared2)))
         return fail(MOET_EINVAL, "shared expert pointers must be non-NULL and 16-byte aligned");
     if (L->n_slots < 0) return fail(MOET_EINVAL, "n_slots (%d) must be >= 0", L->n_slots);
+    if (L->base_slot_of_expert && (!aligned16(L->base_slot_of_expert) || L->n_base_slots < 0))
+        return fail(MOET_EINVAL, "expert cache: base_slot_of_expert must be 16-byte aligned and n_base_slots >= 0");
     if (L->n_slots > 0 && (!aligned16(L->slot_of_expert) || !fp4_ok(L->d13) || !fp4_ok(L->d2)))
         return fail(MOET_EINVAL, "delta cache pointers must be non-NULL and 16-byte aligned");
     if (!(L->swiglu_limit >= 0.f)) return fail(MOET_EINVAL, "swiglu_limit must be >= 0");
@@ -102,7 +105,7 @@ const char *moet_status_str(int s)
 
 const char *moet_last_error(void) { return g_err; }
 
-int moet_abi_version(void) { return 1; }
+int moet_abi_version(void) { return 2; }
 
 int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
                  int64_t N, int64_t K, uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2,
@@ -151,7 +154,8 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k)
 
 int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k, const int32_t *topk_ids,
                      const float *topk_w, const int32_t *expert_offsets, const int32_t *sorted_pairs,
-                     const uint8_t *gate_flags, uint16_t *out, void *workspace, size_t workspace_bytes, void *stream)
+                     const uint8_t *gate_flags, uint16_t *out, int32_t *miss_count, void *workspace,
+                     size_t workspace_bytes, void *stream)
 {
     g_err[0] = 0;
     int rc = check_layer(L);
@@ -162,15 +166,16 @@ int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t 
         !aligned16(sorted_pairs) || !aligned16(out))
         return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
     if (gate_flags && !aligned16(gate_flags)) return fail(MOET_EINVAL, "gate_flags must be 16-byte aligned");
+    if (miss_count && (reinterpret_cast<uintptr_t>(miss_count) & 3u)) return fail(MOET_EINVAL, "miss_count must be 4-byte aligned");
     const size_t need = moet_moe_workspace_bytes(L, T, top_k);
     if (!workspace || workspace_bytes < need)
         return fail(MOET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOET_EINVAL, "workspace must be 256-byte aligned");
     if (use_decode(T, top_k))
-        return launch_decode(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, workspace,
-                             (hipStream_t)stream);
-    return launch_prefill(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, workspace,
-                          (hipStream_t)stream);
+        return launch_decode(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count,
+                             workspace, (hipStream_t)stream);
+    return launch_prefill(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count,
+                          workspace, (hipStream_t)stream);
 }
 
 int moet_set_timing_events(void *start, void *stop)

@@ -37,7 +37,8 @@ class FP4(ctypes.Structure):
 class LayerC(ctypes.Structure):
     _fields_ = [("H", _i32), ("I", _i32), ("E", _i32), ("w13", W2), ("w2", W2), ("has_shared", _i32),
                 ("shared13", W2), ("shared2", W2), ("n_slots", _i32), ("slot_of_expert", _vp),
-                ("d13", FP4), ("d2", FP4), ("swiglu_limit", ctypes.c_float)]
+                ("d13", FP4), ("d2", FP4), ("swiglu_limit", ctypes.c_float),
+                ("base_slot_of_expert", _vp), ("n_base_slots", _i32)]
 
 
 _lib = None
@@ -68,7 +69,7 @@ def lib():
         L.moet_moe_workspace_bytes.argtypes = [ctypes.POINTER(LayerC), _i32, _i32]
         L.moet_moe_workspace_bytes.restype = ctypes.c_size_t
         L.moet_moe_forward.argtypes = [ctypes.POINTER(LayerC), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                       ctypes.c_size_t, _vp]
+                                       _vp, ctypes.c_size_t, _vp]
         L.moet_moe_forward.restype = ctypes.c_int
         L.moet_delta_forward.argtypes = [ctypes.POINTER(FP4), _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp]
         L.moet_delta_forward.restype = ctypes.c_int
@@ -193,6 +194,8 @@ class Layer:
     d13: Optional[FP4Planes] = None                 # 2*n_slots matrices [I][H]
     d2: Optional[FP4Planes] = None                  # n_slots matrices [H][I]
     swiglu_limit: float = 0.0
+    # expert cache: w13/w2 hold only the experts with base_slot_of_expert[e] >= 0 (int32 [E]), at that slot
+    base_slot_of_expert: Optional[torch.Tensor] = None
 
     def c(self) -> LayerC:
         z = W2(None, None, None)
@@ -204,7 +207,33 @@ class Layer:
                       self.shared2.c() if self.shared2 is not None else z,
                       n_slots, self.slot_of_expert.data_ptr() if n_slots else None,
                       self.d13.c() if n_slots else zf, self.d2.c() if n_slots else zf,
-                      float(self.swiglu_limit))
+                      float(self.swiglu_limit),
+                      self.base_slot_of_expert.data_ptr() if self.base_slot_of_expert is not None else None,
+                      int(self.w2.scale2.numel()) if self.base_slot_of_expert is not None else 0)
+
+
+def expert_cache(layer: Layer, slot_of_expert) -> Layer:
+    """A copy of ``layer`` whose w13/w2 stacks hold only the experts with slot_of_expert[e] >= 0 (int [E],
+    host array or tensor), each at its slot; the others are missing from the cache (their routings
+    contribute nothing and are counted by moe_forward's miss_count).  Shared expert and delta cache are
+    kept as they are."""
+    import dataclasses
+    soe = torch.as_tensor(slot_of_expert, dtype=torch.int64).cpu()
+    if soe.numel() != layer.E:
+        raise ValueError(f"slot_of_expert has {soe.numel()} entries, the layer {layer.E} experts")
+    n = int(soe.max().item()) + 1 if bool((soe >= 0).any()) else 1
+    order = torch.zeros(n, dtype=torch.int64)      # slot -> expert (an unused slot repeats expert 0)
+    res = torch.nonzero(soe >= 0).flatten()
+    order[soe[res]] = res
+    dev = layer.w2.codes.device
+    idx13 = torch.stack([2 * order, 2 * order + 1], 1).reshape(-1).to(dev)
+    idx2 = order.to(dev)
+
+    def pick(pl: W2Planes, idx) -> W2Planes:
+        return W2Planes(pl.codes[idx].contiguous(), pl.scales[idx].contiguous(), pl.scale2[idx].contiguous(),
+                        pl.N, pl.K)
+    return dataclasses.replace(layer, w13=pick(layer.w13, idx13), w2=pick(layer.w2, idx2),
+                               base_slot_of_expert=soe.to(torch.int32).to(dev))
 
 
 def moe_workspace_bytes(layer: Layer, T: int, top_k: int) -> int:
@@ -219,7 +248,7 @@ def alloc_workspace(layer: Layer, T: int, top_k: int, device="cuda") -> torch.Te
 
 def moe_forward(layer: Layer, x: torch.Tensor, topk_ids, topk_w, expert_offsets, sorted_pairs,
                 gate_flags: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                workspace: Optional[torch.Tensor] = None, miss_count: Optional[torch.Tensor] = None) -> torch.Tensor:
     _need(x, torch.bfloat16, "x")
     T, H = x.shape
     k = topk_ids.shape[1]
@@ -229,10 +258,12 @@ def moe_forward(layer: Layer, x: torch.Tensor, topk_ids, topk_w, expert_offsets,
         workspace = alloc_workspace(layer, T, k, x.device)
     if gate_flags is not None:
         _need(gate_flags, torch.uint8, "gate_flags")
+    if miss_count is not None:
+        _need(miss_count, torch.int32, "miss_count")
     Lc = layer.c()
     _check(lib().moet_moe_forward(ctypes.byref(Lc), _ptr(x), T, k, _ptr(topk_ids), _ptr(topk_w),
                                   _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(gate_flags), _ptr(out),
-                                  _ptr(workspace), workspace.numel(), _stream()))
+                                  _ptr(miss_count), _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 

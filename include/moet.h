@@ -18,7 +18,10 @@
  *                       down + routing-weighted combine, optional shared
  *                       expert), with the FP4 delta added for tokens flagged by
  *                       the confidence gate on experts resident in the delta
- *                       cache (README, "How it fits")
+ *                       cache (README, "How it fits"); optionally over a cache
+ *                       that holds only some experts' 2-bit planes, zeroing and
+ *                       counting routings to missing experts (README, "When the
+ *                       model doesn't fit at all — the GPU as an expert cache")
  *   moet_delta_forward  the standalone FP4 delta GEMM/GEMV (README, "How it fits")
  *
  * Conventions (all entry points):
@@ -163,6 +166,12 @@ typedef struct {
  * slot_of_expert int32 [E] (device; -1 = not resident), d13: stack of
  * 2*n_slots matrices [I][H] (slot s: gate 2s, up 2s+1), d2: n_slots matrices
  * [H][I].  swiglu_limit > 0 clamps gate <= L and |up| <= L before SwiGLU.
+ * Expert cache (README, "When the model doesn't fit at all — the GPU as an
+ * expert cache"): base_slot_of_expert == NULL means w13/w2 hold every expert
+ * as above.  Otherwise base_slot_of_expert int32 [E] (device) places expert e
+ * at cache slot base_slot_of_expert[e] of w13 (2*n_base_slots matrices) and
+ * w2 (n_base_slots matrices); a slot outside [0, n_base_slots) marks the
+ * expert missing: its routings contribute nothing and are counted.
  */
 typedef struct {
     int32_t H, I, E;
@@ -173,6 +182,8 @@ typedef struct {
     const int32_t *slot_of_expert;
     moet_fp4 d13, d2;
     float swiglu_limit;
+    const int32_t *base_slot_of_expert;
+    int32_t n_base_slots;
 } moet_layer;
 
 /* Workspace bytes moet_moe_forward needs for T tokens and top_k. */
@@ -185,6 +196,9 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
  *
  * x bf16 [T][H]; topk_ids/topk_w/expert_offsets/sorted_pairs as produced by
  * moet_route; gate_flags uint8 [T] (device, may be NULL = none flagged).
+ * miss_count int32 (device, may be NULL): set to the number of (token,
+ * expert) routings whose expert is missing from the expert cache (0 without
+ * a cache); the call writes it, the caller need not clear it.
  * For every pair (t, e): u = W13_e x_t (+ D13_slot x_t when gate_flags[t] and
  * slot_of_expert[e] >= 0), h = bf16(silu(u_gate) * u_up), y = W2_e h
  * (+ D2_slot h); out bf16 [T][H] = bf16(sum_j topk_w[t][j] * y_(t,j) +
@@ -205,7 +219,7 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
 int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
                      const int32_t *topk_ids, const float *topk_w,
                      const int32_t *expert_offsets, const int32_t *sorted_pairs,
-                     const uint8_t *gate_flags, uint16_t *out,
+                     const uint8_t *gate_flags, uint16_t *out, int32_t *miss_count,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*

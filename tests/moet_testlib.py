@@ -87,11 +87,11 @@ class OracleLayer:
         dn = self._mat(self.src.shared2, 0, False)
         return g.w2bit(), u.w2bit(), dn.w2bit()
 
-    def forward(self, x_bits, ids, w, gate_flags=None, tokens=None):
+    def forward(self, x_bits, ids, w, gate_flags=None, tokens=None, resident=None):
         return OFF.moe_forward(x_bits, ids, w, self.expert_weights, self.shared_weights(),
                                gate_flags=gate_flags, slot_of_expert=self.soe,
                                delta_weights=self.delta_weights_of_slot if self.soe is not None else None,
-                               swiglu_limit=self.cfg.swiglu_limit, tokens=tokens)
+                               swiglu_limit=self.cfg.swiglu_limit, tokens=tokens, resident=resident)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -66,7 +66,7 @@ def _layer(H=256, I=128, E=8):
     from bit_moe_expert_nvfp4_amd import moet
     z = moet.W2(16, 16, 16)
     return moet.LayerC(H, I, E, z, z, 0, moet.W2(None, None, None), moet.W2(None, None, None), 0, None,
-                       moet.FP4(None, None, None), moet.FP4(None, None, None), 0.0)
+                       moet.FP4(None, None, None), moet.FP4(None, None, None), 0.0, None, 0)
 
 
 def test_forward_rejects_bad_args_and_short_workspace(L):
@@ -77,22 +77,31 @@ def test_forward_rejects_bad_args_and_short_workspace(L):
     assert need > 0
     assert L.moet_moe_workspace_bytes(ctypes.byref(lay), 8, 2) >= need
     # short workspace
-    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, b, need - 1, None) == 3
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, None, b, need - 1, None) == 3
     # bad shapes
     for H, I, E in [(200, 128, 8), (256, 64, 8), (256, 128, 0), (256, 128, 2000)]:
         bad = _layer(H, I, E)
-        assert L.moet_moe_forward(ctypes.byref(bad), b, 4, 2, b, b, b, b, None, b, b, 1 << 30, None) == 1
-    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 9, b, b, b, b, None, b, b, 1 << 30, None) == 1
-    assert L.moet_moe_forward(ctypes.byref(lay), b, 0, 2, b, b, b, b, None, b, b, 1 << 30, None) == 1
+        assert L.moet_moe_forward(ctypes.byref(bad), b, 4, 2, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 9, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 0, 2, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
     # delta cache with missing pointers
     lay.n_slots = 2
-    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, b, 1 << 30, None) == 1
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
     # shared expert with missing pointers
     lay2 = _layer()
     lay2.has_shared = 1
-    assert L.moet_moe_forward(ctypes.byref(lay2), b, 4, 2, b, b, b, b, None, b, b, 1 << 30, None) == 1
+    assert L.moet_moe_forward(ctypes.byref(lay2), b, 4, 2, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
+    # misaligned miss counter; expert cache with a bad map or slot count
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, ctypes.c_void_p(258), b, 1 << 30,
+                              None) == 1
+    lay3 = _layer()
+    lay3.base_slot_of_expert = ctypes.c_void_p(264)
+    assert L.moet_moe_forward(ctypes.byref(lay3), b, 4, 2, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
+    lay3.base_slot_of_expert = b
+    lay3.n_base_slots = -1
+    assert L.moet_moe_forward(ctypes.byref(lay3), b, 4, 2, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
     # unaligned workspace
-    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, ctypes.c_void_p(272), 1 << 30,
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, None, ctypes.c_void_p(272), 1 << 30,
                               None) == 1
 
 

@@ -253,3 +253,54 @@ def test_delta_forward_random_planes():
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     print(f"rel_l2={rel:.3e}", flush=True)
     assert rel <= 1e-5
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=3, E=16, k=4, shared=True, score=synth.SIGMOID),             # GEMV path
+    dict(T=300, E=16, k=8, H=512, I=256, score=synth.SIGMOID),          # grouped-GEMM path
+])
+def test_expert_cache_miss_and_replay(case):
+    """Missing experts contribute nothing and are counted; with every expert fetched (in another slot
+    order) the forward is bit-identical to the fully resident layer."""
+    cfg = _small_cfg(**case)
+    _print_case(f"expert cache {case}")
+    seed = zlib.crc32(str(sorted(case.items())).encode()) & 0xFFFF
+    src = synth.make_layer(cfg, seed=seed)
+    layer = moet.layer_from_nvfp4(src)
+    x = synth.make_activations(cfg.T, cfg.H, seed)
+    lg = synth.make_logits(cfg, seed)
+    xd = x.to(DEV)
+    ids, w, offs, pairs = moet.route(lg.to(DEV), cfg.k, cfg.score, cfg.renormalize)
+    o_ids, o_w, _, _ = oracle_route(lg, cfg.k, cfg.score, cfg.renormalize)
+    ol = OracleLayer(src)
+    rng = np.random.default_rng(seed)
+    resident = rng.random(cfg.E) < 0.5
+    resident[o_ids[0, 0]] = True          # at least one hit and (below) one miss
+    resident[o_ids[0, -1]] = False
+    soe = np.full(cfg.E, -1, dtype=np.int64)
+    soe[np.nonzero(resident)[0]] = rng.permutation(int(resident.sum()))
+    cached = moet.expert_cache(layer, soe)
+    miss = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    out = moet.moe_forward(cached, xd, ids, w, offs, pairs, miss_count=miss)
+    torch.cuda.synchronize()
+    ref = ol.forward(bf16_bits(x), o_ids, o_w, resident=resident)
+    err = rel_l2(bf16_bits(out), ref)
+    print(f"rel_l2={err:.3e} misses={int(miss.item())}", flush=True)
+    assert err <= REL_L2_BAR and err <= 3e-4 * max(1.0, cfg.H / 512)
+    assert int(miss.item()) == OFF.miss_count(o_ids, resident) > 0
+    # fetch every expert (a different slot order) and replay: bit-identical to the resident layer
+    full = moet.expert_cache(layer, rng.permutation(cfg.E))
+    again = moet.moe_forward(full, xd, ids, w, offs, pairs, miss_count=miss)
+    plain = moet.moe_forward(layer, xd, ids, w, offs, pairs)
+    torch.cuda.synchronize()
+    assert (bf16_bits(again) == bf16_bits(plain)).all()
+    assert int(miss.item()) == 0
+    # nothing resident: only the shared expert (or nothing) remains, every routing missed
+    none = moet.expert_cache(layer, np.full(cfg.E, -1))
+    out0 = moet.moe_forward(none, xd, ids, w, offs, pairs, miss_count=miss)
+    torch.cuda.synchronize()
+    ref0 = ol.forward(bf16_bits(x), o_ids, o_w, resident=np.zeros(cfg.E, bool))
+    assert rel_l2(bf16_bits(out0), ref0) <= 3e-4 or not np.any(OF.bf16_bits_to_f64(ref0))
+    if not cfg.shared:
+        assert (bf16_bits(out0) & 0x7FFF == 0).all()
+    assert int(miss.item()) == cfg.T * cfg.k

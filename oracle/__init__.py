@@ -19,5 +19,7 @@ Modules:
   layout   - packing of the oracle's plain arrays into the library's tiled
              storage layout (written independently of the kernels)
   route    - router top-k, routing weights, token permutation
-  ffn      - expert FFN with fixed rounding points, combine, FP4 GEMM
+  ffn      - expert FFN with fixed rounding points, combine, FP4 GEMM,
+             expert-cache residency mask and miss count
+  gate     - confidence gate (largest next-token probability below tau)
 """

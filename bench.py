@@ -282,6 +282,32 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_f
     return res
 
 
+def gate_leg(seed, dev, steps=200, V=151552):
+    """moet_confidence_gate on next-token logits of one decode step (T=3) and of 8 batched streams (T=24)."""
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet
+    res = {}
+    for T in (3, 24):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed + T)
+        lg = torch.randn((T, V), generator=g, device=dev) * torch.linspace(0.5, 14.0, T, device=dev).unsqueeze(1)
+        flags = torch.empty((T,), dtype=torch.uint8, device=dev)
+        for _ in range(10):
+            moet.confidence_gate(lg, 0.60, flags=flags)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            moet.confidence_gate(lg, 0.60, flags=flags)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        res[f"T{T}"] = {"workload": f"T={T} rows of V={V} fp32 next-token logits, tau=0.60",
+                        "us": round(us, 2), "GBps": round(T * V * 4 / (us * 1e-6) / 1e9, 1),
+                        "flagged": int(flags.sum().item())}
+    return res
+
+
 def prefill_leg(layer, cfg5, steps, seed, dev):
     """Time route + forward of a prefill chunk (MFMA grouped GEMM path) on one pool layer."""
     import numpy as np
@@ -507,6 +533,8 @@ def main():
         pl = dataclasses.replace(layers[0], shared13=None, shared2=None)
         result["prefill"] = prefill_leg(pl, synth.CONFIGS[5], args.prefill_steps, args.seed, dev)
     if not args.no_extra:
+        print("[bench] timing the confidence gate", file=sys.stderr, flush=True)
+        result["confidence_gate"] = gate_leg(args.seed, dev)
         del layers
         torch.cuda.empty_cache()
         result["other_decode"] = {}

@@ -55,6 +55,7 @@ size_t decode_workspace_bytes(int T, int k, int H, int I);
 int launch_decode(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
                   const int32_t *, const uint8_t *, uint16_t *, int32_t *, void *, hipStream_t);
 int launch_delta(const moet_fp4 *, int, int, int, const uint16_t *, const int32_t *, int, float *, hipStream_t);
+int launch_gate(const float *, int, int, float, uint8_t *, float *, hipStream_t);
 size_t prefill_workspace_bytes(int T, int k, int H, int I, int E);
 int launch_prefill(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
                    const int32_t *, const uint8_t *, uint16_t *, int32_t *, void *, hipStream_t);
@@ -201,6 +202,19 @@ int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
         !aligned16(row_slot) || !aligned16(acc))
         return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
     return launch_delta(D, n_slots, N, K, act, row_slot, R, acc, (hipStream_t)stream);
+}
+
+int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
+                         float *confidence_out, void *stream)
+{
+    g_err[0] = 0;
+    if (T < 1 || T > 65535) return fail(MOET_EINVAL, "T (%d) must be in [1, 65535]", T);
+    if (V < 1) return fail(MOET_EINVAL, "V (%d) must be >= 1", V);
+    if (!(tau == tau) || tau > 3.4e38f || tau < -3.4e38f) return fail(MOET_EINVAL, "tau must be finite");
+    if (!aligned16(logits) || !gate_flags) return fail(MOET_EINVAL, "logits (16-byte aligned) and gate_flags must be non-NULL");
+    if (confidence_out && (reinterpret_cast<uintptr_t>(confidence_out) & 3u))
+        return fail(MOET_EINVAL, "confidence_out must be 4-byte aligned");
+    return launch_gate(logits, T, V, tau, gate_flags, confidence_out, (hipStream_t)stream);
 }
 
 }  // extern "C"

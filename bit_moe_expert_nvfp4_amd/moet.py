@@ -73,6 +73,8 @@ def lib():
         L.moet_moe_forward.restype = ctypes.c_int
         L.moet_delta_forward.argtypes = [ctypes.POINTER(FP4), _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp]
         L.moet_delta_forward.restype = ctypes.c_int
+        L.moet_confidence_gate.argtypes = [_vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp]
+        L.moet_confidence_gate.restype = ctypes.c_int
         L.moet_set_timing_events.argtypes = [_vp, _vp]
         L.moet_set_timing_events.restype = ctypes.c_int
         _lib = L
@@ -280,6 +282,21 @@ def delta_forward(D: FP4Planes, act: torch.Tensor, row_slot: torch.Tensor, acc: 
     _check(lib().moet_delta_forward(ctypes.byref(Dc), int(D.scale2.numel()), D.N, K, _ptr(act), _ptr(row_slot), R,
                                     _ptr(acc), _stream()))
     return acc
+
+
+def confidence_gate(logits: torch.Tensor, tau: float = 0.60, flags: Optional[torch.Tensor] = None,
+                    confidence: Optional[torch.Tensor] = None):
+    """moet_confidence_gate: uint8 [T] flags (1 = largest next-token probability below tau) from fp32
+    logits [T, V]; optionally the confidence itself into an fp32 [T] tensor.  Returns the flags."""
+    _need(logits, torch.float32, "logits")
+    T, V = logits.shape
+    if flags is None:
+        flags = torch.empty((T,), dtype=torch.uint8, device=logits.device)
+    _need(flags, torch.uint8, "flags")
+    if confidence is not None:
+        _need(confidence, torch.float32, "confidence")
+    _check(lib().moet_confidence_gate(_ptr(logits), T, V, float(tau), _ptr(flags), _ptr(confidence), _stream()))
+    return flags
 
 
 def set_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cuda.Event]) -> None:

@@ -23,6 +23,9 @@
  *                       counting routings to missing experts (README, "When the
  *                       model doesn't fit at all — the GPU as an expert cache")
  *   moet_delta_forward  the standalone FP4 delta GEMM/GEMV (README, "How it fits")
+ *   moet_confidence_gate  the confidence gate: flags low-confidence tokens for
+ *                       the FP4 delta from their next-token logits (README,
+ *                       "How it fits")
  *
  * Conventions (all entry points):
  *  - Every array argument is DEVICE memory owned by the caller (e.g. a torch
@@ -236,6 +239,24 @@ int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t 
 int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
                        const uint16_t *act, const int32_t *row_slot, int32_t R, float *acc,
                        void *stream);
+
+/*
+ * moet_confidence_gate - flags the tokens whose next-token distribution is not
+ * confident, so that moet_moe_forward adds the FP4 delta for them.
+ * (README "Frontier MoE on consumer Blackwell (SM120)", section "How it fits
+ * — 2-bit experts at FP4 quality": the confidence gate re-runs low-confidence
+ * steps at FP4; its benchmark runs use tau = 0.60.)
+ *
+ * logits fp32 [T][V] (device; finite, or -inf for masked entries, with a
+ * finite maximum per row).  confidence(t) = max_v softmax(logits[t])_v =
+ * 1 / sum_v exp(l_v - l_max), computed in float64; gate_flags uint8 [T]
+ * (device) = 1 where confidence < tau, else 0; confidence_out fp32 [T]
+ * (device, may be NULL) receives the confidence rounded to fp32.
+ * Errors: MOET_EINVAL for T outside [1, 65535], V < 1, tau not finite, NULL
+ * or misaligned pointers (logits 16-byte aligned).
+ */
+int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
+                         float *confidence_out, void *stream);
 
 /*
  * moet_set_timing_events - benchmark instrumentation.  While set (per host

@@ -116,3 +116,16 @@ def test_delta_forward_rejects_bad_args(L):
     assert L.moet_delta_forward(None, 1, 64, 128, b, b, 1, b, None) == 1
     # R == 0 is a no-op that touches nothing
     assert L.moet_delta_forward(ctypes.byref(D), 1, 64, 128, b, b, 0, b, None) == 0
+
+
+def test_confidence_gate_rejects_bad_args(L):
+    b = ctypes.c_void_p(256)
+    f = ctypes.c_float(0.6)
+    assert L.moet_confidence_gate(b, 0, 10, f, b, None, None) == 1
+    assert L.moet_confidence_gate(b, 70000, 10, f, b, None, None) == 1
+    assert L.moet_confidence_gate(b, 2, 0, f, b, None, None) == 1
+    assert L.moet_confidence_gate(b, 2, 10, ctypes.c_float(float("nan")), b, None, None) == 1
+    assert L.moet_confidence_gate(None, 2, 10, f, b, None, None) == 1
+    assert L.moet_confidence_gate(ctypes.c_void_p(260), 2, 10, f, b, None, None) == 1
+    assert L.moet_confidence_gate(b, 2, 10, f, None, None, None) == 1
+    assert L.moet_confidence_gate(b, 2, 10, f, b, ctypes.c_void_p(258), None) == 1

@@ -304,3 +304,56 @@ def test_expert_cache_miss_and_replay(case):
     if not cfg.shared:
         assert (bf16_bits(out0) & 0x7FFF == 0).all()
     assert int(miss.item()) == cfg.T * cfg.k
+
+
+@pytest.mark.parametrize("T,V", [(64, 151552), (5, 1001), (1, 4)])
+def test_confidence_gate(T, V):
+    """Flags and confidence against the oracle (largest next-token probability below tau = 0.60, decided
+    in float64 on both sides); rows are scaled from flat to sharp, some logits masked to -inf."""
+    from oracle import gate as OG
+    _print_case(f"confidence gate T={T} V={V}")
+    g = torch.Generator().manual_seed(T * 7 + V)
+    lg = torch.randn((T, V), generator=g) * torch.linspace(0.5, 14.0, T).unsqueeze(1)
+    if V > 8:
+        lg[:, ::7] = float("-inf")
+        lg[:, 1] = lg[:, 1].clamp(min=0.0)            # a finite maximum in every row
+    tau = 0.60
+    conf = torch.empty((T,), dtype=torch.float32, device=DEV)
+    flags = moet.confidence_gate(lg.to(DEV), tau, confidence=conf)
+    again = moet.confidence_gate(lg.to(DEV), tau)
+    torch.cuda.synchronize()
+    ref_c = OG.confidence(np_(lg))
+    ref_f = OG.gate_flags(np_(lg), tau)
+    # decisions closer than 1e-9 (relative) to tau may round either way; none of these rows is that close
+    assert (np.abs(ref_c - np.float32(tau)) > 1e-9 * tau).all()
+    assert (np_(flags) == ref_f).all() and (np_(again) == np_(flags)).all()
+    assert np.allclose(np_(conf), ref_c, rtol=1e-6, atol=0)
+    if T > 4:
+        assert 0 < ref_f.sum() < T           # both outcomes occur
+
+
+def test_confidence_gate_feeds_delta_forward():
+    """Gate flags from next-token logits select the tokens that take the FP4 delta in the forward."""
+    from oracle import gate as OG
+    cfg = _small_cfg(T=6, E=8, k=2, n_resident=4, n_flagged=0, score=synth.SIGMOID)
+    _print_case("gate -> forward")
+    seed = 4242
+    src = synth.make_layer(cfg, seed=seed)
+    soe = torch.full((cfg.E,), -1, dtype=torch.int32)
+    soe[torch.tensor([0, 2, 5, 7])] = torch.arange(4, dtype=torch.int32)
+    layer = moet.layer_from_nvfp4(src, soe)
+    x = synth.make_activations(cfg.T, cfg.H, seed)
+    lg = synth.make_logits(cfg, seed)
+    nt = torch.randn((cfg.T, 32000), generator=torch.Generator().manual_seed(5)) * torch.tensor(
+        [0.5, 20.0, 1.0, 30.0, 0.2, 25.0]).unsqueeze(1)
+    flags = moet.confidence_gate(nt.to(DEV), 0.60)
+    ids, w, offs, pairs = moet.route(lg.to(DEV), cfg.k, cfg.score, cfg.renormalize)
+    out = moet.moe_forward(layer, x.to(DEV), ids, w, offs, pairs, flags)
+    torch.cuda.synchronize()
+    ref_flags = OG.gate_flags(np_(nt), 0.60)
+    assert (np_(flags) == ref_flags).all() and 0 < ref_flags.sum() < cfg.T
+    o_ids, o_w, _, _ = oracle_route(lg, cfg.k, cfg.score, cfg.renormalize)
+    ref = OracleLayer(src, soe).forward(bf16_bits(x), o_ids, o_w, gate_flags=ref_flags)
+    err = rel_l2(bf16_bits(out), ref)
+    print(f"rel_l2={err:.3e}", flush=True)
+    assert err <= REL_L2_BAR and err <= 3e-4

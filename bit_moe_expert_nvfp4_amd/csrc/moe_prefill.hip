@@ -410,28 +410,44 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
 
 // out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order;
 // routings to experts missing from the expert cache contribute nothing and are
-// counted once per token (by the first column block)
+// counted once per token (by the first column block).  The token's ids and
+// weights are wave-uniform (scalar loads) and all its y loads are issued
+// before the sum, so the kernel pays about two memory round trips.
+constexpr int kCombineMaxK = 16;
+
 __global__ __launch_bounds__(256) void combine_prefill_kernel(PrefillParams p)
 {
     const int n = blockIdx.x * 256 + threadIdx.x;
     const int t = blockIdx.y;
     const int P = p.T * p.k;
-    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0) {
-        int miss = 0;
-        for (int j = 0; j < p.k; ++j) {
-            const int e = p.ids[t * p.k + j];
-            if (e >= 0 && e < p.E && weight_slot(p, e) < 0) ++miss;
-        }
-        if (miss) atomicAdd(p.miss_count, miss);
+    const cu32 *idr = as_const(p.ids + (size_t)t * p.k);
+    const cu32 *wr = as_const(p.w + (size_t)t * p.k);
+    int e[kCombineMaxK];
+    float wt[kCombineMaxK];
+#pragma unroll
+    for (int j = 0; j < kCombineMaxK; ++j) {
+        e[j] = (j < p.k) ? (int)idr[j] : -1;
+        wt[j] = (j < p.k) ? __uint_as_float(wr[j]) : 0.f;
     }
+    bool live[kCombineMaxK];
+    int miss = 0;
+#pragma unroll
+    for (int j = 0; j < kCombineMaxK; ++j) {
+        const bool valid = e[j] >= 0 && e[j] < p.E;
+        live[j] = valid && weight_slot(p, e[j]) >= 0;
+        miss += (valid && !live[j]) ? 1 : 0;
+    }
+    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0 && miss) atomicAdd(p.miss_count, miss);
     if (n >= p.H) return;
+    float y[kCombineMaxK];
+#pragma unroll
+    for (int j = 0; j < kCombineMaxK; ++j) y[j] = live[j] ? p.ypart[(size_t)(t * p.k + j) * p.H + n] : 0.f;
+    const float ysh = p.has_shared ? p.ypart[(size_t)(P + t) * p.H + n] : 0.f;
     float acc = 0.f;
-    for (int j = 0; j < p.k; ++j) {
-        const int pair = t * p.k + j;
-        const int e = p.ids[pair];
-        if (e >= 0 && e < p.E && weight_slot(p, e) >= 0) acc = fmaf(p.w[pair], p.ypart[(size_t)pair * p.H + n], acc);
-    }
-    if (p.has_shared) acc += p.ypart[(size_t)(P + t) * p.H + n];
+#pragma unroll
+    for (int j = 0; j < kCombineMaxK; ++j)
+        if (live[j]) acc = fmaf(wt[j], y[j], acc);
+    if (p.has_shared) acc += ysh;
     p.out[(size_t)t * p.H + n] = (uint16_t)f32_to_bf16_rne(acc);
 }
 

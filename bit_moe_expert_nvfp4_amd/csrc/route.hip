@@ -158,10 +158,16 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float *__restri
     for (int t = wave; t < T; t += nwaves) topk_any(logits, t, E, k, fn, renorm, rscale, ids, w, s_ids, s_scr[wave]);
     __syncthreads();
     const int P = T * k;
-    // offsets[e] = number of pairs routed to experts < e
+    // offsets[e] = number of pairs routed to experts < e (LDS reads in unrolled
+    // groups of 8 so their latencies overlap; s_ids is padded with E)
+    for (int p = P + tid; p < ((P + 7) & ~7); p += nthr) s_ids[p] = E;
+    __syncthreads();
     for (int e = tid; e <= E; e += nthr) {
         int c = 0;
-        for (int p = 0; p < P; ++p) c += (s_ids[p] < e) ? 1 : 0;
+        for (int p = 0; p < P; p += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c += (s_ids[p + u] < e) ? 1 : 0;
+        }
         s_off[e] = c;
         offsets[e] = c;
     }
@@ -169,7 +175,10 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float *__restri
     for (int p = tid; p < P; p += nthr) {
         const int e = s_ids[p];
         int rank = 0;
-        for (int q = 0; q < p; ++q) rank += (s_ids[q] == e) ? 1 : 0;
+        for (int q = 0; q < p; q += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rank += (q + u < p && s_ids[q + u] == e) ? 1 : 0;
+        }
         sorted[s_off[e] + rank] = p;
     }
 }

@@ -77,9 +77,10 @@ def _gen(device, *parts) -> torch.Generator:
 _E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
 
 
-def nvfp4_export(W: torch.Tensor):
+def nvfp4_export(W: torch.Tensor, plus_zeros: bool = False):
     """modelopt-style NVFP4 export of one fp32 matrix [N, K] (synthetic checkpoint maker).
 
+    plus_zeros: write every zero code as +0, as an export from integer weights does.
     Returns (codes uint8 [N, K/2], scales uint8 [N, K/16], scale_2 float32 0-dim)."""
     N, K = W.shape
     amax = W.abs().amax().clamp_min(1e-30)
@@ -92,13 +93,15 @@ def nvfp4_export(W: torch.Tensor):
                     torch.zeros_like(blk))
     bounds = torch.tensor(_E2M1_MIDPOINTS, dtype=torch.float32, device=W.device)
     mag = torch.bucketize(r.abs().contiguous(), bounds, right=False).to(torch.uint8)
-    code = mag | ((blk < 0).to(torch.uint8) << 3)
+    neg = (blk < 0) & (mag > 0) if plus_zeros else (blk < 0)
+    code = mag | (neg.to(torch.uint8) << 3)
     code = code.view(N, K)
     packed = (code[:, 0::2] & 15) | ((code[:, 1::2] & 15) << 4)
     return packed.contiguous(), s.view(torch.uint8).contiguous(), scale_2
 
 
-def make_nvfp4_stack(n_mat: int, N: int, K: int, seed: int, tag: str, device="cpu", std: float = 0.02):
+def make_nvfp4_stack(n_mat: int, N: int, K: int, seed: int, tag: str, device="cpu", std: float = 0.02,
+                     plus_zeros: bool = False):
     """A stack of n_mat NVFP4 matrices [N, K]; matrix i is seeded by (seed, tag, i)."""
     codes = torch.empty((n_mat, N, K // 2), dtype=torch.uint8, device=device)
     scales = torch.empty((n_mat, N, K // 16), dtype=torch.uint8, device=device)
@@ -106,10 +109,67 @@ def make_nvfp4_stack(n_mat: int, N: int, K: int, seed: int, tag: str, device="cp
     for i in range(n_mat):
         g = _gen(device, seed, tag, i)
         W = torch.randn((N, K), generator=g, device=device, dtype=torch.float32) * std
-        c, s, sc2 = nvfp4_export(W)
+        c, s, sc2 = nvfp4_export(W, plus_zeros=plus_zeros)
         codes[i], scales[i], s2[i] = c, s, sc2
         del W
     return codes, scales, s2
+
+
+def mxfp4_export(W: torch.Tensor):
+    """OCP microscaling FP4 export of one fp32 matrix [N, K]: per 32 weights along K
+    the e8m0 scale is 2^(floor(log2(amax32)) - 2) (2 = the largest e2m1 exponent),
+    E = 127 for an all-zero block; each weight is the nearest e2m1 magnitude to
+    W / scale (ties to the smaller magnitude, saturating at 6) with W's sign.
+    Returns (codes uint8 [N, K/2], scales uint8 [N, K/32])."""
+    N, K = W.shape
+    blk = W.view(N, K // 32, 32)
+    bmax = blk.abs().amax(dim=-1)
+    _, ex = torch.frexp(bmax)                       # bmax = f * 2^ex, 0.5 <= f < 1
+    E = torch.where(bmax > 0, ex - 1 - 2 + 127, torch.full_like(ex, 127)).clamp(0, 254)
+    scale = torch.exp2((E - 127).to(torch.float64)).to(torch.float32).unsqueeze(-1)
+    r = blk / scale
+    bounds = torch.tensor(_E2M1_MIDPOINTS, dtype=torch.float32, device=W.device)
+    mag = torch.bucketize(r.abs().contiguous(), bounds, right=False).to(torch.uint8)
+    code = (mag | ((blk < 0).to(torch.uint8) << 3)).view(N, K)
+    packed = (code[:, 0::2] & 15) | ((code[:, 1::2] & 15) << 4)
+    return packed.contiguous(), E.to(torch.uint8).contiguous()
+
+
+def fp8_block_export(W: torch.Tensor):
+    """FP8 block-quant export of one fp32 matrix [N, K]: one fp32 scale per
+    128 x 128 block, amax / 448 (1 for an all-zero block); weight = e4m3fn
+    nearest-even cast of W / scale (torch's float8 cast).
+    Returns (w uint8 [N, K], bscale float32 [ceil(N/128), K/128])."""
+    N, K = W.shape
+    Np = (N + 127) // 128 * 128
+    Wp = torch.zeros((Np, K), dtype=torch.float32, device=W.device)
+    Wp[:N] = W
+    blk = Wp.view(Np // 128, 128, K // 128, 128)
+    bmax = blk.abs().amax(dim=(1, 3))
+    s = torch.where(bmax > 0, bmax / 448.0, torch.ones_like(bmax))
+    q = (blk / s[:, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).reshape(Np, K)[:N].contiguous(), s.contiguous()
+
+
+def make_mxfp4_stack(n_mat: int, N: int, K: int, seed: int, tag: str, std: float = 0.02):
+    """A stack of n_mat MXFP4 matrices [N, K] (codes [n_mat, N, K/2], e8m0 scales [n_mat, N, K/32])."""
+    codes = torch.empty((n_mat, N, K // 2), dtype=torch.uint8)
+    scales = torch.empty((n_mat, N, K // 32), dtype=torch.uint8)
+    for i in range(n_mat):
+        W = torch.randn((N, K), generator=_gen("cpu", seed, tag, i), dtype=torch.float32) * std
+        codes[i], scales[i] = mxfp4_export(W)
+    return codes, scales
+
+
+def make_fp8_stack(n_mat: int, N: int, K: int, seed: int, tag: str, std: float = 0.02):
+    """A stack of n_mat FP8 block-quant matrices [N, K] (weights [n_mat, N, K], scales
+    [n_mat, ceil(N/128), K/128])."""
+    w = torch.empty((n_mat, N, K), dtype=torch.uint8)
+    s = torch.empty((n_mat, (N + 127) // 128, K // 128), dtype=torch.float32)
+    for i in range(n_mat):
+        W = torch.randn((N, K), generator=_gen("cpu", seed, tag, i), dtype=torch.float32) * std
+        w[i], s[i] = fp8_block_export(W)
+    return w, s
 
 
 @dataclass

@@ -26,6 +26,12 @@
  *    over all finite non-negative e4m3 codes t = 0x00..0x7E, ties -> smaller t;
  *  - element code = (s << 1) | m with s = the NVFP4 sign bit (also for -0) and
  *    m = 1 iff 2|Y| > 5a (a tie keeps magnitude 1); levels: 0:+1 1:+4 2:-1 3:-4;
+ *  - zero-sign balancing (same README, section "Kimi-K2.7-Code (1T MoE) on
+ *    4x RTX PRO 6000": an export that writes every exact zero as +0 biases the
+ *    2-bit weights, and the fix balances the zero signs): when asked for, the
+ *    zeros of a block take alternating signs in k order, the first one +, and
+ *    the source sign bit of a zero is ignored.  Zeros cost a^2 whatever their
+ *    sign, so the block scale does not change;
  *  - delta D = Y_nvfp4 - Y_2bit (exact integer in units of u), re-encoded as
  *    NVFP4 with the source scale_2: block-16 scale = e4m3 nearest (ties to the
  *    even code, saturating at 448) to max|D| / (6 * 2^10); element = e2m1
@@ -35,6 +41,7 @@
  * All arithmetic is int64 and exact.  OpenMP parallelises over rows only.
  */
 #include <stdint.h>
+#include <math.h>
 #include <stdlib.h>
 
 /* e4m3fn value * 2^9 for the finite non-negative codes 0x00..0x7E. */
@@ -63,7 +70,7 @@ static inline int nib(const uint8_t *row, int64_t k)
 
 /* Returns 0 on success, -1 if a block scale byte is negative or NaN. */
 int oracle_requant(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                   int64_t B, uint8_t *codes2, uint8_t *tau, int64_t *err_out)
+                   int64_t B, int balance, uint8_t *codes2, uint8_t *tau, int64_t *err_out)
 {
     int64_t T9[127];
     for (int t = 0; t < 127; ++t)
@@ -101,9 +108,12 @@ int oracle_requant(const uint8_t *codes, const uint8_t *scales, int64_t N, int64
             if (err_out)
                 err_out[n * nb + b] = best_err;
             int64_t a = 4 * T9[best_t];
+            int zeros = 0;
             for (int64_t i = 0; i < B; ++i) {
                 int64_t k = b * B + i;
                 int s = (nib(crow, k) >> 3) & 1;
+                if (balance && y[i] == 0)
+                    s = (zeros++) & 1;
                 int m = (2 * y[i] > 5 * a) ? 1 : 0;
                 codes2[n * K + k] = (uint8_t)((s << 1) | m);
             }
@@ -177,4 +187,94 @@ int oracle_delta(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t
         }
     }
     return bad ? -1 : 0;
+}
+
+/*
+ * FP8 block-quantised source (README "Frontier MoE on consumer Blackwell
+ * (SM120)", section "How it fits — 2-bit experts at FP4 quality": FP8
+ * block-quant checkpoints are requantised to the same sign-symmetric codebook
+ * at load, in float64).  Readings taken where the pages say no more:
+ *  - source: e4m3fn weights [N][K] and one fp32 scale per 128 x 128 block,
+ *    [ceil(N/128)][K/128]; weight = e4m3(code) * scale;
+ *  - the 2-bit tensor scale is a power of two, S = 2^p with p the smallest
+ *    integer >= -149 (so that S is a float32) such that 4 * 448 * S >= amax
+ *    (the largest level at the largest e4m3 block scale covers the largest
+ *    weight), S = 1 for an all-zero tensor;
+ *  - per block of B weights along K the e4m3 scale t minimises
+ *        Err(t) = sum_i min((y_i - a)^2, (y_i - 4a)^2),  a = e4m3(t) * S,
+ *    y_i = |weight|, evaluated in float64 in this order: d1 = y - a,
+ *    d4 = y - 4a, q = min(d1*d1, d4*d4), Err += q for i = 0..B-1 in k order,
+ *    over every finite code t = 0x00..0x7E, ties -> smaller t.  y_i and a are
+ *    exact in float64; the squares and the sum are rounded, so the decision is
+ *    the one this float64 evaluation makes;
+ *  - element code as for NVFP4: m = 1 iff 2y > 5a (exact), sign from the e4m3
+ *    sign bit, or balanced zeros when asked for.
+ * Returns 0, or -1 for a NaN weight code or a negative / non-finite block
+ * scale.  Compile with -ffp-contract=off.
+ */
+static double e4m3_f64(int t) { return (double)e4m3_x512(t) / 512.0; }
+
+int oracle_requant_fp8(const uint8_t *w, const float *bscale, int64_t N, int64_t K, int64_t B,
+                       int balance, uint8_t *codes2, uint8_t *tau, float *scale2_out)
+{
+    const int64_t KB = K / 128;
+    double amax = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int c = w[n * K + k] & 0x7F;
+            float s = bscale[(n / 128) * KB + k / 128];
+            if (c == 0x7F || !(s >= 0.0f) || s > 3.4028235e38f)
+                return -1;
+            double y = e4m3_f64(c) * (double)s;
+            if (y > amax)
+                amax = y;
+        }
+    int p = 0;
+    if (amax > 0.0) {
+        p = -149;
+        while (1792.0 * ldexp(1.0, p) < amax)
+            ++p;
+    }
+    const double S = ldexp(1.0, p);
+    *scale2_out = (float)S;
+    const int64_t nb = K / B;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t n = 0; n < N; ++n) {
+        double *y = (double *)malloc(sizeof(double) * B);
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int64_t i = 0; i < B; ++i) {
+                int64_t k = b * B + i;
+                y[i] = e4m3_f64(w[n * K + k] & 0x7F) * (double)bscale[(n / 128) * KB + k / 128];
+            }
+            int best_t = 0;
+            double best_err = -1.0;
+            for (int t = 0; t < 127; ++t) {
+                double a = e4m3_f64(t) * S;
+                double a4 = 4.0 * a;
+                double e = 0.0;
+                for (int64_t i = 0; i < B; ++i) {
+                    double d1 = y[i] - a, d4 = y[i] - a4;
+                    double q1 = d1 * d1, q4 = d4 * d4;
+                    e += q1 < q4 ? q1 : q4;
+                }
+                if (best_err < 0.0 || e < best_err) {
+                    best_err = e;
+                    best_t = t;
+                }
+            }
+            tau[n * nb + b] = (uint8_t)best_t;
+            double a = e4m3_f64(best_t) * S;
+            int zeros = 0;
+            for (int64_t i = 0; i < B; ++i) {
+                int64_t k = b * B + i;
+                int s = (w[n * K + k] >> 7) & 1;
+                if (balance && y[i] == 0.0)
+                    s = (zeros++) & 1;
+                int m = (2.0 * y[i] > 5.0 * a) ? 1 : 0;
+                codes2[n * K + k] = (uint8_t)((s << 1) | m);
+            }
+        }
+        free(y);
+    }
+    return 0;
 }

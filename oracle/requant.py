@@ -30,7 +30,7 @@ def build_oracle_lib(force: bool = False) -> str:
     """Compile the C oracle with gcc (OpenMP over rows)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC])
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC", "-o", tmp, _SRC])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -42,8 +42,10 @@ def _get():
         lib = ctypes.CDLL(_LIB)
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
-        lib.oracle_requant.argtypes = [p, p, i64, i64, i64, p, p, p]
+        lib.oracle_requant.argtypes = [p, p, i64, i64, i64, ctypes.c_int, p, p, p]
         lib.oracle_requant.restype = ctypes.c_int
+        lib.oracle_requant_fp8.argtypes = [p, p, i64, i64, i64, ctypes.c_int, p, p, p]
+        lib.oracle_requant_fp8.restype = ctypes.c_int
         lib.oracle_delta.argtypes = [p, p, i64, i64, i64, p, p, p, p]
         lib.oracle_delta.restype = ctypes.c_int
         _lib = lib
@@ -55,9 +57,11 @@ def _ptr(a):
 
 
 def requant(codes: np.ndarray, scales: np.ndarray, scale_2: float, block: int = BLOCK,
-            return_err: bool = False):
+            return_err: bool = False, balance_zero_signs: bool = False):
     """Requantise one NVFP4 matrix [N, K] (codes uint8 [N, K/2], scales uint8 [N, K/16]).
 
+    balance_zero_signs: zeros of a block take alternating signs (+, -, +, ...)
+    in k order instead of their own sign bit.
     Returns (codes2 uint8 [N, K] in 0..3, tau uint8 [N, K/block], scale2_out float32[, err int64]).
     """
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
@@ -68,8 +72,8 @@ def requant(codes: np.ndarray, scales: np.ndarray, scale_2: float, block: int = 
     codes2 = np.empty((N, K), dtype=np.uint8)
     tau = np.empty((N, K // block), dtype=np.uint8)
     err = np.empty((N, K // block), dtype=np.int64) if return_err else None
-    rc = _get().oracle_requant(_ptr(codes), _ptr(scales), N, K, block, _ptr(codes2), _ptr(tau),
-                               _ptr(err) if err is not None else None)
+    rc = _get().oracle_requant(_ptr(codes), _ptr(scales), N, K, block, int(bool(balance_zero_signs)),
+                               _ptr(codes2), _ptr(tau), _ptr(err) if err is not None else None)
     if rc != 0:
         raise ValueError("NVFP4 block scale is negative or NaN")
     s2 = np.float32(2.0) * np.float32(scale_2)

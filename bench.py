@@ -308,6 +308,37 @@ def gate_leg(seed, dev, steps=200, V=151552):
     return res
 
 
+def conversion_leg(seed, dev, n_mat=16, N=2048, K=7168, steps=5):
+    """Load-time conversions into 2-bit planes of a stack of gate/up-shaped matrices
+    [2048][7168] (8 experts): NVFP4 requant, MXFP4 codes remap, FP8 block-quant requant."""
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet, synth
+    nv = synth.make_nvfp4_stack(n_mat, N, K, seed, "conv_nvfp4", device=dev)
+    mx = synth.make_mxfp4_stack(n_mat, N, K, seed, "conv_mxfp4", device=dev)
+    f8 = synth.make_fp8_stack(n_mat, N, K, seed, "conv_fp8", device=dev)
+    out_bytes = n_mat * (N * K // 4 + N * K // 32)
+    legs = (("nvfp4_requant", lambda: moet.requant(*nv), n_mat * (N * K // 2 + N * K // 16)),
+            ("mxfp4_remap", lambda: moet.remap_mxfp4(*mx), n_mat * (N * K // 2 + N * K // 32)),
+            ("fp8_requant", lambda: moet.requant_fp8(*f8), n_mat * (N * K + 4 * ((N + 127) // 128) * (K // 128))))
+    res = {}
+    for name, fn, src_bytes in legs:
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"workload": f"{n_mat} matrices [{N}][{K}]", "ms": round(ms, 3),
+                     "ms_per_matrix": round(ms / n_mat, 4),
+                     "GBps_source_plus_planes": round((src_bytes + out_bytes) / (ms * 1e-3) / 1e9, 1)}
+    del nv, mx, f8
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_leg(layer, cfg5, steps, seed, dev):
     """Time route + forward of a prefill chunk (MFMA grouped GEMM path) on one pool layer."""
     import numpy as np
@@ -535,6 +566,8 @@ def main():
     if not args.no_extra:
         print("[bench] timing the confidence gate", file=sys.stderr, flush=True)
         result["confidence_gate"] = gate_leg(args.seed, dev)
+        print("[bench] timing the load-time conversions", file=sys.stderr, flush=True)
+        result["load_conversions"] = conversion_leg(args.seed, dev)
         del layers
         torch.cuda.empty_cache()
         result["other_decode"] = {}

@@ -49,7 +49,11 @@ int check_launch(const char *what)
 bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int launch_requant(const uint8_t *, const uint8_t *, const float *, int64_t, int, int, uint32_t *, uint8_t *, float *,
-                   const int32_t *, int64_t, uint8_t *, uint8_t *, float *, hipStream_t);
+                   const int32_t *, int64_t, uint8_t *, uint8_t *, float *, int, hipStream_t);
+int launch_remap_mxfp4(const uint8_t *, const uint8_t *, int64_t, int, int, int, uint32_t *, uint8_t *, float *,
+                       hipStream_t);
+int launch_requant_fp8(const uint8_t *, const float *, int64_t, int, int, int, uint32_t *, uint8_t *, float *,
+                       hipStream_t);
 int launch_route(const float *, int, int, int, int, int, float, int32_t *, float *, int32_t *, int32_t *, hipStream_t);
 size_t decode_workspace_bytes(int T, int k, int H, int I);
 int launch_decode(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
@@ -106,27 +110,63 @@ const char *moet_status_str(int s)
 
 const char *moet_last_error(void) { return g_err; }
 
-int moet_abi_version(void) { return 2; }
+int moet_abi_version(void) { return 3; }
 
-int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
-                 int64_t N, int64_t K, uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2,
-                 const int32_t *delta_sel, int64_t n_sel, uint8_t *d_codes, uint8_t *d_scales, float *d_scale2,
-                 void *stream)
+// shape checks shared by the load-time conversions
+static int check_stack(int64_t n_mat, int64_t N, int64_t K, uint32_t flags)
 {
-    g_err[0] = 0;
     if (n_mat < 1) return fail(MOET_EINVAL, "n_mat (%lld) must be >= 1", (long long)n_mat);
     if (N < 64 || N % 64 || N > (1 << 24)) return fail(MOET_EINVAL, "N (%lld) must be a positive multiple of 64", (long long)N);
     if (K < 128 || K % 128 || K > (1 << 24)) return fail(MOET_EINVAL, "K (%lld) must be a positive multiple of 128", (long long)K);
     if ((unsigned long long)n_mat * N * (K / 32) >= (1ull << 40)) return fail(MOET_EINVAL, "stack too large");
+    if ((unsigned long long)n_mat * N * (K / 32) / 256 >= (1ull << 31)) return fail(MOET_EINVAL, "stack too large for one launch");
+    if (flags & ~(uint32_t)MOET_BALANCE_ZERO_SIGNS) return fail(MOET_EINVAL, "unknown flags 0x%x", flags);
+    return MOET_OK;
+}
+
+int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
+                 int64_t N, int64_t K, uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2,
+                 const int32_t *delta_sel, int64_t n_sel, uint8_t *d_codes, uint8_t *d_scales, float *d_scale2,
+                 uint32_t flags, void *stream)
+{
+    g_err[0] = 0;
+    int rc = check_stack(n_mat, N, K, flags);
+    if (rc != MOET_OK) return rc;
     if (!aligned16(fp4_codes) || !aligned16(fp4_scales) || !aligned16(fp4_scale2) || !aligned16(w2_codes) ||
         !aligned16(w2_scales) || !aligned16(w2_scale2))
         return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
     if (n_sel < 0 || n_sel > n_mat) return fail(MOET_EINVAL, "n_sel (%lld) must be in [0, n_mat]", (long long)n_sel);
     if (n_sel > 0 && (!aligned16(delta_sel) || !aligned16(d_codes) || !aligned16(d_scales) || !aligned16(d_scale2)))
         return fail(MOET_EINVAL, "delta pointers must be non-NULL and 16-byte aligned when n_sel > 0");
-    if ((unsigned long long)n_mat * N * (K / 32) / 256 >= (1ull << 31)) return fail(MOET_EINVAL, "stack too large for one launch");
     return launch_requant(fp4_codes, fp4_scales, fp4_scale2, n_mat, (int)N, (int)K, w2_codes, w2_scales, w2_scale2,
-                          delta_sel, n_sel, d_codes, d_scales, d_scale2, (hipStream_t)stream);
+                          delta_sel, n_sel, d_codes, d_scales, d_scale2, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
+                          (hipStream_t)stream);
+}
+
+int moet_remap_mxfp4(const uint8_t *mx_codes, const uint8_t *mx_scales, int64_t n_mat, int64_t N, int64_t K,
+                     uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint32_t flags, void *stream)
+{
+    g_err[0] = 0;
+    int rc = check_stack(n_mat, N, K, flags);
+    if (rc != MOET_OK) return rc;
+    if (!aligned16(mx_codes) || !aligned16(mx_scales) || !aligned16(w2_codes) || !aligned16(w2_scales) ||
+        !aligned16(w2_scale2))
+        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
+    return launch_remap_mxfp4(mx_codes, mx_scales, n_mat, (int)N, (int)K, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
+                              w2_codes, w2_scales, w2_scale2, (hipStream_t)stream);
+}
+
+int moet_requant_fp8(const uint8_t *fp8_w, const float *fp8_scales, int64_t n_mat, int64_t N, int64_t K,
+                     uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint32_t flags, void *stream)
+{
+    g_err[0] = 0;
+    int rc = check_stack(n_mat, N, K, flags);
+    if (rc != MOET_OK) return rc;
+    if (!aligned16(fp8_w) || !aligned16(fp8_scales) || !aligned16(w2_codes) || !aligned16(w2_scales) ||
+        !aligned16(w2_scale2))
+        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
+    return launch_requant_fp8(fp8_w, fp8_scales, n_mat, (int)N, (int)K, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
+                              w2_codes, w2_scales, w2_scale2, (hipStream_t)stream);
 }
 
 int moet_route(const float *logits, int32_t T, int32_t E, int32_t top_k, int32_t score_fn, int32_t renormalize,

@@ -103,6 +103,27 @@ __device__ __forceinline__ size_t fp4_chunk_idx(int tile, int c, int r, int K) {
 // uint2 index of the scale group g (8 bytes) of row (tile, r) in an FP4 matrix
 __device__ __forceinline__ size_t fp4_scale_idx(int tile, int g, int r, int K) { return ((size_t)tile * (K / 128) + g) * 64 + r; }
 
+// bit positions of element e (0..15) of a 2-bit word: nibble e%8, upper bit
+// pair for e < 8, lower pair for e >= 8 (m below s)
+__device__ __forceinline__ int mbit(int e) { return 4 * (e & 7) + ((e & 8) ? 0 : 2); }
+__device__ __forceinline__ int sbit(int e) { return mbit(e) + 1; }
+
+// writes the two code words and the scale byte of block b (k = 32b .. 32b+31)
+// of row n of matrix mat in the tiled 2-bit layout
+__device__ __forceinline__ void store_w2_block(uint32_t *wcodes, uint8_t *wscales, size_t mat, int N, int K, int n,
+                                               int b, const uint32_t out[2], int tau)
+{
+    const int tile = n / 64, r = n % 64;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int q = 2 * b + half;  // 16-k word index along the row
+        const size_t widx = (((size_t)tile * (K / 64) + q / 4) * 64 + r) * 4 + (q % 4);
+        wcodes[mat * (size_t)N * (K / 16) + widx] = out[half];
+    }
+    const size_t sidx = (((size_t)tile * (K / 128) + b / 4) * 64 + r) * 4 + (b % 4);
+    wscales[mat * (size_t)N * (K / 32) + sidx] = (uint8_t)tau;
+}
+
 }  // namespace moet
 
 // ---------------------------------------------------------------------------

@@ -55,16 +55,12 @@ __device__ __forceinline__ int mag2_of(int L)  // 2*|e2m1| for magnitude code L 
     return L < 2 ? L : ((2 + (L & 1)) << ((L >> 1) - 1));
 }
 
-// bit positions of element e (0..15) of a 2-bit word: nibble e%8, upper bit
-// pair for e < 8, lower pair for e >= 8 (m below s)
-__device__ __forceinline__ int mbit(int e) { return 4 * (e & 7) + ((e & 8) ? 0 : 2); }
-__device__ __forceinline__ int sbit(int e) { return mbit(e) + 1; }
 
 __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales,
                                                       const float *__restrict__ s2in, int64_t n_mat, int N, int K,
                                                       uint32_t *__restrict__ wcodes, uint8_t *__restrict__ wscales,
-                                                      float *__restrict__ ws2)
+                                                      float *__restrict__ ws2, int balance)
 {
     const int nb = K / 32;
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -131,24 +127,20 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict_
     const int a = 4 * e4m3_x512(best_t);
 
     // element codes -> two output words (k = 32b .. 32b+31 = words 2b, 2b+1)
-    const int tile = n / 64, r = n % 64;
+    uint32_t out[2] = {0, 0};
+    int zeros = 0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        uint32_t out = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const uint32_t nib = (words[2 * half + (e >> 3)] >> (4 * (e & 7))) & 15u;
             const int y = mag2_of(nib & 7) * S9[half];
             const uint32_t m = (2 * y > 5 * a) ? 1u : 0u;
-            const uint32_t s = nib >> 3;
-            out |= (m << mbit(e)) | (s << sbit(e));
+            const uint32_t s = (balance && y == 0) ? (uint32_t)(zeros++ & 1) : nib >> 3;
+            out[half] |= (m << mbit(e)) | (s << sbit(e));
         }
-        const int q = 2 * b + half;  // 16-k word index along the row
-        const size_t widx = (((size_t)tile * (K / 64) + q / 4) * 64 + r) * 4 + (q % 4);
-        wcodes[mat * (size_t)N * (K / 16) + widx] = out;
     }
-    const size_t sidx = (((size_t)tile * (K / 128) + b / 4) * 64 + r) * 4 + (b % 4);
-    wscales[mat * (size_t)N * (K / 32) + sidx] = (uint8_t)best_t;
+    store_w2_block(wcodes, wscales, mat, N, K, n, b, out, best_t);
 }
 
 // FP4 re-encoding of the exact residual D = Y_nvfp4 - Y_2bit (units of u).
@@ -237,12 +229,12 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint8_t *__restrict__ 
 
 int launch_requant(const uint8_t *codes, const uint8_t *scales, const float *s2, int64_t n_mat, int N, int K,
                    uint32_t *wc, uint8_t *wsc, float *ws2, const int32_t *sel, int64_t n_sel, uint8_t *dc,
-                   uint8_t *ds, float *ds2, hipStream_t stream)
+                   uint8_t *ds, float *ds2, int balance, hipStream_t stream)
 {
     const size_t total = (size_t)n_mat * N * (K / 32);
     const size_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL(requant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, s2, n_mat, N, K,
-                       wc, wsc, ws2);
+                       wc, wsc, ws2, balance);
     int rc = check_launch("requant_kernel");
     if (rc != MOET_OK || n_sel == 0) return rc;
     const size_t dtotal = (size_t)n_sel * N * (K / 32);

@@ -1,0 +1,259 @@
+// Other checkpoint flavours loaded into the same sign-symmetric 2-bit planes.
+//
+// README "Frontier MoE on consumer Blackwell (SM120)", section "How it fits —
+// 2-bit experts at FP4 quality": FP4 experts are loaded by remapping their
+// codes, FP8 block-quantised experts are requantised at load in float64.
+//
+// MXFP4 codes remap.  The codebook {-4,-1,1,4} is a subset of the e2m1 grid,
+// so every e2m1 code goes to the nearest of those values in units of its
+// block's e8m0 scale (magnitudes 0..2 -> 1, 3..6 -> 4; no ties exist), and the
+// scales carry over: with Emax the largest exponent over blocks that hold a
+// non-zero code, the tensor scale is 2^(Emax - 135) and a block's e4m3 scale
+// is 2^(E - Emax + 8), exact down to e4m3's smallest subnormal 2^-9; blocks
+// below that, and blocks of zeros, get scale 0.
+//
+// FP8 block-quant requant.  e4m3fn weights with one fp32 scale per 128 x 128
+// block.  The tensor scale is the power of two S = 2^p, p >= -149 smallest
+// with 4 * 448 * S >= amax; per 32 weights along K the e4m3 block scale t
+// minimises sum_i min((y_i - a)^2, (y_i - 4a)^2), a = e4m3(t) * S, over every
+// finite code, ties to the smaller code.  Unlike the NVFP4 case the weights are
+// not integer multiples of one unit (each 128 x 128 block has its own fp32
+// scale), so the error is a float64 sum: y_i and a are exact in float64, and
+// the squares and the sum are rounded in a fixed order (k order, no
+// contraction into FMAs), which makes the decision reproducible bit for bit.
+// All 127 candidates are scanned: a window argument only holds for the exact
+// error, not for its rounded value.
+#include "moet_common.h"
+
+namespace moet {
+
+namespace {
+
+// 2^e as a float32, e in [-149, 127]
+__device__ __forceinline__ float pow2f(int e)
+{
+    return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(1u << (e + 149));
+}
+
+// e such that f == 2^e, for a positive power of two f
+__device__ __forceinline__ int log2_pow2f(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    const int be = (int)((u >> 23) & 255u);
+    return be ? be - 127 : (31 - __clz(u)) - 149;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_max_i32(int v)
+{
+    __shared__ int red[NT / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) v = max(v, red[i]);
+    return v;
+}
+
+template <int NT>
+__device__ __forceinline__ double block_max_f64(double v)
+{
+    __shared__ double red[NT / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) v = fmax(v, red[i]);
+    return v;
+}
+
+// e4m3fn value of code t (0x00..0x7E) as a float64, exact
+__device__ __forceinline__ double e4m3_f64(int t) { return (double)e4m3_x512(t) * (1.0 / 512.0); }
+
+constexpr int kScanThreads = 512;
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// MXFP4
+// ---------------------------------------------------------------------------
+
+// one workgroup per matrix: tensor scale from the largest live block exponent
+__global__ __launch_bounds__(kScanThreads) void mx_scale_kernel(const uint8_t *__restrict__ codes,
+                                                                const uint8_t *__restrict__ escales, int N, int K,
+                                                                float *__restrict__ ws2)
+{
+    const size_t mat = blockIdx.x;
+    const size_t nblk = (size_t)N * (K / 32);
+    const uint4 *c = reinterpret_cast<const uint4 *>(codes + mat * nblk * 16);
+    const uint8_t *e = escales + mat * nblk;
+    int emax = -1;
+    for (size_t i = threadIdx.x; i < nblk; i += kScanThreads) {
+        const uint4 w = c[i];
+        if (((w.x | w.y | w.z | w.w) & 0x77777777u) != 0u) emax = max(emax, (int)e[i]);
+    }
+    emax = block_max_i32<kScanThreads>(emax);
+    if (threadIdx.x == 0) ws2[mat] = emax < 0 ? 1.0f : pow2f(emax - 135);
+}
+
+// one thread per 32-weight block
+__global__ __launch_bounds__(256) void mx_remap_kernel(const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ escales, int64_t n_mat, int N, int K,
+                                                       const float *__restrict__ ws2, int balance,
+                                                       uint32_t *__restrict__ wcodes, uint8_t *__restrict__ wscales)
+{
+    const int nb = K / 32;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)n_mat * N * nb) return;
+    const int b = (int)(idx % nb);
+    const size_t rg = idx / nb;
+    const int n = (int)(rg % N);
+    const size_t mat = rg / N;
+
+    const uint4 cw = reinterpret_cast<const uint4 *>(codes)[idx];  // blocks are 16 contiguous bytes
+    const int E = escales[idx];
+    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+    int tau = 0;
+    if (((cw.x | cw.y | cw.z | cw.w) & 0x77777777u) != 0u) {
+        const int emax = log2_pow2f(ws2[mat]) + 135;
+        const int d = E - (emax - 8);                     // block scale 2^d, d <= 8
+        if (d >= -6) tau = (d + 7) << 3;                  // normal: exponent field d + 7
+        else if (d >= -9) tau = 1 << (d + 9);             // subnormal: mantissa 2^(d + 9)
+    }
+    uint32_t out[2] = {0, 0};
+    int zeros = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t nib = (words[2 * half + (e >> 3)] >> (4 * (e & 7))) & 15u;
+            const uint32_t mag = nib & 7u;
+            const uint32_t m = mag >= 5u ? 1u : 0u;       // |e2m1| in {3, 4, 6}
+            const uint32_t s = (balance && mag == 0u) ? (uint32_t)(zeros++ & 1) : nib >> 3;
+            out[half] |= (m << mbit(e)) | (s << sbit(e));
+        }
+    }
+    store_w2_block(wcodes, wscales, mat, N, K, n, b, out, tau);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 block-quant
+// ---------------------------------------------------------------------------
+
+// one workgroup per matrix: amax -> power-of-two tensor scale
+__global__ __launch_bounds__(kScanThreads) void fp8_scale_kernel(const uint8_t *__restrict__ w,
+                                                                 const float *__restrict__ bs, int N, int K,
+                                                                 float *__restrict__ ws2)
+{
+    const size_t mat = blockIdx.x;
+    const int KB = K / 128, NB = (N + 127) / 128;
+    const size_t nchunk = (size_t)N * (K / 16);
+    const uint4 *c = reinterpret_cast<const uint4 *>(w + mat * (size_t)N * K);
+    const float *s = bs + mat * (size_t)NB * KB;
+    double amax = 0.0;
+    for (size_t i = threadIdx.x; i < nchunk; i += kScanThreads) {
+        const uint4 q = c[i];
+        const uint32_t words[4] = {q.x, q.y, q.z, q.w};
+        int mx = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = max(mx, (int)((words[j >> 2] >> (8 * (j & 3))) & 0x7Fu));
+        const int n = (int)(i / (K / 16)), k = (int)(i % (K / 16)) * 16;
+        amax = fmax(amax, e4m3_f64(mx) * (double)s[(size_t)(n / 128) * KB + k / 128]);
+    }
+    amax = block_max_f64<kScanThreads>(amax);
+    if (threadIdx.x == 0) {
+        float S = 1.0f;
+        if (amax > 0.0) {
+            int p = -149;
+            while (1792.0 * ldexp(1.0, p) < amax) ++p;
+            S = pow2f(p);
+        }
+        ws2[mat] = S;
+    }
+}
+
+// one thread per 32-weight block: the float64 scan over all 127 block scales
+__global__ __launch_bounds__(256) void fp8_requant_kernel(const uint8_t *__restrict__ w, const float *__restrict__ bs,
+                                                          int64_t n_mat, int N, int K, const float *__restrict__ ws2,
+                                                          int balance, uint32_t *__restrict__ wcodes,
+                                                          uint8_t *__restrict__ wscales)
+{
+#pragma clang fp contract(off)
+    const int nb = K / 32, KB = K / 128, NB = (N + 127) / 128;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)n_mat * N * nb) return;
+    const int b = (int)(idx % nb);
+    const size_t rg = idx / nb;
+    const int n = (int)(rg % N);
+    const size_t mat = rg / N;
+
+    const uint4 *src = reinterpret_cast<const uint4 *>(w + idx * 32);  // rows are K contiguous bytes
+    const uint4 q0 = src[0], q1 = src[1];
+    const uint32_t words[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const double sb = (double)bs[mat * (size_t)NB * KB + (size_t)(n / 128) * KB + (32 * b) / 128];
+    const double S = (double)ws2[mat];
+    double y[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = e4m3_f64((int)((words[i >> 2] >> (8 * (i & 3))) & 0x7Fu)) * sb;
+
+    int best_t = 0;
+    double best_err = -1.0;
+    for (int t = 0; t < 127; ++t) {
+        const double a = e4m3_f64(t) * S;
+        const double a4 = 4.0 * a;
+        double err = 0.0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const double d1 = y[i] - a, d4 = y[i] - a4;
+            const double s1 = d1 * d1, s4 = d4 * d4;
+            err = err + (s1 < s4 ? s1 : s4);
+        }
+        if (best_err < 0.0 || err < best_err) {
+            best_err = err;
+            best_t = t;
+        }
+    }
+    const double a = e4m3_f64(best_t) * S;
+    uint32_t out[2] = {0, 0};
+    int zeros = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t byte = (words[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        const uint32_t m = (2.0 * y[i] > 5.0 * a) ? 1u : 0u;
+        const uint32_t s = (balance && y[i] == 0.0) ? (uint32_t)(zeros++ & 1) : byte >> 7;
+        const int e = i & 15;
+        out[i >> 4] |= (m << mbit(e)) | (s << sbit(e));
+    }
+    store_w2_block(wcodes, wscales, mat, N, K, n, b, out, best_t);
+}
+
+int launch_remap_mxfp4(const uint8_t *codes, const uint8_t *escales, int64_t n_mat, int N, int K, int balance,
+                       uint32_t *wc, uint8_t *wsc, float *ws2, hipStream_t stream)
+{
+    hipLaunchKernelGGL(mx_scale_kernel, dim3((unsigned)n_mat), dim3(kScanThreads), 0, stream, codes, escales, N, K,
+                       ws2);
+    int rc = check_launch("mx_scale_kernel");
+    if (rc != MOET_OK) return rc;
+    const size_t total = (size_t)n_mat * N * (K / 32);
+    hipLaunchKernelGGL(mx_remap_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, codes, escales,
+                       n_mat, N, K, (const float *)ws2, balance, wc, wsc);
+    return check_launch("mx_remap_kernel");
+}
+
+int launch_requant_fp8(const uint8_t *w, const float *bs, int64_t n_mat, int N, int K, int balance, uint32_t *wc,
+                       uint8_t *wsc, float *ws2, hipStream_t stream)
+{
+    hipLaunchKernelGGL(fp8_scale_kernel, dim3((unsigned)n_mat), dim3(kScanThreads), 0, stream, w, bs, N, K, ws2);
+    int rc = check_launch("fp8_scale_kernel");
+    if (rc != MOET_OK) return rc;
+    const size_t total = (size_t)n_mat * N * (K / 32);
+    hipLaunchKernelGGL(fp8_requant_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, w, bs, n_mat,
+                       N, K, (const float *)ws2, balance, wc, wsc);
+    return check_launch("fp8_requant_kernel");
+}
+
+}  // namespace moet

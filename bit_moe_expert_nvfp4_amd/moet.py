@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libmoet.so")
 
 MOET_OK, MOET_EINVAL, MOET_EUNSUPPORTED, MOET_EWORKSPACE, MOET_EHIP = range(5)
 SOFTMAX, SIGMOID = 0, 1
+BALANCE_ZERO_SIGNS = 1
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -62,8 +63,13 @@ def lib():
         L.moet_last_error.argtypes = []
         L.moet_last_error.restype = ctypes.c_char_p
         L.moet_abi_version.restype = ctypes.c_int
-        L.moet_requant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp]
+        L.moet_requant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                   ctypes.c_uint32, _vp]
         L.moet_requant.restype = ctypes.c_int
+        L.moet_remap_mxfp4.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_uint32, _vp]
+        L.moet_remap_mxfp4.restype = ctypes.c_int
+        L.moet_requant_fp8.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_uint32, _vp]
+        L.moet_requant_fp8.restype = ctypes.c_int
         L.moet_route.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp]
         L.moet_route.restype = ctypes.c_int
         L.moet_moe_workspace_bytes.argtypes = [ctypes.POINTER(LayerC), _i32, _i32]
@@ -129,8 +135,14 @@ class FP4Planes:
         return FP4(self.codes.data_ptr(), self.scales.data_ptr(), self.scale2.data_ptr())
 
 
+def _new_w2(n: int, N: int, K: int, dev) -> W2Planes:
+    return W2Planes(torch.empty((n, N * K // 16), dtype=torch.int32, device=dev),
+                    torch.empty((n, N * K // 32), dtype=torch.uint8, device=dev),
+                    torch.empty((n,), dtype=torch.float32, device=dev), N, K)
+
+
 def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
-            delta_sel: Optional[torch.Tensor] = None):
+            delta_sel: Optional[torch.Tensor] = None, balance_zero_signs: bool = False):
     """NVFP4 stack (codes uint8 [n, N, K/2], scales uint8 [n, N, K/16], scale2 f32 [n]) ->
     W2Planes (and FP4Planes of the matrices listed in delta_sel, int32)."""
     _need(codes, torch.uint8, "codes")
@@ -139,9 +151,7 @@ def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
     n, N, Kh = codes.shape
     K = 2 * Kh
     dev = codes.device
-    w = W2Planes(torch.empty((n, N * K // 16), dtype=torch.int32, device=dev),
-                 torch.empty((n, N * K // 32), dtype=torch.uint8, device=dev),
-                 torch.empty((n,), dtype=torch.float32, device=dev), N, K)
+    w = _new_w2(n, N, K, dev)
     d = None
     n_sel = 0
     if delta_sel is not None:
@@ -154,8 +164,34 @@ def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
                               _ptr(w.codes), _ptr(w.scales), _ptr(w.scale2),
                               _ptr(delta_sel) if n_sel else None, n_sel,
                               _ptr(d.codes) if d else None, _ptr(d.scales) if d else None,
-                              _ptr(d.scale2) if d else None, _stream()))
+                              _ptr(d.scale2) if d else None,
+                              BALANCE_ZERO_SIGNS if balance_zero_signs else 0, _stream()))
     return (w, d) if delta_sel is not None else w
+
+
+def remap_mxfp4(codes: torch.Tensor, scales: torch.Tensor, balance_zero_signs: bool = False) -> W2Planes:
+    """MXFP4 stack (codes uint8 [n, N, K/2], e8m0 scales uint8 [n, N, K/32]) -> W2Planes."""
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    n, N, Kh = codes.shape
+    K = 2 * Kh
+    w = _new_w2(n, N, K, codes.device)
+    _check(lib().moet_remap_mxfp4(_ptr(codes), _ptr(scales), n, N, K, _ptr(w.codes), _ptr(w.scales),
+                                  _ptr(w.scale2), BALANCE_ZERO_SIGNS if balance_zero_signs else 0, _stream()))
+    return w
+
+
+def requant_fp8(weights: torch.Tensor, block_scales: torch.Tensor, balance_zero_signs: bool = False) -> W2Planes:
+    """FP8 block-quant stack (e4m3fn bytes uint8 [n, N, K], fp32 scales [n, ceil(N/128), K/128]) -> W2Planes."""
+    _need(weights, torch.uint8, "weights")
+    _need(block_scales, torch.float32, "block_scales")
+    n, N, K = weights.shape
+    if tuple(block_scales.shape) != (n, (N + 127) // 128, K // 128):
+        raise ValueError(f"block_scales must be [{n}, {(N + 127) // 128}, {K // 128}], got {tuple(block_scales.shape)}")
+    w = _new_w2(n, N, K, weights.device)
+    _check(lib().moet_requant_fp8(_ptr(weights), _ptr(block_scales), n, N, K, _ptr(w.codes), _ptr(w.scales),
+                                  _ptr(w.scale2), BALANCE_ZERO_SIGNS if balance_zero_signs else 0, _stream()))
+    return w
 
 
 # ---------------------------------------------------------------------------

@@ -151,23 +151,23 @@ def fp8_block_export(W: torch.Tensor):
     return q.view(torch.uint8).reshape(Np, K)[:N].contiguous(), s.contiguous()
 
 
-def make_mxfp4_stack(n_mat: int, N: int, K: int, seed: int, tag: str, std: float = 0.02):
+def make_mxfp4_stack(n_mat: int, N: int, K: int, seed: int, tag: str, std: float = 0.02, device="cpu"):
     """A stack of n_mat MXFP4 matrices [N, K] (codes [n_mat, N, K/2], e8m0 scales [n_mat, N, K/32])."""
-    codes = torch.empty((n_mat, N, K // 2), dtype=torch.uint8)
-    scales = torch.empty((n_mat, N, K // 32), dtype=torch.uint8)
+    codes = torch.empty((n_mat, N, K // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((n_mat, N, K // 32), dtype=torch.uint8, device=device)
     for i in range(n_mat):
-        W = torch.randn((N, K), generator=_gen("cpu", seed, tag, i), dtype=torch.float32) * std
+        W = torch.randn((N, K), generator=_gen(device, seed, tag, i), device=device, dtype=torch.float32) * std
         codes[i], scales[i] = mxfp4_export(W)
     return codes, scales
 
 
-def make_fp8_stack(n_mat: int, N: int, K: int, seed: int, tag: str, std: float = 0.02):
+def make_fp8_stack(n_mat: int, N: int, K: int, seed: int, tag: str, std: float = 0.02, device="cpu"):
     """A stack of n_mat FP8 block-quant matrices [N, K] (weights [n_mat, N, K], scales
     [n_mat, ceil(N/128), K/128])."""
-    w = torch.empty((n_mat, N, K), dtype=torch.uint8)
-    s = torch.empty((n_mat, (N + 127) // 128, K // 128), dtype=torch.float32)
+    w = torch.empty((n_mat, N, K), dtype=torch.uint8, device=device)
+    s = torch.empty((n_mat, (N + 127) // 128, K // 128), dtype=torch.float32, device=device)
     for i in range(n_mat):
-        W = torch.randn((N, K), generator=_gen("cpu", seed, tag, i), dtype=torch.float32) * std
+        W = torch.randn((N, K), generator=_gen(device, seed, tag, i), device=device, dtype=torch.float32) * std
         w[i], s[i] = fp8_block_export(W)
     return w, s
 

@@ -23,6 +23,10 @@
  *                       counting routings to missing experts (README, "When the
  *                       model doesn't fit at all — the GPU as an expert cache")
  *   moet_delta_forward  the standalone FP4 delta GEMM/GEMV (README, "How it fits")
+ *   moet_remap_mxfp4    FP4 (MXFP4) experts -> the same 2-bit planes by a
+ *                       code remap (README, "How it fits")
+ *   moet_requant_fp8    FP8 block-quantised experts -> the same 2-bit planes
+ *                       (README, "How it fits")
  *   moet_confidence_gate  the confidence gate: flags low-confidence tokens for
  *                       the FP4 delta from their next-token logits (README,
  *                       "How it fits")
@@ -47,6 +51,10 @@
  * the reduction axis; N % 64 == 0 and K % 128 == 0):
  *  NVFP4 source (standard modelopt layout): codes uint8 [N][K/2], even k in the
  *    low nibble; block scales e4m3fn uint8 [N][K/16]; per-tensor scale_2 fp32.
+ *  MXFP4 source (OCP microscaling): codes as NVFP4; block scales e8m0 uint8
+ *    [N][K/32], value 2^(E-127); no tensor scale.
+ *  FP8 block-quant source: weights e4m3fn uint8 [N][K]; one fp32 scale per
+ *    128 x 128 block, [ceil(N/128)][K/128]; weight = e4m3 * scale.
  *  2-bit planes ("W2"): rows are grouped in tiles of 64;
  *    codes uint32 word index ((n/64 * K/64 + k/64) * 64 + n%64) * 4 + (k%64)/16;
  *    inside a word, element e = k%16 has code c = (s<<1)|m (levels 0:+1 1:+4
@@ -83,6 +91,15 @@ typedef enum {
 
 enum { MOET_SOFTMAX = 0, MOET_SIGMOID = 1 };
 
+/* Flags of the load-time conversions (moet_requant, moet_remap_mxfp4,
+ * moet_requant_fp8).  MOET_BALANCE_ZERO_SIGNS: the zeros of each 32-weight
+ * block take alternating signs in k order (+ first) instead of their source
+ * sign bit, for checkpoints whose export wrote every zero as +0 (README
+ * "Frontier MoE on consumer Blackwell (SM120)", section "Kimi-K2.7-Code (1T
+ * MoE) on 4x RTX PRO 6000": such zeros would all land on +1 and bias the
+ * layer).  Block scales are unaffected: a zero costs the same either way. */
+enum { MOET_BALANCE_ZERO_SIGNS = 1 };
+
 /* Static string for a status code. */
 const char *moet_status_str(int status);
 /* Thread-local detail of the last failed call on this thread ("" if none). */
@@ -114,16 +131,70 @@ int moet_abi_version(void);
  *   keeps D's sign), is written at slot i of d_codes uint8 [n_sel][N*K/2],
  *   d_scales uint8 [n_sel][N*K/16], d_scale2 fp32 [n_sel] (FP4 layout).
  *   n_sel == 0: delta_sel and d_* may be NULL.
+ * flags: 0 or MOET_BALANCE_ZERO_SIGNS (the delta then follows the balanced
+ *   codes).
  * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
- *   pointers, n_sel < 0 or n_sel > n_mat.  Out-of-range delta_sel entries are
- *   skipped by the kernel (their slots are left unwritten).
+ *   pointers, n_sel < 0 or n_sel > n_mat, unknown flags.  Out-of-range
+ *   delta_sel entries are skipped by the kernel (their slots are left
+ *   unwritten).
  */
 int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2,
                  int64_t n_mat, int64_t N, int64_t K,
                  uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2,
                  const int32_t *delta_sel, int64_t n_sel,
                  uint8_t *d_codes, uint8_t *d_scales, float *d_scale2,
-                 void *stream);
+                 uint32_t flags, void *stream);
+
+/*
+ * moet_remap_mxfp4 - MXFP4 experts -> sign-symmetric 2-bit planes by a code
+ * remap, for a stack of n_mat equal-shape matrices [N][K].  (README "Frontier
+ * MoE on consumer Blackwell (SM120)", section "How it fits — 2-bit experts at
+ * FP4 quality": FP4 experts load by remapping their codes.)
+ *
+ * {-4,-1,1,4} is a subset of the e2m1 grid, so each e2m1 code becomes the
+ * nearest of those values in units of its block scale (magnitudes 0, 0.5, 1,
+ * 1.5, 2 -> 1; 3, 4, 6 -> 4; sign from the code, or balanced zeros).  The
+ * scales carry over exactly: with Emax the largest e8m0 exponent over the
+ * blocks holding a non-zero code, w2_scale2 = 2^(Emax - 135) and a block's
+ * e4m3 scale is 2^(E - Emax + 8); blocks with E < Emax - 17 (below e4m3's
+ * range) and blocks with no non-zero code get scale 0.  A matrix with no
+ * non-zero code gets w2_scale2 = 1 and scale 0 everywhere.  No search: two
+ * kernels (one reduction per matrix, then one thread per 32-weight block).
+ *
+ * Inputs: mx_codes uint8 [n_mat][N][K/2], mx_scales uint8 [n_mat][N][K/32]
+ *   (e8m0; 0xFF (NaN) gives undefined results).
+ * Outputs: w2_codes, w2_scales, w2_scale2 as for moet_requant.
+ * flags: 0 or MOET_BALANCE_ZERO_SIGNS.
+ * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
+ *   pointers, unknown flags.
+ */
+int moet_remap_mxfp4(const uint8_t *mx_codes, const uint8_t *mx_scales, int64_t n_mat, int64_t N, int64_t K,
+                     uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint32_t flags, void *stream);
+
+/*
+ * moet_requant_fp8 - FP8 block-quantised experts -> sign-symmetric 2-bit
+ * planes, for a stack of n_mat equal-shape matrices [N][K].  (README
+ * "Frontier MoE on consumer Blackwell (SM120)", section "How it fits — 2-bit
+ * experts at FP4 quality": FP8 block-quant checkpoints are requantised to the
+ * same codebook at load, in float64.)
+ *
+ * w2_scale2 = 2^p, the smallest p >= -149 with 4 * 448 * 2^p >= max|weight|
+ * (1 for an all-zero matrix).  Per 32 weights along K the e4m3 block scale t
+ * minimises sum_i min((y_i - a)^2, (y_i - 4a)^2), y_i = |weight_i|,
+ * a = e4m3(t) * w2_scale2, over all 127 finite codes (ties -> smaller t),
+ * evaluated in float64 in k order without fused multiply-adds; each weight
+ * takes the nearest level (2y > 5a -> magnitude 4; a tie keeps 1) and its
+ * sign from the e4m3 sign bit, or balanced zeros.
+ *
+ * Inputs: fp8_w uint8 [n_mat][N][K] (e4m3fn; 0x7F / 0xFF (NaN) give undefined
+ *   results), fp8_scales fp32 [n_mat][ceil(N/128)][K/128] (finite, >= 0).
+ * Outputs: w2_codes, w2_scales, w2_scale2 as for moet_requant.
+ * flags: 0 or MOET_BALANCE_ZERO_SIGNS.
+ * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
+ *   pointers, unknown flags.
+ */
+int moet_requant_fp8(const uint8_t *fp8_w, const float *fp8_scales, int64_t n_mat, int64_t N, int64_t K,
+                     uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint32_t flags, void *stream);
 
 /*
  * moet_route - router top-k and token permutation.

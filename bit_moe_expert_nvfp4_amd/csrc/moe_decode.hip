@@ -60,6 +60,8 @@ struct DecodeParams {
     const int32_t *base_slot;   // expert -> cache slot of w13/w2 (null: expert e at e)
     int n_base_slots;
     int32_t *miss_count;        // routings to missing experts (null: not counted)
+    int shared_fp4;             // the shared expert is NVFP4 (shf13 / shf2) instead of 2-bit
+    moet_fp4 shf13, shf2;
     uint16_t *h;        // [P + T][I] bf16
     float *ypart;       // [P + T][H] fp32
     uint16_t *out;      // [T][H] bf16
@@ -500,6 +502,17 @@ __device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2,
     for (int t = 0; t < kTT; ++t) part[t] = s2 * acc[t] + ((any_flag && flag[t]) ? ds2 * dacc[t] : 0.f);
 }
 
+// The same for an NVFP4 shared expert: FP4 planes only, scaled by their scale2.
+__device__ __forceinline__ void lane_pass_fp4(const LaneRow &L, float s2, int K, int g0, int g1,
+                                              const cu32 *const xr[kTT], int n, float part[kTT])
+{
+    float acc[kTT] = {0.f, 0.f};
+    if (n == 1) fp4_gemv<1>(L, K, g0, g1, xr, acc);
+    else fp4_gemv<2>(L, K, g0, g1, xr, acc);
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) part[t] = s2 * acc[t];
+}
+
 __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_DECODE_WAVES))) void fc1_decode_kernel(DecodeParams p)
 {
     if (p.miss_count && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.miss_count = 0;   // counted by the combine
@@ -517,7 +530,7 @@ __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_D
     L.cb = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * I * H / 16);
     L.sb = W.scales + (size_t)m0 * I * H / 32;
     lane_offsets(L, mat, row >> 6, row & 63, I, H);
-    const float s2 = W.scale2[m0 + mat];
+    const float s2 = (si.shared && p.shared_fp4) ? 0.f : W.scale2[m0 + mat];
     float ds2 = 0.f;
     L.dc4 = nullptr;
     L.ds8 = nullptr;
@@ -526,6 +539,12 @@ __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_D
         L.dc4 = reinterpret_cast<const uint4 *>(p.d13.codes + (size_t)dm * I * H / 2);
         L.ds8 = reinterpret_cast<const uint2 *>(p.d13.scales + (size_t)dm * I * H / 16);
         ds2 = p.d13.scale2[dm];
+    }
+    const bool fp4_shared = si.shared && p.shared_fp4;
+    if (fp4_shared) {
+        L.dc4 = reinterpret_cast<const uint4 *>(p.shf13.codes + (size_t)mat * I * H / 2);
+        L.ds8 = reinterpret_cast<const uint2 *>(p.shf13.scales + (size_t)mat * I * H / 16);
+        ds2 = p.shf13.scale2[mat];
     }
     const int G = H / 128;
     const int g0 = wave * G / kW1, g1 = (wave + 1) * G / kW1;
@@ -542,7 +561,8 @@ __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_D
             xr[j] = as_const(p.x + (size_t)t * H);
         }
         float part[kTT];
-        lane_pass(L, s2, ds2, H, g0, g1, xr, flag, n, part);
+        if (fp4_shared) lane_pass_fp4(L, ds2, H, g0, g1, xr, n, part);
+        else lane_pass(L, s2, ds2, H, g0, g1, xr, flag, n, part);
 #pragma unroll
         for (int t = 0; t < kTT; ++t)
             if (t < n) red[wave][t][lane] = part[t];
@@ -576,11 +596,12 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_D
     if (!resolve_slot(p, s, si)) return;
     const moet_w2 &W = si.shared ? p.sh2 : p.w2;
     const int m0 = si.shared ? 0 : si.ws;
+    const bool fp4_shared = si.shared && p.shared_fp4;
     LaneRow L;
     L.cb = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16);
     L.sb = W.scales + (size_t)m0 * H * I / 32;
     lane_offsets(L, 0, tile, lane, H, I);
-    const float s2 = W.scale2[m0];
+    const float s2 = fp4_shared ? 0.f : W.scale2[m0];
     float ds2 = 0.f;
     L.dc4 = nullptr;
     L.ds8 = nullptr;
@@ -588,6 +609,11 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_D
         L.dc4 = reinterpret_cast<const uint4 *>(p.d2.codes + (size_t)si.dslot * H * I / 2);
         L.ds8 = reinterpret_cast<const uint2 *>(p.d2.scales + (size_t)si.dslot * H * I / 16);
         ds2 = p.d2.scale2[si.dslot];
+    }
+    if (fp4_shared) {
+        L.dc4 = reinterpret_cast<const uint4 *>(p.shf2.codes);
+        L.ds8 = reinterpret_cast<const uint2 *>(p.shf2.scales);
+        ds2 = p.shf2.scale2[0];
     }
     const int G = I / 128;
     const int g0 = wave * G / kW2, g1 = (wave + 1) * G / kW2;
@@ -604,7 +630,8 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_D
             xr[j] = as_const(p.h + (size_t)hrow[j] * I);
         }
         float part[kTT];
-        lane_pass(L, s2, ds2, I, g0, g1, xr, flag, n, part);
+        if (fp4_shared) lane_pass_fp4(L, ds2, I, g0, g1, xr, n, part);
+        else lane_pass(L, s2, ds2, I, g0, g1, xr, flag, n, part);
 #pragma unroll
         for (int t = 0; t < kTT; ++t)
             if (t < n) red[wave][t][lane] = part[t];
@@ -742,6 +769,9 @@ int launch_decode(const moet_layer *L, const uint16_t *x, int T, int k, const in
     p.base_slot = L->base_slot_of_expert;
     p.n_base_slots = L->n_base_slots;
     p.miss_count = miss_count;
+    p.shared_fp4 = (L->has_shared && L->shared_fp4) ? 1 : 0;
+    p.shf13 = L->shared13_fp4;
+    p.shf2 = L->shared2_fp4;
     const size_t rows = (size_t)T * k + T;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     char *base = static_cast<char *>(ws);

@@ -30,6 +30,16 @@
 //    in sorted-pair order (the down kernel reads it contiguously).
 //  * down kernel: 256 output features per workgroup, y (fp32) scattered to
 //    the pair's row for the shared combine kernel.
+//  * FP4 operand (README "How it fits": FP4 delta GEMM for gate-flagged tokens
+//    on delta-cache experts; a shared expert kept in NVFP4): the same pipeline
+//    with a B stage of two 32-k FP4 chunks per row and one dword of four
+//    block-16 scales.  One MFMA k-step is exactly one block-16, so a lane
+//    dequantises its 8 values as e2m1 -> f32 -> * scale -> bf16, exact
+//    (e2m1 * e4m3 has at most 6 significant bits).  The delta pass runs after
+//    the 2-bit pass of a tile into the same accumulators, with the A rows of
+//    unflagged tokens zeroed in registers and the delta values pre-multiplied
+//    by scale2_delta / scale2 (exactly 1/2 for planes built by moet_requant);
+//    an NVFP4 shared expert runs the FP4 pass alone.
 #include <algorithm>
 
 #include "moet_common.h"
@@ -62,6 +72,12 @@ struct PrefillParams {
     const int32_t *base_slot;   // expert -> cache slot of w13/w2 (null: expert e at e)
     int n_base_slots;
     int32_t *miss_count;        // routings to missing experts (null: not counted)
+    const uint8_t *gate;        // confidence-gate flags per token (null: no delta)
+    int n_slots;                // delta cache
+    const int32_t *slot_of_expert;
+    moet_fp4 d13, d2;
+    int shared_fp4;             // the shared expert is NVFP4 (shf13 / shf2)
+    moet_fp4 shf13, shf2;
 };
 
 // cache slot of expert e's 2-bit planes, or -1 when it is missing from the expert cache
@@ -284,17 +300,190 @@ __device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, con
     }
 }
 
+// ---------------------------------------------------------------------------
+// FP4 operand pipeline.  Per stage and wavefront: the same 4 A segments, two
+// B chunks (32-k FP4 chunks 2s and 2s+1 of the wave's 64 storage rows, 1 KiB
+// each) and one scale dword per row (the four block-16 scales of the step).
+// ---------------------------------------------------------------------------
+constexpr int kStageB4 = 8 * 1024;
+constexpr int kStage4 = kStageA + kStageB4 + kStageS;
+constexpr int kDmaPerStage4 = 7;
+constexpr int kSmem = (kPS * kStage4 > kPS * kStage) ? kPS * kStage4 : kPS * kStage;
+
+__device__ __forceinline__ void issue_stage4(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage4);
+    const int c = (lane & 7) ^ ((lane >> 3) & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((4 * wave + i) * 1024));
+    dma16(src.bsrc + ((size_t)(2 * s) * 64 + lane) * 16, base + kStageA + wave * 2048);
+    dma16(src.bsrc + ((size_t)(2 * s + 1) * 64 + lane) * 16, base + kStageA + wave * 2048 + 1024);
+    dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 8 + (s & 1) * 4, base + kStageA + kStageB4 + wave * 256);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// e2m1 byte B of w (low nibble first) as two bf16 of value * sc (exact)
+template <int B>
+__device__ __forceinline__ void deq_fp4_pair(uint32_t w, float sc, bf16x8 &r)
+{
+    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+    r[2 * B] = (__bf16)(v.x * sc);
+    r[2 * B + 1] = (__bf16)(v.y * sc);
+}
+
+// 8 bf16 of one row for one MFMA k-step from 8 e2m1 codes, times `sc` (exact)
+__device__ __forceinline__ bf16x8 deq_fp4(uint32_t w, float sc)
+{
+    bf16x8 r;
+    deq_fp4_pair<0>(w, sc, r);
+    deq_fp4_pair<1>(w, sc, r);
+    deq_fp4_pair<2>(w, sc, r);
+    deq_fp4_pair<3>(w, sc, r);
+    return r;
+}
+
+// block-16 scale byte Q of a scale dword as a float
+template <int Q>
+__device__ __forceinline__ float fp8_byte(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8(w, Q); }
+
+// one MFMA k-step (16 k = one FP4 block) of the FP4 pipeline
+template <int NMB, int Q>
+__device__ __forceinline__ void fp4_kstep(const uint8_t *aT, const uint8_t *bT, const int boff[2], const uint32_t sw[2],
+                                          const float rat[2], uint32_t rmask, f32x16 acc[kPMB][2])
+{
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    bf16x8 bfr[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t wv = *reinterpret_cast<const uint32_t *>(bT + boff[nb] + (Q >> 1) * 1024 + (Q & 1) * 8);
+        bfr[nb] = deq_fp4(wv, fp8_byte<Q>(sw[nb]) * rat[nb]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+        bf16x8 afr = a_frag(aT, 32 * mb + (lane & 31), 2 * Q + h);
+        if (!((rmask >> mb) & 1u)) afr = bf16x8{};
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[nb], acc[mb][nb], 0, 0, 0);
+    }
+}
+
+// acc[mb][nb] += A(tile rows, rows of mb with bit mb of rmask clear zeroed) x
+// (FP4 row brow[nb] * rat[nb])
+template <int NMB>
+__device__ __forceinline__ void gemm_pipe4_n(const PipeSrc &src, uint8_t *smem, const int brow[2], const float rat[2],
+                                             uint32_t rmask, f32x16 acc[kPMB][2])
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;
+    const int nsteps = src.K / kPK;
+#pragma unroll
+    for (int st = 0; st < kPS - 1; ++st)
+        if (st < nsteps) issue_stage4(src, smem, st, st, wave, lane);
+    int boff[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) boff[nb] = (brow[nb] >> 6) * 2048 + (brow[nb] & 63) * 16 + 4 * h;
+    for (int s = 0; s < nsteps; ++s) {
+        if (s + 1 < nsteps) wait_barrier<kDmaPerStage4 * (kPS - 2)>();
+        else wait_barrier<0>();
+        if (s + kPS - 1 < nsteps) issue_stage4(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
+        const uint8_t *stg = smem + (s % kPS) * kStage4;
+        const uint8_t *aT = stg;
+        const uint8_t *bT = stg + kStageA;
+        const uint8_t *sT = stg + kStageA + kStageB4;
+        uint32_t sw[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sw[nb] = *reinterpret_cast<const uint32_t *>(sT + brow[nb] * 4);
+        fp4_kstep<NMB, 0>(aT, bT, boff, sw, rat, rmask, acc);
+        fp4_kstep<NMB, 1>(aT, bT, boff, sw, rat, rmask, acc);
+        fp4_kstep<NMB, 2>(aT, bT, boff, sw, rat, rmask, acc);
+        fp4_kstep<NMB, 3>(aT, bT, boff, sw, rat, rmask, acc);
+    }
+}
+
+__device__ __forceinline__ void gemm_pipe4(const PipeSrc &src, uint8_t *smem, const int brow[2], const float rat[2],
+                                           uint32_t rmask, f32x16 acc[kPMB][2], int nmb)
+{
+    switch (nmb) {
+    case 1: gemm_pipe4_n<1>(src, smem, brow, rat, rmask, acc); break;
+    case 2: gemm_pipe4_n<2>(src, smem, brow, rat, rmask, acc); break;
+    case 3: gemm_pipe4_n<3>(src, smem, brow, rat, rmask, acc); break;
+    default: gemm_pipe4_n<4>(src, smem, brow, rat, rmask, acc); break;
+    }
+}
+
+// Delta slot of a tile's expert when it has an FP4 delta and at least one of
+// the tile's rows belongs to a gate-flagged token, else -1.  rmask gets bit mb
+// set when this lane's row 32 mb + lane % 32 is flagged (rows are the same in
+// every wave, so the answer is uniform over the workgroup).
+__device__ __forceinline__ int delta_rows(const PrefillParams &p, const MTile &mt, int nmb, uint32_t &rmask)
+{
+    rmask = 0;
+    if (mt.e < 0 || p.n_slots <= 0 || p.gate == nullptr) return -1;
+    const int ds = p.slot_of_expert[mt.e];
+    if (ds < 0 || ds >= p.n_slots) return -1;
+    const int lane = threadIdx.x & 63, P = p.T * p.k;
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb) {
+        const int r = 32 * mb + (lane & 31);
+        if (mb < nmb && r < mt.rows) {
+            const int t = min(max(p.sorted[mt.row0 + r], 0), P - 1) / p.k;
+            if (p.gate[t]) rmask |= 1u << mb;
+        }
+    }
+    return __ballot(rmask != 0u) ? ds : -1;
+}
+
+// epilogue scale and delta pre-scale of one B matrix: the delta is folded into
+// the 2-bit accumulators as delta * (ds2 / s2); with s2 == 0 the 2-bit part is
+// zero, so the accumulators restart and the epilogue scale becomes 1.
+__device__ __forceinline__ void fold_scales(float s2, float ds2, f32x16 acc[kPMB][2], int nb, float &scl, float &rat)
+{
+    if (s2 != 0.f) {
+        scl = s2;
+        rat = ds2 / s2;
+    } else {
+        scl = 1.f;
+        rat = ds2;
+#pragma unroll
+        for (int mb = 0; mb < kPMB; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+    }
+}
+
+// Tiles with FP4 work (a gate-flagged row on a delta-cache expert, or the
+// NVFP4 shared expert) run in their own kernels (FP4 = true), which hold the
+// accumulators through both passes at one wavefront per SIMD; the 2-bit-only
+// kernels (FP4 = false) skip those tiles and keep their register budget.
+// Returns whether this tile belongs to the kernel, with the delta slot (or -1)
+// and the row mask of the FP4 pass.
+template <bool FP4>
+__device__ __forceinline__ bool tile_kind(const PrefillParams &p, const MTile &mt, int nmb, int &ds, uint32_t &rmask)
+{
+    ds = -1;
+    rmask = 0xFu;
+    const bool sh4 = mt.e < 0 && p.shared_fp4;
+    if (!sh4) ds = delta_rows(p, mt, nmb, rmask);
+    return (sh4 || ds >= 0) == FP4;
+}
+
 // gate/up + SwiGLU.  N-tile nt covers h columns [128 nt, 128 nt + 128); wave w
 // owns gate rows and up rows [128 nt + 32 w, + 32).
-__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc1_prefill_kernel(PrefillParams p)
+template <bool FP4>
+__device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t *smem)
 {
-    __shared__ __align__(1024) uint8_t smem[kPS * kStage];
-    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0) *p.miss_count = 0;   // counted by the combine
     int ms, nt;
     decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
     if (ms >= p.n_mslots) return;
     MTile mt;
     if (!locate_mtile(p, ms, mt)) return;
+    const int nmb = (mt.rows + 31) / 32;
+    int ds;
+    uint32_t rmask;
+    if (!tile_kind<FP4>(p, mt, nmb, ds, rmask)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
     // A rows fetched by this lane: segment i of wave w holds rows 8(4w+i) .. +7; lane -> row + lane/8
@@ -311,14 +500,9 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
     // B: 256 rows = gate rows [128 nt, +128) then up rows [128 nt, +128); wave w fetches storage tile w
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
     if (ws < 0) return;   // missing expert: no work, the combine skips its routings
+    const bool sh4 = mt.e < 0 && p.shared_fp4;
     const moet_w2 &W = (mt.e >= 0) ? p.w13 : p.sh13;
     const int m0 = (mt.e >= 0) ? 2 * ws : 0;
-    {
-        const int mat = m0 + (wave >> 1);
-        const int tile = 2 * nt + (wave & 1);
-        src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)mat * I * H / 16) + (size_t)tile * (H / 64) * 1024;
-        src.ssrc = W.scales + (size_t)mat * I * H / 32 + (size_t)tile * (H / 128) * 256;
-    }
     const int jl = 32 * wave + (lane & 31);          // h column within the tile
     const int j = 128 * nt + jl;
     const int brow[2] = {jl, 128 + jl};               // gate row, up row in the stage
@@ -329,9 +513,34 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-    const int nmb = (mt.rows + 31) / 32;
-    gemm_pipe(src, smem, brow, acc, nmb);
-    const float sg = W.scale2[m0], su = W.scale2[m0 + 1];
+    float scl[2] = {1.f, 1.f}, rat[2] = {1.f, 1.f};
+    if (!sh4) {
+        const int mat = m0 + (wave >> 1);
+        const int tile = 2 * nt + (wave & 1);
+        src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)mat * I * H / 16) + (size_t)tile * (H / 64) * 1024;
+        src.ssrc = W.scales + (size_t)mat * I * H / 32 + (size_t)tile * (H / 128) * 256;
+        gemm_pipe(src, smem, brow, acc, nmb);
+        scl[0] = W.scale2[m0];
+        scl[1] = W.scale2[m0 + 1];
+    }
+    if constexpr (FP4) {
+        const moet_fp4 &F = sh4 ? p.shf13 : p.d13;
+        const int fm0 = sh4 ? 0 : 2 * ds;
+        if (sh4) {
+            scl[0] = F.scale2[0];
+            scl[1] = F.scale2[1];
+        } else {
+            fold_scales(W.scale2[m0], F.scale2[fm0], acc, 0, scl[0], rat[0]);
+            fold_scales(W.scale2[m0 + 1], F.scale2[fm0 + 1], acc, 1, scl[1], rat[1]);
+            __syncthreads();   // every wave is done with the ring before it refills
+        }
+        const int mat = fm0 + (wave >> 1);
+        const int tile = 2 * nt + (wave & 1);
+        src.bsrc = F.codes + (size_t)mat * I * H / 2 + (size_t)tile * (H / 32) * 1024;
+        src.ssrc = F.scales + (size_t)mat * I * H / 16 + (size_t)tile * (H / 128) * 512;
+        gemm_pipe4(src, smem, brow, rat, rmask, acc, nmb);
+    }
+    const float sg = scl[0], su = scl[1];
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
 #pragma unroll
     for (int mb = 0; mb < kPMB; ++mb) {
@@ -351,15 +560,32 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 }
 
-// down: N-tile nt covers output features [256 nt, 256 nt + 256); wave w owns 64 of them.
-__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc2_prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc1_prefill_kernel(PrefillParams p)
 {
     __shared__ __align__(1024) uint8_t smem[kPS * kStage];
+    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0) *p.miss_count = 0;   // counted by the combine
+    fc1_prefill_body<false>(p, smem);
+}
+
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(1))) void fc1_prefill_fp4_kernel(PrefillParams p)
+{
+    __shared__ __align__(1024) uint8_t smem[kSmem];
+    fc1_prefill_body<true>(p, smem);
+}
+
+// down: N-tile nt covers output features [256 nt, 256 nt + 256); wave w owns 64 of them.
+template <bool FP4>
+__device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t *smem)
+{
     int ms, nt;
     decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
     if (ms >= p.n_mslots) return;
     MTile mt;
     if (!locate_mtile(p, ms, mt)) return;
+    const int nmb = (mt.rows + 31) / 32;
+    int ds;
+    uint32_t rmask;
+    if (!tile_kind<FP4>(p, mt, nmb, ds, rmask)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;
@@ -372,13 +598,10 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
     if (ws < 0) return;
+    const bool sh4 = mt.e < 0 && p.shared_fp4;
     const moet_w2 &W = (mt.e >= 0) ? p.w2 : p.sh2;
     const int m0 = (mt.e >= 0) ? ws : 0;
-    {
-        const int tile = 4 * nt + wave;
-        src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
-        src.ssrc = W.scales + (size_t)m0 * H * I / 32 + (size_t)tile * (I / 128) * 256;
-    }
+    const int tile = 4 * nt + wave;
     const int brow[2] = {64 * wave + (lane & 31), 64 * wave + 32 + (lane & 31)};
     int ncol[2];
 #pragma unroll
@@ -390,9 +613,29 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-    const int nmb = (mt.rows + 31) / 32;
-    gemm_pipe(src, smem, brow, acc, nmb);
-    const float s2 = W.scale2[m0];
+    float s2 = 1.f;
+    if (!sh4) {
+        src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
+        src.ssrc = W.scales + (size_t)m0 * H * I / 32 + (size_t)tile * (I / 128) * 256;
+        gemm_pipe(src, smem, brow, acc, nmb);
+        s2 = W.scale2[m0];
+    }
+    if constexpr (FP4) {
+        const moet_fp4 &F = sh4 ? p.shf2 : p.d2;
+        const int fm = sh4 ? 0 : ds;
+        float rat[2] = {1.f, 1.f};
+        if (sh4) {
+            s2 = F.scale2[0];
+        } else {
+            float scl1;
+            fold_scales(W.scale2[m0], F.scale2[fm], acc, 0, s2, rat[0]);
+            fold_scales(W.scale2[m0], F.scale2[fm], acc, 1, scl1, rat[1]);
+            __syncthreads();   // every wave is done with the ring before it refills
+        }
+        src.bsrc = F.codes + (size_t)fm * H * I / 2 + (size_t)tile * (I / 32) * 1024;
+        src.ssrc = F.scales + (size_t)fm * H * I / 16 + (size_t)tile * (I / 128) * 512;
+        gemm_pipe4(src, smem, brow, rat, rmask, acc, nmb);
+    }
 #pragma unroll
     for (int mb = 0; mb < kPMB; ++mb) {
         if (mb >= nmb) break;
@@ -406,6 +649,18 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
     }
+}
+
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc2_prefill_kernel(PrefillParams p)
+{
+    __shared__ __align__(1024) uint8_t smem[kPS * kStage];
+    fc2_prefill_body<false>(p, smem);
+}
+
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(1))) void fc2_prefill_fp4_kernel(PrefillParams p)
+{
+    __shared__ __align__(1024) uint8_t smem[kSmem];
+    fc2_prefill_body<true>(p, smem);
 }
 
 // out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order;
@@ -467,12 +722,11 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
                    const int32_t *offsets, const int32_t *sorted, const uint8_t *gate, uint16_t *out, int32_t *miss_count,
                    void *ws, hipStream_t stream)
 {
-    if ((L->n_slots > 0 && gate != nullptr) || L->I % 128 || L->H % 256) {
-        // the FP4 delta on gated tokens is fused only into the GEMV kernels, and
+    if (L->I % 128 || L->H % 256) {
         // the grouped GEMM tiles need I % 128 == 0 and H % 256 == 0
         if ((int64_t)T * k + (T + 1) / 2 > 65535)
-            return fail(MOET_EUNSUPPORTED, "this batch needs the GEMV kernels (delta cache, or I %% 128 / H %% 256 "
-                                            "not 0), which take at most T*top_k + T/2 = 65535 entries");
+            return fail(MOET_EUNSUPPORTED, "this batch needs the GEMV kernels (I %% 128 or H %% 256 not 0), which "
+                                            "take at most T*top_k + T/2 = 65535 entries");
         return launch_decode(L, x, T, k, ids, w, offsets, sorted, gate, out, miss_count, ws, stream);
     }
     PrefillParams p;
@@ -495,6 +749,14 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     p.base_slot = L->base_slot_of_expert;
     p.n_base_slots = L->n_base_slots;
     p.miss_count = miss_count;
+    p.gate = gate;
+    p.n_slots = (gate != nullptr) ? L->n_slots : 0;
+    p.slot_of_expert = L->slot_of_expert;
+    p.d13 = L->d13;
+    p.d2 = L->d2;
+    p.shared_fp4 = (L->has_shared && L->shared_fp4) ? 1 : 0;
+    p.shf13 = L->shared13_fp4;
+    p.shf2 = L->shared2_fp4;
     const size_t rows = (size_t)T * k + T;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     char *base = static_cast<char *>(ws);
@@ -506,15 +768,27 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     p.n_mslots = mslots;
     const int ms8 = (mslots + 7) / 8 * 8;
     p.n_ntiles = L->I / 128;
+    // tiles with FP4 work (delta rows, NVFP4 shared expert) go to the *_fp4 kernels
+    const bool fp4 = (p.n_slots > 0) || p.shared_fp4;
     timing_start(stream);
     hipLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
     timing_stop(stream);
     int rc = check_launch("fc1_prefill_kernel");
     if (rc != MOET_OK) return rc;
+    if (fp4) {
+        hipLaunchKernelGGL(fc1_prefill_fp4_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
+        rc = check_launch("fc1_prefill_fp4_kernel");
+        if (rc != MOET_OK) return rc;
+    }
     p.n_ntiles = L->H / 256;
     hipLaunchKernelGGL(fc2_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
     rc = check_launch("fc2_prefill_kernel");
     if (rc != MOET_OK) return rc;
+    if (fp4) {
+        hipLaunchKernelGGL(fc2_prefill_fp4_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
+        rc = check_launch("fc2_prefill_fp4_kernel");
+        if (rc != MOET_OK) return rc;
+    }
     hipLaunchKernelGGL(combine_prefill_kernel, dim3((L->H + 255) / 256, T), dim3(256), 0, stream, p);
     return check_launch("combine_prefill_kernel");
 }

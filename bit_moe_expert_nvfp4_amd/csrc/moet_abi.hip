@@ -52,6 +52,8 @@ int launch_requant(const uint8_t *, const uint8_t *, const float *, int64_t, int
                    const int32_t *, int64_t, uint8_t *, uint8_t *, float *, int, hipStream_t);
 int launch_remap_mxfp4(const uint8_t *, const uint8_t *, int64_t, int, int, int, uint32_t *, uint8_t *, float *,
                        hipStream_t);
+int launch_pack_nvfp4(const uint8_t *, const uint8_t *, const float *, int64_t, int, int, uint8_t *, uint8_t *, float *,
+                      hipStream_t);
 int launch_requant_fp8(const uint8_t *, const float *, int64_t, int, int, int, uint32_t *, uint8_t *, float *,
                        hipStream_t);
 int launch_route(const float *, int, int, int, int, int, float, int32_t *, float *, int32_t *, int32_t *, hipStream_t);
@@ -75,8 +77,10 @@ static int check_layer(const moet_layer *L)
     if (L->E < 1 || L->E > 1024) return fail(MOET_EINVAL, "E (%d) must be in [1, 1024]", L->E);
     if ((!L->base_slot_of_expert || L->n_base_slots > 0) && (!w2_ok(L->w13) || !w2_ok(L->w2)))
         return fail(MOET_EINVAL, "w13 / w2 pointers must be non-NULL and 16-byte aligned");
-    if (L->has_shared && (!w2_ok(L->shared13) || !w2_ok(L->shared2)))
+    if (L->has_shared && !L->shared_fp4 && (!w2_ok(L->shared13) || !w2_ok(L->shared2)))
         return fail(MOET_EINVAL, "shared expert pointers must be non-NULL and 16-byte aligned");
+    if (L->has_shared && L->shared_fp4 && (!fp4_ok(L->shared13_fp4) || !fp4_ok(L->shared2_fp4)))
+        return fail(MOET_EINVAL, "NVFP4 shared expert pointers must be non-NULL and 16-byte aligned");
     if (L->n_slots < 0) return fail(MOET_EINVAL, "n_slots (%d) must be >= 0", L->n_slots);
     if (L->base_slot_of_expert && (!aligned16(L->base_slot_of_expert) || L->n_base_slots < 0))
         return fail(MOET_EINVAL, "expert cache: base_slot_of_expert must be 16-byte aligned and n_base_slots >= 0");
@@ -110,7 +114,7 @@ const char *moet_status_str(int s)
 
 const char *moet_last_error(void) { return g_err; }
 
-int moet_abi_version(void) { return 3; }
+int moet_abi_version(void) { return 4; }
 
 // shape checks shared by the load-time conversions
 static int check_stack(int64_t n_mat, int64_t N, int64_t K, uint32_t flags)
@@ -141,6 +145,19 @@ int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const floa
     return launch_requant(fp4_codes, fp4_scales, fp4_scale2, n_mat, (int)N, (int)K, w2_codes, w2_scales, w2_scale2,
                           delta_sel, n_sel, d_codes, d_scales, d_scale2, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
                           (hipStream_t)stream);
+}
+
+int moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
+                    int64_t N, int64_t K, uint8_t *d_codes, uint8_t *d_scales, float *d_scale2, void *stream)
+{
+    g_err[0] = 0;
+    int rc = check_stack(n_mat, N, K, 0);
+    if (rc != MOET_OK) return rc;
+    if (!aligned16(fp4_codes) || !aligned16(fp4_scales) || !aligned16(fp4_scale2) || !aligned16(d_codes) ||
+        !aligned16(d_scales) || !aligned16(d_scale2))
+        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
+    return launch_pack_nvfp4(fp4_codes, fp4_scales, fp4_scale2, n_mat, (int)N, (int)K, d_codes, d_scales, d_scale2,
+                             (hipStream_t)stream);
 }
 
 int moet_remap_mxfp4(const uint8_t *mx_codes, const uint8_t *mx_scales, int64_t n_mat, int64_t N, int64_t K,

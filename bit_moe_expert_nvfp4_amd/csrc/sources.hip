@@ -231,6 +231,44 @@ __global__ __launch_bounds__(256) void fp8_requant_kernel(const uint8_t *__restr
     store_w2_block(wcodes, wscales, mat, N, K, n, b, out, best_t);
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 -> FP4 layout (values unchanged)
+// ---------------------------------------------------------------------------
+
+// one thread per (matrix, row, 32-k chunk); the thread of every fourth chunk
+// also moves the row's eight block scales of that 128-k group
+__global__ __launch_bounds__(256) void pack_nvfp4_kernel(const uint8_t *__restrict__ codes,
+                                                         const uint8_t *__restrict__ scales,
+                                                         const float *__restrict__ s2in, int64_t n_mat, int N, int K,
+                                                         uint8_t *__restrict__ dcodes, uint8_t *__restrict__ dscales,
+                                                         float *__restrict__ ds2)
+{
+    const int nc = K / 32;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)n_mat * N * nc) return;
+    const int c = (int)(idx % nc);
+    const size_t rg = idx / nc;
+    const int n = (int)(rg % N);
+    const size_t mat = rg / N;
+    if (n == 0 && c == 0) ds2[mat] = s2in[mat];
+    const int tile = n / 64, r = n % 64;
+    const uint4 v = reinterpret_cast<const uint4 *>(codes)[idx];   // chunk c of row n: 16 contiguous bytes
+    reinterpret_cast<uint4 *>(dcodes + mat * (size_t)N * (K / 2))[fp4_chunk_idx(tile, c, r, K)] = v;
+    if ((c & 3) == 0) {
+        const uint2 sv = reinterpret_cast<const uint2 *>(scales)[idx / 4];   // 8 scales of group c / 4
+        reinterpret_cast<uint2 *>(dscales + mat * (size_t)N * (K / 16))[fp4_scale_idx(tile, c / 4, r, K)] = sv;
+    }
+}
+
+int launch_pack_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *s2, int64_t n_mat, int N, int K,
+                      uint8_t *dc, uint8_t *ds, float *ds2, hipStream_t stream)
+{
+    const size_t total = (size_t)n_mat * N * (K / 32);
+    hipLaunchKernelGGL(pack_nvfp4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, codes, scales,
+                       s2, n_mat, N, K, dc, ds, ds2);
+    return check_launch("pack_nvfp4_kernel");
+}
+
 int launch_remap_mxfp4(const uint8_t *codes, const uint8_t *escales, int64_t n_mat, int N, int K, int balance,
                        uint32_t *wc, uint8_t *wsc, float *ws2, hipStream_t stream)
 {

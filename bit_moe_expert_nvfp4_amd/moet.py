@@ -39,7 +39,8 @@ class LayerC(ctypes.Structure):
     _fields_ = [("H", _i32), ("I", _i32), ("E", _i32), ("w13", W2), ("w2", W2), ("has_shared", _i32),
                 ("shared13", W2), ("shared2", W2), ("n_slots", _i32), ("slot_of_expert", _vp),
                 ("d13", FP4), ("d2", FP4), ("swiglu_limit", ctypes.c_float),
-                ("base_slot_of_expert", _vp), ("n_base_slots", _i32)]
+                ("base_slot_of_expert", _vp), ("n_base_slots", _i32),
+                ("shared_fp4", _i32), ("shared13_fp4", FP4), ("shared2_fp4", FP4)]
 
 
 _lib = None
@@ -66,6 +67,8 @@ def lib():
         L.moet_requant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                    ctypes.c_uint32, _vp]
         L.moet_requant.restype = ctypes.c_int
+        L.moet_pack_nvfp4.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
+        L.moet_pack_nvfp4.restype = ctypes.c_int
         L.moet_remap_mxfp4.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_uint32, _vp]
         L.moet_remap_mxfp4.restype = ctypes.c_int
         L.moet_requant_fp8.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_uint32, _vp]
@@ -169,6 +172,23 @@ def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
     return (w, d) if delta_sel is not None else w
 
 
+def pack_nvfp4(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor) -> FP4Planes:
+    """NVFP4 stack (codes uint8 [n, N, K/2], scales uint8 [n, N, K/16], scale2 f32 [n]) in the FP4
+    layout, values unchanged (the form of an NVFP4 shared expert)."""
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    _need(scale2, torch.float32, "scale2")
+    n, N, Kh = codes.shape
+    K = 2 * Kh
+    dev = codes.device
+    d = FP4Planes(torch.empty((n, N * K // 2), dtype=torch.uint8, device=dev),
+                  torch.empty((n, N * K // 16), dtype=torch.uint8, device=dev),
+                  torch.empty((n,), dtype=torch.float32, device=dev), N, K)
+    _check(lib().moet_pack_nvfp4(_ptr(codes), _ptr(scales), _ptr(scale2), n, N, K, _ptr(d.codes), _ptr(d.scales),
+                                 _ptr(d.scale2), _stream()))
+    return d
+
+
 def remap_mxfp4(codes: torch.Tensor, scales: torch.Tensor, balance_zero_signs: bool = False) -> W2Planes:
     """MXFP4 stack (codes uint8 [n, N, K/2], e8m0 scales uint8 [n, N, K/32]) -> W2Planes."""
     _need(codes, torch.uint8, "codes")
@@ -234,20 +254,26 @@ class Layer:
     swiglu_limit: float = 0.0
     # expert cache: w13/w2 hold only the experts with base_slot_of_expert[e] >= 0 (int32 [E]), at that slot
     base_slot_of_expert: Optional[torch.Tensor] = None
+    # NVFP4 shared expert (instead of shared13 / shared2): gate + up [I][H] and down [H][I] in the FP4 layout
+    shared13_fp4: Optional[FP4Planes] = None
+    shared2_fp4: Optional[FP4Planes] = None
 
     def c(self) -> LayerC:
         z = W2(None, None, None)
         zf = FP4(None, None, None)
         n_slots = 0 if self.d2 is None else int(self.d2.scale2.numel())
+        sh4 = self.shared13_fp4 is not None
         return LayerC(self.H, self.I, self.E, self.w13.c(), self.w2.c(),
-                      1 if self.shared13 is not None else 0,
+                      1 if (self.shared13 is not None or sh4) else 0,
                       self.shared13.c() if self.shared13 is not None else z,
                       self.shared2.c() if self.shared2 is not None else z,
                       n_slots, self.slot_of_expert.data_ptr() if n_slots else None,
                       self.d13.c() if n_slots else zf, self.d2.c() if n_slots else zf,
                       float(self.swiglu_limit),
                       self.base_slot_of_expert.data_ptr() if self.base_slot_of_expert is not None else None,
-                      int(self.w2.scale2.numel()) if self.base_slot_of_expert is not None else 0)
+                      int(self.w2.scale2.numel()) if self.base_slot_of_expert is not None else 0,
+                      1 if sh4 else 0, self.shared13_fp4.c() if sh4 else zf,
+                      self.shared2_fp4.c() if sh4 else zf)
 
 
 def expert_cache(layer: Layer, slot_of_expert) -> Layer:
@@ -348,10 +374,11 @@ def set_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cu
 # Building a layer from NVFP4 sources
 # ---------------------------------------------------------------------------
 def layer_from_nvfp4(src, slot_of_expert: Optional[torch.Tensor] = None, swiglu_limit: float = 0.0,
-                     device="cuda") -> Layer:
+                     device="cuda", shared_nvfp4: bool = False) -> Layer:
     """Requantise an NVFP4 layer (synth.NVFP4Layer-like: w13/w2/shared13/shared2 tuples of
     (codes, scales, scale2)) on the GPU and build the library layer; experts with
-    slot_of_expert >= 0 also get their FP4 delta."""
+    slot_of_expert >= 0 also get their FP4 delta.  shared_nvfp4 keeps the shared expert
+    in NVFP4 instead of requantising it."""
     cfg = src.cfg
 
     def dev(t):
@@ -376,8 +403,12 @@ def layer_from_nvfp4(src, slot_of_expert: Optional[torch.Tensor] = None, swiglu_
         w13 = requant(*w13_src)
         w2 = requant(*w2_src)
         slot_dev = None
-    sh13 = sh2 = None
-    if src.shared13 is not None:
+    sh13 = sh2 = f13 = f2 = None
+    if src.shared13 is not None and shared_nvfp4:
+        f13 = pack_nvfp4(*(dev(t) for t in src.shared13))
+        f2 = pack_nvfp4(*(dev(t) for t in src.shared2))
+    elif src.shared13 is not None:
         sh13 = requant(*(dev(t) for t in src.shared13))
         sh2 = requant(*(dev(t) for t in src.shared2))
-    return Layer(cfg.H, cfg.I, cfg.E, w13, w2, sh13, sh2, slot_dev, d13, d2, swiglu_limit)
+    return Layer(cfg.H, cfg.I, cfg.E, w13, w2, sh13, sh2, slot_dev, d13, d2, swiglu_limit,
+                 shared13_fp4=f13, shared2_fp4=f2)

@@ -23,6 +23,8 @@
  *                       counting routings to missing experts (README, "When the
  *                       model doesn't fit at all — the GPU as an expert cache")
  *   moet_delta_forward  the standalone FP4 delta GEMM/GEMV (README, "How it fits")
+ *   moet_pack_nvfp4     NVFP4 matrices -> the FP4 layout (an NVFP4 shared
+ *                       expert; README, "How it fits")
  *   moet_remap_mxfp4    FP4 (MXFP4) experts -> the same 2-bit planes by a
  *                       code remap (README, "How it fits")
  *   moet_requant_fp8    FP8 block-quantised experts -> the same 2-bit planes
@@ -146,6 +148,25 @@ int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const floa
                  uint32_t flags, void *stream);
 
 /*
+ * moet_pack_nvfp4 - a stack of n_mat modelopt NVFP4 matrices [N][K] in the
+ * library's FP4 layout, unchanged in value (codes, block scales and scale_2
+ * are moved, not re-encoded): the form the forward reads an NVFP4 shared
+ * expert in.  (README "Frontier MoE on consumer Blackwell (SM120)", section
+ * "How it fits — 2-bit experts at FP4 quality": only the routed experts are
+ * compressed to 2 bits.)
+ *
+ * Inputs: fp4_codes uint8 [n_mat][N][K/2], fp4_scales uint8 [n_mat][N][K/16],
+ *   fp4_scale2 fp32 [n_mat] (modelopt layout).
+ * Outputs: d_codes uint8 [n_mat][N*K/2], d_scales uint8 [n_mat][N*K/16],
+ *   d_scale2 fp32 [n_mat] (FP4 layout).
+ * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
+ *   pointers.
+ */
+int moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2,
+                    int64_t n_mat, int64_t N, int64_t K,
+                    uint8_t *d_codes, uint8_t *d_scales, float *d_scale2, void *stream);
+
+/*
  * moet_remap_mxfp4 - MXFP4 experts -> sign-symmetric 2-bit planes by a code
  * remap, for a stack of n_mat equal-shape matrices [N][K].  (README "Frontier
  * MoE on consumer Blackwell (SM120)", section "How it fits — 2-bit experts at
@@ -246,6 +267,12 @@ typedef struct {
  * at cache slot base_slot_of_expert[e] of w13 (2*n_base_slots matrices) and
  * w2 (n_base_slots matrices); a slot outside [0, n_base_slots) marks the
  * expert missing: its routings contribute nothing and are counted.
+ * NVFP4 shared expert (README, "How it fits": only the routed experts go to
+ * 2 bits, the rest keeps the checkpoint's precision): has_shared != 0 and
+ * shared_fp4 != 0 take the shared expert from shared13_fp4 (gate = matrix 0,
+ * up = matrix 1, [I][H]) and shared2_fp4 ([H][I]) in the FP4 layout
+ * (moet_pack_nvfp4 builds them from a modelopt export); shared13 / shared2
+ * are then unused.
  */
 typedef struct {
     int32_t H, I, E;
@@ -258,6 +285,8 @@ typedef struct {
     float swiglu_limit;
     const int32_t *base_slot_of_expert;
     int32_t n_base_slots;
+    int32_t shared_fp4;
+    moet_fp4 shared13_fp4, shared2_fp4;
 } moet_layer;
 
 /* Workspace bytes moet_moe_forward needs for T tokens and top_k. */
@@ -278,10 +307,12 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
  * (+ D2_slot h); out bf16 [T][H] = bf16(sum_j topk_w[t][j] * y_(t,j) +
  * y_shared(t)).  Accumulation is fp32; h and out are rounded to nearest-even.
  * Decode-sized batches (T*top_k <= 1024) run the GEMV kernels; larger
- * batches run the MFMA grouped-GEMM kernels when I % 128 == 0, H % 256 == 0
- * and no token is gated onto the delta cache, else the GEMV kernels, which
- * take at most T*top_k + ceil(T/2) = 65535 work entries (MOET_EUNSUPPORTED
- * beyond).
+ * batches run the MFMA grouped-GEMM kernels when I % 128 == 0 and
+ * H % 256 == 0 (the FP4 delta and an NVFP4 shared expert then run as an FP4
+ * MFMA pass; a delta is added as D * (d_scale2 / scale2), exact when the
+ * ratio is a power of two, as it is (1/2) for planes built by moet_requant),
+ * else the GEMV kernels, which take at most T*top_k + ceil(T/2) = 65535 work
+ * entries (MOET_EUNSUPPORTED beyond).
  * workspace: at least moet_moe_workspace_bytes(L, T, top_k) bytes of device
  * memory, 256-byte aligned; its contents need no initialisation.
  * Expert ids outside [0, E) and slots outside [0, n_slots) contribute

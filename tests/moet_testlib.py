@@ -47,10 +47,11 @@ class OracleMatrix:
 class OracleLayer:
     """Lazily requantises the experts the oracle needs, straight from the NVFP4 bytes."""
 
-    def __init__(self, src, slot_of_expert=None):
+    def __init__(self, src, slot_of_expert=None, shared_nvfp4=False):
         self.src = src
         self.cfg = src.cfg
         self.soe = None if slot_of_expert is None else np_(slot_of_expert)
+        self.shared_nvfp4 = shared_nvfp4
         self._cache = {}
 
     def _mat(self, stack, i, with_delta):
@@ -82,6 +83,9 @@ class OracleLayer:
     def shared_weights(self):
         if self.src.shared13 is None:
             return None
+        if self.shared_nvfp4:      # the shared expert keeps its NVFP4 values
+            dq = lambda st, i: OF.nvfp4_decode(np_(st[0][i]), np_(st[1][i]), float(st[2][i]))
+            return dq(self.src.shared13, 0), dq(self.src.shared13, 1), dq(self.src.shared2, 0)
         g = self._mat(self.src.shared13, 0, False)
         u = self._mat(self.src.shared13, 1, False)
         dn = self._mat(self.src.shared2, 0, False)

@@ -132,10 +132,10 @@ def _small_cfg(**kw):
     return synth.LayerConfig(**base)
 
 
-def _run_forward_case(cfg, seed=0, check_determinism=False):
+def _run_forward_case(cfg, seed=0, check_determinism=False, shared_nvfp4=False):
     src = synth.make_layer(cfg, seed=seed)
     soe = synth.slot_of_expert(cfg, seed) if cfg.n_resident else None
-    layer = moet.layer_from_nvfp4(src, soe, swiglu_limit=cfg.swiglu_limit)
+    layer = moet.layer_from_nvfp4(src, soe, swiglu_limit=cfg.swiglu_limit, shared_nvfp4=shared_nvfp4)
     x = synth.make_activations(cfg.T, cfg.H, seed)
     lg = synth.make_logits(cfg, seed)
     flags = synth.gate_flags(cfg, seed) if cfg.n_flagged else None
@@ -145,7 +145,7 @@ def _run_forward_case(cfg, seed=0, check_determinism=False):
     torch.cuda.synchronize()
     o_ids, o_w, _, _ = oracle_route(lg, cfg.k, cfg.score, cfg.renormalize)
     assert (np_(ids) == o_ids).all()
-    ol = OracleLayer(src, soe)
+    ol = OracleLayer(src, soe, shared_nvfp4=shared_nvfp4)
     ref = ol.forward(bf16_bits(x), o_ids, o_w, gate_flags=np_(flags) if flags is not None else None)
     got = bf16_bits(out)
     err = rel_l2(got, ref)
@@ -173,6 +173,14 @@ def _run_forward_case(cfg, seed=0, check_determinism=False):
     dict(T=200, E=64, k=8, H=512, I=256, score=synth.SIGMOID, swiglu_limit=0.01),
     dict(T=1500, E=4, k=1, H=512, I=256),
     dict(T=300, E=16, k=8, H=384, score=synth.SIGMOID),   # batch above the GEMV size, H not a GEMM tile multiple
+    # one GPU's share of a tensor-parallel layer at the full hidden size: I = 2048 / 4 and 2048 / 2
+    dict(T=3, E=16, k=4, H=7168, I=512, shared=True, score=synth.SIGMOID),
+    dict(T=3, E=8, k=2, H=7168, I=1024, n_resident=3, n_flagged=2, score=synth.SIGMOID),
+    dict(T=200, E=8, k=4, H=7168, I=512, score=synth.SIGMOID),
+    # grouped-GEMM batches with gate-flagged tokens on delta-cache experts: the FP4 MFMA pass
+    dict(T=300, E=16, k=8, H=512, I=256, n_resident=6, n_flagged=120, shared=True, score=synth.SIGMOID),
+    dict(T=1100, E=4, k=1, H=256, I=128, n_resident=4, n_flagged=1100),
+    dict(T=200, E=8, k=8, H=512, I=256, n_resident=8, n_flagged=1, swiglu_limit=0.01, score=synth.SIGMOID),
 ])
 def test_forward_small(case):
     cfg = _small_cfg(**case)
@@ -189,6 +197,35 @@ def test_forward_small(case):
     # top-8, T=300: 100 flips in 1.2M -> 1.05e-4.  Flips grow with the reduction
     # length, so the alarm scales with H.
     assert err <= 3e-4 * max(1.0, cfg.H / 512)
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=5, E=16, k=4, shared=True, score=synth.SIGMOID),                                   # GEMV path
+    dict(T=3, E=8, k=2, shared=True, n_resident=3, n_flagged=2, H=512, I=256),
+    dict(T=300, E=16, k=8, H=512, I=256, shared=True, score=synth.SIGMOID),                   # grouped GEMM
+    dict(T=260, E=8, k=4, H=512, I=256, shared=True, n_resident=3, n_flagged=100, score=synth.SIGMOID),
+])
+def test_forward_nvfp4_shared_expert(case):
+    """The shared expert kept in NVFP4 (moet_pack_nvfp4 planes) on both paths."""
+    cfg = _small_cfg(**case)
+    _print_case(f"forward NVFP4 shared expert {case}")
+    err, got, ref = _run_forward_case(cfg, seed=zlib.crc32(str(sorted(case.items())).encode()) & 0xFFFF,
+                                      shared_nvfp4=True)
+    print(f"rel_l2={err:.3e}", flush=True)
+    assert err <= REL_L2_BAR
+    assert err <= 3e-4 * max(1.0, cfg.H / 512)
+
+
+def test_pack_nvfp4_bitexact():
+    _print_case("pack nvfp4 random bytes n=3 N=192 K=384")
+    rng = np.random.default_rng(12)
+    codes, scales, s2 = _nvfp4_stack_random(rng, 3, 192, 384)
+    d = moet.pack_nvfp4(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), torch.from_numpy(s2).to(DEV))
+    torch.cuda.synchronize()
+    for m in range(3):
+        assert (np_(d.codes[m]) == OL.pack_fp4_codes(OF.unpack_nibbles(codes[m]))).all(), f"codes of matrix {m}"
+        assert (np_(d.scales[m]) == OL.pack_fp4_scales(scales[m])).all(), f"scales of matrix {m}"
+        assert np_(d.scale2)[m] == s2[m]
 
 
 def test_forward_random_planes_every_scale_code():

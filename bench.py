@@ -109,15 +109,15 @@ def counted_traffic():
         return None
 
 
-def step_bytes(cfg, ids_np, flags_np, soe_np, resident=None):
+def step_bytes(cfg, ids_np, flags_np, soe_np, resident=None, shared_nvfp4=False):
     """Algorithmic bytes of one decode step and of its gate/up kernel launch (with an expert cache, only
-    the resident experts' planes are read)."""
+    the resident experts' planes are read; an NVFP4 shared expert reads its FP4 planes)."""
     w13 = 2 * cfg.I * cfg.H * W2_BYTES_PER_WEIGHT
     w2 = cfg.H * cfg.I * W2_BYTES_PER_WEIGHT
     d13 = 2 * cfg.I * cfg.H * FP4_BYTES_PER_WEIGHT
     d2 = cfg.H * cfg.I * FP4_BYTES_PER_WEIGHT
     experts = set(int(e) for e in ids_np.reshape(-1) if resident is None or resident[int(e)])
-    n = len(experts) + (1 if cfg.shared else 0)
+    n = len(experts) + (1 if cfg.shared and not shared_nvfp4 else 0)
     delta_experts = set()
     if flags_np is not None and soe_np is not None:
         for t in range(cfg.T):
@@ -126,6 +126,8 @@ def step_bytes(cfg, ids_np, flags_np, soe_np, resident=None):
                     if soe_np[int(e)] >= 0 and (resident is None or resident[int(e)]):
                         delta_experts.add(int(e))
     nd = len(delta_experts)
+    if cfg.shared and shared_nvfp4:
+        nd += 1                       # the shared expert's FP4 planes
     io = 2 * cfg.T * cfg.H * 2 + 4 * cfg.T * cfg.E
     total = n * (w13 + w2) + nd * (d13 + d2) + io
     fc1 = n * w13 + nd * d13 + 2 * cfg.T * cfg.H + 2 * (cfg.T * cfg.k + cfg.T) * cfg.I
@@ -185,14 +187,18 @@ def _blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_fraction=None):
-    """Route + forward of another decode configuration (FP4 delta cache, batched streams), timed like the
-    main step over its own pool of layers and input sets."""
+def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_fraction=None, tp=1,
+               shared_nvfp4=False):
+    """Route + forward of another decode configuration (FP4 delta cache, batched streams, one GPU's
+    share of a tensor-parallel layer), timed like the main step over its own pool of layers and input sets."""
+    import dataclasses
     import numpy as np
     import torch
     from bit_moe_expert_nvfp4_amd import moet, synth
 
     cfg = synth.CONFIGS[cfg_no]
+    if tp > 1:                         # rows I/tp of gate/up and columns I/tp of down per GPU
+        cfg = dataclasses.replace(cfg, name=f"{cfg.name}_tp{tp}_shard", I=cfg.I // tp)
     soe = synth.slot_of_expert(cfg, seed) if cfg.n_resident else None
     layers = []
     resident = None
@@ -205,7 +211,7 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_f
         resident = (base_soe >= 0).numpy()
     for li in range(n_layers):
         src = synth.make_layer(cfg, seed=seed, device=dev, layer_index=li)
-        lay = moet.layer_from_nvfp4(src, soe)
+        lay = moet.layer_from_nvfp4(src, soe, shared_nvfp4=shared_nvfp4)
         del src
         if resident is not None:
             lay = moet.expert_cache(lay, base_soe)
@@ -233,7 +239,8 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_f
     torch.cuda.synchronize()
     flags_np = flags.cpu().numpy() if flags is not None else None
     soe_np = soe.numpy() if soe is not None else None
-    per_input = [step_bytes(cfg, ro[j][0].cpu().numpy(), flags_np, soe_np, resident) for j in range(n_inputs)]
+    per_input = [step_bytes(cfg, ro[j][0].cpu().numpy(), flags_np, soe_np, resident, shared_nvfp4)
+                 for j in range(n_inputs)]
     misses = [int((~resident[ro[j][0].cpu().numpy().reshape(-1)]).sum()) if resident is not None else 0
               for j in range(n_inputs)]
     if resident is not None:          # the on-device counter of the last warm-up step
@@ -261,7 +268,7 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_f
     res = {
         "workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} top{cfg.k} sigmoid+renorm"
                     f"{' (Zipf-skewed logits)' if cfg.logits == 'zipf' else ''}"
-                    f"{' + shared expert' if cfg.shared else ''}"
+                    f"{(' + NVFP4 shared expert' if shared_nvfp4 else ' + shared expert') if cfg.shared else ''}"
                     f"{f' + FP4 delta ({cfg.n_resident} resident, {cfg.n_flagged} of {cfg.T} tokens flagged)' if cfg.n_resident else ''}"
                     f"{cache_txt}, {n_layers}-layer pool, {n_inputs} input sets",
         "us_per_layer": round(ms * 1e3, 2),
@@ -339,8 +346,9 @@ def conversion_leg(seed, dev, n_mat=16, N=2048, K=7168, steps=5):
     return res
 
 
-def prefill_leg(layer, cfg5, steps, seed, dev):
-    """Time route + forward of a prefill chunk (MFMA grouped GEMM path) on one pool layer."""
+def prefill_leg(layer, cfg5, steps, seed, dev, flags=None, soe=None):
+    """Time route + forward of a prefill chunk (MFMA grouped GEMM path) on one pool layer; with
+    gate flags and a delta cache, flagged rows of resident experts also run the FP4 pass."""
     import numpy as np
     import torch
     from bit_moe_expert_nvfp4_amd import moet, synth
@@ -355,11 +363,17 @@ def prefill_leg(layer, cfg5, steps, seed, dev):
 
     def step():
         ids, w, offs, pairs = moet.route(lg, k, cfg5.score, cfg5.renormalize, out=ro)
-        moet.moe_forward(layer, x, ids, w, offs, pairs, None, out=out, workspace=ws)
+        moet.moe_forward(layer, x, ids, w, offs, pairs, flags, out=out, workspace=ws)
 
     for _ in range(3):
         step()
     torch.cuda.synchronize()
+    delta_pairs = 0
+    if flags is not None:
+        ids_np = ro[0].cpu().numpy()
+        fl_np = flags.cpu().numpy().astype(bool)
+        soe_np = soe.cpu().numpy()
+        delta_pairs = int((fl_np[:, None] & (soe_np[ids_np] >= 0)).sum())
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in ev:
         a.record()
@@ -379,9 +393,15 @@ def prefill_leg(layer, cfg5, steps, seed, dev):
     fl_fc1 = 2.0 * P * 2 * cfg5.I * cfg5.H
     fl = fl_fc1 + 2.0 * P * cfg5.H * cfg5.I
     peak = MFMA_BF16_PEAK_TFLOPS
+    extra = ""
+    if flags is not None:
+        extra = (f", FP4 delta for {int(flags.sum().item())} gate-flagged tokens on {int((soe >= 0).sum().item())} "
+                 f"delta-cache experts ({delta_pairs} flagged pairs; their FP4 pass is counted in the flops)")
+        fl_fc1 += 2.0 * delta_pairs * 2 * cfg5.I * cfg5.H
+        fl += 2.0 * delta_pairs * 3 * cfg5.I * cfg5.H
     return {
         "workload": f"prefill chunk: T={T} H={cfg5.H} I={cfg5.I} E={cfg5.E} top{k} sigmoid+renorm, "
-                    f"N(0,1) logits, no shared expert, 2-bit planes -> bf16 MFMA grouped GEMM",
+                    f"N(0,1) logits, no shared expert, 2-bit planes -> bf16 MFMA grouped GEMM{extra}",
         "us_per_layer": round(ms * 1e3, 1),
         "tokens_per_s": round(T / (ms / 1e3), 1),
         "useful_tflops": round(fl / (ms / 1e3) / 1e12, 1),
@@ -568,12 +588,31 @@ def main():
         result["confidence_gate"] = gate_leg(args.seed, dev)
         print("[bench] timing the load-time conversions", file=sys.stderr, flush=True)
         result["load_conversions"] = conversion_leg(args.seed, dev)
+        if not args.no_prefill:
+            print("[bench] timing the prefill chunk with the FP4 delta", file=sys.stderr, flush=True)
+            import dataclasses
+            cfgd = dataclasses.replace(synth.CONFIGS[5], name="prefill_delta", n_resident=32, n_flagged=2048)
+            srcd = synth.make_layer(cfgd, seed=args.seed, device=dev)
+            soed = synth.slot_of_expert(cfgd, args.seed)
+            ld = moet.layer_from_nvfp4(srcd, soed)
+            del srcd
+            torch.cuda.empty_cache()
+            result["prefill_delta"] = prefill_leg(ld, cfgd, max(3, args.prefill_steps // 2), args.seed, dev,
+                                                  flags=synth.gate_flags(cfgd, args.seed).to(dev), soe=soed)
+            del ld
+            torch.cuda.empty_cache()
         del layers
         torch.cuda.empty_cache()
         result["other_decode"] = {}
-        for cno, key, frac in ((3, "delta_cache", None), (4, "batched", None), (2, "expert_cache_half", 0.5)):
+        for cno, key, frac, tp in ((3, "delta_cache", None, 1), (4, "batched", None, 1),
+                                   (2, "expert_cache_half", 0.5, 1), (2, "tp2_shard", None, 2),
+                                   (2, "tp4_shard", None, 4)):
             print(f"[bench] timing decode config {key}", file=sys.stderr, flush=True)
-            result["other_decode"][key] = decode_leg(cno, args.extra_steps, 10, args.seed, dev, cache_fraction=frac)
+            result["other_decode"][key] = decode_leg(cno, args.extra_steps, 10, args.seed, dev,
+                                                     cache_fraction=frac, tp=tp)
+        print("[bench] timing decode with an NVFP4 shared expert", file=sys.stderr, flush=True)
+        result["other_decode"]["nvfp4_shared"] = decode_leg(2, args.extra_steps, 10, args.seed, dev,
+                                                            shared_nvfp4=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
         cb = cpu_baseline(cfg, srcs[0], xs[0], lgs[0], args.seed)

@@ -35,11 +35,11 @@
 //    with a B stage of two 32-k FP4 chunks per row and one dword of four
 //    block-16 scales.  One MFMA k-step is exactly one block-16, so a lane
 //    dequantises its 8 values as e2m1 -> f32 -> * scale -> bf16, exact
-//    (e2m1 * e4m3 has at most 6 significant bits).  The delta pass runs after
-//    the 2-bit pass of a tile into the same accumulators, with the A rows of
-//    unflagged tokens zeroed in registers and the delta values pre-multiplied
-//    by scale2_delta / scale2 (exactly 1/2 for planes built by moet_requant);
-//    an NVFP4 shared expert runs the FP4 pass alone.
+//    (e2m1 * e4m3 has at most 6 significant bits).  FP4 work runs in kernels
+//    of its own after the 2-bit ones: for a tile with gate-flagged rows, the
+//    2-bit gate/up kernel leaves fp32 pre-activations, the FP4 kernel adds the
+//    delta (rows of unflagged tokens zeroed in registers) and applies SwiGLU;
+//    the FP4 down kernel adds its y to the 2-bit y.
 #include <algorithm>
 
 #include "moet_common.h"
@@ -66,6 +66,7 @@ struct PrefillParams {
     float swiglu_limit;
     uint16_t *h;        // [P + T][I] bf16, rows in sorted-pair order (shared expert: P + t)
     float *ypart;       // [P + T][H] fp32, rows by pair id (shared expert: P + t)
+    float *pre;         // [P + T][2I] fp32 gate/up pre-activations of delta tiles (aliases ypart)
     uint16_t *out;
     int n_mslots;       // upper bound on M-tiles (grid)
     int n_ntiles;
@@ -308,7 +309,6 @@ __device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, con
 constexpr int kStageB4 = 8 * 1024;
 constexpr int kStage4 = kStageA + kStageB4 + kStageS;
 constexpr int kDmaPerStage4 = 7;
-constexpr int kSmem = (kPS * kStage4 > kPS * kStage) ? kPS * kStage4 : kPS * kStage;
 
 __device__ __forceinline__ void issue_stage4(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
 {
@@ -351,14 +351,14 @@ __device__ __forceinline__ float fp8_byte(uint32_t w) { return __builtin_amdgcn_
 // one MFMA k-step (16 k = one FP4 block) of the FP4 pipeline
 template <int NMB, int Q>
 __device__ __forceinline__ void fp4_kstep(const uint8_t *aT, const uint8_t *bT, const int boff[2], const uint32_t sw[2],
-                                          const float rat[2], uint32_t rmask, f32x16 acc[kPMB][2])
+                                          uint32_t rmask, f32x16 acc[kPMB][2])
 {
     const int lane = threadIdx.x & 63, h = lane >> 5;
     bf16x8 bfr[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const uint32_t wv = *reinterpret_cast<const uint32_t *>(bT + boff[nb] + (Q >> 1) * 1024 + (Q & 1) * 8);
-        bfr[nb] = deq_fp4(wv, fp8_byte<Q>(sw[nb]) * rat[nb]);
+        bfr[nb] = deq_fp4(wv, fp8_byte<Q>(sw[nb]));
     }
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
@@ -371,10 +371,10 @@ __device__ __forceinline__ void fp4_kstep(const uint8_t *aT, const uint8_t *bT, 
 }
 
 // acc[mb][nb] += A(tile rows, rows of mb with bit mb of rmask clear zeroed) x
-// (FP4 row brow[nb] * rat[nb])
+// FP4 row brow[nb]
 template <int NMB>
-__device__ __forceinline__ void gemm_pipe4_n(const PipeSrc &src, uint8_t *smem, const int brow[2], const float rat[2],
-                                             uint32_t rmask, f32x16 acc[kPMB][2])
+__device__ __forceinline__ void gemm_pipe4_n(const PipeSrc &src, uint8_t *smem, const int brow[2], uint32_t rmask,
+                                             f32x16 acc[kPMB][2])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
@@ -396,21 +396,21 @@ __device__ __forceinline__ void gemm_pipe4_n(const PipeSrc &src, uint8_t *smem, 
         uint32_t sw[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) sw[nb] = *reinterpret_cast<const uint32_t *>(sT + brow[nb] * 4);
-        fp4_kstep<NMB, 0>(aT, bT, boff, sw, rat, rmask, acc);
-        fp4_kstep<NMB, 1>(aT, bT, boff, sw, rat, rmask, acc);
-        fp4_kstep<NMB, 2>(aT, bT, boff, sw, rat, rmask, acc);
-        fp4_kstep<NMB, 3>(aT, bT, boff, sw, rat, rmask, acc);
+        fp4_kstep<NMB, 0>(aT, bT, boff, sw, rmask, acc);
+        fp4_kstep<NMB, 1>(aT, bT, boff, sw, rmask, acc);
+        fp4_kstep<NMB, 2>(aT, bT, boff, sw, rmask, acc);
+        fp4_kstep<NMB, 3>(aT, bT, boff, sw, rmask, acc);
     }
 }
 
-__device__ __forceinline__ void gemm_pipe4(const PipeSrc &src, uint8_t *smem, const int brow[2], const float rat[2],
-                                           uint32_t rmask, f32x16 acc[kPMB][2], int nmb)
+__device__ __forceinline__ void gemm_pipe4(const PipeSrc &src, uint8_t *smem, const int brow[2], uint32_t rmask,
+                                           f32x16 acc[kPMB][2], int nmb)
 {
     switch (nmb) {
-    case 1: gemm_pipe4_n<1>(src, smem, brow, rat, rmask, acc); break;
-    case 2: gemm_pipe4_n<2>(src, smem, brow, rat, rmask, acc); break;
-    case 3: gemm_pipe4_n<3>(src, smem, brow, rat, rmask, acc); break;
-    default: gemm_pipe4_n<4>(src, smem, brow, rat, rmask, acc); break;
+    case 1: gemm_pipe4_n<1>(src, smem, brow, rmask, acc); break;
+    case 2: gemm_pipe4_n<2>(src, smem, brow, rmask, acc); break;
+    case 3: gemm_pipe4_n<3>(src, smem, brow, rmask, acc); break;
+    default: gemm_pipe4_n<4>(src, smem, brow, rmask, acc); break;
     }
 }
 
@@ -436,38 +436,27 @@ __device__ __forceinline__ int delta_rows(const PrefillParams &p, const MTile &m
     return __ballot(rmask != 0u) ? ds : -1;
 }
 
-// epilogue scale and delta pre-scale of one B matrix: the delta is folded into
-// the 2-bit accumulators as delta * (ds2 / s2); with s2 == 0 the 2-bit part is
-// zero, so the accumulators restart and the epilogue scale becomes 1.
-__device__ __forceinline__ void fold_scales(float s2, float ds2, f32x16 acc[kPMB][2], int nb, float &scl, float &rat)
-{
-    if (s2 != 0.f) {
-        scl = s2;
-        rat = ds2 / s2;
-    } else {
-        scl = 1.f;
-        rat = ds2;
-#pragma unroll
-        for (int mb = 0; mb < kPMB; ++mb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-    }
-}
+// FP4 work runs in kernels of its own (FP4 = true) after the 2-bit kernels
+// (FP4 = false), so that the 2-bit kernels keep their register budget:
+//  * an NVFP4 shared expert's tiles run only in the FP4 kernels;
+//  * a tile with gate-flagged rows on a delta-cache expert runs its 2-bit
+//    pass in the 2-bit kernel, which stores the fp32 pre-activations (gate/up)
+//    or adds y (down) as usual; the FP4 kernel then adds the delta pass, with
+//    the rows of unflagged tokens zeroed, and (gate/up) applies SwiGLU.
+struct TileKind {
+    bool sh4;       // NVFP4 shared expert tile
+    int ds;         // delta slot when the tile has gate-flagged rows, else -1
+    uint32_t rmask; // this lane's flagged 32-row blocks (delta tiles)
+};
 
-// Tiles with FP4 work (a gate-flagged row on a delta-cache expert, or the
-// NVFP4 shared expert) run in their own kernels (FP4 = true), which hold the
-// accumulators through both passes at one wavefront per SIMD; the 2-bit-only
-// kernels (FP4 = false) skip those tiles and keep their register budget.
-// Returns whether this tile belongs to the kernel, with the delta slot (or -1)
-// and the row mask of the FP4 pass.
-template <bool FP4>
-__device__ __forceinline__ bool tile_kind(const PrefillParams &p, const MTile &mt, int nmb, int &ds, uint32_t &rmask)
+__device__ __forceinline__ TileKind tile_kind(const PrefillParams &p, const MTile &mt, int nmb)
 {
-    ds = -1;
-    rmask = 0xFu;
-    const bool sh4 = mt.e < 0 && p.shared_fp4;
-    if (!sh4) ds = delta_rows(p, mt, nmb, rmask);
-    return (sh4 || ds >= 0) == FP4;
+    TileKind tk;
+    tk.sh4 = mt.e < 0 && p.shared_fp4;
+    tk.ds = -1;
+    tk.rmask = 0xFu;
+    if (!tk.sh4) tk.ds = delta_rows(p, mt, nmb, tk.rmask);
+    return tk;
 }
 
 // gate/up + SwiGLU.  N-tile nt covers h columns [128 nt, 128 nt + 128); wave w
@@ -481,9 +470,8 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     MTile mt;
     if (!locate_mtile(p, ms, mt)) return;
     const int nmb = (mt.rows + 31) / 32;
-    int ds;
-    uint32_t rmask;
-    if (!tile_kind<FP4>(p, mt, nmb, ds, rmask)) return;
+    const TileKind tk = tile_kind(p, mt, nmb);
+    if (FP4 ? !(tk.sh4 || tk.ds >= 0) : tk.sh4) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
     // A rows fetched by this lane: segment i of wave w holds rows 8(4w+i) .. +7; lane -> row + lane/8
@@ -500,9 +488,6 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     // B: 256 rows = gate rows [128 nt, +128) then up rows [128 nt, +128); wave w fetches storage tile w
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
     if (ws < 0) return;   // missing expert: no work, the combine skips its routings
-    const bool sh4 = mt.e < 0 && p.shared_fp4;
-    const moet_w2 &W = (mt.e >= 0) ? p.w13 : p.sh13;
-    const int m0 = (mt.e >= 0) ? 2 * ws : 0;
     const int jl = 32 * wave + (lane & 31);          // h column within the tile
     const int j = 128 * nt + jl;
     const int brow[2] = {jl, 128 + jl};               // gate row, up row in the stage
@@ -513,35 +498,31 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-    float scl[2] = {1.f, 1.f}, rat[2] = {1.f, 1.f};
-    if (!sh4) {
+    float sg, su;
+    if constexpr (!FP4) {
+        const moet_w2 &W = (mt.e >= 0) ? p.w13 : p.sh13;
+        const int m0 = (mt.e >= 0) ? 2 * ws : 0;
         const int mat = m0 + (wave >> 1);
         const int tile = 2 * nt + (wave & 1);
         src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)mat * I * H / 16) + (size_t)tile * (H / 64) * 1024;
         src.ssrc = W.scales + (size_t)mat * I * H / 32 + (size_t)tile * (H / 128) * 256;
         gemm_pipe(src, smem, brow, acc, nmb);
-        scl[0] = W.scale2[m0];
-        scl[1] = W.scale2[m0 + 1];
-    }
-    if constexpr (FP4) {
-        const moet_fp4 &F = sh4 ? p.shf13 : p.d13;
-        const int fm0 = sh4 ? 0 : 2 * ds;
-        if (sh4) {
-            scl[0] = F.scale2[0];
-            scl[1] = F.scale2[1];
-        } else {
-            fold_scales(W.scale2[m0], F.scale2[fm0], acc, 0, scl[0], rat[0]);
-            fold_scales(W.scale2[m0 + 1], F.scale2[fm0 + 1], acc, 1, scl[1], rat[1]);
-            __syncthreads();   // every wave is done with the ring before it refills
-        }
+        sg = W.scale2[m0];
+        su = W.scale2[m0 + 1];
+    } else {
+        const moet_fp4 &F = tk.sh4 ? p.shf13 : p.d13;
+        const int fm0 = tk.sh4 ? 0 : 2 * tk.ds;
         const int mat = fm0 + (wave >> 1);
         const int tile = 2 * nt + (wave & 1);
         src.bsrc = F.codes + (size_t)mat * I * H / 2 + (size_t)tile * (H / 32) * 1024;
         src.ssrc = F.scales + (size_t)mat * I * H / 16 + (size_t)tile * (H / 128) * 512;
-        gemm_pipe4(src, smem, brow, rat, rmask, acc, nmb);
+        gemm_pipe4(src, smem, brow, tk.rmask, acc, nmb);
+        sg = F.scale2[fm0];
+        su = F.scale2[fm0 + 1];
     }
-    const float sg = scl[0], su = scl[1];
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
+    const bool to_pre = !FP4 && tk.ds >= 0;                     // 2-bit pass of a delta tile
+    const bool from_pre = FP4 && !tk.sh4;                       // delta pass: add to it
 #pragma unroll
     for (int mb = 0; mb < kPMB; ++mb) {
         if (mb >= nmb) break;
@@ -550,6 +531,16 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
             const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             if (r < mt.rows) {
                 float g = acc[mb][0][v] * sg, u = acc[mb][1][v] * su;
+                float *pre = p.pre + (size_t)(rowbase + r) * (2 * I) + j;
+                if (to_pre) {
+                    pre[0] = g;
+                    pre[I] = u;
+                    continue;
+                }
+                if (from_pre) {
+                    g += pre[0];
+                    u += pre[I];
+                }
                 if (p.swiglu_limit > 0.f) {
                     g = fminf(g, p.swiglu_limit);
                     u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
@@ -567,9 +558,9 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
     fc1_prefill_body<false>(p, smem);
 }
 
-__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(1))) void fc1_prefill_fp4_kernel(PrefillParams p)
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc1_prefill_fp4_kernel(PrefillParams p)
 {
-    __shared__ __align__(1024) uint8_t smem[kSmem];
+    __shared__ __align__(1024) uint8_t smem[kPS * kStage4];
     fc1_prefill_body<true>(p, smem);
 }
 
@@ -583,9 +574,8 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     MTile mt;
     if (!locate_mtile(p, ms, mt)) return;
     const int nmb = (mt.rows + 31) / 32;
-    int ds;
-    uint32_t rmask;
-    if (!tile_kind<FP4>(p, mt, nmb, ds, rmask)) return;
+    const TileKind tk = tile_kind(p, mt, nmb);
+    if (FP4 ? !(tk.sh4 || tk.ds >= 0) : tk.sh4) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;
@@ -598,9 +588,6 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     }
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
     if (ws < 0) return;
-    const bool sh4 = mt.e < 0 && p.shared_fp4;
-    const moet_w2 &W = (mt.e >= 0) ? p.w2 : p.sh2;
-    const int m0 = (mt.e >= 0) ? ws : 0;
     const int tile = 4 * nt + wave;
     const int brow[2] = {64 * wave + (lane & 31), 64 * wave + 32 + (lane & 31)};
     int ncol[2];
@@ -613,29 +600,23 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-    float s2 = 1.f;
-    if (!sh4) {
+    float s2;
+    if constexpr (!FP4) {
+        const moet_w2 &W = (mt.e >= 0) ? p.w2 : p.sh2;
+        const int m0 = (mt.e >= 0) ? ws : 0;
         src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
         src.ssrc = W.scales + (size_t)m0 * H * I / 32 + (size_t)tile * (I / 128) * 256;
         gemm_pipe(src, smem, brow, acc, nmb);
         s2 = W.scale2[m0];
-    }
-    if constexpr (FP4) {
-        const moet_fp4 &F = sh4 ? p.shf2 : p.d2;
-        const int fm = sh4 ? 0 : ds;
-        float rat[2] = {1.f, 1.f};
-        if (sh4) {
-            s2 = F.scale2[0];
-        } else {
-            float scl1;
-            fold_scales(W.scale2[m0], F.scale2[fm], acc, 0, s2, rat[0]);
-            fold_scales(W.scale2[m0], F.scale2[fm], acc, 1, scl1, rat[1]);
-            __syncthreads();   // every wave is done with the ring before it refills
-        }
+    } else {
+        const moet_fp4 &F = tk.sh4 ? p.shf2 : p.d2;
+        const int fm = tk.sh4 ? 0 : tk.ds;
         src.bsrc = F.codes + (size_t)fm * H * I / 2 + (size_t)tile * (I / 32) * 1024;
         src.ssrc = F.scales + (size_t)fm * H * I / 16 + (size_t)tile * (I / 128) * 512;
-        gemm_pipe4(src, smem, brow, rat, rmask, acc, nmb);
+        gemm_pipe4(src, smem, brow, tk.rmask, acc, nmb);
+        s2 = F.scale2[fm];
     }
+    const bool add = FP4 && !tk.sh4;   // delta pass: add to the 2-bit y
 #pragma unroll
     for (int mb = 0; mb < kPMB; ++mb) {
         if (mb >= nmb) break;
@@ -645,7 +626,11 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
             if (r < mt.rows) {
                 const int prow = (mt.e >= 0) ? min(max(p.sorted[mt.row0 + r], 0), P - 1) : P + mt.row0 + r;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) p.ypart[(size_t)prow * H + ncol[nb]] = acc[mb][nb][v] * s2;
+                for (int nb = 0; nb < 2; ++nb) {
+                    float *y = p.ypart + (size_t)prow * H + ncol[nb];
+                    const float d = acc[mb][nb][v] * s2;
+                    *y = add ? *y + d : d;
+                }
             }
         }
     }
@@ -657,9 +642,9 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
     fc2_prefill_body<false>(p, smem);
 }
 
-__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(1))) void fc2_prefill_fp4_kernel(PrefillParams p)
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc2_prefill_fp4_kernel(PrefillParams p)
 {
-    __shared__ __align__(1024) uint8_t smem[kSmem];
+    __shared__ __align__(1024) uint8_t smem[kPS * kStage4];
     fc2_prefill_body<true>(p, smem);
 }
 
@@ -715,7 +700,7 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I, int E)
     (void)E;
     const size_t rows = (size_t)T * k + T;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    return al(rows * I * 2) + al(rows * H * 4);
+    return al(rows * I * 2) + al(rows * (size_t)std::max(H, 2 * I) * 4);
 }
 
 int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const int32_t *ids, const float *w,
@@ -762,6 +747,7 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     char *base = static_cast<char *>(ws);
     p.h = reinterpret_cast<uint16_t *>(base);
     p.ypart = reinterpret_cast<float *>(base + al(rows * L->I * 2));
+    p.pre = p.ypart;   // read by the FP4 gate/up kernel before the down kernels write y there
     p.out = out;
     const int P = T * k;
     const int mslots = (P + kPM - 1) / kPM + L->E + (p.has_shared ? (T + kPM - 1) / kPM : 0);

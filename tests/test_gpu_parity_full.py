@@ -5,6 +5,8 @@ bytes (its own requantisation of every expert those tokens touch), routing of
 all tokens is compared bit for bit, the requantised planes of every touched
 expert are compared byte for byte, and the forward is checked for bitwise
 determinism."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -21,13 +23,27 @@ def _u32(t):
     return np_(t).view(np.uint32)
 
 
-@pytest.mark.parametrize("cfg_id,n_tok", [(2, 3), (3, 3), (4, 2), (5, 2)])
-def test_full_size_forward_sampled(cfg_id, n_tok):
+def _variant(cfg_id, variant):
+    """The benchmark's other full-size workloads: the prefill chunk with a gated FP4 delta,
+    the decode layer with an NVFP4 shared expert, one GPU's share of a TP4 layer."""
     cfg = synth.CONFIGS[cfg_id]
-    print(f"[case] full-size config {cfg.name} T={cfg.T} E={cfg.E}", flush=True)
+    if variant == "prefill_delta":
+        cfg = dataclasses.replace(cfg, name="prefill_delta", n_resident=32, n_flagged=2048)
+    elif variant == "tp4_shard":
+        cfg = dataclasses.replace(cfg, name=f"{cfg.name}_tp4_shard", I=cfg.I // 4)
+    return cfg
+
+
+@pytest.mark.parametrize("cfg_id,n_tok,variant", [(2, 3, None), (3, 3, None), (4, 2, None), (5, 2, None),
+                                                  (5, 2, "prefill_delta"), (2, 3, "nvfp4_shared"),
+                                                  (2, 3, "tp4_shard")])
+def test_full_size_forward_sampled(cfg_id, n_tok, variant):
+    cfg = _variant(cfg_id, variant)
+    shared_nvfp4 = variant == "nvfp4_shared"
+    print(f"[case] full-size config {cfg.name} T={cfg.T} E={cfg.E} I={cfg.I} variant={variant}", flush=True)
     src = synth.make_layer(cfg, seed=SEED, device=DEV)
     soe = synth.slot_of_expert(cfg, SEED) if cfg.n_resident else None
-    layer = moet.layer_from_nvfp4(src, soe)
+    layer = moet.layer_from_nvfp4(src, soe, shared_nvfp4=shared_nvfp4)
     x = synth.make_activations(cfg.T, cfg.H, SEED, device=DEV)
     lg = synth.make_logits(cfg, SEED, device=DEV)
     flags = synth.gate_flags(cfg, SEED).to(DEV) if cfg.n_flagged else None
@@ -50,7 +66,7 @@ def test_full_size_forward_sampled(cfg_id, n_tok):
         fl = np_(flags)
         cand = sorted(cand, key=lambda t: (-int(fl[t]), t))
     toks = sorted(set([cand[0], cfg.T - 1] + list(rng.choice(cfg.T, size=n_tok, replace=False))))[:n_tok]
-    ol = OracleLayer(src, soe)
+    ol = OracleLayer(src, soe, shared_nvfp4=shared_nvfp4)
     ref = ol.forward(bf16_bits(x), o_ids, o_w, gate_flags=np_(flags) if flags is not None else None, tokens=toks)
     got = bf16_bits(out)[toks]
     err = rel_l2(got, ref)
@@ -77,6 +93,8 @@ def test_full_size_forward_sampled(cfg_id, n_tok):
             planes, dpl, dslot = layer.shared13, None, None
         else:
             planes, dpl, dslot = layer.shared2, None, None
+        if planes is None:      # NVFP4 shared expert: no 2-bit planes (the oracle decodes NVFP4 itself)
+            continue
         assert (_u32(planes.codes[i]) == om.packed_codes()).all()
         assert (np_(planes.scales[i]) == om.packed_scales()).all()
         if dslot is not None:

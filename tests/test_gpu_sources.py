@@ -151,3 +151,27 @@ def test_forward_on_converted_weights(fmt):
     print(f"rel_l2={err:.3e}", flush=True)
     assert err <= REL_L2_BAR
     assert err <= 3e-4
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "fp8"])
+def test_full_size_conversions_sampled(fmt):
+    """The load-time conversions at the benchmark's size (16 gate/up matrices [2048][7168]),
+    two sampled matrices compared with the oracle byte for byte."""
+    n, N, K = 16, 2048, 7168
+    _print_case(f"full-size {fmt} conversion n={n} N={N} K={K}")
+    if fmt == "nvfp4":
+        src = synth.make_nvfp4_stack(n, N, K, 0, "conv_nvfp4", device=DEV)
+        w = moet.requant(*src)
+        conv = lambda m: OR.requant(np_(src[0][m]), np_(src[1][m]), float(np_(src[2])[m]))
+    elif fmt == "mxfp4":
+        src = synth.make_mxfp4_stack(n, N, K, 0, "conv_mxfp4", device=DEV)
+        w = moet.remap_mxfp4(*src)
+        conv = lambda m: OS.remap_mxfp4(np_(src[0][m]), np_(src[1][m]))
+    else:
+        src = synth.make_fp8_stack(n, N, K, 0, "conv_fp8", device=DEV)
+        w = moet.requant_fp8(*src)
+        conv = lambda m: OS.requant_fp8(np_(src[0][m]), np_(src[1][m]))
+    torch.cuda.synchronize()
+    for m in (3, n - 1):
+        c2, tau, s2 = conv(m)
+        _check_planes(w, m, c2, tau, s2, f"{fmt} full size")

@@ -38,7 +38,7 @@ __device__ __forceinline__ uint32_t fkey(float f)
 // ballots (no cross-lane shuffles); ties at the threshold are filled in
 // increasing expert id; the k winners are then ordered by (key desc, id asc).
 template <int NPL>
-__device__ void topk_token(const float *__restrict__ logits, int t, int E, int k, int fn, int renorm, float rscale,
+__device__ __forceinline__ void topk_token(const float *__restrict__ logits, int t, int E, int k, int fn, int renorm, float rscale,
                            int32_t *__restrict__ ids, float *__restrict__ w, int32_t *lds_ids, uint32_t *scratch)
 {
     const int lane = threadIdx.x & 63;
@@ -90,16 +90,28 @@ __device__ void topk_token(const float *__restrict__ logits, int t, int E, int k
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // LDS writes done before other lanes read them
     __builtin_amdgcn_wave_barrier();
     uint32_t my_key = 0, my_id = 0;
-    int rank = 0;
     if (lane < k) {
         my_key = scratch[2 * lane];
         my_id = scratch[2 * lane + 1];
-        for (int j = 0; j < k; ++j) {
-            const uint32_t kj = scratch[2 * j], ij = scratch[2 * j + 1];
-            rank += (kj > my_key || (kj == my_key && ij < my_id)) ? 1 : 0;
-        }
     }
-    const float my_val = (lane < k) ? row[my_id] : 0.f;
+    // rank among the k winners by (key desc, id asc): the other winners are read
+    // from their lanes (wave-uniform loop, no memory round trips)
+    int rank = 0;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t kj = __builtin_amdgcn_readlane(my_key, j), ij = __builtin_amdgcn_readlane(my_id, j);
+        rank += (kj > my_key || (kj == my_key && ij < my_id)) ? 1 : 0;
+    }
+    // the winner's logit from the lane that loaded it (no second read of the row)
+    float my_val = 0.f;
+    {
+        const int src = (int)(my_id & 63u), slot = (int)(my_id >> 6);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const float vi = __shfl(v[i], src, 64);
+            if (slot == i) my_val = vi;
+        }
+        if (lane >= k) my_val = 0.f;
+    }
     // largest selected logit (rank 0)
     const uint64_t r0 = __ballot(lane < k && rank == 0);
     const float lmax = __shfl(my_val, (int)__builtin_ctzll(r0), 64);
@@ -128,45 +140,32 @@ __device__ void topk_token(const float *__restrict__ logits, int t, int E, int k
     }
 }
 
+// NPL = logits per lane (E <= 64 NPL), chosen on the host so that one top-k
+// body is inlined per kernel
 template <int NPL>
-__device__ void topk_dispatch_token(const float *logits, int t, int E, int k, int fn, int renorm, float rscale, int32_t *ids,
-                                    float *w, int32_t *lds_ids, uint32_t *scratch)
-{
-    topk_token<NPL>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
-}
-
-__device__ void topk_any(const float *logits, int t, int E, int k, int fn, int renorm, float rscale, int32_t *ids, float *w,
-                         int32_t *lds_ids, uint32_t *scratch)
-{
-    if (E <= 64) topk_token<1>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
-    else if (E <= 128) topk_token<2>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
-    else if (E <= 256) topk_token<4>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
-    else if (E <= 512) topk_token<8>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
-    else topk_token<16>(logits, t, E, k, fn, renorm, rscale, ids, w, lds_ids, scratch);
-}
-
 __global__ __launch_bounds__(1024) void route_small_kernel(const float *__restrict__ logits, int T, int E, int k, int fn,
                                                            int renorm, float rscale, int32_t *__restrict__ ids,
                                                            float *__restrict__ w, int32_t *__restrict__ offsets,
                                                            int32_t *__restrict__ sorted)
 {
-    __shared__ int32_t s_ids[kSmallPairs];
+    __shared__ __align__(16) int32_t s_ids[kSmallPairs + 8];
     __shared__ int32_t s_off[kMaxE + 1];
     __shared__ uint32_t s_scr[16][32];
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int wave = tid >> 6, nwaves = nthr >> 6;
-    for (int t = wave; t < T; t += nwaves) topk_any(logits, t, E, k, fn, renorm, rscale, ids, w, s_ids, s_scr[wave]);
+    for (int t = wave; t < T; t += nwaves) topk_token<NPL>(logits, t, E, k, fn, renorm, rscale, ids, w, s_ids, s_scr[wave]);
     __syncthreads();
     const int P = T * k;
     // offsets[e] = number of pairs routed to experts < e (LDS reads in unrolled
     // groups of 8 so their latencies overlap; s_ids is padded with E)
     for (int p = P + tid; p < ((P + 7) & ~7); p += nthr) s_ids[p] = E;
     __syncthreads();
+    const int4 *ids4 = reinterpret_cast<const int4 *>(s_ids);
     for (int e = tid; e <= E; e += nthr) {
         int c = 0;
-        for (int p = 0; p < P; p += 8) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) c += (s_ids[p + u] < e) ? 1 : 0;
+        for (int p = 0; p < P; p += 8) {   // two 16-byte LDS reads per group of 8 ids
+            const int4 a = ids4[p >> 2], b = ids4[(p >> 2) + 1];
+            c += (a.x < e) + (a.y < e) + (a.z < e) + (a.w < e) + (b.x < e) + (b.y < e) + (b.z < e) + (b.w < e);
         }
         s_off[e] = c;
         offsets[e] = c;
@@ -176,21 +175,28 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float *__restri
         const int e = s_ids[p];
         int rank = 0;
         for (int q = 0; q < p; q += 8) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) rank += (q + u < p && s_ids[q + u] == e) ? 1 : 0;
+            const int4 a = ids4[q >> 2], b = ids4[(q >> 2) + 1];
+            rank += (q + 0 < p && a.x == e) + (q + 1 < p && a.y == e) + (q + 2 < p && a.z == e) +
+                    (q + 3 < p && a.w == e) + (q + 4 < p && b.x == e) + (q + 5 < p && b.y == e) +
+                    (q + 6 < p && b.z == e) + (q + 7 < p && b.w == e);
         }
         sorted[s_off[e] + rank] = p;
     }
 }
 
+template <int NPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int T, int E, int k, int fn,
                                                          int renorm, float rscale, int32_t *__restrict__ ids,
                                                          float *__restrict__ w)
 {
     __shared__ uint32_t s_scr[4][32];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t < T) topk_any(logits, t, E, k, fn, renorm, rscale, ids, w, nullptr, s_scr[threadIdx.x >> 6]);
+    if (t < T) topk_token<NPL>(logits, t, E, k, fn, renorm, rscale, ids, w, nullptr, s_scr[threadIdx.x >> 6]);
 }
+
+template <int NPL>
+static int launch_route_n(const float *logits, int T, int E, int k, int fn, int renorm, float rscale, int32_t *ids,
+                          float *w, int32_t *offsets, int32_t *sorted, hipStream_t stream);
 
 // One workgroup per expert e: offset = #pairs with id < e, then its pairs in order.
 __global__ __launch_bounds__(256) void route_permute_kernel(const int32_t *__restrict__ ids, int P, int E,
@@ -228,24 +234,35 @@ __global__ __launch_bounds__(256) void route_permute_kernel(const int32_t *__res
     }
 }
 
-int launch_route(const float *logits, int T, int E, int k, int fn, int renorm, float rscale, int32_t *ids, float *w,
-                 int32_t *offsets, int32_t *sorted, hipStream_t stream)
+template <int NPL>
+static int launch_route_n(const float *logits, int T, int E, int k, int fn, int renorm, float rscale, int32_t *ids,
+                          float *w, int32_t *offsets, int32_t *sorted, hipStream_t stream)
 {
     const int P = T * k;
     if (P <= kSmallPairs) {
-        int threads = ((T + 0) * 64);
+        int threads = T * 64;
         if (threads > 1024) threads = 1024;
         if (threads < 256) threads = 256;
-        hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(threads), 0, stream, logits, T, E, k, fn, renorm, rscale,
-                           ids, w, offsets, sorted);
+        hipLaunchKernelGGL(route_small_kernel<NPL>, dim3(1), dim3(threads), 0, stream, logits, T, E, k, fn, renorm,
+                           rscale, ids, w, offsets, sorted);
         return check_launch("route_small_kernel");
     }
-    hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, fn, renorm, rscale,
-                       ids, w);
+    hipLaunchKernelGGL(route_topk_kernel<NPL>, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, fn, renorm,
+                       rscale, ids, w);
     int rc = check_launch("route_topk_kernel");
     if (rc != MOET_OK) return rc;
     hipLaunchKernelGGL(route_permute_kernel, dim3(E), dim3(256), 0, stream, (const int32_t *)ids, P, E, offsets, sorted);
     return check_launch("route_permute_kernel");
+}
+
+int launch_route(const float *logits, int T, int E, int k, int fn, int renorm, float rscale, int32_t *ids, float *w,
+                 int32_t *offsets, int32_t *sorted, hipStream_t stream)
+{
+    if (E <= 64) return launch_route_n<1>(logits, T, E, k, fn, renorm, rscale, ids, w, offsets, sorted, stream);
+    if (E <= 128) return launch_route_n<2>(logits, T, E, k, fn, renorm, rscale, ids, w, offsets, sorted, stream);
+    if (E <= 256) return launch_route_n<4>(logits, T, E, k, fn, renorm, rscale, ids, w, offsets, sorted, stream);
+    if (E <= 512) return launch_route_n<8>(logits, T, E, k, fn, renorm, rscale, ids, w, offsets, sorted, stream);
+    return launch_route_n<16>(logits, T, E, k, fn, renorm, rscale, ids, w, offsets, sorted, stream);
 }
 
 }  // namespace moet

@@ -650,8 +650,8 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_D
 // out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order;
 // routings to experts missing from the expert cache contribute nothing and are
 // counted once per token (by the first column block).  The token's ids and
-// weights are wave-uniform (scalar loads) and all its y loads are issued
-// before the sum, so the kernel pays about two memory round trips.
+// weights are wave-uniform (scalar loads); its y loads do not depend on them
+// and are issued first, so the kernel pays about one memory round trip.
 constexpr int kCombineMaxK = 16;
 
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p)
@@ -659,6 +659,13 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p)
     const int n = blockIdx.x * 256 + threadIdx.x;
     const int t = blockIdx.y;
     const int P = p.T * p.k;
+    const bool in = n < p.H;
+    // the y rows sit at fixed positions (pair t*k + j, shared P + t): their loads
+    // go out before the ids and weights arrive, so the two round trips overlap
+    float y[kCombineMaxK];
+#pragma unroll
+    for (int j = 0; j < kCombineMaxK; ++j) y[j] = (j < p.k && in) ? p.ypart[(size_t)(t * p.k + j) * p.H + n] : 0.f;
+    const float ysh = (p.has_shared && in) ? p.ypart[(size_t)(P + t) * p.H + n] : 0.f;
     const cu32 *idr = as_const(p.ids + (size_t)t * p.k);
     const cu32 *wr = as_const(p.w + (size_t)t * p.k);
     int e[kCombineMaxK];
@@ -677,12 +684,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p)
         miss += (valid && !live[j]) ? 1 : 0;
     }
     if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0 && miss) atomicAdd(p.miss_count, miss);
-    if (n >= p.H) return;
-    float y[kCombineMaxK];
-#pragma unroll
-    for (int j = 0; j < kCombineMaxK; ++j) y[j] = live[j] ? p.ypart[(size_t)(t * p.k + j) * p.H + n] : 0.f;
-    const float ysh = p.has_shared ? p.ypart[(size_t)(P + t) * p.H + n] : 0.f;
-    float acc = 0.f;
+    if (!in) return;
+    float acc = 0.f;   // rows of missing experts were not written this call: selected out, never used
 #pragma unroll
     for (int j = 0; j < kCombineMaxK; ++j)
         if (live[j]) acc = fmaf(wt[j], y[j], acc);

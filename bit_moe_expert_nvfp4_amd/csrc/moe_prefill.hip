@@ -49,8 +49,9 @@ namespace moet {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPM = 128;    // rows per M-tile
-constexpr int kPMB = 4;     // 32-row MFMA blocks per M-tile
+constexpr int kPM = 160;    // rows per M-tile
+constexpr int kPMB = 5;     // 32-row MFMA blocks per M-tile
+constexpr int kASeg = kPM / 32;   // 8-row A segments each wavefront stages per step
 constexpr int kPK = 64;     // k per pipeline step
 constexpr int kPW = 4;      // wavefronts per workgroup
 
@@ -192,11 +193,11 @@ __device__ __forceinline__ bf16x8 deq_frag(uint32_t w, uint32_t sh, uint32_t mas
 // compiler's wait-count pass, and waited explicitly (6 per stage).
 // ---------------------------------------------------------------------------
 constexpr int kPS = 3;                         // stages
-constexpr int kStageA = kPM * 128;             // 16 KiB: 128 rows x 64 k bf16
+constexpr int kStageA = kPM * 128;             // kPM rows x 64 k bf16
 constexpr int kStageB = 4 * 1024;              // 256 B-rows x 16 B
 constexpr int kStageS = 4 * 256;               // 256 rows x one scale dword
 constexpr int kStage = kStageA + kStageB + kStageS;
-constexpr int kDmaPerStage = 6;
+constexpr int kDmaPerStage = kASeg + 2;
 
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
 {
@@ -222,7 +223,7 @@ __device__ __forceinline__ bf16x8 a_frag(const uint8_t *a, int r, int c)
 }
 
 struct PipeSrc {
-    const uint8_t *arow[4];     // this lane's A source rows, one per A segment it fetches
+    const uint8_t *arow[kASeg]; // this lane's A source rows, one per A segment it fetches
     const uint8_t *bsrc;        // this wave's B storage tile (codes), row = lane
     const uint8_t *ssrc;        // this wave's B storage tile (scales), row = lane
     int K;
@@ -234,8 +235,8 @@ __device__ __forceinline__ void issue_stage(const PipeSrc &src, uint8_t *smem, i
     const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage);
     const int c = (lane & 7) ^ ((lane >> 3) & 7);   // logical 16-B column for this lane's LDS slot
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((4 * wave + i) * 1024));
+    for (int i = 0; i < kASeg; ++i)
+        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((kASeg * wave + i) * 1024));
     dma16(src.bsrc + ((size_t)s * 64 + lane) * 16, base + kStageA + wave * 1024);
     dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 4, base + kStageA + kStageB + wave * 256);
 }
@@ -297,7 +298,8 @@ __device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, con
     case 1: gemm_pipe_n<1>(src, smem, brow, acc); break;
     case 2: gemm_pipe_n<2>(src, smem, brow, acc); break;
     case 3: gemm_pipe_n<3>(src, smem, brow, acc); break;
-    default: gemm_pipe_n<4>(src, smem, brow, acc); break;
+    case 4: gemm_pipe_n<4>(src, smem, brow, acc); break;
+    default: gemm_pipe_n<5>(src, smem, brow, acc); break;
     }
 }
 
@@ -308,15 +310,15 @@ __device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, con
 // ---------------------------------------------------------------------------
 constexpr int kStageB4 = 8 * 1024;
 constexpr int kStage4 = kStageA + kStageB4 + kStageS;
-constexpr int kDmaPerStage4 = 7;
+constexpr int kDmaPerStage4 = kASeg + 3;
 
 __device__ __forceinline__ void issue_stage4(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
 {
     const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage4);
     const int c = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((4 * wave + i) * 1024));
+    for (int i = 0; i < kASeg; ++i)
+        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((kASeg * wave + i) * 1024));
     dma16(src.bsrc + ((size_t)(2 * s) * 64 + lane) * 16, base + kStageA + wave * 2048);
     dma16(src.bsrc + ((size_t)(2 * s + 1) * 64 + lane) * 16, base + kStageA + wave * 2048 + 1024);
     dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 8 + (s & 1) * 4, base + kStageA + kStageB4 + wave * 256);
@@ -410,7 +412,8 @@ __device__ __forceinline__ void gemm_pipe4(const PipeSrc &src, uint8_t *smem, co
     case 1: gemm_pipe4_n<1>(src, smem, brow, rmask, acc); break;
     case 2: gemm_pipe4_n<2>(src, smem, brow, rmask, acc); break;
     case 3: gemm_pipe4_n<3>(src, smem, brow, rmask, acc); break;
-    default: gemm_pipe4_n<4>(src, smem, brow, rmask, acc); break;
+    case 4: gemm_pipe4_n<4>(src, smem, brow, rmask, acc); break;
+    default: gemm_pipe4_n<5>(src, smem, brow, rmask, acc); break;
     }
 }
 
@@ -454,7 +457,7 @@ __device__ __forceinline__ TileKind tile_kind(const PrefillParams &p, const MTil
     TileKind tk;
     tk.sh4 = mt.e < 0 && p.shared_fp4;
     tk.ds = -1;
-    tk.rmask = 0xFu;
+    tk.rmask = (1u << kPMB) - 1u;
     if (!tk.sh4) tk.ds = delta_rows(p, mt, nmb, tk.rmask);
     return tk;
 }
@@ -478,8 +481,8 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     PipeSrc src;
     src.K = H;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = min(8 * (4 * wave + i) + (lane >> 3), mt.rows - 1);
+    for (int i = 0; i < kASeg; ++i) {
+        const int r = min(8 * (kASeg * wave + i) + (lane >> 3), mt.rows - 1);
         int tok;
         if (mt.e >= 0) tok = min(max(p.sorted[mt.row0 + r], 0), P - 1) / p.k;
         else tok = mt.row0 + r;
@@ -582,8 +585,8 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     PipeSrc src;
     src.K = I;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = min(8 * (4 * wave + i) + (lane >> 3), mt.rows - 1);
+    for (int i = 0; i < kASeg; ++i) {
+        const int r = min(8 * (kASeg * wave + i) + (lane >> 3), mt.rows - 1);
         src.arow[i] = reinterpret_cast<const uint8_t *>(p.h + (size_t)(rowbase + r) * I);
     }
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;

@@ -10,7 +10,8 @@
 // scales carry over: with Emax the largest exponent over blocks that hold a
 // non-zero code, the tensor scale is 2^(Emax - 135) and a block's e4m3 scale
 // is 2^(E - Emax + 8), exact down to e4m3's smallest subnormal 2^-9; blocks
-// below that, and blocks of zeros, get scale 0.
+// below that, and blocks of zeros, get scale 0.  Emax comes from an integer
+// atomic max over 64 workgroups per matrix.
 //
 // FP8 block-quant requant.  e4m3fn weights with one fp32 scale per 128 x 128
 // block.  The tensor scale is the power of two S = 2^p, p >= -149 smallest
@@ -33,14 +34,6 @@ namespace {
 __device__ __forceinline__ float pow2f(int e)
 {
     return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(1u << (e + 149));
-}
-
-// e such that f == 2^e, for a positive power of two f
-__device__ __forceinline__ int log2_pow2f(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    const int be = (int)((u >> 23) & 255u);
-    return be ? be - 127 : (31 - __clz(u)) - 149;
 }
 
 template <int NT>
@@ -82,28 +75,50 @@ constexpr int kScanThreads = 512;
 // MXFP4
 // ---------------------------------------------------------------------------
 
-// one workgroup per matrix: tensor scale from the largest live block exponent
-__global__ __launch_bounds__(kScanThreads) void mx_scale_kernel(const uint8_t *__restrict__ codes,
-                                                                const uint8_t *__restrict__ escales, int N, int K,
-                                                                float *__restrict__ ws2)
+// Tensor scale from the largest live block exponent, in three steps that keep
+// the int in the scale2 output slot: -1, then an integer atomic max over
+// workgroup maxima (kMxSlices workgroups per matrix), then (after the remap has
+// read it) the float 2^(Emax - 135).
+constexpr int kMxSlices = 64;
+
+__global__ void mx_emax_init_kernel(int32_t *emax, int64_t n_mat)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n_mat) emax[i] = -1;
+}
+
+__global__ __launch_bounds__(kScanThreads) void mx_emax_kernel(const uint8_t *__restrict__ codes,
+                                                               const uint8_t *__restrict__ escales, int N, int K,
+                                                               int32_t *__restrict__ emax_out)
 {
     const size_t mat = blockIdx.x;
     const size_t nblk = (size_t)N * (K / 32);
+    const size_t per = (nblk + kMxSlices - 1) / kMxSlices;
+    const size_t b0 = per * blockIdx.y, b1 = b0 + per < nblk ? b0 + per : nblk;
     const uint4 *c = reinterpret_cast<const uint4 *>(codes + mat * nblk * 16);
     const uint8_t *e = escales + mat * nblk;
     int emax = -1;
-    for (size_t i = threadIdx.x; i < nblk; i += kScanThreads) {
+    for (size_t i = b0 + threadIdx.x; i < b1; i += kScanThreads) {
         const uint4 w = c[i];
         if (((w.x | w.y | w.z | w.w) & 0x77777777u) != 0u) emax = max(emax, (int)e[i]);
     }
     emax = block_max_i32<kScanThreads>(emax);
-    if (threadIdx.x == 0) ws2[mat] = emax < 0 ? 1.0f : pow2f(emax - 135);
+    if (threadIdx.x == 0 && emax >= 0) atomicMax(emax_out + mat, emax);
+}
+
+__global__ void mx_scale_final_kernel(float *ws2, int64_t n_mat)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n_mat) {
+        const int emax = __float_as_int(ws2[i]);
+        ws2[i] = emax < 0 ? 1.0f : pow2f(emax - 135);
+    }
 }
 
 // one thread per 32-weight block
 __global__ __launch_bounds__(256) void mx_remap_kernel(const uint8_t *__restrict__ codes,
                                                        const uint8_t *__restrict__ escales, int64_t n_mat, int N, int K,
-                                                       const float *__restrict__ ws2, int balance,
+                                                       const int32_t *__restrict__ emax_in, int balance,
                                                        uint32_t *__restrict__ wcodes, uint8_t *__restrict__ wscales)
 {
     const int nb = K / 32;
@@ -119,7 +134,7 @@ __global__ __launch_bounds__(256) void mx_remap_kernel(const uint8_t *__restrict
     const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
     int tau = 0;
     if (((cw.x | cw.y | cw.z | cw.w) & 0x77777777u) != 0u) {
-        const int emax = log2_pow2f(ws2[mat]) + 135;
+        const int emax = emax_in[mat];   // >= 0: this block is live
         const int d = E - (emax - 8);                     // block scale 2^d, d <= 8
         if (d >= -6) tau = (d + 7) << 3;                  // normal: exponent field d + 7
         else if (d >= -9) tau = 1 << (d + 9);             // subnormal: mantissa 2^(d + 9)
@@ -144,18 +159,33 @@ __global__ __launch_bounds__(256) void mx_remap_kernel(const uint8_t *__restrict
 // FP8 block-quant
 // ---------------------------------------------------------------------------
 
-// one workgroup per matrix: amax -> power-of-two tensor scale
-__global__ __launch_bounds__(kScanThreads) void fp8_scale_kernel(const uint8_t *__restrict__ w,
-                                                                 const float *__restrict__ bs, int N, int K,
-                                                                 float *__restrict__ ws2)
+// Tensor scale 2^p.  p(amax) (smallest p >= -149 with 1792 * 2^p >= amax) is
+// monotone in amax, so the largest p over workgroup maxima is p of the tensor
+// maximum: each of kMxSlices workgroups per matrix finds its own p exactly in
+// float64 and takes an integer atomic max into the scale2 slot (kNoP first:
+// no positive weight seen), and the requant reads that int before the last
+// step turns it into the float scale.
+constexpr int kNoP = -1000;
+
+__global__ void fp8_p_init_kernel(int32_t *pmax, int64_t n_mat)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n_mat) pmax[i] = kNoP;
+}
+
+__global__ __launch_bounds__(kScanThreads) void fp8_p_kernel(const uint8_t *__restrict__ w,
+                                                             const float *__restrict__ bs, int N, int K,
+                                                             int32_t *__restrict__ pmax)
 {
     const size_t mat = blockIdx.x;
     const int KB = K / 128, NB = (N + 127) / 128;
     const size_t nchunk = (size_t)N * (K / 16);
+    const size_t per = (nchunk + kMxSlices - 1) / kMxSlices;
+    const size_t c0 = per * blockIdx.y, c1 = c0 + per < nchunk ? c0 + per : nchunk;
     const uint4 *c = reinterpret_cast<const uint4 *>(w + mat * (size_t)N * K);
     const float *s = bs + mat * (size_t)NB * KB;
     double amax = 0.0;
-    for (size_t i = threadIdx.x; i < nchunk; i += kScanThreads) {
+    for (size_t i = c0 + threadIdx.x; i < c1; i += kScanThreads) {
         const uint4 q = c[i];
         const uint32_t words[4] = {q.x, q.y, q.z, q.w};
         int mx = 0;
@@ -165,20 +195,24 @@ __global__ __launch_bounds__(kScanThreads) void fp8_scale_kernel(const uint8_t *
         amax = fmax(amax, e4m3_f64(mx) * (double)s[(size_t)(n / 128) * KB + k / 128]);
     }
     amax = block_max_f64<kScanThreads>(amax);
-    if (threadIdx.x == 0) {
-        float S = 1.0f;
-        if (amax > 0.0) {
-            int p = -149;
-            while (1792.0 * ldexp(1.0, p) < amax) ++p;
-            S = pow2f(p);
-        }
-        ws2[mat] = S;
+    if (threadIdx.x == 0 && amax > 0.0) {
+        int p = -149;
+        while (1792.0 * ldexp(1.0, p) < amax) ++p;
+        atomicMax(pmax + mat, p);
     }
+}
+
+__device__ __forceinline__ float scale_of_p(int p) { return p == kNoP ? 1.0f : pow2f(p); }
+
+__global__ void fp8_scale_final_kernel(float *ws2, int64_t n_mat)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n_mat) ws2[i] = scale_of_p(__float_as_int(ws2[i]));
 }
 
 // one thread per 32-weight block: the float64 scan over all 127 block scales
 __global__ __launch_bounds__(256) void fp8_requant_kernel(const uint8_t *__restrict__ w, const float *__restrict__ bs,
-                                                          int64_t n_mat, int N, int K, const float *__restrict__ ws2,
+                                                          int64_t n_mat, int N, int K, const int32_t *__restrict__ pmax,
                                                           int balance, uint32_t *__restrict__ wcodes,
                                                           uint8_t *__restrict__ wscales)
 {
@@ -195,22 +229,25 @@ __global__ __launch_bounds__(256) void fp8_requant_kernel(const uint8_t *__restr
     const uint4 q0 = src[0], q1 = src[1];
     const uint32_t words[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     const double sb = (double)bs[mat * (size_t)NB * KB + (size_t)(n / 128) * KB + (32 * b) / 128];
-    const double S = (double)ws2[mat];
+    const double S = (double)scale_of_p(pmax[mat]);
     double y[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) y[i] = e4m3_f64((int)((words[i >> 2] >> (8 * (i & 3))) & 0x7Fu)) * sb;
 
+    // The per-element term is min(fl((y-a)^2), fl((y-4a)^2)).  Rounding is
+    // monotone, so that minimum is the rounded square of whichever difference is
+    // smaller exactly, and y > 2.5a (exact: y and a have few significant bits)
+    // says which: one difference and one square instead of two, same bits.
     int best_t = 0;
     double best_err = -1.0;
     for (int t = 0; t < 127; ++t) {
         const double a = e4m3_f64(t) * S;
-        const double a4 = 4.0 * a;
+        const double a4 = 4.0 * a, a25 = 2.5 * a;
         double err = 0.0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            const double d1 = y[i] - a, d4 = y[i] - a4;
-            const double s1 = d1 * d1, s4 = d4 * d4;
-            err = err + (s1 < s4 ? s1 : s4);
+            const double d = y[i] - (y[i] > a25 ? a4 : a);
+            err = err + d * d;
         }
         if (best_err < 0.0 || err < best_err) {
             best_err = err;
@@ -272,26 +309,42 @@ int launch_pack_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *
 int launch_remap_mxfp4(const uint8_t *codes, const uint8_t *escales, int64_t n_mat, int N, int K, int balance,
                        uint32_t *wc, uint8_t *wsc, float *ws2, hipStream_t stream)
 {
-    hipLaunchKernelGGL(mx_scale_kernel, dim3((unsigned)n_mat), dim3(kScanThreads), 0, stream, codes, escales, N, K,
-                       ws2);
-    int rc = check_launch("mx_scale_kernel");
+    int32_t *emax = reinterpret_cast<int32_t *>(ws2);   // the int lives in the output slot until the last step
+    const unsigned mb = (unsigned)((n_mat + 255) / 256);
+    hipLaunchKernelGGL(mx_emax_init_kernel, dim3(mb), dim3(256), 0, stream, emax, n_mat);
+    int rc = check_launch("mx_emax_init_kernel");
+    if (rc != MOET_OK) return rc;
+    hipLaunchKernelGGL(mx_emax_kernel, dim3((unsigned)n_mat, kMxSlices), dim3(kScanThreads), 0, stream, codes, escales,
+                       N, K, emax);
+    rc = check_launch("mx_emax_kernel");
     if (rc != MOET_OK) return rc;
     const size_t total = (size_t)n_mat * N * (K / 32);
     hipLaunchKernelGGL(mx_remap_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, codes, escales,
-                       n_mat, N, K, (const float *)ws2, balance, wc, wsc);
-    return check_launch("mx_remap_kernel");
+                       n_mat, N, K, (const int32_t *)emax, balance, wc, wsc);
+    rc = check_launch("mx_remap_kernel");
+    if (rc != MOET_OK) return rc;
+    hipLaunchKernelGGL(mx_scale_final_kernel, dim3(mb), dim3(256), 0, stream, ws2, n_mat);
+    return check_launch("mx_scale_final_kernel");
 }
 
 int launch_requant_fp8(const uint8_t *w, const float *bs, int64_t n_mat, int N, int K, int balance, uint32_t *wc,
                        uint8_t *wsc, float *ws2, hipStream_t stream)
 {
-    hipLaunchKernelGGL(fp8_scale_kernel, dim3((unsigned)n_mat), dim3(kScanThreads), 0, stream, w, bs, N, K, ws2);
-    int rc = check_launch("fp8_scale_kernel");
+    int32_t *pmax = reinterpret_cast<int32_t *>(ws2);   // the int lives in the output slot until the last step
+    const unsigned mb = (unsigned)((n_mat + 255) / 256);
+    hipLaunchKernelGGL(fp8_p_init_kernel, dim3(mb), dim3(256), 0, stream, pmax, n_mat);
+    int rc = check_launch("fp8_p_init_kernel");
+    if (rc != MOET_OK) return rc;
+    hipLaunchKernelGGL(fp8_p_kernel, dim3((unsigned)n_mat, kMxSlices), dim3(kScanThreads), 0, stream, w, bs, N, K, pmax);
+    rc = check_launch("fp8_p_kernel");
     if (rc != MOET_OK) return rc;
     const size_t total = (size_t)n_mat * N * (K / 32);
     hipLaunchKernelGGL(fp8_requant_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, w, bs, n_mat,
-                       N, K, (const float *)ws2, balance, wc, wsc);
-    return check_launch("fp8_requant_kernel");
+                       N, K, (const int32_t *)pmax, balance, wc, wsc);
+    rc = check_launch("fp8_requant_kernel");
+    if (rc != MOET_OK) return rc;
+    hipLaunchKernelGGL(fp8_scale_final_kernel, dim3(mb), dim3(256), 0, stream, ws2, n_mat);
+    return check_launch("fp8_scale_final_kernel");
 }
 
 }  // namespace moet

@@ -179,8 +179,9 @@ int moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const f
  * blocks holding a non-zero code, w2_scale2 = 2^(Emax - 135) and a block's
  * e4m3 scale is 2^(E - Emax + 8); blocks with E < Emax - 17 (below e4m3's
  * range) and blocks with no non-zero code get scale 0.  A matrix with no
- * non-zero code gets w2_scale2 = 1 and scale 0 everywhere.  No search: two
- * kernels (one reduction per matrix, then one thread per 32-weight block).
+ * non-zero code gets w2_scale2 = 1 and scale 0 everywhere.  No search: a
+ * reduction (64 workgroups per matrix, integer atomic max into the w2_scale2
+ * slot), then one thread per 32-weight block, then the float scale.
  *
  * Inputs: mx_codes uint8 [n_mat][N][K/2], mx_scales uint8 [n_mat][N][K/32]
  *   (e8m0; 0xFF (NaN) gives undefined results).

@@ -65,6 +65,15 @@ def test_source_conversions_reject_bad_args(L):
         assert b"aligned" in L.moet_last_error()
 
 
+def test_pack_nvfp4_rejects_bad_args(L):
+    buf = ctypes.c_void_p(16)      # never dereferenced: checks fail first
+    args = [buf, buf, buf, 1, 64, 128, buf, buf, buf, None]
+    for i, bad in [(4, 63), (5, 96), (3, 0), (0, None), (7, ctypes.c_void_p(8))]:
+        a = list(args)
+        a[i] = bad
+        assert L.moet_pack_nvfp4(*a) == 1, (i, bad)
+
+
 def test_route_rejects_bad_args(L):
     b = ctypes.c_void_p(16)
     f = ctypes.c_float(1.0)
@@ -105,6 +114,13 @@ def test_forward_rejects_bad_args_and_short_workspace(L):
     lay2 = _layer()
     lay2.has_shared = 1
     assert L.moet_moe_forward(ctypes.byref(lay2), b, 4, 2, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
+    # NVFP4 shared expert with missing FP4 planes (the 2-bit shared planes are then not needed)
+    lay4 = _layer()
+    lay4.has_shared = 1
+    lay4.shared_fp4 = 1
+    lay4.shared13_fp4 = moet.FP4(16, 16, 16)
+    assert L.moet_moe_forward(ctypes.byref(lay4), b, 4, 2, b, b, b, b, None, b, None, b, 1 << 30, None) == 1
+    assert b"NVFP4 shared" in L.moet_last_error()
     # misaligned miss counter; expert cache with a bad map or slot count
     assert L.moet_moe_forward(ctypes.byref(lay), b, 4, 2, b, b, b, b, None, b, ctypes.c_void_p(258), b, 1 << 30,
                               None) == 1

@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--inputs", type=int, default=8, help="input sets in the rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps (1 GiB written between steps)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk (T=4096) measurement")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the delta-cache and batched decode legs")
@@ -487,16 +488,39 @@ def main():
         a.record()
         b.record()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K - 1)]   # step boundaries inside the region
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(K):
         moet.set_timing_events(*ev[i])
         step(args.warmup + i)
+        if i < K - 1:
+            marks[i].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     moet.set_timing_events(None, None)
+    bounds = [t_start] + marks + [t_end]
+    step_us = np.array([bounds[i].elapsed_time(bounds[i + 1]) * 1e3 for i in range(K)])
+
+    # cold steps: 1 GiB written between steps evicts the caches; only the step is timed
+    cold = None
+    if not args.no_cold:
+        scratch = torch.empty((1 << 28,), dtype=torch.float32, device=dev)
+        nc = min(K, 50)
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nc)]
+        for i in range(nc):
+            scratch.fill_(float(i))
+            ce[i][0].record()
+            step(args.warmup + i)
+            ce[i][1].record()
+        torch.cuda.synchronize()
+        cus = np.array([a.elapsed_time(b) * 1e3 for a, b in ce])
+        cold = {"steps": nc, "median_us": round(float(np.median(cus)), 2), "p10_us": round(float(np.percentile(cus, 10)), 2),
+                "p90_us": round(float(np.percentile(cus, 90)), 2)}
+        del scratch
+        torch.cuda.empty_cache()
 
     # the same steps replayed from HIP graphs (one graph per layer/input combination)
     graph = None
@@ -568,6 +592,10 @@ def main():
         "mean_experts_per_step": round(float(n_experts), 2),
         "algorithmic_bytes_per_step": round(tot_bytes / K),
         "requant_ms_per_layer": round(float(np.median(rq_ms)), 2),
+        "step_us_median": round(float(np.median(step_us)), 2),
+        "step_us_p10": round(float(np.percentile(step_us, 10)), 2),
+        "step_us_p90": round(float(np.percentile(step_us, 90)), 2),
+        "cold": cold,
         "wall_s_timed_region": round(wall, 4),
         "graph_replay": graph,
         "roofline": {

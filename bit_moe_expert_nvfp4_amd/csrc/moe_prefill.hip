@@ -658,18 +658,23 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
 // and are issued first, so the kernel pays about one memory round trip.
 constexpr int kCombineMaxK = 16;
 
+// Four output features per thread (16-byte y loads, 8-byte stores): the
+// kernel streams (k + 1) fp32 rows of H per token.
 __global__ __launch_bounds__(256) void combine_prefill_kernel(PrefillParams p)
 {
-    const int n = blockIdx.x * 256 + threadIdx.x;
+    const int n = 4 * (blockIdx.x * 256 + threadIdx.x);
     const int t = blockIdx.y;
     const int P = p.T * p.k;
-    const bool in = n < p.H;
+    const bool in = n < p.H;   // H % 4 == 0
     // the y rows sit at fixed positions (pair t*k + j, shared P + t): their loads
     // go out before the ids and weights arrive, so the two round trips overlap
-    float y[kCombineMaxK];
+    float4 y[kCombineMaxK];
 #pragma unroll
-    for (int j = 0; j < kCombineMaxK; ++j) y[j] = (j < p.k && in) ? p.ypart[(size_t)(t * p.k + j) * p.H + n] : 0.f;
-    const float ysh = (p.has_shared && in) ? p.ypart[(size_t)(P + t) * p.H + n] : 0.f;
+    for (int j = 0; j < kCombineMaxK; ++j)
+        y[j] = (j < p.k && in) ? *reinterpret_cast<const float4 *>(p.ypart + (size_t)(t * p.k + j) * p.H + n)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 ysh = (p.has_shared && in) ? *reinterpret_cast<const float4 *>(p.ypart + (size_t)(P + t) * p.H + n)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
     const cu32 *idr = as_const(p.ids + (size_t)t * p.k);
     const cu32 *wr = as_const(p.w + (size_t)t * p.k);
     int e[kCombineMaxK];
@@ -689,12 +694,24 @@ __global__ __launch_bounds__(256) void combine_prefill_kernel(PrefillParams p)
     }
     if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0 && miss) atomicAdd(p.miss_count, miss);
     if (!in) return;
-    float acc = 0.f;   // rows of missing experts were not written this call: selected out, never used
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;   // rows of missing experts: selected out, never used
 #pragma unroll
     for (int j = 0; j < kCombineMaxK; ++j)
-        if (live[j]) acc = fmaf(wt[j], y[j], acc);
-    if (p.has_shared) acc += ysh;
-    p.out[(size_t)t * p.H + n] = (uint16_t)f32_to_bf16_rne(acc);
+        if (live[j]) {
+            a0 = fmaf(wt[j], y[j].x, a0);
+            a1 = fmaf(wt[j], y[j].y, a1);
+            a2 = fmaf(wt[j], y[j].z, a2);
+            a3 = fmaf(wt[j], y[j].w, a3);
+        }
+    if (p.has_shared) {
+        a0 += ysh.x;
+        a1 += ysh.y;
+        a2 += ysh.z;
+        a3 += ysh.w;
+    }
+    const uint32_t lo = f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+    const uint32_t hi = f32_to_bf16_rne(a2) | (f32_to_bf16_rne(a3) << 16);
+    *reinterpret_cast<uint2 *>(p.out + (size_t)t * p.H + n) = make_uint2(lo, hi);
 }
 
 size_t decode_workspace_bytes(int T, int k, int H, int I);
@@ -781,7 +798,7 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
         rc = check_launch("fc2_prefill_fp4_kernel");
         if (rc != MOET_OK) return rc;
     }
-    hipLaunchKernelGGL(combine_prefill_kernel, dim3((L->H + 255) / 256, T), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(combine_prefill_kernel, dim3((L->H + 1023) / 1024, T), dim3(256), 0, stream, p);
     return check_launch("combine_prefill_kernel");
 }
 

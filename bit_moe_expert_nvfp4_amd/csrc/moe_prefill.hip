@@ -7,13 +7,15 @@
 // (one wide load per operand fragment), not by DRAM.
 //
 // MI355X design (bf16 v_mfma_f32_32x32x16, fp32 accumulation):
-//  * Work item = (M-tile of up to 128 consecutive sorted pairs of one expert,
-//    N-tile).  M-tiles are numbered per expert from expert_offsets, so the
+//  * Work item = (M-tile of up to 160 consecutive sorted pairs of one expert,
+//    N-tile).  160 rows (5 MFMA blocks) hold a whole expert at the usual
+//    prefill load (T*k/E ~ 128 +- 11 rows), so the weights are staged and
+//    dequantised once per expert instead of twice for about half of them.  M-tiles are numbered per expert from expert_offsets, so the
 //    routing never round-trips to the host.  Linear workgroup ids are mapped
 //    so that every N-tile of one M-tile lands on the same XCD (workgroups are
 //    dispatched round-robin over the 8 XCDs): the gathered activation rows
 //    are then read from that XCD's L2 by all of them.
-//  * A (activations): 128 rows x 64 k bf16 per step, gathered by token
+//  * A (activations): 160 rows x 64 k bf16 per step, gathered by token
 //    (gate/up) or read from h in sorted order (down), staged in LDS with an
 //    XOR swizzle of the 16-byte columns so each MFMA A fragment is one
 //    conflict-free ds_read_b128.  A, B codes and B scales of each 64-k step
@@ -187,10 +189,10 @@ __device__ __forceinline__ bf16x8 deq_frag(uint32_t w, uint32_t sh, uint32_t mas
 
 // ---------------------------------------------------------------------------
 // Pipeline: kPS-stage LDS ring filled by LDS-DMA (global_load_lds) so no
-// registers are held for prefetch.  Per stage and wavefront: 4 A segments
+// registers are held for prefetch.  Per stage and wavefront: kASeg A segments
 // (1 KiB each), 1 B chunk (1 KiB = 64 rows x 16 B), 1 scale dword per row of
 // the B chunk (256 B).  The DMA is issued from inline asm, invisible to the
-// compiler's wait-count pass, and waited explicitly (6 per stage).
+// compiler's wait-count pass, and waited explicitly (kASeg + 2 per stage).
 // ---------------------------------------------------------------------------
 constexpr int kPS = 3;                         // stages
 constexpr int kStageA = kPM * 128;             // kPM rows x 64 k bf16
@@ -304,7 +306,7 @@ __device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, con
 }
 
 // ---------------------------------------------------------------------------
-// FP4 operand pipeline.  Per stage and wavefront: the same 4 A segments, two
+// FP4 operand pipeline.  Per stage and wavefront: the same kASeg A segments, two
 // B chunks (32-k FP4 chunks 2s and 2s+1 of the wave's 64 storage rows, 1 KiB
 // each) and one scale dword per row (the four block-16 scales of the step).
 // ---------------------------------------------------------------------------

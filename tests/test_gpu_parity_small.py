@@ -343,6 +343,42 @@ def test_expert_cache_miss_and_replay(case):
     assert int(miss.item()) == cfg.T * cfg.k
 
 
+@pytest.mark.parametrize("case", [
+    dict(T=5, E=16, k=4, shared=True, n_resident=6, n_flagged=3, score=synth.SIGMOID),               # GEMV path
+    dict(T=300, E=16, k=8, H=512, I=256, shared=True, n_resident=6, n_flagged=120, score=synth.SIGMOID),  # MFMA
+])
+def test_expert_cache_delta_and_nvfp4_shared_together(case):
+    """Every optional part at once: an expert cache holding half the experts, the FP4 delta on
+    gate-flagged tokens and the shared expert in NVFP4.  Missing experts drop their delta too."""
+    cfg = _small_cfg(**case)
+    _print_case(f"expert cache + delta + NVFP4 shared {case}")
+    seed = zlib.crc32(str(sorted(case.items())).encode()) & 0xFFFF
+    src = synth.make_layer(cfg, seed=seed)
+    soe = synth.slot_of_expert(cfg, seed)
+    layer = moet.layer_from_nvfp4(src, soe, shared_nvfp4=True)
+    x = synth.make_activations(cfg.T, cfg.H, seed)
+    lg = synth.make_logits(cfg, seed)
+    flags = synth.gate_flags(cfg, seed)
+    ids, w, offs, pairs = moet.route(lg.to(DEV), cfg.k, cfg.score, cfg.renormalize)
+    o_ids, o_w, _, _ = oracle_route(lg, cfg.k, cfg.score, cfg.renormalize)
+    rng = np.random.default_rng(seed)
+    resident = rng.random(cfg.E) < 0.5
+    resident[o_ids[0, 0]] = True
+    resident[o_ids[0, -1]] = False
+    base_soe = np.full(cfg.E, -1, dtype=np.int64)
+    base_soe[np.nonzero(resident)[0]] = rng.permutation(int(resident.sum()))
+    cached = moet.expert_cache(layer, base_soe)
+    miss = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    out = moet.moe_forward(cached, x.to(DEV), ids, w, offs, pairs, flags.to(DEV), miss_count=miss)
+    torch.cuda.synchronize()
+    ol = OracleLayer(src, soe, shared_nvfp4=True)
+    ref = ol.forward(bf16_bits(x), o_ids, o_w, gate_flags=np_(flags), resident=resident)
+    err = rel_l2(bf16_bits(out), ref)
+    print(f"rel_l2={err:.3e} misses={int(miss.item())}", flush=True)
+    assert err <= REL_L2_BAR and err <= 3e-4 * max(1.0, cfg.H / 512)
+    assert int(miss.item()) == OFF.miss_count(o_ids, resident) > 0
+
+
 @pytest.mark.parametrize("T,V", [(64, 151552), (5, 1001), (1, 4)])
 def test_confidence_gate(T, V):
     """Flags and confidence against the oracle (largest next-token probability below tau = 0.60, decided

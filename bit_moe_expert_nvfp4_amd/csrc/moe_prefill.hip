@@ -71,7 +71,8 @@ struct PrefillParams {
     float *ypart;       // [P + T][H] fp32, rows by pair id (shared expert: P + t)
     float *pre;         // [P + T][2I] fp32 gate/up pre-activations of delta tiles (aliases ypart)
     uint16_t *out;
-    int n_mslots;       // upper bound on M-tiles (grid)
+    int n_mslots;       // upper bound on 160-row M-tiles (grid of the 2-bit kernels)
+    int n_mslots4;      // upper bound on 128-row M-tiles (grid of the FP4 kernels)
     int n_ntiles;
     const int32_t *base_slot;   // expert -> cache slot of w13/w2 (null: expert e at e)
     int n_base_slots;
@@ -95,14 +96,16 @@ __device__ __forceinline__ int weight_slot(const PrefillParams &p, int e)
 struct MTile {
     int e;        // expert, or -1 for the shared expert
     int row0;     // first row in sorted order (shared: first token)
-    int rows;     // valid rows (<= kPM)
+    int rows;     // valid rows (<= the tile size)
 };
 
-// M-tile number ms -> (expert, rows).  Tiles are enumerated expert by expert
-// (ceil(count / kPM) each), then the shared expert's tiles.  One wavefront
-// computes it: per-lane tile counts, inclusive scan, ballot search.
+// M-tile number ms -> (expert, rows).  Tiles of PM rows are enumerated expert
+// by expert (ceil(count / PM) each), then the shared expert's tiles.  One
+// wavefront computes it: per-lane tile counts, inclusive scan, ballot search.
+template <int PM>
 __device__ bool locate_mtile(const PrefillParams &p, int ms, MTile &mt)
 {
+    constexpr int kPM = PM;
     const int lane = threadIdx.x & 63;
     int base = 0;   // tiles before the current 64-expert chunk
     for (int c = 0; c < p.E; c += 64) {
@@ -310,20 +313,24 @@ __device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, con
 // B chunks (32-k FP4 chunks 2s and 2s+1 of the wave's 64 storage rows, 1 KiB
 // each) and one scale dword per row (the four block-16 scales of the step).
 // ---------------------------------------------------------------------------
+constexpr int kPM4 = 128;                      // rows per FP4 M-tile (4 MFMA blocks: 2 waves per SIMD)
+constexpr int kPMB4 = kPM4 / 32;
+constexpr int kASeg4 = kPM4 / 32;
+constexpr int kStageA4 = kPM4 * 128;
 constexpr int kStageB4 = 8 * 1024;
-constexpr int kStage4 = kStageA + kStageB4 + kStageS;
-constexpr int kDmaPerStage4 = kASeg + 3;
+constexpr int kStage4 = kStageA4 + kStageB4 + kStageS;
+constexpr int kDmaPerStage4 = kASeg4 + 3;
 
 __device__ __forceinline__ void issue_stage4(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
 {
     const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage4);
     const int c = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
-    for (int i = 0; i < kASeg; ++i)
-        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((kASeg * wave + i) * 1024));
-    dma16(src.bsrc + ((size_t)(2 * s) * 64 + lane) * 16, base + kStageA + wave * 2048);
-    dma16(src.bsrc + ((size_t)(2 * s + 1) * 64 + lane) * 16, base + kStageA + wave * 2048 + 1024);
-    dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 8 + (s & 1) * 4, base + kStageA + kStageB4 + wave * 256);
+    for (int i = 0; i < kASeg4; ++i)
+        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((kASeg4 * wave + i) * 1024));
+    dma16(src.bsrc + ((size_t)(2 * s) * 64 + lane) * 16, base + kStageA4 + wave * 2048);
+    dma16(src.bsrc + ((size_t)(2 * s + 1) * 64 + lane) * 16, base + kStageA4 + wave * 2048 + 1024);
+    dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 8 + (s & 1) * 4, base + kStageA4 + kStageB4 + wave * 256);
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -355,7 +362,7 @@ __device__ __forceinline__ float fp8_byte(uint32_t w) { return __builtin_amdgcn_
 // one MFMA k-step (16 k = one FP4 block) of the FP4 pipeline
 template <int NMB, int Q>
 __device__ __forceinline__ void fp4_kstep(const uint8_t *aT, const uint8_t *bT, const int boff[2], const uint32_t sw[2],
-                                          uint32_t rmask, f32x16 acc[kPMB][2])
+                                          uint32_t rmask, f32x16 acc[kPMB4][2])
 {
     const int lane = threadIdx.x & 63, h = lane >> 5;
     bf16x8 bfr[2];
@@ -378,7 +385,7 @@ __device__ __forceinline__ void fp4_kstep(const uint8_t *aT, const uint8_t *bT, 
 // FP4 row brow[nb]
 template <int NMB>
 __device__ __forceinline__ void gemm_pipe4_n(const PipeSrc &src, uint8_t *smem, const int brow[2], uint32_t rmask,
-                                             f32x16 acc[kPMB][2])
+                                             f32x16 acc[kPMB4][2])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
@@ -395,8 +402,8 @@ __device__ __forceinline__ void gemm_pipe4_n(const PipeSrc &src, uint8_t *smem, 
         if (s + kPS - 1 < nsteps) issue_stage4(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
         const uint8_t *stg = smem + (s % kPS) * kStage4;
         const uint8_t *aT = stg;
-        const uint8_t *bT = stg + kStageA;
-        const uint8_t *sT = stg + kStageA + kStageB4;
+        const uint8_t *bT = stg + kStageA4;
+        const uint8_t *sT = stg + kStageA4 + kStageB4;
         uint32_t sw[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) sw[nb] = *reinterpret_cast<const uint32_t *>(sT + brow[nb] * 4);
@@ -408,59 +415,74 @@ __device__ __forceinline__ void gemm_pipe4_n(const PipeSrc &src, uint8_t *smem, 
 }
 
 __device__ __forceinline__ void gemm_pipe4(const PipeSrc &src, uint8_t *smem, const int brow[2], uint32_t rmask,
-                                           f32x16 acc[kPMB][2], int nmb)
+                                           f32x16 acc[kPMB4][2], int nmb)
 {
     switch (nmb) {
     case 1: gemm_pipe4_n<1>(src, smem, brow, rmask, acc); break;
     case 2: gemm_pipe4_n<2>(src, smem, brow, rmask, acc); break;
     case 3: gemm_pipe4_n<3>(src, smem, brow, rmask, acc); break;
-    case 4: gemm_pipe4_n<4>(src, smem, brow, rmask, acc); break;
-    default: gemm_pipe4_n<5>(src, smem, brow, rmask, acc); break;
+    default: gemm_pipe4_n<4>(src, smem, brow, rmask, acc); break;
     }
 }
 
-// Delta slot of a tile's expert when it has an FP4 delta and at least one of
-// the tile's rows belongs to a gate-flagged token, else -1.  rmask gets bit mb
-// set when this lane's row 32 mb + lane % 32 is flagged (rows are the same in
-// every wave, so the answer is uniform over the workgroup).
-__device__ __forceinline__ int delta_rows(const PrefillParams &p, const MTile &mt, int nmb, uint32_t &rmask)
+// Delta slot of expert e when it has an FP4 delta and at least one of its
+// pairs belongs to a gate-flagged token, else -1.  Decided per expert, so the
+// 2-bit kernels (160-row tiles) and the FP4 kernels (128-row tiles) agree on
+// which rows go through the pre-activation buffer.
+__device__ __forceinline__ int expert_delta_slot(const PrefillParams &p, int e)
 {
-    rmask = 0;
-    if (mt.e < 0 || p.n_slots <= 0 || p.gate == nullptr) return -1;
-    const int ds = p.slot_of_expert[mt.e];
+    if (e < 0 || p.n_slots <= 0 || p.gate == nullptr) return -1;
+    const int ds = p.slot_of_expert[e];
     if (ds < 0 || ds >= p.n_slots) return -1;
     const int lane = threadIdx.x & 63, P = p.T * p.k;
+    const int o1 = p.offsets[e + 1];
+    bool any = false;
+    for (int i = p.offsets[e] + lane; i < o1; i += 64) {
+        const int t = min(max(p.sorted[i], 0), P - 1) / p.k;
+        any |= p.gate[t] != 0;
+    }
+    return __ballot(any) ? ds : -1;
+}
+
+// bit mb set when this lane's A row 32 mb + lane % 32 of an FP4 tile is flagged
+__device__ __forceinline__ uint32_t flagged_rows(const PrefillParams &p, const MTile &mt, int nmb)
+{
+    uint32_t rmask = 0;
+    const int lane = threadIdx.x & 63, P = p.T * p.k;
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb) {
+    for (int mb = 0; mb < kPMB4; ++mb) {
         const int r = 32 * mb + (lane & 31);
         if (mb < nmb && r < mt.rows) {
             const int t = min(max(p.sorted[mt.row0 + r], 0), P - 1) / p.k;
             if (p.gate[t]) rmask |= 1u << mb;
         }
     }
-    return __ballot(rmask != 0u) ? ds : -1;
+    return rmask;
 }
 
 // FP4 work runs in kernels of its own (FP4 = true) after the 2-bit kernels
 // (FP4 = false), so that the 2-bit kernels keep their register budget:
 //  * an NVFP4 shared expert's tiles run only in the FP4 kernels;
-//  * a tile with gate-flagged rows on a delta-cache expert runs its 2-bit
-//    pass in the 2-bit kernel, which stores the fp32 pre-activations (gate/up)
-//    or adds y (down) as usual; the FP4 kernel then adds the delta pass, with
-//    the rows of unflagged tokens zeroed, and (gate/up) applies SwiGLU.
+//  * an expert with gate-flagged rows and a delta runs its 2-bit pass in the
+//    2-bit kernel, which stores the fp32 pre-activations (gate/up) or writes y
+//    (down) as usual; the FP4 kernel then adds the delta pass, with the rows
+//    of unflagged tokens zeroed, and (gate/up) applies SwiGLU.
+// The FP4 kernels tile by 128 rows (2 waves per SIMD, 2 workgroups per CU),
+// the 2-bit kernels by 160.
 struct TileKind {
     bool sh4;       // NVFP4 shared expert tile
-    int ds;         // delta slot when the tile has gate-flagged rows, else -1
-    uint32_t rmask; // this lane's flagged 32-row blocks (delta tiles)
+    int ds;         // delta slot when the expert has gate-flagged rows, else -1
+    uint32_t rmask; // FP4 kernels: this lane's flagged 32-row blocks
 };
 
+template <bool FP4>
 __device__ __forceinline__ TileKind tile_kind(const PrefillParams &p, const MTile &mt, int nmb)
 {
     TileKind tk;
     tk.sh4 = mt.e < 0 && p.shared_fp4;
-    tk.ds = -1;
-    tk.rmask = (1u << kPMB) - 1u;
-    if (!tk.sh4) tk.ds = delta_rows(p, mt, nmb, tk.rmask);
+    tk.ds = tk.sh4 ? -1 : expert_delta_slot(p, mt.e);
+    tk.rmask = (1u << kPMB4) - 1u;
+    if (FP4 && tk.ds >= 0) tk.rmask = flagged_rows(p, mt, nmb);
     return tk;
 }
 
@@ -469,22 +491,23 @@ __device__ __forceinline__ TileKind tile_kind(const PrefillParams &p, const MTil
 template <bool FP4>
 __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t *smem)
 {
+    constexpr int NB = FP4 ? kPMB4 : kPMB, SEG = FP4 ? kASeg4 : kASeg;
     int ms, nt;
     decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
-    if (ms >= p.n_mslots) return;
+    if (ms >= (FP4 ? p.n_mslots4 : p.n_mslots)) return;
     MTile mt;
-    if (!locate_mtile(p, ms, mt)) return;
+    if (!(FP4 ? locate_mtile<kPM4>(p, ms, mt) : locate_mtile<kPM>(p, ms, mt))) return;
     const int nmb = (mt.rows + 31) / 32;
-    const TileKind tk = tile_kind(p, mt, nmb);
+    const TileKind tk = tile_kind<FP4>(p, mt, nmb);
     if (FP4 ? !(tk.sh4 || tk.ds >= 0) : tk.sh4) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
-    // A rows fetched by this lane: segment i of wave w holds rows 8(4w+i) .. +7; lane -> row + lane/8
+    // A rows fetched by this lane: segment i of wave w holds rows 8(SEG w + i) .. +7; lane -> row + lane/8
     PipeSrc src;
     src.K = H;
 #pragma unroll
-    for (int i = 0; i < kASeg; ++i) {
-        const int r = min(8 * (kASeg * wave + i) + (lane >> 3), mt.rows - 1);
+    for (int i = 0; i < SEG; ++i) {
+        const int r = min(8 * (SEG * wave + i) + (lane >> 3), mt.rows - 1);
         int tok;
         if (mt.e >= 0) tok = min(max(p.sorted[mt.row0 + r], 0), P - 1) / p.k;
         else tok = mt.row0 + r;
@@ -496,9 +519,9 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     const int jl = 32 * wave + (lane & 31);          // h column within the tile
     const int j = 128 * nt + jl;
     const int brow[2] = {jl, 128 + jl};               // gate row, up row in the stage
-    f32x16 acc[kPMB][2];
+    f32x16 acc[NB][2];
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb)
+    for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -526,10 +549,10 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
         su = F.scale2[fm0 + 1];
     }
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
-    const bool to_pre = !FP4 && tk.ds >= 0;                     // 2-bit pass of a delta tile
+    const bool to_pre = !FP4 && tk.ds >= 0;                     // 2-bit pass of a delta expert
     const bool from_pre = FP4 && !tk.sh4;                       // delta pass: add to it
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb) {
+    for (int mb = 0; mb < NB; ++mb) {
         if (mb >= nmb) break;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -573,13 +596,14 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
 template <bool FP4>
 __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t *smem)
 {
+    constexpr int NB = FP4 ? kPMB4 : kPMB, SEG = FP4 ? kASeg4 : kASeg;
     int ms, nt;
     decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
-    if (ms >= p.n_mslots) return;
+    if (ms >= (FP4 ? p.n_mslots4 : p.n_mslots)) return;
     MTile mt;
-    if (!locate_mtile(p, ms, mt)) return;
+    if (!(FP4 ? locate_mtile<kPM4>(p, ms, mt) : locate_mtile<kPM>(p, ms, mt))) return;
     const int nmb = (mt.rows + 31) / 32;
-    const TileKind tk = tile_kind(p, mt, nmb);
+    const TileKind tk = tile_kind<FP4>(p, mt, nmb);
     if (FP4 ? !(tk.sh4 || tk.ds >= 0) : tk.sh4) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
@@ -587,8 +611,8 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     PipeSrc src;
     src.K = I;
 #pragma unroll
-    for (int i = 0; i < kASeg; ++i) {
-        const int r = min(8 * (kASeg * wave + i) + (lane >> 3), mt.rows - 1);
+    for (int i = 0; i < SEG; ++i) {
+        const int r = min(8 * (SEG * wave + i) + (lane >> 3), mt.rows - 1);
         src.arow[i] = reinterpret_cast<const uint8_t *>(p.h + (size_t)(rowbase + r) * I);
     }
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
@@ -598,9 +622,9 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     int ncol[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) ncol[nb] = 256 * nt + brow[nb];
-    f32x16 acc[kPMB][2];
+    f32x16 acc[NB][2];
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb)
+    for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -623,7 +647,7 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     }
     const bool add = FP4 && !tk.sh4;   // delta pass: add to the 2-bit y
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb) {
+    for (int mb = 0; mb < NB; ++mb) {
         if (mb >= nmb) break;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -781,13 +805,15 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     p.n_ntiles = L->I / 128;
     // tiles with FP4 work (delta rows, NVFP4 shared expert) go to the *_fp4 kernels
     const bool fp4 = (p.n_slots > 0) || p.shared_fp4;
+    p.n_mslots4 = (P + kPM4 - 1) / kPM4 + L->E + (p.has_shared ? (T + kPM4 - 1) / kPM4 : 0);
+    const int ms8_4 = (p.n_mslots4 + 7) / 8 * 8;
     timing_start(stream);
     hipLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
     timing_stop(stream);
     int rc = check_launch("fc1_prefill_kernel");
     if (rc != MOET_OK) return rc;
     if (fp4) {
-        hipLaunchKernelGGL(fc1_prefill_fp4_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
+        hipLaunchKernelGGL(fc1_prefill_fp4_kernel, dim3(ms8_4 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
         rc = check_launch("fc1_prefill_fp4_kernel");
         if (rc != MOET_OK) return rc;
     }
@@ -796,7 +822,7 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     rc = check_launch("fc2_prefill_kernel");
     if (rc != MOET_OK) return rc;
     if (fp4) {
-        hipLaunchKernelGGL(fc2_prefill_fp4_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
+        hipLaunchKernelGGL(fc2_prefill_fp4_kernel, dim3(ms8_4 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
         rc = check_launch("fc2_prefill_fp4_kernel");
         if (rc != MOET_OK) return rc;
     }

@@ -310,8 +310,9 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
  * Decode-sized batches (T*top_k <= 1024) run the GEMV kernels; larger
  * batches run the MFMA grouped-GEMM kernels when I % 128 == 0 and
  * H % 256 == 0 (the FP4 delta and an NVFP4 shared expert then run as an FP4
- * MFMA pass; a delta is added as D * (d_scale2 / scale2), exact when the
- * ratio is a power of two, as it is (1/2) for planes built by moet_requant),
+ * MFMA pass: the 2-bit gate/up kernel stores the fp32 pre-activations of a
+ * delta expert's rows, the FP4 kernel adds D13 x_t, each product scaled by
+ * its own scale2, before SwiGLU, and the FP4 down kernel adds D2 h to y),
  * else the GEMV kernels, which take at most T*top_k + ceil(T/2) = 65535 work
  * entries (MOET_EUNSUPPORTED beyond).
  * workspace: at least moet_moe_workspace_bytes(L, T, top_k) bytes of device

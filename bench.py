@@ -86,15 +86,16 @@ def summarize_counters(path):
         print(f"{ctr:12s} dispatches {n:6d} mean {tot / n:14.1f}  {name[:110]}")
 
 
-def counted_traffic():
-    """HBM bytes per launch of the gate/up decode kernel from the committed counter summary, if that summary
+def counted_traffic(profile="fc1_decode_kernel_hbm_counters_T3_H7168_I2048_E256.md",
+                    sources=("moe_decode.hip", "moet_common.h")):
+    """HBM bytes per launch of a kernel from a committed counter summary under profiles/, if that summary
     was taken on the current kernel source (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "fc1_decode_kernel_hbm_counters_T3_H7168_I2048_E256.md")
+    path = os.path.join(ROOT, "profiles", profile)
     src = os.path.join(ROOT, "bit_moe_expert_nvfp4_amd", "csrc")
     try:
         h = hashlib.sha256()
-        for name in ("moe_decode.hip", "moet_common.h"):
+        for name in sources:
             with open(os.path.join(src, name), "rb") as f:
                 h.update(f.read())
         fields = {}
@@ -411,7 +412,11 @@ def prefill_leg(layer, cfg5, steps, seed, dev, flags=None, soe=None):
         "mfma_frac": round(fl / (ms / 1e3) / 1e12 / peak, 4),
         "roofline": {"kernel": "fc1_prefill_kernel (gate/up grouped GEMM + SwiGLU)", "bound": "mfma",
                      "achieved": round(fl_fc1 / (fc1_ms / 1e3) / 1e12, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(fl_fc1 / (fc1_ms / 1e3) / 1e12 / peak, 4), "traffic": None,
+                     "frac": round(fl_fc1 / (fc1_ms / 1e3) / 1e12 / peak, 4),
+                     # counters were taken on the chunk without gated tokens
+                     "traffic": None if flags is not None else counted_traffic(
+                         "prefill_kernels_mfma_hbm_counters_T4096_H7168_I2048_E256.md",
+                         ("moe_prefill.hip", "moet_common.h")),
                      "avg_launch_us": round(fc1_ms * 1e3, 1), "algorithmic_flop_per_launch": fl_fc1},
     }
 

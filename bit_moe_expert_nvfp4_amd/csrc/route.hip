@@ -58,6 +58,9 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
 #pragma unroll
         for (int i = 0; i < NPL; ++i) c += __popcll(__ballot(key[i] >= cand));
         if (c >= k) thr = cand;
+        // exactly k keys >= cand: they are the top k (ties at thr below are then
+        // all selected, since k - #{key > thr} = #{key == thr})
+        if (c == k) break;
     }
     int c_gt = 0;
 #pragma unroll

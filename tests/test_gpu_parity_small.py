@@ -181,6 +181,13 @@ def _run_forward_case(cfg, seed=0, check_determinism=False, shared_nvfp4=False):
     dict(T=300, E=16, k=8, H=512, I=256, n_resident=6, n_flagged=120, shared=True, score=synth.SIGMOID),
     dict(T=1100, E=4, k=1, H=256, I=128, n_resident=4, n_flagged=1100),
     dict(T=200, E=8, k=8, H=512, I=256, n_resident=8, n_flagged=1, swiglu_limit=0.01, score=synth.SIGMOID),
+    # more decode shapes: H, I multiples of 256, shared expert with delta runs beside plain runs, clamp
+    dict(T=4, E=8, k=2, H=512, I=256),
+    dict(T=1, E=4, k=1, H=256, I=256),
+    dict(T=5, E=16, k=4, H=768, I=512, shared=True, score=synth.SIGMOID),
+    dict(T=11, E=8, k=4, H=512, I=512, shared=True, n_resident=3, n_flagged=5, score=synth.SIGMOID),
+    dict(T=6, E=8, k=2, H=512, I=256, swiglu_limit=0.004),
+    dict(T=64, E=16, k=8, H=1024, I=512, score=synth.SIGMOID),
 ])
 def test_forward_small(case):
     cfg = _small_cfg(**case)

@@ -93,32 +93,48 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict_
         for (int L = 1; L < 8; ++L) cnt[h][0] -= cnt[h][L];
     }
 
+    // Err(a) with the bins split at the level boundary: a bin (value y, count
+    // c) sits on level 1 iff 2y <= 5a (then (y-a)^2 <= (y-4a)^2), so with
+    // S1, C1 the sums of c*y and c over level-1 bins and S4, C4 over level-4
+    // bins,
+    //   Err(a) = sum c*y^2 - 2a (S1 + 4 S4) + a^2 (zeros + C1 + 16 C4),
+    // the same exact integer as the per-bin sum (every product and partial
+    // sum is an integer below 2^53, so float64 holds it exactly).
     int best_t = 0;
     if (amax > 0) {
         const int t_lo = e4m3_floor_code(amax / 512);
         const int t_hi = e4m3_ceil_code((amax + 3) / 4);
-        double yv[2][8], cf[2][8];
+        int yv[14], cy[14], cc[14];
+        double y2 = 0.0;
+        int stot = 0, ctot = 0;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int L = 0; L < 8; ++L) {
-                yv[h][L] = (double)(mag2_of(L) * S9[h]);
-                cf[h][L] = (double)cnt[h][L];
+            for (int L = 1; L < 8; ++L) {
+                const int i = 7 * h + L - 1;
+                yv[i] = mag2_of(L) * S9[h];                    // < 2^22
+                cc[i] = cnt[h][L];
+                cy[i] = cc[i] * yv[i];                         // < 2^27
+                y2 = fma((double)cy[i], (double)yv[i], y2);    // < 2^49, exact
+                stot += cy[i];
+                ctot += cc[i];
             }
-        const double nzero = cf[0][0] + cf[1][0];
+        const int nzero = cnt[0][0] + cnt[1][0];
         double best_err = -1.0;
         for (int t = t_lo; t <= t_hi; ++t) {
-            const double a = 4.0 * (double)e4m3_x512(t);
-            const double a4 = 4.0 * a;
-            double err = nzero * a * a;
+            const int ai = 4 * e4m3_x512(t);                   // < 2^20
+            int s1 = 0, c1 = 0;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int L = 1; L < 8; ++L) {
-                    const double d1 = yv[h][L] - a, d4 = yv[h][L] - a4;
-                    err = fma(cf[h][L], fmin(d1 * d1, d4 * d4), err);
-                }
-            if (best_err < 0.0 || err < best_err) {
+            for (int i = 0; i < 14; ++i) {
+                const bool l1 = 2 * yv[i] <= 5 * ai;
+                s1 += l1 ? cy[i] : 0;
+                c1 += l1 ? cc[i] : 0;
+            }
+            const int lin = s1 + 4 * (stot - s1);              // < 2^29
+            const int quad = nzero + c1 + 16 * (ctot - c1);    // <= 512
+            const double ad = (double)ai;
+            const double err = fma(ad * ad, (double)quad, fma(-2.0 * ad, (double)lin, y2));
+            if (best_err < 0.0 || err < best_err) {   // ascending scan: ties keep the smaller scale
                 best_err = err;
                 best_t = t;
             }

@@ -201,40 +201,56 @@ template <int NPL>
 static int launch_route_n(const float *logits, int T, int E, int k, int fn, int renorm, float rscale, int32_t *ids,
                           float *w, int32_t *offsets, int32_t *sorted, hipStream_t stream);
 
-// One workgroup per expert e: offset = #pairs with id < e, then its pairs in order.
+// One workgroup per expert e: offset = #pairs with id < e, then its pairs in
+// pair order.  Thread t owns a contiguous range of pairs: one pass counts the
+// ids below e and equal to e, one block-wide exclusive scan of the equal counts
+// gives every thread its first output slot, and a second pass over its range
+// writes its pairs, so the order is stable with a single barrier phase.
 __global__ __launch_bounds__(256) void route_permute_kernel(const int32_t *__restrict__ ids, int P, int E,
                                                             int32_t *__restrict__ offsets,
                                                             int32_t *__restrict__ sorted)
 {
-    __shared__ int s_wave[4];
+    __shared__ int s_lt[4], s_eq[4];
     const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int lt = 0;
-    for (int p = tid; p < P; p += 256) lt += (ids[p] < e) ? 1 : 0;
+    const int per = (((P + 255) / 256) + 3) & ~3;   // a multiple of 4: 16-byte loads (ids is 16-byte aligned)
+    const int p0 = min(tid * per, P), p1 = min(p0 + per, P);
+    int lt = 0, eq = 0;
+    int p = p0;
+    for (; p + 4 <= p1; p += 4) {
+        const int4 v = *reinterpret_cast<const int4 *>(ids + p);
+        lt += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
+        eq += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+    }
+    for (; p < p1; ++p) {
+        const int v = ids[p];
+        lt += v < e;
+        eq += v == e;
+    }
+    // wave sums of lt; wave-inclusive scan of eq
+    int ltw = lt, inc = eq;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off, 64);
-    if (lane == 0) s_wave[wave] = lt;
+    for (int off = 32; off > 0; off >>= 1) ltw += __shfl_xor(ltw, off, 64);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += o;
+    }
+    if (lane == 63) {
+        s_lt[wave] = ltw;
+        s_eq[wave] = inc;
+    }
     __syncthreads();
-    const int off_e = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    const int off_e = s_lt[0] + s_lt[1] + s_lt[2] + s_lt[3];
+    int base = off_e + inc - eq;   // exclusive within the wave
+    for (int i = 0; i < wave; ++i) base += s_eq[i];
     if (tid == 0) {
         offsets[e] = off_e;
         if (e == E - 1) offsets[E] = P;
     }
-    __syncthreads();
-    int base = 0;
-    for (int start = 0; start < P; start += 256) {
-        const int p = start + tid;
-        const bool eq = (p < P) && (ids[p] == e);
-        const uint64_t bal = __ballot(eq);
-        const int before = __popcll(bal & ((1ull << lane) - 1ull));
-        __syncthreads();
-        if (lane == 0) s_wave[wave] = __popcll(bal);
-        __syncthreads();
-        int wbase = base;
-        for (int i = 0; i < wave; ++i) wbase += s_wave[i];
-        if (eq) sorted[off_e + wbase + before] = p;
-        base += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-    }
+    if (eq == 0) return;
+    for (p = p0; p < p1; ++p)
+        if (ids[p] == e) sorted[base++] = p;
 }
 
 template <int NPL>

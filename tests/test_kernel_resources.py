@@ -74,3 +74,30 @@ def test_hot_kernels_keep_their_occupancy(usage, frag, waves):
     hits = [n for n in usage if re.search(rf"\d{frag}E", n)]
     assert len(hits) == 1, f"{frag}: found {hits}"
     assert usage[hits[0]].get("Occupancy", 0) >= waves, f"{frag}: occupancy {usage[hits[0]]}"
+
+
+@pytest.mark.skipif(not _HAVE_HIPCC, reason="hipcc not available")
+def test_m0_written_only_by_the_lds_dma_asm():
+    """The prefill pipeline's inline asm sets m0 (the LDS destination of
+    global_load_lds_dwordx4) and lists it as clobbered.  m0 is a reserved
+    register the compiler does not preserve across such asm, so no other
+    instruction of these kernels may read or write it: every m0 access in the
+    generated code must be the asm's own s_mov_b32 m0 directly followed by its
+    LDS-DMA load (global_load_lds_dword or _dwordx4)."""
+    src = os.path.join(CSRC, "moe_prefill.hip")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "--cuda-device-only", "-S", src, "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l.strip() for l in r.stdout.splitlines()]
+    code = [l for l in lines if l and not l.startswith((";", ".", "//")) and not l.endswith(":")]
+    writes = 0
+    for i, l in enumerate(code):
+        if re.search(r"\bm0\b", l):
+            assert l.startswith("s_mov_b32 m0,"), f"m0 used outside the LDS-DMA asm: {l}"
+            assert i + 1 < len(code) and code[i + 1].startswith("global_load_lds_dword"), \
+                f"m0 write not followed by its LDS-DMA load: {l} / {code[i + 1] if i + 1 < len(code) else ''}"
+            writes += 1
+    assert writes > 0, "no LDS-DMA loads found"

@@ -782,9 +782,11 @@ int launch_decode(const moet_layer *L, const uint16_t *x, int T, int k, const in
     p.ypart = reinterpret_cast<float *>(base + al(rows * L->I * 2));
     p.out = out;
     const int slots = decode_entries(T, k, p.has_shared);
-    timing_start(stream);
-    hipLaunchKernelGGL(fc1_decode_kernel, dim3(L->I / 32, slots), dim3(64 * kW1), 0, stream, p);
-    timing_stop(stream);
+    hipEvent_t ev0, ev1;
+    if (timing_events(&ev0, &ev1))
+        hipExtLaunchKernelGGL(fc1_decode_kernel, dim3(L->I / 32, slots), dim3(64 * kW1), 0, stream, ev0, ev1, 0, p);
+    else
+        hipLaunchKernelGGL(fc1_decode_kernel, dim3(L->I / 32, slots), dim3(64 * kW1), 0, stream, p);
     int rc = check_launch("fc1_decode_kernel");
     if (rc != MOET_OK) return rc;
     hipLaunchKernelGGL(fc2_decode_kernel, dim3(L->H / 64, slots), dim3(64 * kW2), 0, stream, p);

@@ -807,9 +807,11 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     const bool fp4 = (p.n_slots > 0) || p.shared_fp4;
     p.n_mslots4 = (P + kPM4 - 1) / kPM4 + L->E + (p.has_shared ? (T + kPM4 - 1) / kPM4 : 0);
     const int ms8_4 = (p.n_mslots4 + 7) / 8 * 8;
-    timing_start(stream);
-    hipLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
-    timing_stop(stream);
+    hipEvent_t ev0, ev1;
+    if (timing_events(&ev0, &ev1))
+        hipExtLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, ev0, ev1, 0, p);
+    else
+        hipLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
     int rc = check_launch("fc1_prefill_kernel");
     if (rc != MOET_OK) return rc;
     if (fp4) {

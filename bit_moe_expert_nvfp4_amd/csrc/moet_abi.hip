@@ -12,14 +12,14 @@ namespace moet {
 static thread_local char g_err[512];
 static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
-void timing_start(hipStream_t s)
+// The timing events for the next timed launch, or false when none are set.
+// The launch hands them to hipExtLaunchKernel, which stamps them from the
+// kernel's own dispatch (no separate marker packets in the stream).
+bool timing_events(hipEvent_t *start, hipEvent_t *stop)
 {
-    if (g_ev_start) (void)hipEventRecord(g_ev_start, s);
-}
-
-void timing_stop(hipStream_t s)
-{
-    if (g_ev_stop) (void)hipEventRecord(g_ev_stop, s);
+    *start = g_ev_start;
+    *stop = g_ev_stop;
+    return g_ev_start != nullptr;
 }
 
 void set_error(const char *fmt, ...)

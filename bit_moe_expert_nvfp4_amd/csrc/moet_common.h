@@ -1,6 +1,7 @@
 // Shared device helpers and launch utilities of libmoet (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -134,6 +135,5 @@ void set_error(const char *fmt, ...);
 int fail(int status, const char *fmt, ...);
 int check_launch(const char *what);
 bool aligned16(const void *p);
-void timing_start(hipStream_t s);  // records the caller's start event, if set
-void timing_stop(hipStream_t s);
+bool timing_events(hipEvent_t *start, hipEvent_t *stop);  // the caller's timing events, if set
 }  // namespace moet

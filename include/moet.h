@@ -364,9 +364,10 @@ int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, u
 
 /*
  * moet_set_timing_events - benchmark instrumentation.  While set (per host
- * thread), every moet_moe_forward call records `start` on its stream right
- * before it launches its first expert kernel (the gate/up kernel) and `stop`
- * right after that launch, so the caller can time that one kernel with
+ * thread), every moet_moe_forward call launches its first expert kernel (the
+ * gate/up kernel) with hipExtLaunchKernel and these two events, which the
+ * runtime stamps at that kernel's start and end (no marker packets between
+ * the launches), so the caller can time that one kernel with
  * hipEventElapsedTime.  `start` / `stop` are caller-owned hipEvent_t handles;
  * pass NULL, NULL to disable.  Returns MOET_EINVAL if only one is NULL.
  */

@@ -192,17 +192,17 @@ __device__ __forceinline__ bf16x8 deq_frag(uint32_t w, uint32_t sh, uint32_t mas
 
 // ---------------------------------------------------------------------------
 // Pipeline: kPS-stage LDS ring filled by LDS-DMA (global_load_lds) so no
-// registers are held for prefetch.  Per stage and wavefront: kASeg A segments
-// (1 KiB each), 1 B chunk (1 KiB = 64 rows x 16 B), 1 scale dword per row of
-// the B chunk (256 B).  The DMA is issued from inline asm, invisible to the
-// compiler's wait-count pass, and waited explicitly (kASeg + 2 per stage).
+// registers are held for prefetch.  Per stage and wavefront: one A segment
+// (1 KiB) per valid 32-row block of the tile (at most kASeg), 1 B chunk
+// (1 KiB = 64 rows x 16 B), 1 scale dword per row of the B chunk (256 B).  The
+// DMA is issued from inline asm, invisible to the compiler's wait-count pass,
+// and waited explicitly (segments + 2 per stage).
 // ---------------------------------------------------------------------------
 constexpr int kPS = 3;                         // stages
 constexpr int kStageA = kPM * 128;             // kPM rows x 64 k bf16
 constexpr int kStageB = 4 * 1024;              // 256 B-rows x 16 B
 constexpr int kStageS = 4 * 256;               // 256 rows x one scale dword
 constexpr int kStage = kStageA + kStageB + kStageS;
-constexpr int kDmaPerStage = kASeg + 2;
 
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds_base)
 {
@@ -234,14 +234,17 @@ struct PipeSrc {
     int K;
 };
 
-// issue the DMA of pipeline step s into stage buffer `stage`
+// issue the DMA of pipeline step s into stage buffer `stage`.  Only the NSEG * 32
+// rows of the tile's valid 32-row blocks are staged: wave w fetches A segments
+// NSEG w .. NSEG w + NSEG - 1.
+template <int NSEG>
 __device__ __forceinline__ void issue_stage(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
 {
     const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage);
     const int c = (lane & 7) ^ ((lane >> 3) & 7);   // logical 16-B column for this lane's LDS slot
 #pragma unroll
-    for (int i = 0; i < kASeg; ++i)
-        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((kASeg * wave + i) * 1024));
+    for (int i = 0; i < NSEG; ++i)
+        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((NSEG * wave + i) * 1024));
     dma16(src.bsrc + ((size_t)s * 64 + lane) * 16, base + kStageA + wave * 1024);
     dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 4, base + kStageA + kStageB + wave * 256);
 }
@@ -257,12 +260,12 @@ __device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, c
     const int nsteps = src.K / kPK;
 #pragma unroll
     for (int st = 0; st < kPS - 1; ++st)
-        if (st < nsteps) issue_stage(src, smem, st, st, wave, lane);
+        if (st < nsteps) issue_stage<NMB>(src, smem, st, st, wave, lane);
     for (int s = 0; s < nsteps; ++s) {
-        // stages issued after s: min(kPS - 2, nsteps - 1 - s)
-        if (s + 1 < nsteps) wait_barrier<kDmaPerStage * (kPS - 2)>();
+        // stages issued after s: min(kPS - 2, nsteps - 1 - s), NMB + 2 DMAs each
+        if (s + 1 < nsteps) wait_barrier<(NMB + 2) * (kPS - 2)>();
         else wait_barrier<0>();
-        if (s + kPS - 1 < nsteps) issue_stage(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
+        if (s + kPS - 1 < nsteps) issue_stage<NMB>(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
         const uint8_t *stg = smem + (s % kPS) * kStage;
         const uint8_t *aT = stg;
         const uint8_t *bT = stg + kStageA;
@@ -502,12 +505,14 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     if (FP4 ? !(tk.sh4 || tk.ds >= 0) : tk.sh4) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
-    // A rows fetched by this lane: segment i of wave w holds rows 8(SEG w + i) .. +7; lane -> row + lane/8
+    // A rows fetched by this lane: segment i of wave w holds rows 8(nseg w + i) .. +7; lane -> row + lane/8
+    // (2-bit kernels stage only the nmb valid 32-row blocks: nseg = nmb)
+    const int nseg = FP4 ? SEG : nmb;
     PipeSrc src;
     src.K = H;
 #pragma unroll
     for (int i = 0; i < SEG; ++i) {
-        const int r = min(8 * (SEG * wave + i) + (lane >> 3), mt.rows - 1);
+        const int r = min(8 * (nseg * wave + i) + (lane >> 3), mt.rows - 1);
         int tok;
         if (mt.e >= 0) tok = min(max(p.sorted[mt.row0 + r], 0), P - 1) / p.k;
         else tok = mt.row0 + r;
@@ -608,11 +613,12 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;
+    const int nseg = FP4 ? SEG : nmb;   // A segments per wave (2-bit kernels: the valid 32-row blocks)
     PipeSrc src;
     src.K = I;
 #pragma unroll
     for (int i = 0; i < SEG; ++i) {
-        const int r = min(8 * (SEG * wave + i) + (lane >> 3), mt.rows - 1);
+        const int r = min(8 * (nseg * wave + i) + (lane >> 3), mt.rows - 1);
         src.arow[i] = reinterpret_cast<const uint8_t *>(p.h + (size_t)(rowbase + r) * I);
     }
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;

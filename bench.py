@@ -306,13 +306,14 @@ def gate_leg(seed, dev, steps=200, V=151552):
         g.manual_seed(seed + T)
         lg = torch.randn((T, V), generator=g, device=dev) * torch.linspace(0.5, 14.0, T, device=dev).unsqueeze(1)
         flags = torch.empty((T,), dtype=torch.uint8, device=dev)
+        ws = torch.empty((max(1, moet.gate_workspace_bytes(T, V)),), dtype=torch.uint8, device=dev)
         for _ in range(10):
-            moet.confidence_gate(lg, 0.60, flags=flags)
+            moet.confidence_gate(lg, 0.60, flags=flags, workspace=ws)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            moet.confidence_gate(lg, 0.60, flags=flags)
+            moet.confidence_gate(lg, 0.60, flags=flags, workspace=ws)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / steps * 1e3

@@ -61,7 +61,8 @@ size_t decode_workspace_bytes(int T, int k, int H, int I);
 int launch_decode(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
                   const int32_t *, const uint8_t *, uint16_t *, int32_t *, void *, hipStream_t);
 int launch_delta(const moet_fp4 *, int, int, int, const uint16_t *, const int32_t *, int, float *, hipStream_t);
-int launch_gate(const float *, int, int, float, uint8_t *, float *, hipStream_t);
+int launch_gate(const float *, int, int, float, uint8_t *, float *, void *, hipStream_t);
+size_t gate_workspace_bytes(int T, int V);
 size_t prefill_workspace_bytes(int T, int k, int H, int I, int E);
 int launch_prefill(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
                    const int32_t *, const uint8_t *, uint16_t *, int32_t *, void *, hipStream_t);
@@ -114,7 +115,7 @@ const char *moet_status_str(int s)
 
 const char *moet_last_error(void) { return g_err; }
 
-int moet_abi_version(void) { return 4; }
+int moet_abi_version(void) { return 5; }
 
 // shape checks shared by the load-time conversions
 static int check_stack(int64_t n_mat, int64_t N, int64_t K, uint32_t flags)
@@ -261,8 +262,14 @@ int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
     return launch_delta(D, n_slots, N, K, act, row_slot, R, acc, (hipStream_t)stream);
 }
 
+size_t moet_gate_workspace_bytes(int32_t T, int32_t V)
+{
+    if (T < 1 || T > 65535 || V < 1) return 0;
+    return gate_workspace_bytes(T, V);
+}
+
 int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
-                         float *confidence_out, void *stream)
+                         float *confidence_out, void *workspace, size_t workspace_bytes, void *stream)
 {
     g_err[0] = 0;
     if (T < 1 || T > 65535) return fail(MOET_EINVAL, "T (%d) must be in [1, 65535]", T);
@@ -271,7 +278,11 @@ int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, u
     if (!aligned16(logits) || !gate_flags) return fail(MOET_EINVAL, "logits (16-byte aligned) and gate_flags must be non-NULL");
     if (confidence_out && (reinterpret_cast<uintptr_t>(confidence_out) & 3u))
         return fail(MOET_EINVAL, "confidence_out must be 4-byte aligned");
-    return launch_gate(logits, T, V, tau, gate_flags, confidence_out, (hipStream_t)stream);
+    const size_t need = gate_workspace_bytes(T, V);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(MOET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (need && !aligned16(workspace)) return fail(MOET_EINVAL, "workspace must be 16-byte aligned");
+    return launch_gate(logits, T, V, tau, gate_flags, confidence_out, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

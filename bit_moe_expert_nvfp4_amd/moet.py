@@ -82,7 +82,9 @@ def lib():
         L.moet_moe_forward.restype = ctypes.c_int
         L.moet_delta_forward.argtypes = [ctypes.POINTER(FP4), _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp]
         L.moet_delta_forward.restype = ctypes.c_int
-        L.moet_confidence_gate.argtypes = [_vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp]
+        L.moet_confidence_gate.argtypes = [_vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moet_gate_workspace_bytes.argtypes = [_i32, _i32]
+        L.moet_gate_workspace_bytes.restype = ctypes.c_size_t
         L.moet_confidence_gate.restype = ctypes.c_int
         L.moet_set_timing_events.argtypes = [_vp, _vp]
         L.moet_set_timing_events.restype = ctypes.c_int
@@ -346,10 +348,16 @@ def delta_forward(D: FP4Planes, act: torch.Tensor, row_slot: torch.Tensor, acc: 
     return acc
 
 
+def gate_workspace_bytes(T: int, V: int) -> int:
+    """moet_gate_workspace_bytes: device bytes the confidence gate needs for T rows of V logits."""
+    return int(lib().moet_gate_workspace_bytes(int(T), int(V)))
+
+
 def confidence_gate(logits: torch.Tensor, tau: float = 0.60, flags: Optional[torch.Tensor] = None,
-                    confidence: Optional[torch.Tensor] = None):
+                    confidence: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """moet_confidence_gate: uint8 [T] flags (1 = largest next-token probability below tau) from fp32
-    logits [T, V]; optionally the confidence itself into an fp32 [T] tensor.  Returns the flags."""
+    logits [T, V]; optionally the confidence itself into an fp32 [T] tensor.  The workspace (uint8,
+    gate_workspace_bytes(T, V) bytes) is allocated per call unless given.  Returns the flags."""
     _need(logits, torch.float32, "logits")
     T, V = logits.shape
     if flags is None:
@@ -357,7 +365,12 @@ def confidence_gate(logits: torch.Tensor, tau: float = 0.60, flags: Optional[tor
     _need(flags, torch.uint8, "flags")
     if confidence is not None:
         _need(confidence, torch.float32, "confidence")
-    _check(lib().moet_confidence_gate(_ptr(logits), T, V, float(tau), _ptr(flags), _ptr(confidence), _stream()))
+    need = gate_workspace_bytes(T, V)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=logits.device)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().moet_confidence_gate(_ptr(logits), T, V, float(tau), _ptr(flags), _ptr(confidence),
+                                      _ptr(workspace), nbytes, _stream()))
     return flags
 
 

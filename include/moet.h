@@ -356,11 +356,19 @@ int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
  * 1 / sum_v exp(l_v - l_max), computed in float64; gate_flags uint8 [T]
  * (device) = 1 where confidence < tau, else 0; confidence_out fp32 [T]
  * (device, may be NULL) receives the confidence rounded to fp32.
+ * workspace: at least moet_gate_workspace_bytes(T, V) bytes of device memory,
+ * 16-byte aligned, owned by the caller and free again when the stream reaches
+ * the end of the call (may be NULL when that size is 0, i.e. when every row
+ * runs in one workgroup).  Few rows are cut into chunks spread over the chip;
+ * the chunk partials go through the workspace and are combined in a fixed
+ * order, so the result is bitwise repeatable.
  * Errors: MOET_EINVAL for T outside [1, 65535], V < 1, tau not finite, NULL
- * or misaligned pointers (logits 16-byte aligned).
+ * or misaligned pointers (logits 16-byte aligned); MOET_EWORKSPACE if the
+ * workspace is missing or short.
  */
+size_t moet_gate_workspace_bytes(int32_t T, int32_t V);
 int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
-                         float *confidence_out, void *stream);
+                         float *confidence_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * moet_set_timing_events - benchmark instrumentation.  While set (per host

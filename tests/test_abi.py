@@ -151,11 +151,29 @@ def test_delta_forward_rejects_bad_args(L):
 def test_confidence_gate_rejects_bad_args(L):
     b = ctypes.c_void_p(256)
     f = ctypes.c_float(0.6)
-    assert L.moet_confidence_gate(b, 0, 10, f, b, None, None) == 1
-    assert L.moet_confidence_gate(b, 70000, 10, f, b, None, None) == 1
-    assert L.moet_confidence_gate(b, 2, 0, f, b, None, None) == 1
-    assert L.moet_confidence_gate(b, 2, 10, ctypes.c_float(float("nan")), b, None, None) == 1
-    assert L.moet_confidence_gate(None, 2, 10, f, b, None, None) == 1
-    assert L.moet_confidence_gate(ctypes.c_void_p(260), 2, 10, f, b, None, None) == 1
-    assert L.moet_confidence_gate(b, 2, 10, f, None, None, None) == 1
-    assert L.moet_confidence_gate(b, 2, 10, f, b, ctypes.c_void_p(258), None) == 1
+    # T = 1024 rows run one workgroup each: no workspace needed
+    assert L.moet_confidence_gate(b, 0, 10, f, b, None, None, 0, None) == 1
+    assert L.moet_confidence_gate(b, 70000, 10, f, b, None, None, 0, None) == 1
+    assert L.moet_confidence_gate(b, 2, 0, f, b, None, None, 0, None) == 1
+    assert L.moet_confidence_gate(b, 2, 10, ctypes.c_float(float("nan")), b, None, None, 0, None) == 1
+    assert L.moet_confidence_gate(None, 2, 10, f, b, None, None, 0, None) == 1
+    assert L.moet_confidence_gate(ctypes.c_void_p(260), 2, 10, f, b, None, None, 0, None) == 1
+    assert L.moet_confidence_gate(b, 2, 10, f, None, None, None, 0, None) == 1
+    assert L.moet_confidence_gate(b, 2, 10, f, b, ctypes.c_void_p(258), None, 0, None) == 1
+    # split rows need the workspace: missing or short -> MOET_EWORKSPACE, misaligned -> MOET_EINVAL
+    need = L.moet_gate_workspace_bytes(3, 151552)
+    assert L.moet_confidence_gate(b, 3, 151552, f, b, None, None, 0, None) == 3
+    assert L.moet_confidence_gate(b, 3, 151552, f, b, None, b, need - 1, None) == 3
+    assert L.moet_confidence_gate(b, 3, 151552, f, b, None, ctypes.c_void_p(264), need, None) == 1
+
+
+def test_gate_workspace_bytes(L):
+    """Chunking of the confidence gate: rows of at least 2048 logits per chunk, about 1024 chunk
+    workgroups over all rows; one 16-byte partial per chunk."""
+    ws = L.moet_gate_workspace_bytes
+    assert ws(3, 151552) == 3 * 74 * 16          # 74 chunks of 2048
+    assert ws(24, 151552) == 24 * 43 * 16        # 43 chunks of 3528
+    assert ws(1, 4) == 0 and ws(5, 1001) == 0    # one chunk: the one-workgroup-per-row kernel
+    assert ws(1024, 151552) == 0 and ws(4096, 151552) == 0
+    assert ws(1, 4097) == 3 * 16                  # 3 chunks of 1368 (the last 1361)
+    assert ws(0, 10) == 0 and ws(2, 0) == 0

@@ -386,7 +386,8 @@ def test_expert_cache_delta_and_nvfp4_shared_together(case):
     assert int(miss.item()) == OFF.miss_count(o_ids, resident) > 0
 
 
-@pytest.mark.parametrize("T,V", [(64, 151552), (5, 1001), (1, 4)])
+@pytest.mark.parametrize("T,V", [(64, 151552), (3, 151552), (24, 151552), (2, 50001), (1, 4097), (5, 1001), (1, 4),
+                                 (1100, 3000)])
 def test_confidence_gate(T, V):
     """Flags and confidence against the oracle (largest next-token probability below tau = 0.60, decided
     in float64 on both sides); rows are scaled from flat to sharp, some logits masked to -inf."""
@@ -397,6 +398,8 @@ def test_confidence_gate(T, V):
     if V > 8:
         lg[:, ::7] = float("-inf")
         lg[:, 1] = lg[:, 1].clamp(min=0.0)            # a finite maximum in every row
+    if V > 40000:
+        lg[0, 2:30000] = float("-inf")                # whole chunks of row 0 masked
     tau = 0.60
     conf = torch.empty((T,), dtype=torch.float32, device=DEV)
     flags = moet.confidence_gate(lg.to(DEV), tau, confidence=conf)

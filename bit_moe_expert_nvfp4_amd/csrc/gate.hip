@@ -107,15 +107,15 @@ struct GatePart {
 // chunks per row and logits per chunk (a multiple of 4, so float4 rows stay aligned)
 int gate_chunks(int T, int V, int *len)
 {
-    const int by_v = (V + kChunkMin - 1) / kChunkMin, by_t = (kGateTargetWG + T - 1) / T;
-    const int c0 = std::max(1, std::min(by_v, by_t));
+    const int64_t by_v = ((int64_t)V + kChunkMin - 1) / kChunkMin, by_t = (kGateTargetWG + (int64_t)T - 1) / T;
+    const int64_t c0 = std::max<int64_t>(1, std::min(by_v, by_t));
     if (c0 == 1) {
         *len = V;
         return 1;
     }
-    const int L = (((V + c0 - 1) / c0) + 3) & ~3;
-    *len = L;
-    return (V + L - 1) / L;
+    const int64_t L = ((((int64_t)V + c0 - 1) / c0) + 3) & ~(int64_t)3;
+    *len = (int)L;
+    return (int)(((int64_t)V + L - 1) / L);
 }
 
 size_t gate_workspace_bytes(int T, int V)
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kPartThreads) void gate_partial_kernel(const float 
     __shared__ double s_sum[kPartThreads / 64];
     const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float *row = logits + (size_t)t * V;
-    const int b = c * L, e = min(V, b + L);
+    const int b = c * L, e = (int)min((int64_t)V, (int64_t)b + L);
     const bool vec = (V % 4) == 0;   // b and e are then multiples of 4
     float m = -INFINITY;
     if (vec) {

@@ -177,3 +177,4 @@ def test_gate_workspace_bytes(L):
     assert ws(1024, 151552) == 0 and ws(4096, 151552) == 0
     assert ws(1, 4097) == 3 * 16                  # 3 chunks of 1368 (the last 1361)
     assert ws(0, 10) == 0 and ws(2, 0) == 0
+    assert ws(1, 2**31 - 1) == 1024 * 16          # no int overflow at the largest V

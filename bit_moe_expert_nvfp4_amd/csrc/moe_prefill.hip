@@ -17,8 +17,8 @@
 //    are then read from that XCD's L2 by all of them.
 //  * A (activations): 160 rows x 64 k bf16 per step, gathered by token
 //    (gate/up) or read from h in sorted order (down), staged in LDS with an
-//    XOR swizzle of the 16-byte columns so each MFMA A fragment is one
-//    conflict-free ds_read_b128.  A, B codes and B scales of each 64-k step
+//    XOR swizzle of the 16-byte columns (by row / 2) so each MFMA A fragment
+//    is one conflict-free ds_read_b128 (16-lane phases over 64 banks).  A, B codes and B scales of each 64-k step
 //    travel by LDS-DMA into a 3-stage ring, so two steps are in flight while
 //    one is computed and no registers are spent on prefetching.
 //  * B (weights): each lane dequantises the 8 k-values its MFMA B fragment
@@ -222,10 +222,22 @@ __device__ __forceinline__ void wait_barrier()
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// A tile in LDS: row r (128 B = 8 columns of 16 B) holds logical column c at
+// physical column c ^ ((r >> 1) & 7).  A ds_read_b128 is served 16 lanes at a
+// time over 64 four-byte banks (256 B); the 16 lanes of an A-fragment read
+// cover 16 consecutive rows, and this swizzle puts them in 16 distinct 16-byte
+// slots of a 256-byte window, so the read is conflict-free.
+__device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
+
 __device__ __forceinline__ bf16x8 a_frag(const uint8_t *a, int r, int c)
 {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(a + r * 128 + ((c ^ (r & 7)) << 4)));
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(a + r * 128 + ((c ^ a_swz(r)) << 4)));
 }
+
+// logical 16-byte column that lane `lane` fetches into its LDS slot of A segment g
+// (rows 8g .. 8g + 7, row 8g + lane / 8, physical column lane % 8): the inverse of
+// a_swz for those rows, whose (r >> 1) & 7 is 4 (g & 1) + lane / 16
+__device__ __forceinline__ int a_dma_col(int lane, int g) { return (lane & 7) ^ (4 * (g & 1) + (lane >> 4)); }
 
 struct PipeSrc {
     const uint8_t *arow[kASeg]; // this lane's A source rows, one per A segment it fetches
@@ -241,10 +253,10 @@ template <int NSEG>
 __device__ __forceinline__ void issue_stage(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
 {
     const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage);
-    const int c = (lane & 7) ^ ((lane >> 3) & 7);   // logical 16-B column for this lane's LDS slot
 #pragma unroll
     for (int i = 0; i < NSEG; ++i)
-        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((NSEG * wave + i) * 1024));
+        dma16(src.arow[i] + (size_t)s * 128 + a_dma_col(lane, NSEG * wave + i) * 16,
+              base + (uint32_t)((NSEG * wave + i) * 1024));
     dma16(src.bsrc + ((size_t)s * 64 + lane) * 16, base + kStageA + wave * 1024);
     dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 4, base + kStageA + kStageB + wave * 256);
 }
@@ -327,10 +339,10 @@ constexpr int kDmaPerStage4 = kASeg4 + 3;
 __device__ __forceinline__ void issue_stage4(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
 {
     const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage4);
-    const int c = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
     for (int i = 0; i < kASeg4; ++i)
-        dma16(src.arow[i] + (size_t)s * 128 + c * 16, base + (uint32_t)((kASeg4 * wave + i) * 1024));
+        dma16(src.arow[i] + (size_t)s * 128 + a_dma_col(lane, kASeg4 * wave + i) * 16,
+              base + (uint32_t)((kASeg4 * wave + i) * 1024));
     dma16(src.bsrc + ((size_t)(2 * s) * 64 + lane) * 16, base + kStageA4 + wave * 2048);
     dma16(src.bsrc + ((size_t)(2 * s + 1) * 64 + lane) * 16, base + kStageA4 + wave * 2048 + 1024);
     dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 8 + (s & 1) * 4, base + kStageA4 + kStageB4 + wave * 256);

@@ -23,9 +23,10 @@
 //  fc1: grid (I/32 half-tiles, entries), 4 wavefronts splitting K.  Lanes
 //       0-31 hold 32 gate rows, lanes 32-63 the same 32 up rows, so SwiGLU
 //       pairs lane j with lane j+32 after the cross-wave reduction in LDS.  An
-//       entry is one pass over up to two tokens of one expert (two
-//       consecutive sorted pairs of its run, or two shared-expert tokens), so
-//       every workgroup does the same work; the shared expert's entries come
+//       entry is one pass over up to two tokens of one routed expert (two
+//       consecutive sorted pairs of its run) or over one shared-expert token,
+//       so workgroups do nearly the same work (a two-token shared entry was
+//       the longest one and set the tail); the shared expert's entries come
 //       first in the grid so the hardware dispatches them first.  FP4 delta
 //       rows are added for flagged tokens of resident experts.  Writes
 //       h = bf16(silu(gate) * up).
@@ -83,15 +84,15 @@ __device__ __forceinline__ int weight_slot(const DecodeParams &p, int e)
 constexpr int kTT = 2;     // tokens per pass (more would cost SGPRs / occupancy)
 
 // Number of grid entries (blockIdx.y) of the GEMV kernels: the shared
-// expert's token groups come first, so that their workgroups are dispatched
-// first, then one entry per sorted pair position.
+// expert's tokens come first (one entry each), so that their workgroups are
+// dispatched first, then one entry per sorted pair position.
 __host__ __device__ __forceinline__ int decode_entries(int T, int k, int has_shared)
 {
-    return (has_shared ? (T + kTT - 1) / kTT : 0) + T * k;
+    return (has_shared ? T : 0) + T * k;
 }
 
 // Entry s -> one pass over at most kTT tokens of one expert.  Entries below
-// nsh cover shared-expert tokens [kTT s, kTT s + kTT).  Entry nsh + q covers
+// nsh = T cover shared-expert token s.  Entry nsh + q covers
 // sorted positions [q, q + kTT) of expert e when q starts a group of kTT
 // inside e's run [offsets[e], offsets[e+1]); e is the number of experts whose
 // run ends at or before q.  One round of loads over offsets[1..E] (ballot
@@ -100,12 +101,12 @@ __host__ __device__ __forceinline__ int decode_entries(int T, int k, int has_sha
 __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotInfo &si)
 {
     const int P = p.T * p.k;
-    const int nsh = p.has_shared ? (p.T + kTT - 1) / kTT : 0;
+    const int nsh = p.has_shared ? p.T : 0;
     if (s < nsh) {
         si.e = -1;
         si.ws = 0;
-        si.pbeg = kTT * s;
-        si.pend = min(kTT * s + kTT, p.T);
+        si.pbeg = s;
+        si.pend = s + 1;
         si.shared = true;
         si.dslot = -1;
         return true;

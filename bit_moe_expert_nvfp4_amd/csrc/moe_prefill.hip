@@ -776,9 +776,9 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
 {
     if (L->I % 128 || L->H % 256) {
         // the grouped GEMM tiles need I % 128 == 0 and H % 256 == 0
-        if ((int64_t)T * k + (T + 1) / 2 > 65535)
-            return fail(MOET_EUNSUPPORTED, "this batch needs the GEMV kernels (I %% 128 or H %% 256 not 0), which "
-                                            "take at most T*top_k + T/2 = 65535 entries");
+        if ((int64_t)T * k + (L->has_shared ? T : 0) > 65535)
+            return fail(MOET_EUNSUPPORTED, "this batch needs the GEMV kernels (H %% 256 not 0), which take at most "
+                                            "T*top_k (+ T with a shared expert) = 65535 work entries");
         return launch_decode(L, x, T, k, ids, w, offsets, sorted, gate, out, miss_count, ws, stream);
     }
     PrefillParams p;

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "moet_common.h"
+#include "moet_instrument.h"
 
 namespace moet {
 

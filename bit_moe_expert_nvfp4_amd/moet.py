@@ -111,6 +111,15 @@ def _need(t: torch.Tensor, dtype, name: str):
         raise TypeError(f"{name} must be a contiguous CUDA tensor of dtype {dtype}, got {t.dtype} on {t.device}")
 
 
+def _need_shape(t: torch.Tensor, dtype, shape, name: str, device_check: bool = True):
+    """ValueError unless t has this dtype and shape, then (device_check) the device/contiguity check of _need."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        got = (t.dtype, tuple(t.shape)) if isinstance(t, torch.Tensor) else type(t).__name__
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {got}")
+    if device_check:
+        _need(t, dtype, name)
+
+
 # ---------------------------------------------------------------------------
 # moet_requant
 # ---------------------------------------------------------------------------
@@ -312,20 +321,45 @@ def alloc_workspace(layer: Layer, T: int, top_k: int, device="cuda") -> torch.Te
     return torch.empty((max(n, 256),), dtype=torch.uint8, device=device)
 
 
+def _check_forward_args(layer: Layer, x, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out,
+                        workspace, miss_count):
+    """Shapes and dtypes of moe_forward's tensors against the layer (the kernels index x, out and the
+    routing arrays with the layer's H and the batch's T, top_k, so a mismatch would read or write out of
+    bounds): ValueError on a mismatch, TypeError for a tensor that is not a contiguous CUDA tensor."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != layer.H or x.shape[0] < 1:
+        raise ValueError(f"x must be [T, {layer.H}] (the layer's H), got {tuple(getattr(x, 'shape', ()))}")
+    T = int(x.shape[0])
+    if not isinstance(topk_ids, torch.Tensor) or topk_ids.dim() != 2 or topk_ids.shape[0] != T:
+        raise ValueError(f"topk_ids must be int32 [{T}, top_k], got {tuple(getattr(topk_ids, 'shape', ()))}")
+    k = int(topk_ids.shape[1])
+    spec = [(x, torch.bfloat16, (T, layer.H), "x"), (topk_ids, torch.int32, (T, k), "topk_ids"),
+            (topk_w, torch.float32, (T, k), "topk_w"), (expert_offsets, torch.int32, (layer.E + 1,), "expert_offsets"),
+            (sorted_pairs, torch.int32, (T * k,), "sorted_pairs")]
+    if gate_flags is not None:
+        spec.append((gate_flags, torch.uint8, (T,), "gate_flags"))
+    if out is not None:
+        spec.append((out, torch.bfloat16, (T, layer.H), "out"))
+    if miss_count is not None:
+        spec.append((miss_count, torch.int32, (1,), "miss_count"))
+    if workspace is not None:
+        spec.append((workspace, torch.uint8, (workspace.numel(),), "workspace"))
+    for t, dt, shape, name in spec:        # every shape first, so a mismatch is reported as such
+        _need_shape(t, dt, shape, name, device_check=False)
+    for t, dt, _, name in spec:
+        _need(t, dt, name)
+    return T, k
+
+
 def moe_forward(layer: Layer, x: torch.Tensor, topk_ids, topk_w, expert_offsets, sorted_pairs,
                 gate_flags: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, miss_count: Optional[torch.Tensor] = None) -> torch.Tensor:
-    _need(x, torch.bfloat16, "x")
-    T, H = x.shape
-    k = topk_ids.shape[1]
+    T, k = _check_forward_args(layer, x, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out,
+                               workspace, miss_count)
+    H = layer.H
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(layer, T, k, x.device)
-    if gate_flags is not None:
-        _need(gate_flags, torch.uint8, "gate_flags")
-    if miss_count is not None:
-        _need(miss_count, torch.int32, "miss_count")
     Lc = layer.c()
     _check(lib().moet_moe_forward(ctypes.byref(Lc), _ptr(x), T, k, _ptr(topk_ids), _ptr(topk_w),
                                   _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(gate_flags), _ptr(out),

@@ -313,8 +313,8 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
  * MFMA pass: the 2-bit gate/up kernel stores the fp32 pre-activations of a
  * delta expert's rows, the FP4 kernel adds D13 x_t, each product scaled by
  * its own scale2, before SwiGLU, and the FP4 down kernel adds D2 h to y),
- * else the GEMV kernels, which take at most T*top_k + ceil(T/2) = 65535 work
- * entries (MOET_EUNSUPPORTED beyond).
+ * else the GEMV kernels, which take at most T*top_k work entries, plus T
+ * with a shared expert, up to 65535 (MOET_EUNSUPPORTED beyond).
  * workspace: at least moet_moe_workspace_bytes(L, T, top_k) bytes of device
  * memory, 256-byte aligned; its contents need no initialisation.
  * Expert ids outside [0, E) and slots outside [0, n_slots) contribute
@@ -369,17 +369,6 @@ int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
 size_t moet_gate_workspace_bytes(int32_t T, int32_t V);
 int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
                          float *confidence_out, void *workspace, size_t workspace_bytes, void *stream);
-
-/*
- * moet_set_timing_events - benchmark instrumentation.  While set (per host
- * thread), every moet_moe_forward call launches its first expert kernel (the
- * gate/up kernel) with hipExtLaunchKernel and these two events, which the
- * runtime stamps at that kernel's start and end (no marker packets between
- * the launches), so the caller can time that one kernel with
- * hipEventElapsedTime.  `start` / `stop` are caller-owned hipEvent_t handles;
- * pass NULL, NULL to disable.  Returns MOET_EINVAL if only one is NULL.
- */
-int moet_set_timing_events(void *start, void *stop);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,8 @@
 """C ABI checks that need no GPU: the library loads, exports every function
-include/moet.h declares, and rejects bad arguments on the host before any
-HIP call."""
+the headers under include/ declare, and rejects bad arguments on the host
+before any HIP call."""
 import ctypes
+import glob
 import os
 import re
 
@@ -11,9 +12,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
-    txt = open(os.path.join(ROOT, "include", "moet.h")).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(moet_[a-z_0-9]+)\s*\(", txt)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        txt = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moet_[a-z_0-9]+)\s*\(", txt))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +30,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert {"moet_requant", "moet_route", "moet_moe_forward", "moet_delta_forward"} <= set(names)
+    assert {"moet_requant", "moet_route", "moet_moe_forward", "moet_delta_forward",
+            "moet_set_timing_events"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -178,3 +182,51 @@ def test_gate_workspace_bytes(L):
     assert ws(1, 4097) == 3 * 16                  # 3 chunks of 1368 (the last 1361)
     assert ws(0, 10) == 0 and ws(2, 0) == 0
     assert ws(1, 2**31 - 1) == 1024 * 16          # no int overflow at the largest V
+
+def test_gemv_fallback_grid_bound(L):
+    """Large batches whose H is not a multiple of 256 run the GEMV kernels, one grid row per routed pair
+    plus one per token of the shared expert; past 65535 rows the call is MOET_EUNSUPPORTED (host check,
+    no launch)."""
+    from bit_moe_expert_nvfp4_amd import moet
+    b = ctypes.c_void_p(256)
+    z = moet.W2(16, 16, 16)
+    lay = moet.LayerC(384, 128, 8, z, z, 1, z, z, 0, None, moet.FP4(None, None, None), moet.FP4(None, None, None),
+                      0.0, None, 0)
+    T = 65535 // 3 + 1                     # T * 2 + T = 65538 rows with the shared expert
+    assert L.moet_moe_forward(ctypes.byref(lay), b, T, 2, b, b, b, b, None, b, None, b, 1 << 40, None) == 2
+    assert b"65535" in L.moet_last_error()
+    lay.has_shared = 0
+    assert L.moet_moe_forward(ctypes.byref(lay), b, 32768, 2, b, b, b, b, None, b, None, b, 1 << 40, None) == 2
+
+
+def test_moe_forward_binding_checks_shapes():
+    """The binding compares every tensor with the layer before calling the library: a narrower x, an out
+    of the wrong shape, int64 offsets or routing arrays of the wrong length raise ValueError (the kernels
+    would index them with the layer's H and the batch's T, top_k)."""
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet
+    z = moet.W2Planes(torch.zeros(1, dtype=torch.int32), torch.zeros(1, dtype=torch.uint8), torch.zeros(1), 1, 1)
+    layer = moet.Layer(256, 128, 8, z, z)
+    T, k = 4, 2
+    good = dict(x=torch.zeros(T, 256, dtype=torch.bfloat16), topk_ids=torch.zeros(T, k, dtype=torch.int32),
+                topk_w=torch.zeros(T, k), expert_offsets=torch.zeros(9, dtype=torch.int32),
+                sorted_pairs=torch.zeros(T * k, dtype=torch.int32))
+    bad = [dict(x=torch.zeros(T, 128, dtype=torch.bfloat16)),
+           dict(x=torch.zeros(T, 256, dtype=torch.float32)),
+           dict(topk_ids=torch.zeros(T, k, dtype=torch.int64)),
+           dict(topk_ids=torch.zeros(T + 1, k, dtype=torch.int32)),
+           dict(topk_w=torch.zeros(T, k + 1)),
+           dict(expert_offsets=torch.zeros(9, dtype=torch.int64)),
+           dict(expert_offsets=torch.zeros(8, dtype=torch.int32)),
+           dict(sorted_pairs=torch.zeros(T * k - 1, dtype=torch.int32)),
+           dict(gate_flags=torch.zeros(T + 1, dtype=torch.uint8)),
+           dict(out=torch.zeros(T, 128, dtype=torch.bfloat16)),
+           dict(out=torch.zeros(T, 256, dtype=torch.float32)),
+           dict(miss_count=torch.zeros(1, dtype=torch.int64))]
+    for b in bad:
+        args = dict(good, **b)
+        with pytest.raises(ValueError):
+            moet.moe_forward(layer, **args)
+    # right shapes on CPU tensors: rejected as not on the GPU, before any library call
+    with pytest.raises(TypeError):
+        moet.moe_forward(layer, **good)

@@ -45,18 +45,18 @@ def _bit_positions():
 
 def pack_2bit_codes(codes2: np.ndarray) -> np.ndarray:
     """codes2 uint8 [N, K] (values 0..3) -> uint32 [N*K/16] in the tiled layout."""
-    c = np.asarray(codes2, dtype=np.uint64)
+    c = np.asarray(codes2, dtype=np.uint32)
     N, K = c.shape
     _check(N, K)
     pm, ps = _bit_positions()
-    m = c & 1
-    s = (c >> 1) & 1
-    # [tile, r, chunk, word, e]
-    m = m.reshape(N // TILE, TILE, K // 64, 4, 16)
-    s = s.reshape(N // TILE, TILE, K // 64, 4, 16)
-    words = ((m << pm.astype(np.uint64)) | (s << ps.astype(np.uint64))).sum(axis=-1, dtype=np.uint64)
+    c = c.reshape(N // TILE, TILE, K // 64, 4, 16)          # [tile, r, chunk, word, e]
+    c = np.ascontiguousarray(np.moveaxis(c, -1, 0))          # [e, tile, r, chunk, word]
+    words = np.zeros(c.shape[1:], dtype=np.uint32)
+    for e in range(16):
+        words |= (c[e] & 1) << np.uint32(pm[e])
+        words |= ((c[e] >> 1) & 1) << np.uint32(ps[e])
     words = words.transpose(0, 2, 1, 3)      # [tile, chunk, r, word]
-    return np.ascontiguousarray(words).reshape(-1).astype(np.uint32)
+    return np.ascontiguousarray(words).reshape(-1)
 
 
 def unpack_2bit_codes(words: np.ndarray, N: int, K: int) -> np.ndarray:

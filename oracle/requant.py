@@ -101,9 +101,12 @@ def delta(codes: np.ndarray, scales: np.ndarray, scale_2: float, codes2: np.ndar
 
 def dequant_2bit(codes2: np.ndarray, tau: np.ndarray, scale2_out: float, block: int = BLOCK) -> np.ndarray:
     """W_2bit[n,k] = level(code) * e4m3(tau[n, k//block]) * scale2_out, exact in float64."""
-    lv = LEVELS[np.asarray(codes2, dtype=np.int64)]
-    s = np.repeat(e4m3fn_value(np.asarray(tau, dtype=np.uint8)), block, axis=1)
-    return lv * s * np.float64(np.float32(scale2_out))
+    c = np.asarray(codes2)
+    N, K = c.shape
+    lv = np.take(LEVELS, c).reshape(N, K // block, block)
+    s = e4m3fn_value(np.asarray(tau, dtype=np.uint8)) * np.float64(np.float32(scale2_out))   # exact
+    lv *= s[:, :, None]
+    return lv.reshape(N, K)
 
 
 def dequant_fp4_codes(dcodes: np.ndarray, dscales: np.ndarray, dscale2: float) -> np.ndarray:

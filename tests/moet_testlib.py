@@ -44,6 +44,38 @@ class OracleMatrix:
         return OR.dequant_fp4_codes(self.dc, self.ds, self.d2)
 
 
+class ExpertPrefetch:
+    """Calls fn(e) for the experts of `order` on a thread pool, up to `window` experts ahead of the
+    caller, who then asks for them in that order (the oracle's C requantisation and numpy's large
+    array operations run without the interpreter lock).  An expert asked for out of order is computed
+    on the spot."""
+
+    def __init__(self, fn, order, window=8, workers=8):
+        from concurrent.futures import ThreadPoolExecutor
+        self.fn = fn
+        self.order = list(order)
+        self.ex = ThreadPoolExecutor(workers)
+        self.fut = {}
+        self.next = 0
+        self.window = window
+        self._fill()
+
+    def _fill(self):
+        while self.next < len(self.order) and len(self.fut) < self.window:
+            e = self.order[self.next]
+            self.fut[e] = self.ex.submit(self.fn, e)
+            self.next += 1
+
+    def __call__(self, e):
+        f = self.fut.pop(e, None)
+        r = f.result() if f is not None else self.fn(e)
+        self._fill()
+        return r
+
+    def close(self):
+        self.ex.shutdown(wait=True)
+
+
 class OracleLayer:
     """Lazily requantises the experts the oracle needs, straight from the NVFP4 bytes."""
 
@@ -53,12 +85,29 @@ class OracleLayer:
         self.soe = None if slot_of_expert is None else np_(slot_of_expert)
         self.shared_nvfp4 = shared_nvfp4
         self._cache = {}
+        self._prefetch = None
+        # host copies of the NVFP4 stacks, made once (threads then slice them without the GPU)
+        self._host = {}
+
+    def prefetch(self, experts):
+        """Compute expert_weights for these experts (ascending order) ahead of their use."""
+        if self._prefetch is not None:
+            self._prefetch.close()
+        self._host_stack(self.src.w13)       # one host copy of each stack before the threads start
+        self._host_stack(self.src.w2)
+        self._prefetch = ExpertPrefetch(self._expert_weights, sorted(int(e) for e in experts))
+
+    def _host_stack(self, stack):
+        key = id(stack)
+        if key not in self._host:
+            self._host[key] = tuple(np_(t) if isinstance(t, torch.Tensor) else t for t in stack)
+        return self._host[key]
 
     def _mat(self, stack, i, with_delta):
         key = (id(stack), i, with_delta)
         if key not in self._cache:
-            c, s, s2 = stack
-            self._cache[key] = OracleMatrix(np_(c[i]), np_(s[i]), float(s2[i]), with_delta)
+            c, s, s2 = self._host_stack(stack)
+            self._cache[key] = OracleMatrix(c[i], s[i], float(s2[i]), with_delta)
         return self._cache[key]
 
     def resident(self, e):
@@ -71,9 +120,14 @@ class OracleLayer:
         dn = self._mat(self.src.w2, e, d)
         return g, u, dn
 
-    def expert_weights(self, e):
+    def _expert_weights(self, e):
         g, u, dn = self.expert(e)
         return g.w2bit(), u.w2bit(), dn.w2bit()
+
+    def expert_weights(self, e):
+        if self._prefetch is not None:
+            return self._prefetch(e)
+        return self._expert_weights(e)
 
     def delta_weights_of_slot(self, slot):
         e = int(np.nonzero(self.soe == slot)[0][0])
@@ -114,3 +168,233 @@ def oracle_route(logits: torch.Tensor, k: int, fn: int, renorm: bool = True, sca
 
 #: floating-point bar of the method (relative L2 error of the layer output)
 REL_L2_BAR = 2e-3
+
+
+# ---------------------------------------------------------------------------
+# Element-wise comparison of the layer's intermediate rows (h, y) and output.
+# The forward's workspace holds, after a call, h = bf16(silu(g) * u) rows and
+# fp32 y rows: h by pair id on the GEMV path, by sorted position on the MFMA
+# grouped-GEMM path (the shared expert at row T*k + t on both); y by pair id.
+# ---------------------------------------------------------------------------
+def _al256(b: int) -> int:
+    return (b + 255) & ~255
+
+
+def workspace_views(ws: torch.Tensor, T: int, k: int, H: int, I: int):
+    """(h bits uint16 [T*k + T, I], y fp32 [T*k + T, H]) views of a forward's workspace."""
+    rows = T * k + T
+    hb = ws[:rows * I * 2].view(torch.int16).view(rows, I)
+    off = _al256(rows * I * 2)
+    y = ws[off:off + rows * H * 4].view(torch.float32).view(rows, H)
+    return hb, y
+
+
+def mfma_path(T: int, k: int, H: int) -> bool:
+    """Whether moet_moe_forward runs the grouped-GEMM kernels for this batch (else the GEMV kernels)."""
+    return T * k > 1024 and H % 256 == 0
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |v| (subnormal spacing below 2^-126)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    return np.exp2(np.maximum(ex - 1, -126) - 7.0)
+
+
+class ElementCheck:
+    """Accumulates element-wise differences between GPU and oracle rows.
+
+    h (bf16): an element passes when it equals the oracle's, or is its bf16
+    neighbour of the same sign (the fp32 sum landed on the other side of a
+    rounding boundary), or differs by at most 2^-14 of its row's rms (sign
+    flips of values near zero after cancellation).  The number of non-equal
+    elements is reported.
+    y, out: |gpu - oracle| <= bound, an element-wise bound given by the caller
+    (the propagated h differences plus the fp32 accumulation error).
+    """
+
+    def __init__(self, name: str):
+        self.name = name
+        self.n = 0
+        self.n_diff = 0
+        self.bad = []
+        self.worst = 0.0     # largest |gpu - oracle| / bound
+
+    def h_rows(self, gpu_bits: np.ndarray, ref_bits: np.ndarray, tag=""):
+        g = np.asarray(gpu_bits, dtype=np.uint16).astype(np.int64)
+        r = np.asarray(ref_bits, dtype=np.uint16).astype(np.int64)
+        a, b = OF.bf16_bits_to_f64(g), OF.bf16_bits_to_f64(r)
+        rms = np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
+        diff = g != r
+        adjacent = ((g & 0x8000) == (r & 0x8000)) & (np.abs(g - r) == 1)
+        tiny = np.abs(a - b) <= 2.0 ** -14 * rms
+        bad = diff & ~adjacent & ~tiny
+        self.n += g.size
+        self.n_diff += int(diff.sum())
+        if bad.any():
+            idx = np.argwhere(bad)[:5]
+            self.bad += [(tag, tuple(i), float(a[tuple(i)]), float(b[tuple(i)])) for i in idx]
+        return self
+
+    def f_rows(self, gpu: np.ndarray, ref: np.ndarray, bound: np.ndarray, tag=""):
+        a = np.asarray(gpu, dtype=np.float64)
+        b = np.asarray(ref, dtype=np.float64)
+        err = np.abs(a - b)
+        bad = err > bound
+        self.n += a.size
+        self.n_diff += int((a != b).sum())
+        if a.size:
+            self.worst = max(self.worst, float(np.max(err / np.maximum(bound, 1e-300))))
+        if bad.any():
+            idx = np.argwhere(bad)[:5]
+            self.bad += [(tag, tuple(i), float(a[tuple(i)]), float(b[tuple(i)]), float(bound[tuple(i)]))
+                         for i in idx]
+        return self
+
+    def report(self) -> str:
+        frac = self.n_diff / max(self.n, 1)
+        return (f"{self.name}: {self.n} elements, {self.n_diff} not identical ({frac:.2e}), "
+                f"worst |d|/bound {self.worst:.2e}, {len(self.bad)} outside the bound")
+
+
+#: fp32 accumulation error allowed, as a fraction of the sum of |terms| (a 2048-long K loop in
+#: steps of 16 rounds about 130 times: 130 * 2^-24 = 7.7e-6, well inside 2^-14 = 6.1e-5)
+ACC_REL = 2.0 ** -14
+#: error of the combine's fp32 sum (k + 1 terms, routing weights rounded to fp32), relative to sum |w y|
+COMBINE_REL = 2.0 ** -16
+#: non-identical h elements allowed (one-ulp neighbours), as a fraction of the compared elements
+H_DIFF_FRAC = 2e-3
+
+
+def alarm_rel_l2(H: int) -> float:
+    """Tighter-than-bar rel-L2 alarm: h rounding flips grow with the reduction length, so the alarm
+    scales with H, capped at half the bar."""
+    return min(3e-4 * max(1.0, H / 512), 0.5 * REL_L2_BAR)
+
+
+def oracle_pair_rows(ol: "OracleLayer", x_bits: np.ndarray, ids: np.ndarray, gate_flags=None, experts=None,
+                     resident=None, with_shared=True):
+    """Yield (pair ids or None for shared, tokens, h bits [n, I], y float64 [n, H], |W_d| (+ |D_d|) [H, I])
+    from the oracle, expert by expert (only experts in ``experts`` when given; missing experts of an
+    expert cache are skipped, their rows are never written)."""
+    x = OF.bf16_bits_to_f64(x_bits)
+    T, k = ids.shape
+    L = ol.cfg.swiglu_limit
+    by_e = {}
+    for p in range(T * k):
+        by_e.setdefault(int(ids[p // k, p % k]), []).append(p)
+    for e in sorted(by_e):
+        if experts is not None and e not in experts:
+            continue
+        if resident is not None and not resident[e]:
+            continue
+        Wg, Wu, Wd = ol.expert_weights(e)
+        pairs = np.array(by_e[e], dtype=np.int64)
+        toks = pairs // k
+        flag = np.zeros(len(pairs), dtype=bool)
+        if gate_flags is not None and ol.soe is not None and ol.soe[e] >= 0:
+            flag = np.asarray(gate_flags)[toks] != 0
+        for sel, use_d in ((~flag, False), (flag, True)):
+            if not sel.any():
+                continue
+            if use_d:
+                Dg, Du, Dd = ol.delta_weights_of_slot(int(ol.soe[e]))
+            else:
+                Dg = Du = Dd = None
+            h = OFF.expert_hidden(x[toks[sel]], Wg, Wu, L, Dg, Du)
+            y = OFF.expert_out(h, Wd, Dd)
+            absw = np.abs(Wd) if Dd is None else np.abs(Wd) + np.abs(Dd)
+            yield pairs[sel], toks[sel], OF.bf16_rne_bits(h), y, absw
+    sh = ol.shared_weights() if with_shared else None
+    if sh is not None:
+        h = OFF.expert_hidden(x, sh[0], sh[1], L)
+        yield None, np.arange(T), OF.bf16_rne_bits(h), OFF.expert_out(h, sh[2]), np.abs(sh[2])
+
+
+class PairRows:
+    """Result of check_pair_rows: the h / y checks and, per pair (and per token for the shared
+    expert), the element-wise bound on y that carries over to the layer output."""
+
+    def __init__(self):
+        self.h = ElementCheck("h")
+        self.y = ElementCheck("y")
+        self.ybound = {}       # pair id -> bound on |y_gpu - y_oracle| + COMBINE_REL |y_oracle|
+        self.ybound_sh = {}    # token -> the same for the shared expert's y
+
+
+def check_pair_rows(ws: torch.Tensor, ol: "OracleLayer", x_bits, ids, sorted_pairs, H, I, gate_flags=None,
+                    experts=None, resident=None, with_shared=True, out_tokens=None) -> PairRows:
+    """Compare the workspace's h and y rows with the oracle's, element by element.
+
+    h: each element equal to the oracle's or its bf16 neighbour (ElementCheck.h_rows).
+    y: |y_gpu - y_oracle| <= |W_d| |h_gpu - h_oracle| + ACC_REL |W_d| |h_oracle| per element: the h
+    elements that landed one ulp away carry through the down projection, plus the fp32 accumulation
+    error.  The bounds of the pairs of ``out_tokens`` are kept for check_out_rows."""
+    T, k = ids.shape
+    hb, y = workspace_views(ws, T, k, H, I)
+    hb = np_(hb).astype(np.uint16)
+    y = np_(y)
+    if mfma_path(T, k, H):
+        row_of_pair = np.empty(T * k, dtype=np.int64)
+        row_of_pair[np.asarray(sorted_pairs, dtype=np.int64)] = np.arange(T * k)
+    else:
+        row_of_pair = np.arange(T * k)
+    keep = set(range(T)) if out_tokens is None else set(int(t) for t in out_tokens)
+    res = PairRows()
+    for pairs, toks, h_ref, y_ref, absw in oracle_pair_rows(ol, x_bits, ids, gate_flags, experts, resident,
+                                                           with_shared):
+        if pairs is None:
+            hr = yr = T * k + toks
+            tag = "shared"
+        else:
+            hr = row_of_pair[pairs]
+            yr = pairs
+            tag = f"expert {int(ids[pairs[0] // k, pairs[0] % k])}"
+        hg = hb[hr]
+        res.h.h_rows(hg, h_ref, tag)
+        dh = np.abs(OF.bf16_bits_to_f64(hg) - OF.bf16_bits_to_f64(h_ref))
+        bound = dh @ absw.T + ACC_REL * (np.abs(OF.bf16_bits_to_f64(h_ref)) @ absw.T)
+        res.y.f_rows(y[yr], y_ref, bound, tag)
+        carry = bound + COMBINE_REL * np.abs(y_ref)
+        for i, t in enumerate(toks):
+            if int(t) in keep:
+                if pairs is None:
+                    res.ybound_sh[int(t)] = carry[i]
+                else:
+                    res.ybound[int(pairs[i])] = carry[i]
+    return res
+
+
+def check_out_rows(gpu_bits: np.ndarray, ref_bits: np.ndarray, tokens=None, topk_w=None, rows: PairRows = None,
+                   resident=None, ids=None) -> ElementCheck:
+    """Layer output against the oracle's.  With the per-pair y bounds of check_pair_rows the bound is
+    sum_j |w_j| bound_y(t, j) + bound_y_shared(t) + 1.5 bf16 ulps of the oracle value (each side rounds
+    once, by at most half an ulp of its own binade, and the GPU value may sit one binade up); without
+    them (a test that has no rows) it is 2^-7 of the row's rms plus 1.5 ulps, which still rejects any
+    wrong column or row (errors of the order of the rms)."""
+    a = OF.bf16_bits_to_f64(gpu_bits)
+    b = OF.bf16_bits_to_f64(ref_bits)
+    if rows is None:
+        rms = np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
+        bound = 2.0 ** -7 * rms + 1.5 * ulp_bf16(b)
+    else:
+        k = topk_w.shape[1]
+        bound = 1.5 * np.array(ulp_bf16(b), dtype=np.float64)
+        for i, t in enumerate(tokens):
+            for j in range(k):
+                p = int(t) * k + j
+                if resident is not None and not resident[int(ids[t, j])]:
+                    continue
+                bound[i] += abs(float(topk_w[t, j])) * rows.ybound[p]
+            if int(t) in rows.ybound_sh:
+                bound[i] += rows.ybound_sh[int(t)]
+    return ElementCheck("out").f_rows(a, b, bound)
+
+
+def assert_elementwise(*checks: ElementCheck, h_frac: float = H_DIFF_FRAC):
+    for c in checks:
+        print(c.report(), flush=True)
+    for c in checks:
+        assert not c.bad, f"{c.name}: elements outside the bound, e.g. {c.bad[:3]}"
+        if c.name == "h":
+            assert c.n_diff <= h_frac * c.n + 8, f"h: {c.n_diff} of {c.n} elements differ"

@@ -96,6 +96,47 @@ constexpr int kDecodeMaxPairs = 1024;
 
 static bool use_decode(int T, int k) { return (int64_t)T * k <= kDecodeMaxPairs; }
 
+// Checks of moet_moe_forward's arguments other than the workspace (host only, no HIP call).
+int check_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k, const int32_t *topk_ids,
+                  const float *topk_w, const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                  const uint8_t *gate_flags, const uint16_t *out, const int32_t *miss_count)
+{
+    int rc = check_layer(L);
+    if (rc != MOET_OK) return rc;
+    if (T < 1 || T > 65536) return fail(MOET_EINVAL, "T (%d) must be in [1, 65536]", T);
+    if (top_k < 1 || top_k > L->E || top_k > 16) return fail(MOET_EINVAL, "top_k (%d) must be in [1, min(E, 16)]", top_k);
+    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(expert_offsets) ||
+        !aligned16(sorted_pairs) || !aligned16(out))
+        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
+    if (gate_flags && !aligned16(gate_flags)) return fail(MOET_EINVAL, "gate_flags must be 16-byte aligned");
+    if (miss_count && (reinterpret_cast<uintptr_t>(miss_count) & 3u)) return fail(MOET_EINVAL, "miss_count must be 4-byte aligned");
+    return MOET_OK;
+}
+
+size_t forward_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k)
+{
+    if (!L || T < 1 || top_k < 1 || L->H <= 0 || L->I <= 0 || L->E < 1) return 0;
+    if (use_decode(T, top_k)) return decode_workspace_bytes(T, top_k, L->H, L->I);
+    return prefill_workspace_bytes(T, top_k, L->H, L->I, L->E);
+}
+
+// The workspace checks, then the decode (GEMV) or prefill (grouped-GEMM) launches.
+int dispatch_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k, const int32_t *topk_ids,
+                     const float *topk_w, const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                     const uint8_t *gate_flags, uint16_t *out, int32_t *miss_count, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream)
+{
+    const size_t need = forward_workspace_bytes(L, T, top_k);
+    if (!workspace || workspace_bytes < need)
+        return fail(MOET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOET_EINVAL, "workspace must be 256-byte aligned");
+    if (use_decode(T, top_k))
+        return launch_decode(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count,
+                             workspace, stream);
+    return launch_prefill(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count,
+                          workspace, stream);
+}
+
 }  // namespace moet
 
 using namespace moet;
@@ -207,9 +248,7 @@ int moet_route(const float *logits, int32_t T, int32_t E, int32_t top_k, int32_t
 
 size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k)
 {
-    if (!L || T < 1 || top_k < 1 || L->H <= 0 || L->I <= 0 || L->E < 1) return 0;
-    if (use_decode(T, top_k)) return decode_workspace_bytes(T, top_k, L->H, L->I);
-    return prefill_workspace_bytes(T, top_k, L->H, L->I, L->E);
+    return forward_workspace_bytes(L, T, top_k);
 }
 
 int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k, const int32_t *topk_ids,
@@ -218,24 +257,10 @@ int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t 
                      size_t workspace_bytes, void *stream)
 {
     g_err[0] = 0;
-    int rc = check_layer(L);
+    int rc = check_forward(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count);
     if (rc != MOET_OK) return rc;
-    if (T < 1 || T > 65536) return fail(MOET_EINVAL, "T (%d) must be in [1, 65536]", T);
-    if (top_k < 1 || top_k > L->E || top_k > 16) return fail(MOET_EINVAL, "top_k (%d) must be in [1, min(E, 16)]", top_k);
-    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(expert_offsets) ||
-        !aligned16(sorted_pairs) || !aligned16(out))
-        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
-    if (gate_flags && !aligned16(gate_flags)) return fail(MOET_EINVAL, "gate_flags must be 16-byte aligned");
-    if (miss_count && (reinterpret_cast<uintptr_t>(miss_count) & 3u)) return fail(MOET_EINVAL, "miss_count must be 4-byte aligned");
-    const size_t need = moet_moe_workspace_bytes(L, T, top_k);
-    if (!workspace || workspace_bytes < need)
-        return fail(MOET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MOET_EINVAL, "workspace must be 256-byte aligned");
-    if (use_decode(T, top_k))
-        return launch_decode(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count,
-                             workspace, (hipStream_t)stream);
-    return launch_prefill(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count,
-                          workspace, (hipStream_t)stream);
+    return dispatch_forward(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out,
+                            miss_count, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int moet_set_timing_events(void *start, void *stop)

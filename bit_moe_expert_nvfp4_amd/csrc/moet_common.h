@@ -136,4 +136,14 @@ int fail(int status, const char *fmt, ...);
 int check_launch(const char *what);
 bool aligned16(const void *p);
 bool timing_events(hipEvent_t *start, hipEvent_t *stop);  // the caller's timing events, if set
+
+// moet_moe_forward in two halves: argument checks (host only), then the workspace checks and launches
+int check_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k, const int32_t *topk_ids,
+                  const float *topk_w, const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                  const uint8_t *gate_flags, const uint16_t *out, const int32_t *miss_count);
+size_t forward_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
+int dispatch_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k, const int32_t *topk_ids,
+                     const float *topk_w, const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                     const uint8_t *gate_flags, uint16_t *out, int32_t *miss_count, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 }  // namespace moet

@@ -80,6 +80,9 @@ def lib():
         L.moet_moe_forward.argtypes = [ctypes.POINTER(LayerC), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, ctypes.c_size_t, _vp]
         L.moet_moe_forward.restype = ctypes.c_int
+        L.moet_moe_forward_noalloc.argtypes = [ctypes.POINTER(LayerC), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                               _vp, _vp, _vp]
+        L.moet_moe_forward_noalloc.restype = ctypes.c_int
         L.moet_delta_forward.argtypes = [ctypes.POINTER(FP4), _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp]
         L.moet_delta_forward.restype = ctypes.c_int
         L.moet_confidence_gate.argtypes = [_vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -364,6 +367,24 @@ def moe_forward(layer: Layer, x: torch.Tensor, topk_ids, topk_w, expert_offsets,
     _check(lib().moet_moe_forward(ctypes.byref(Lc), _ptr(x), T, k, _ptr(topk_ids), _ptr(topk_w),
                                   _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(gate_flags), _ptr(out),
                                   _ptr(miss_count), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+#: bytes of the static scratch of moe_forward_noalloc (MOET_NOALLOC_SCRATCH_BYTES in include/moet.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def moe_forward_noalloc(layer: Layer, x: torch.Tensor, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                        out: torch.Tensor, gate_flags: Optional[torch.Tensor] = None,
+                        miss_count: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moet_moe_forward_noalloc: the layer forward with the library's static scratch instead of a
+    workspace; the caller passes every input and the output (nothing is allocated)."""
+    T, k = _check_forward_args(layer, x, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out,
+                               None, miss_count)
+    Lc = layer.c()
+    _check(lib().moet_moe_forward_noalloc(ctypes.byref(Lc), _ptr(x), T, k, _ptr(topk_ids), _ptr(topk_w),
+                                          _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(gate_flags), _ptr(out),
+                                          _ptr(miss_count), _stream()))
     return out
 
 

@@ -330,6 +330,29 @@ int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t 
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * moet_moe_forward_noalloc - moet_moe_forward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts that
+ * forbid allocation.  It allocates nothing and takes no workspace: the h and
+ * y rows the kernels pass between launches live in a static device array of
+ * the library, MOET_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends.  Arguments, results
+ * and errors are those of moet_moe_forward (same kernels, bitwise the same
+ * output), except that a batch whose moet_moe_workspace_bytes exceeds
+ * MOET_NOALLOC_SCRATCH_BYTES returns MOET_EWORKSPACE before any HIP call
+ * (16 MiB holds decode steps up to T * (top_k + 1) = 500 at H = 7168,
+ * I = 2048).  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents: calls that overlap on one GPU (other streams or
+ * threads) race and must be ordered by the caller.  The first call on each
+ * device looks up the array's device address (hipGetSymbolAddress).
+ */
+#define MOET_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int moet_moe_forward_noalloc(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
+                             const int32_t *topk_ids, const float *topk_w,
+                             const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                             const uint8_t *gate_flags, uint16_t *out, int32_t *miss_count,
+                             void *stream);
+
+/*
  * moet_delta_forward - standalone FP4 delta GEMM/GEMV accumulate.
  * (README "Frontier MoE on consumer Blackwell (SM120)", section "How it fits".)
  *

@@ -33,15 +33,16 @@
 //  * down kernel: 256 output features per workgroup, y (fp32) scattered to
 //    the pair's row for the shared combine kernel.
 //  * FP4 operand (README "How it fits": FP4 delta GEMM for gate-flagged tokens
-//    on delta-cache experts; a shared expert kept in NVFP4): the same pipeline
-//    with a B stage of two 32-k FP4 chunks per row and one dword of four
-//    block-16 scales.  One MFMA k-step is exactly one block-16, so a lane
-//    dequantises its 8 values as e2m1 -> f32 -> * scale -> bf16, exact
-//    (e2m1 * e4m3 has at most 6 significant bits).  FP4 work runs in kernels
-//    of its own after the 2-bit ones: for a tile with gate-flagged rows, the
-//    2-bit gate/up kernel leaves fp32 pre-activations, the FP4 kernel adds the
-//    delta (rows of unflagged tokens zeroed in registers) and applies SwiGLU;
-//    the FP4 down kernel adds its y to the 2-bit y.
+//    on delta-cache experts; a shared expert kept in NVFP4): a partition step
+//    reorders each delta expert's run of pairs so that its gate-flagged pairs
+//    come first.  The 2-bit kernels run every expert's whole run and leave the
+//    fp32 pre-activations of the flagged rows; FP4 kernels of their own then
+//    run only the flagged rows, 128 per tile, so no MFMA multiplies a row that
+//    takes no delta: gate/up adds the delta and applies SwiGLU, down adds its
+//    product to y.  One MFMA k-step is one FP4 block-16: a lane dequantises its
+//    8 values as e2m1 -> f32 -> * scale -> bf16, exact (e2m1 * e4m3 has at
+//    most 6 significant bits).  An NVFP4 shared expert's tiles run only in the
+//    FP4 kernels.
 #include <algorithm>
 
 #include "moet_common.h"
@@ -67,12 +68,13 @@ struct PrefillParams {
     moet_w2 w13, w2, sh13, sh2;
     int has_shared;
     float swiglu_limit;
-    uint16_t *h;        // [P + T][I] bf16, rows in sorted-pair order (shared expert: P + t)
+    uint16_t *h;        // [P + T][I] bf16, rows in `order` (shared expert: P + t)
     float *ypart;       // [P + T][H] fp32, rows by pair id (shared expert: P + t)
-    float *pre;         // [P + T][2I] fp32 gate/up pre-activations of delta tiles (aliases ypart)
+    float *pre;         // [P][2I] fp32 gate/up pre-activations of flagged rows, rows in `order` (aliases ypart)
     uint16_t *out;
+    const int32_t *order;   // the pairs in expert order, a delta expert's flagged pairs first (= sorted without delta)
+    const int32_t *nflag;   // per expert: its flagged pairs at the head of its run in `order` (null: none)
     int n_mslots;       // upper bound on 160-row M-tiles (grid of the 2-bit kernels)
-    int n_mslots4;      // upper bound on 128-row M-tiles (grid of the FP4 kernels)
     int n_ntiles;
     const int32_t *base_slot;   // expert -> cache slot of w13/w2 (null: expert e at e)
     int n_base_slots;
@@ -95,13 +97,15 @@ __device__ __forceinline__ int weight_slot(const PrefillParams &p, int e)
 
 struct MTile {
     int e;        // expert, or -1 for the shared expert
-    int row0;     // first row in sorted order (shared: first token)
+    int row0;     // first row in `order` (shared: first token)
     int rows;     // valid rows (<= the tile size)
+    int fl_end;   // rows of `order` below this take the FP4 delta (the flagged head of a delta expert's run)
 };
 
-// M-tile number ms -> (expert, rows).  Tiles of PM rows are enumerated expert
-// by expert (ceil(count / PM) each), then the shared expert's tiles.  One
-// wavefront computes it: per-lane tile counts, inclusive scan, ballot search.
+// M-tile number ms -> (expert, rows) of the 2-bit kernels.  Tiles of PM rows
+// are enumerated expert by expert over its run in `order` (ceil(count / PM)
+// each), then the 2-bit shared expert's tiles.  One wavefront computes it:
+// per-lane tile counts, inclusive scan, ballot search.
 template <int PM>
 __device__ bool locate_mtile(const PrefillParams &p, int ms, MTile &mt)
 {
@@ -133,16 +137,18 @@ __device__ bool locate_mtile(const PrefillParams &p, int ms, MTile &mt)
             mt.e = ee;
             mt.row0 = oo + t * kPM;
             mt.rows = min(kPM, cc - t * kPM);
+            mt.fl_end = oo + (p.nflag ? p.nflag[ee] : 0);
             return true;
         }
         base += __shfl(incl, 63, 64);
     }
-    if (p.has_shared) {
+    if (p.has_shared && !p.shared_fp4) {
         const int t = ms - base;
         if (t >= 0 && t * kPM < p.T) {
             mt.e = -1;
             mt.row0 = t * kPM;
             mt.rows = min(kPM, p.T - t * kPM);
+            mt.fl_end = 0;
             return true;
         }
     }
@@ -324,28 +330,238 @@ __device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, con
 }
 
 // ---------------------------------------------------------------------------
-// FP4 operand pipeline.  Per stage and wavefront: the same kASeg A segments, two
-// B chunks (32-k FP4 chunks 2s and 2s+1 of the wave's 64 storage rows, 1 KiB
-// each) and one scale dword per row (the four block-16 scales of the step).
+// Partition of the delta experts' rows.  One workgroup per expert e: its run
+// [offsets[e], offsets[e+1]) of sorted pairs is copied to `order`, with the
+// pairs of gate-flagged tokens first when e takes the FP4 delta (both parts
+// keep their order), and nflag[e] = the number of flagged pairs (0 when e
+// takes no delta).  e takes the delta when it holds a delta-cache slot that no
+// lower expert holds and its 2-bit planes are resident.  Each thread owns a
+// contiguous range of the run: one pass counts its flagged pairs, a block-wide
+// exclusive scan gives its first slots, a second pass writes its pairs.
 // ---------------------------------------------------------------------------
-constexpr int kPM4 = 128;                      // rows per FP4 M-tile (4 MFMA blocks: 2 waves per SIMD)
-constexpr int kPMB4 = kPM4 / 32;
-constexpr int kASeg4 = kPM4 / 32;
-constexpr int kStageA4 = kPM4 * 128;
-constexpr int kStageB4 = 8 * 1024;
-constexpr int kStage4 = kStageA4 + kStageB4 + kStageS;
-constexpr int kDmaPerStage4 = kASeg4 + 3;
-
-__device__ __forceinline__ void issue_stage4(const PipeSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
+__device__ __forceinline__ int delta_slot_of(const PrefillParams &p, int e)
 {
-    const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kStage4);
+    const int lane = threadIdx.x & 63;
+    const int ds = p.slot_of_expert[e];
+    if (ds < 0 || ds >= p.n_slots || weight_slot(p, e) < 0) return -1;
+    bool lower = false;
+    for (int i = lane; i < e; i += 64) lower |= p.slot_of_expert[i] == ds;
+    return __ballot(lower) ? -1 : ds;
+}
+
+__global__ __launch_bounds__(256) void partition_kernel(PrefillParams p, int32_t *__restrict__ order,
+                                                        int32_t *__restrict__ nflag)
+{
+    __shared__ int s_cnt[4];
+    __shared__ int s_delta;
+    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int P = p.T * p.k;
+    if (wave == 0) {
+        const int ds = delta_slot_of(p, e);
+        if (lane == 0) s_delta = ds >= 0;
+    }
+    __syncthreads();
+    const bool delta = s_delta != 0;
+    const int o0 = p.offsets[e], o1 = p.offsets[e + 1], n = o1 - o0;
+    const int per = (n + 255) / 256;
+    const int b0 = o0 + min(tid * per, n), b1 = o0 + min(tid * per + per, n);
+    int f = 0;
+    if (delta)
+        for (int i = b0; i < b1; ++i) f += p.gate[min(max(p.sorted[i], 0), P - 1) / p.k] != 0;
+    int inc = f;
 #pragma unroll
-    for (int i = 0; i < kASeg4; ++i)
-        dma16(src.arow[i] + (size_t)s * 128 + a_dma_col(lane, kASeg4 * wave + i) * 16,
-              base + (uint32_t)((kASeg4 * wave + i) * 1024));
-    dma16(src.bsrc + ((size_t)(2 * s) * 64 + lane) * 16, base + kStageA4 + wave * 2048);
-    dma16(src.bsrc + ((size_t)(2 * s + 1) * 64 + lane) * 16, base + kStageA4 + wave * 2048 + 1024);
-    dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 8 + (s & 1) * 4, base + kStageA4 + kStageB4 + wave * 256);
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += v;
+    }
+    if (lane == 63) s_cnt[wave] = inc;
+    __syncthreads();
+    int before = inc - f;
+    for (int w = 0; w < wave; ++w) before += s_cnt[w];
+    const int F = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    int fi = o0 + before, ui = o0 + F + (b0 - o0) - before;
+    for (int i = b0; i < b1; ++i) {
+        const int pr = p.sorted[i];
+        const bool fl = delta && p.gate[min(max(pr, 0), P - 1) / p.k] != 0;
+        if (fl) order[fi++] = pr;
+        else order[ui++] = pr;
+    }
+    if (tid == 0) nflag[e] = F;
+}
+
+// gate/up + SwiGLU.  N-tile nt covers h columns [128 nt, 128 nt + 128); wave w
+// owns gate rows and up rows [128 nt + 32 w, + 32).
+__device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t *smem)
+{
+    int ms, nt;
+    decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
+    if (ms >= p.n_mslots) return;
+    MTile mt;
+    if (!locate_mtile<kPM>(p, ms, mt)) return;
+    const int nmb = (mt.rows + 31) / 32;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = p.H, I = p.I, P = p.T * p.k;
+    // A rows fetched by this lane: segment i of wave w holds rows 8(nmb w + i) .. +7; lane -> row + lane/8
+    // (only the nmb valid 32-row blocks are staged)
+    PipeSrc src;
+    src.K = H;
+#pragma unroll
+    for (int i = 0; i < kASeg; ++i) {
+        const int r = min(8 * (nmb * wave + i) + (lane >> 3), mt.rows - 1);
+        int tok;
+        if (mt.e >= 0) tok = min(max(p.order[mt.row0 + r], 0), P - 1) / p.k;
+        else tok = mt.row0 + r;
+        src.arow[i] = reinterpret_cast<const uint8_t *>(p.x + (size_t)tok * H);
+    }
+    // B: 256 rows = gate rows [128 nt, +128) then up rows [128 nt, +128); wave w fetches storage tile w
+    const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
+    if (ws < 0) return;   // missing expert: no work, the combine skips its routings
+    const int jl = 32 * wave + (lane & 31);          // h column within the tile
+    const int j = 128 * nt + jl;
+    const int brow[2] = {jl, 128 + jl};               // gate row, up row in the stage
+    f32x16 acc[kPMB][2];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+    const moet_w2 &W = (mt.e >= 0) ? p.w13 : p.sh13;
+    const int m0 = (mt.e >= 0) ? 2 * ws : 0;
+    const int mat = m0 + (wave >> 1);
+    const int tile = 2 * nt + (wave & 1);
+    src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)mat * I * H / 16) + (size_t)tile * (H / 64) * 1024;
+    src.ssrc = W.scales + (size_t)mat * I * H / 32 + (size_t)tile * (H / 128) * 256;
+    gemm_pipe(src, smem, brow, acc, nmb);
+    const float sg = W.scale2[m0], su = W.scale2[m0 + 1];
+    const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb) {
+        if (mb >= nmb) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (r < mt.rows) {
+                float g = acc[mb][0][v] * sg, u = acc[mb][1][v] * su;
+                if (rowbase + r < mt.fl_end) {   // flagged row: the FP4 kernel adds its delta, then SwiGLU
+                    float *pre = p.pre + (size_t)(rowbase + r) * (2 * I) + j;
+                    pre[0] = g;
+                    pre[I] = u;
+                    continue;
+                }
+                if (p.swiglu_limit > 0.f) {
+                    g = fminf(g, p.swiglu_limit);
+                    u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+                }
+                p.h[(size_t)(rowbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc1_prefill_kernel(PrefillParams p)
+{
+    __shared__ __align__(1024) uint8_t smem[kPS * kStage];
+    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0) *p.miss_count = 0;   // counted by the combine
+    fc1_prefill_body(p, smem);
+}
+
+// down: N-tile nt covers output features [256 nt, 256 nt + 256); wave w owns 64 of them.
+__device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t *smem)
+{
+    int ms, nt;
+    decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
+    if (ms >= p.n_mslots) return;
+    MTile mt;
+    if (!locate_mtile<kPM>(p, ms, mt)) return;
+    const int nmb = (mt.rows + 31) / 32;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = p.H, I = p.I, P = p.T * p.k;
+    const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;
+    PipeSrc src;
+    src.K = I;
+#pragma unroll
+    for (int i = 0; i < kASeg; ++i) {
+        const int r = min(8 * (nmb * wave + i) + (lane >> 3), mt.rows - 1);
+        src.arow[i] = reinterpret_cast<const uint8_t *>(p.h + (size_t)(rowbase + r) * I);
+    }
+    const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
+    if (ws < 0) return;
+    const int tile = 4 * nt + wave;
+    const int brow[2] = {64 * wave + (lane & 31), 64 * wave + 32 + (lane & 31)};
+    f32x16 acc[kPMB][2];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+    const moet_w2 &W = (mt.e >= 0) ? p.w2 : p.sh2;
+    const int m0 = (mt.e >= 0) ? ws : 0;
+    src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
+    src.ssrc = W.scales + (size_t)m0 * H * I / 32 + (size_t)tile * (I / 128) * 256;
+    gemm_pipe(src, smem, brow, acc, nmb);
+    const float s2 = W.scale2[m0];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb) {
+        if (mb >= nmb) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (r < mt.rows) {
+                const int prow = (mt.e >= 0) ? min(max(p.order[mt.row0 + r], 0), P - 1) : P + mt.row0 + r;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) p.ypart[(size_t)prow * H + 256 * nt + brow[nb]] = acc[mb][nb][v] * s2;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc2_prefill_kernel(PrefillParams p)
+{
+    __shared__ __align__(1024) uint8_t smem[kPS * kStage];
+    fc2_prefill_body(p, smem);
+}
+
+// ---------------------------------------------------------------------------
+// FP4 pass.  Delta tiles hold the gate-flagged rows of a delta expert (the
+// head of its run in `order`), up to 128 per tile, so no MFMA multiplies a row
+// that takes no delta; an NVFP4 shared expert's tiles hold 128 tokens.  Per
+// stage and wavefront the LDS-DMA ring carries the tile's valid A segments and
+// the wave's two 32-k FP4 chunks and FP4 scale dword.  gate/up adds the delta
+// to the 2-bit pre-activations the 2-bit kernel left for these rows and
+// applies SwiGLU; down adds its product to the 2-bit y.
+// ---------------------------------------------------------------------------
+#ifndef MOET_FP4_TILE
+#define MOET_FP4_TILE 128
+#endif
+constexpr int kDM = MOET_FP4_TILE;            // rows per FP4 M-tile (64 or 128)
+constexpr int kDMB = kDM / 32;                // MFMA row blocks
+constexpr int kDSeg = kDM / 32;               // 8-row A segments per wavefront (4 waves x kDSeg x 8 = kDM rows)
+constexpr int kDStageA = kDM * 128;
+constexpr int kDOffB4 = kDStageA;
+constexpr int kDOffS4 = kDOffB4 + 8 * 1024;
+constexpr int kDStage = kDOffS4 + 4 * 256;    // 25 KiB at 128 rows, 17 KiB at 64
+constexpr int kDWaves = kDM == 64 ? 3 : 2;    // waves per SIMD: workgroups per CU the LDS ring allows
+
+struct DeltaSrc {
+    const uint8_t *arow[kDSeg];   // this lane's A source rows, one per A segment it fetches
+    const uint8_t *b4, *s4;       // this wave's FP4 storage tile: codes, scales (row = lane)
+    int K;
+};
+
+// DMA of pipeline step s into stage buffer `stage` (NSEG valid A segments per wave)
+template <int NSEG>
+__device__ __forceinline__ void issue_dstage(const DeltaSrc &src, uint8_t *smem, int stage, int s, int wave, int lane)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)(smem + stage * kDStage);
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i)
+        dma16(src.arow[i] + (size_t)s * 128 + a_dma_col(lane, NSEG * wave + i) * 16,
+              base + (uint32_t)((NSEG * wave + i) * 1024));
+    dma16(src.b4 + ((size_t)(2 * s) * 64 + lane) * 16, base + kDOffB4 + wave * 2048);
+    dma16(src.b4 + ((size_t)(2 * s + 1) * 64 + lane) * 16, base + kDOffB4 + wave * 2048 + 1024);
+    dma4(src.s4 + ((size_t)(s >> 1) * 64 + lane) * 8 + (s & 1) * 4, base + kDOffS4 + wave * 256);
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -374,325 +590,239 @@ __device__ __forceinline__ bf16x8 deq_fp4(uint32_t w, float sc)
 template <int Q>
 __device__ __forceinline__ float fp8_byte(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8(w, Q); }
 
-// one MFMA k-step (16 k = one FP4 block) of the FP4 pipeline
+// one MFMA k-step (16 k = one FP4 block)
 template <int NMB, int Q>
-__device__ __forceinline__ void fp4_kstep(const uint8_t *aT, const uint8_t *bT, const int boff[2], const uint32_t sw[2],
-                                          uint32_t rmask, f32x16 acc[kPMB4][2])
+__device__ __forceinline__ void fp4_kstep(const uint8_t *stg, const int boff[2], const uint32_t sw4[2],
+                                          f32x16 acc[kDMB][2])
 {
     const int lane = threadIdx.x & 63, h = lane >> 5;
-    bf16x8 bfr[2];
+    bf16x8 b4[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-        const uint32_t wv = *reinterpret_cast<const uint32_t *>(bT + boff[nb] + (Q >> 1) * 1024 + (Q & 1) * 8);
-        bfr[nb] = deq_fp4(wv, fp8_byte<Q>(sw[nb]));
+        const uint32_t w4 = *reinterpret_cast<const uint32_t *>(stg + kDOffB4 + boff[nb] + (Q >> 1) * 1024 + (Q & 1) * 8);
+        b4[nb] = deq_fp4(w4, fp8_byte<Q>(sw4[nb]));
     }
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
-        bf16x8 afr = a_frag(aT, 32 * mb + (lane & 31), 2 * Q + h);
-        if (!((rmask >> mb) & 1u)) afr = bf16x8{};
+        const bf16x8 afr = a_frag(stg, 32 * mb + (lane & 31), 2 * Q + h);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[nb], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, b4[nb], acc[mb][nb], 0, 0, 0);
     }
 }
 
-// acc[mb][nb] += A(tile rows, rows of mb with bit mb of rmask clear zeroed) x
-// FP4 row brow[nb]
+// acc[mb][nb] += A(tile rows) x dequantFP4(B row brow[nb])
 template <int NMB>
-__device__ __forceinline__ void gemm_pipe4_n(const PipeSrc &src, uint8_t *smem, const int brow[2], uint32_t rmask,
-                                             f32x16 acc[kPMB4][2])
+__device__ __forceinline__ void fp4_pipe_n(const DeltaSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kDMB][2])
 {
+    constexpr int kDma = NMB + 3;     // DMA instructions per wave per stage
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int nsteps = src.K / kPK;
-#pragma unroll
-    for (int st = 0; st < kPS - 1; ++st)
-        if (st < nsteps) issue_stage4(src, smem, st, st, wave, lane);
     int boff[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) boff[nb] = (brow[nb] >> 6) * 2048 + (brow[nb] & 63) * 16 + 4 * h;
+#pragma unroll
+    for (int st = 0; st < kPS - 1; ++st)
+        if (st < nsteps) issue_dstage<NMB>(src, smem, st, st, wave, lane);
     for (int s = 0; s < nsteps; ++s) {
-        if (s + 1 < nsteps) wait_barrier<kDmaPerStage4 * (kPS - 2)>();
+        if (s + 1 < nsteps) wait_barrier<kDma * (kPS - 2)>();
         else wait_barrier<0>();
-        if (s + kPS - 1 < nsteps) issue_stage4(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
-        const uint8_t *stg = smem + (s % kPS) * kStage4;
-        const uint8_t *aT = stg;
-        const uint8_t *bT = stg + kStageA4;
-        const uint8_t *sT = stg + kStageA4 + kStageB4;
-        uint32_t sw[2];
+        if (s + kPS - 1 < nsteps) issue_dstage<NMB>(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
+        const uint8_t *stg = smem + (s % kPS) * kDStage;
+        uint32_t sw4[2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) sw[nb] = *reinterpret_cast<const uint32_t *>(sT + brow[nb] * 4);
-        fp4_kstep<NMB, 0>(aT, bT, boff, sw, rmask, acc);
-        fp4_kstep<NMB, 1>(aT, bT, boff, sw, rmask, acc);
-        fp4_kstep<NMB, 2>(aT, bT, boff, sw, rmask, acc);
-        fp4_kstep<NMB, 3>(aT, bT, boff, sw, rmask, acc);
+        for (int nb = 0; nb < 2; ++nb) sw4[nb] = *reinterpret_cast<const uint32_t *>(stg + kDOffS4 + brow[nb] * 4);
+        fp4_kstep<NMB, 0>(stg, boff, sw4, acc);
+        fp4_kstep<NMB, 1>(stg, boff, sw4, acc);
+        fp4_kstep<NMB, 2>(stg, boff, sw4, acc);
+        fp4_kstep<NMB, 3>(stg, boff, sw4, acc);
     }
 }
 
-__device__ __forceinline__ void gemm_pipe4(const PipeSrc &src, uint8_t *smem, const int brow[2], uint32_t rmask,
-                                           f32x16 acc[kPMB4][2], int nmb)
+__device__ __forceinline__ void fp4_pipe(const DeltaSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kDMB][2],
+                                         int nmb)
 {
-    switch (nmb) {
-    case 1: gemm_pipe4_n<1>(src, smem, brow, rmask, acc); break;
-    case 2: gemm_pipe4_n<2>(src, smem, brow, rmask, acc); break;
-    case 3: gemm_pipe4_n<3>(src, smem, brow, rmask, acc); break;
-    default: gemm_pipe4_n<4>(src, smem, brow, rmask, acc); break;
-    }
-}
-
-// Delta slot of expert e when it has an FP4 delta and at least one of its
-// pairs belongs to a gate-flagged token, else -1.  Decided per expert, so the
-// 2-bit kernels (160-row tiles) and the FP4 kernels (128-row tiles) agree on
-// which rows go through the pre-activation buffer.
-__device__ __forceinline__ int expert_delta_slot(const PrefillParams &p, int e)
-{
-    if (e < 0 || p.n_slots <= 0 || p.gate == nullptr) return -1;
-    const int ds = p.slot_of_expert[e];
-    if (ds < 0 || ds >= p.n_slots) return -1;
-    const int lane = threadIdx.x & 63, P = p.T * p.k;
-    const int o1 = p.offsets[e + 1];
-    bool any = false;
-    for (int i = p.offsets[e] + lane; i < o1; i += 64) {
-        const int t = min(max(p.sorted[i], 0), P - 1) / p.k;
-        any |= p.gate[t] != 0;
-    }
-    return __ballot(any) ? ds : -1;
-}
-
-// bit mb set when this lane's A row 32 mb + lane % 32 of an FP4 tile is flagged
-__device__ __forceinline__ uint32_t flagged_rows(const PrefillParams &p, const MTile &mt, int nmb)
-{
-    uint32_t rmask = 0;
-    const int lane = threadIdx.x & 63, P = p.T * p.k;
-#pragma unroll
-    for (int mb = 0; mb < kPMB4; ++mb) {
-        const int r = 32 * mb + (lane & 31);
-        if (mb < nmb && r < mt.rows) {
-            const int t = min(max(p.sorted[mt.row0 + r], 0), P - 1) / p.k;
-            if (p.gate[t]) rmask |= 1u << mb;
+    if constexpr (kDMB == 2) {
+        if (nmb == 1) fp4_pipe_n<1>(src, smem, brow, acc);
+        else fp4_pipe_n<2>(src, smem, brow, acc);
+    } else {
+        switch (nmb) {
+        case 1: fp4_pipe_n<1>(src, smem, brow, acc); break;
+        case 2: fp4_pipe_n<2>(src, smem, brow, acc); break;
+        case 3: fp4_pipe_n<3>(src, smem, brow, acc); break;
+        default: fp4_pipe_n<4>(src, smem, brow, acc); break;
         }
     }
-    return rmask;
 }
 
-// FP4 work runs in kernels of its own (FP4 = true) after the 2-bit kernels
-// (FP4 = false), so that the 2-bit kernels keep their register budget:
-//  * an NVFP4 shared expert's tiles run only in the FP4 kernels;
-//  * an expert with gate-flagged rows and a delta runs its 2-bit pass in the
-//    2-bit kernel, which stores the fp32 pre-activations (gate/up) or writes y
-//    (down) as usual; the FP4 kernel then adds the delta pass, with the rows
-//    of unflagged tokens zeroed, and (gate/up) applies SwiGLU.
-// The FP4 kernels tile by 128 rows (2 waves per SIMD, 2 workgroups per CU),
-// the 2-bit kernels by 160.
-struct TileKind {
-    bool sh4;       // NVFP4 shared expert tile
-    int ds;         // delta slot when the expert has gate-flagged rows, else -1
-    uint32_t rmask; // FP4 kernels: this lane's flagged 32-row blocks
+// The FP4 tiles of a workgroup.  Delta mode (SHARED = false): blockIdx.y is a
+// delta-cache slot; its expert is the lowest one holding it, and its tiles are
+// the flagged rows at the head of its run in `order`, taken z, z + Z, ...
+// (blockIdx.z, gridDim.z).  NVFP4 shared expert (SHARED = true): blockIdx.y is
+// the tile of tokens [128 y, 128 y + 128).
+struct DeltaTiles {
+    int e, ds, row0, count;   // expert (-1: shared), delta slot, first row (in `order`, or token), rows
 };
 
-template <bool FP4>
-__device__ __forceinline__ TileKind tile_kind(const PrefillParams &p, const MTile &mt, int nmb)
+template <bool SHARED>
+__device__ __forceinline__ bool delta_tiles(const PrefillParams &p, DeltaTiles &dt)
 {
-    TileKind tk;
-    tk.sh4 = mt.e < 0 && p.shared_fp4;
-    tk.ds = tk.sh4 ? -1 : expert_delta_slot(p, mt.e);
-    tk.rmask = (1u << kPMB4) - 1u;
-    if (FP4 && tk.ds >= 0) tk.rmask = flagged_rows(p, mt, nmb);
-    return tk;
+    if constexpr (SHARED) {
+        dt.e = -1;
+        dt.ds = -1;
+        dt.row0 = kDM * blockIdx.y;
+        dt.count = min(kDM, p.T - dt.row0);
+        return dt.count > 0;
+    } else {
+        const int lane = threadIdx.x & 63, s = blockIdx.y;
+        int e = -1;
+        for (int c = 0; c < p.E && e < 0; c += 64) {
+            const uint64_t b = __ballot(c + lane < p.E && p.slot_of_expert[c + lane] == s);
+            if (b) e = c + __builtin_ctzll(b);
+        }
+        e = __builtin_amdgcn_readfirstlane(e);
+        if (e < 0 || p.nflag[e] == 0) return false;   // nflag is 0 unless e takes the delta
+        dt.e = e;
+        dt.ds = s;
+        dt.row0 = p.offsets[e];
+        dt.count = p.nflag[e];
+        return true;
+    }
 }
 
-// gate/up + SwiGLU.  N-tile nt covers h columns [128 nt, 128 nt + 128); wave w
-// owns gate rows and up rows [128 nt + 32 w, + 32).
-template <bool FP4>
-__device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t *smem)
+template <bool SHARED>
+__device__ __forceinline__ void fc1_delta_body(const PrefillParams &p, uint8_t *smem)
 {
-    constexpr int NB = FP4 ? kPMB4 : kPMB, SEG = FP4 ? kASeg4 : kASeg;
-    int ms, nt;
-    decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
-    if (ms >= (FP4 ? p.n_mslots4 : p.n_mslots)) return;
-    MTile mt;
-    if (!(FP4 ? locate_mtile<kPM4>(p, ms, mt) : locate_mtile<kPM>(p, ms, mt))) return;
-    const int nmb = (mt.rows + 31) / 32;
-    const TileKind tk = tile_kind<FP4>(p, mt, nmb);
-    if (FP4 ? !(tk.sh4 || tk.ds >= 0) : tk.sh4) return;
+    DeltaTiles dt;
+    if (!delta_tiles<SHARED>(p, dt)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = p.H, I = p.I, P = p.T * p.k;
-    // A rows fetched by this lane: segment i of wave w holds rows 8(nseg w + i) .. +7; lane -> row + lane/8
-    // (2-bit kernels stage only the nmb valid 32-row blocks: nseg = nmb)
-    const int nseg = FP4 ? SEG : nmb;
-    PipeSrc src;
+    const int H = p.H, I = p.I, P = p.T * p.k, nt = blockIdx.x;
+    const int jl = 32 * wave + (lane & 31), j = 128 * nt + jl;
+    const int brow[2] = {jl, 128 + jl};
+    const moet_fp4 &F = SHARED ? p.shf13 : p.d13;
+    const int fm0 = SHARED ? 0 : 2 * dt.ds;
+    const int mat = wave >> 1, tile = 2 * nt + (wave & 1);
+    DeltaSrc src;
     src.K = H;
+    src.b4 = F.codes + (size_t)(fm0 + mat) * I * H / 2 + (size_t)tile * (H / 32) * 1024;
+    src.s4 = F.scales + (size_t)(fm0 + mat) * I * H / 16 + (size_t)tile * (H / 128) * 512;
+    const float dsg = F.scale2[fm0], dsu = F.scale2[fm0 + 1];
+    const int ntile = (dt.count + kDM - 1) / kDM;
+    for (int it = SHARED ? 0 : (int)blockIdx.z; it < ntile; it += SHARED ? 1 : (int)gridDim.z) {
+        const int r0 = dt.row0 + kDM * it, rows = min(kDM, dt.count - kDM * it);
+        const int nmb = (rows + 31) / 32;
 #pragma unroll
-    for (int i = 0; i < SEG; ++i) {
-        const int r = min(8 * (nseg * wave + i) + (lane >> 3), mt.rows - 1);
-        int tok;
-        if (mt.e >= 0) tok = min(max(p.sorted[mt.row0 + r], 0), P - 1) / p.k;
-        else tok = mt.row0 + r;
-        src.arow[i] = reinterpret_cast<const uint8_t *>(p.x + (size_t)tok * H);
-    }
-    // B: 256 rows = gate rows [128 nt, +128) then up rows [128 nt, +128); wave w fetches storage tile w
-    const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
-    if (ws < 0) return;   // missing expert: no work, the combine skips its routings
-    const int jl = 32 * wave + (lane & 31);          // h column within the tile
-    const int j = 128 * nt + jl;
-    const int brow[2] = {jl, 128 + jl};               // gate row, up row in the stage
-    f32x16 acc[NB][2];
+        for (int i = 0; i < kDSeg; ++i) {
+            const int r = min(8 * (nmb * wave + i) + (lane >> 3), rows - 1);
+            const int tok = SHARED ? r0 + r : min(max(p.order[r0 + r], 0), P - 1) / p.k;
+            src.arow[i] = reinterpret_cast<const uint8_t *>(p.x + (size_t)tok * H);
+        }
+        f32x16 acc[kDMB][2];
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
+        for (int mb = 0; mb < kDMB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-    float sg, su;
-    if constexpr (!FP4) {
-        const moet_w2 &W = (mt.e >= 0) ? p.w13 : p.sh13;
-        const int m0 = (mt.e >= 0) ? 2 * ws : 0;
-        const int mat = m0 + (wave >> 1);
-        const int tile = 2 * nt + (wave & 1);
-        src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)mat * I * H / 16) + (size_t)tile * (H / 64) * 1024;
-        src.ssrc = W.scales + (size_t)mat * I * H / 32 + (size_t)tile * (H / 128) * 256;
-        gemm_pipe(src, smem, brow, acc, nmb);
-        sg = W.scale2[m0];
-        su = W.scale2[m0 + 1];
-    } else {
-        const moet_fp4 &F = tk.sh4 ? p.shf13 : p.d13;
-        const int fm0 = tk.sh4 ? 0 : 2 * tk.ds;
-        const int mat = fm0 + (wave >> 1);
-        const int tile = 2 * nt + (wave & 1);
-        src.bsrc = F.codes + (size_t)mat * I * H / 2 + (size_t)tile * (H / 32) * 1024;
-        src.ssrc = F.scales + (size_t)mat * I * H / 16 + (size_t)tile * (H / 128) * 512;
-        gemm_pipe4(src, smem, brow, tk.rmask, acc, nmb);
-        sg = F.scale2[fm0];
-        su = F.scale2[fm0 + 1];
-    }
-    const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
-    const bool to_pre = !FP4 && tk.ds >= 0;                     // 2-bit pass of a delta expert
-    const bool from_pre = FP4 && !tk.sh4;                       // delta pass: add to it
+                for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+        fp4_pipe(src, smem, brow, acc, nmb);
+        const int hbase = SHARED ? P + r0 : r0;
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-        if (mb >= nmb) break;
+        for (int mb = 0; mb < kDMB; ++mb) {
+            if (mb >= nmb) break;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (r < mt.rows) {
-                float g = acc[mb][0][v] * sg, u = acc[mb][1][v] * su;
-                float *pre = p.pre + (size_t)(rowbase + r) * (2 * I) + j;
-                if (to_pre) {
-                    pre[0] = g;
-                    pre[I] = u;
-                    continue;
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (r < rows) {
+                    float g = acc[mb][0][v] * dsg, u = acc[mb][1][v] * dsu;
+                    if (!SHARED) {   // plus the 2-bit pre-activations of this row
+                        const float *pre = p.pre + (size_t)(r0 + r) * (2 * I) + j;
+                        g += pre[0];
+                        u += pre[I];
+                    }
+                    if (p.swiglu_limit > 0.f) {
+                        g = fminf(g, p.swiglu_limit);
+                        u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+                    }
+                    p.h[(size_t)(hbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
                 }
-                if (from_pre) {
-                    g += pre[0];
-                    u += pre[I];
-                }
-                if (p.swiglu_limit > 0.f) {
-                    g = fminf(g, p.swiglu_limit);
-                    u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
-                }
-                p.h[(size_t)(rowbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
             }
         }
+        __syncthreads();   // every wave is done with the ring before the next tile refills it
     }
 }
 
-__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc1_prefill_kernel(PrefillParams p)
+template <bool SHARED>
+__device__ __forceinline__ void fc2_delta_body(const PrefillParams &p, uint8_t *smem, int *s_prow)
 {
-    __shared__ __align__(1024) uint8_t smem[kPS * kStage];
-    if (p.miss_count && blockIdx.x == 0 && threadIdx.x == 0) *p.miss_count = 0;   // counted by the combine
-    fc1_prefill_body<false>(p, smem);
-}
-
-__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc1_prefill_fp4_kernel(PrefillParams p)
-{
-    __shared__ __align__(1024) uint8_t smem[kPS * kStage4];
-    fc1_prefill_body<true>(p, smem);
-}
-
-// down: N-tile nt covers output features [256 nt, 256 nt + 256); wave w owns 64 of them.
-template <bool FP4>
-__device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t *smem)
-{
-    constexpr int NB = FP4 ? kPMB4 : kPMB, SEG = FP4 ? kASeg4 : kASeg;
-    int ms, nt;
-    decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
-    if (ms >= (FP4 ? p.n_mslots4 : p.n_mslots)) return;
-    MTile mt;
-    if (!(FP4 ? locate_mtile<kPM4>(p, ms, mt) : locate_mtile<kPM>(p, ms, mt))) return;
-    const int nmb = (mt.rows + 31) / 32;
-    const TileKind tk = tile_kind<FP4>(p, mt, nmb);
-    if (FP4 ? !(tk.sh4 || tk.ds >= 0) : tk.sh4) return;
+    DeltaTiles dt;
+    if (!delta_tiles<SHARED>(p, dt)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = p.H, I = p.I, P = p.T * p.k;
-    const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;
-    const int nseg = FP4 ? SEG : nmb;   // A segments per wave (2-bit kernels: the valid 32-row blocks)
-    PipeSrc src;
-    src.K = I;
-#pragma unroll
-    for (int i = 0; i < SEG; ++i) {
-        const int r = min(8 * (nseg * wave + i) + (lane >> 3), mt.rows - 1);
-        src.arow[i] = reinterpret_cast<const uint8_t *>(p.h + (size_t)(rowbase + r) * I);
-    }
-    const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
-    if (ws < 0) return;
-    const int tile = 4 * nt + wave;
+    const int H = p.H, I = p.I, P = p.T * p.k, nt = blockIdx.x;
     const int brow[2] = {64 * wave + (lane & 31), 64 * wave + 32 + (lane & 31)};
-    int ncol[2];
+    const moet_fp4 &F = SHARED ? p.shf2 : p.d2;
+    const int fm = SHARED ? 0 : dt.ds;
+    const int tile = 4 * nt + wave;
+    DeltaSrc src;
+    src.K = I;
+    src.b4 = F.codes + (size_t)fm * H * I / 2 + (size_t)tile * (I / 32) * 1024;
+    src.s4 = F.scales + (size_t)fm * H * I / 16 + (size_t)tile * (I / 128) * 512;
+    const float ds2 = F.scale2[fm];
+    const int ntile = (dt.count + kDM - 1) / kDM;
+    for (int it = SHARED ? 0 : (int)blockIdx.z; it < ntile; it += SHARED ? 1 : (int)gridDim.z) {
+        const int r0 = dt.row0 + kDM * it, rows = min(kDM, dt.count - kDM * it);
+        const int nmb = (rows + 31) / 32;
+        const int hbase = SHARED ? P + r0 : r0;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) ncol[nb] = 256 * nt + brow[nb];
-    f32x16 acc[NB][2];
+        for (int i = 0; i < kDSeg; ++i) {
+            const int r = min(8 * (nmb * wave + i) + (lane >> 3), rows - 1);
+            src.arow[i] = reinterpret_cast<const uint8_t *>(p.h + (size_t)(hbase + r) * I);
+        }
+        // y row (pair id) of each tile row, staged once for the epilogue
+        if (tid < rows) s_prow[tid] = SHARED ? P + r0 + tid : min(max(p.order[r0 + tid], 0), P - 1);
+        __syncthreads();
+        f32x16 acc[kDMB][2];
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
+        for (int mb = 0; mb < kDMB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-    float s2;
-    if constexpr (!FP4) {
-        const moet_w2 &W = (mt.e >= 0) ? p.w2 : p.sh2;
-        const int m0 = (mt.e >= 0) ? ws : 0;
-        src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
-        src.ssrc = W.scales + (size_t)m0 * H * I / 32 + (size_t)tile * (I / 128) * 256;
-        gemm_pipe(src, smem, brow, acc, nmb);
-        s2 = W.scale2[m0];
-    } else {
-        const moet_fp4 &F = tk.sh4 ? p.shf2 : p.d2;
-        const int fm = tk.sh4 ? 0 : tk.ds;
-        src.bsrc = F.codes + (size_t)fm * H * I / 2 + (size_t)tile * (I / 32) * 1024;
-        src.ssrc = F.scales + (size_t)fm * H * I / 16 + (size_t)tile * (I / 128) * 512;
-        gemm_pipe4(src, smem, brow, tk.rmask, acc, nmb);
-        s2 = F.scale2[fm];
-    }
-    const bool add = FP4 && !tk.sh4;   // delta pass: add to the 2-bit y
+                for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+        fp4_pipe(src, smem, brow, acc, nmb);
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-        if (mb >= nmb) break;
+        for (int mb = 0; mb < kDMB; ++mb) {
+            if (mb >= nmb) break;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (r < mt.rows) {
-                const int prow = (mt.e >= 0) ? min(max(p.sorted[mt.row0 + r], 0), P - 1) : P + mt.row0 + r;
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (r < rows) {
+                    const int prow = s_prow[r];
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    float *y = p.ypart + (size_t)prow * H + ncol[nb];
-                    const float d = acc[mb][nb][v] * s2;
-                    *y = add ? *y + d : d;
+                    for (int nb = 0; nb < 2; ++nb) {
+                        float *y = p.ypart + (size_t)prow * H + 256 * nt + brow[nb];
+                        const float d = acc[mb][nb][v] * ds2;
+                        *y = SHARED ? d : *y + d;   // delta: added to the 2-bit y
+                    }
                 }
             }
         }
+        __syncthreads();
     }
 }
 
-__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc2_prefill_kernel(PrefillParams p)
+template <bool SHARED>
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(kDWaves))) void fc1_prefill_delta_kernel(PrefillParams p)
 {
-    __shared__ __align__(1024) uint8_t smem[kPS * kStage];
-    fc2_prefill_body<false>(p, smem);
+    __shared__ __align__(1024) uint8_t smem[kPS * kDStage];
+    fc1_delta_body<SHARED>(p, smem);
 }
 
-__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) void fc2_prefill_fp4_kernel(PrefillParams p)
+template <bool SHARED>
+__global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(kDWaves))) void fc2_prefill_delta_kernel(PrefillParams p)
 {
-    __shared__ __align__(1024) uint8_t smem[kPS * kStage4];
-    fc2_prefill_body<true>(p, smem);
+    __shared__ __align__(1024) uint8_t smem[kPS * kDStage];
+    __shared__ int s_prow[kDM];
+    fc2_delta_body<SHARED>(p, smem, s_prow);
 }
 
 // out[t][n] = bf16(sum_j w[t][j] * y[(t, j)][n] + y_shared[t][n]), j in slot order;
@@ -764,18 +894,19 @@ int launch_decode(const moet_layer *, const uint16_t *, int, int, const int32_t 
 
 size_t prefill_workspace_bytes(int T, int k, int H, int I, int E)
 {
-    (void)E;
     const size_t rows = (size_t)T * k + T;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    return al(rows * I * 2) + al(rows * (size_t)std::max(H, 2 * I) * 4);
+    // h rows, y rows (or the flagged rows' pre-activations before them), the reordered pairs, the
+    // flagged count per expert
+    return al(rows * I * 2) + al(rows * (size_t)std::max(H, 2 * I) * 4) + al((size_t)T * k * 4) + al((size_t)E * 4);
 }
 
 int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const int32_t *ids, const float *w,
                    const int32_t *offsets, const int32_t *sorted, const uint8_t *gate, uint16_t *out, int32_t *miss_count,
                    void *ws, hipStream_t stream)
 {
-    if (L->I % 128 || L->H % 256) {
-        // the grouped GEMM tiles need I % 128 == 0 and H % 256 == 0
+    if (L->H % 256) {
+        // the grouped GEMM tiles need H % 256 == 0 (and I % 128 == 0, which every layer has)
         if ((int64_t)T * k + (L->has_shared ? T : 0) > 65535)
             return fail(MOET_EUNSUPPORTED, "this batch needs the GEMV kernels (H %% 256 not 0), which take at most "
                                             "T*top_k (+ T with a shared expert) = 65535 work entries");
@@ -809,41 +940,64 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     p.shared_fp4 = (L->has_shared && L->shared_fp4) ? 1 : 0;
     p.shf13 = L->shared13_fp4;
     p.shf2 = L->shared2_fp4;
-    const size_t rows = (size_t)T * k + T;
+    const int P = T * k;
+    const size_t rows = (size_t)P + T;
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     char *base = static_cast<char *>(ws);
     p.h = reinterpret_cast<uint16_t *>(base);
     p.ypart = reinterpret_cast<float *>(base + al(rows * L->I * 2));
     p.pre = p.ypart;   // read by the FP4 gate/up kernel before the down kernels write y there
+    int32_t *order = reinterpret_cast<int32_t *>(base + al(rows * L->I * 2) +
+                                                 al(rows * (size_t)std::max(L->H, 2 * L->I) * 4));
+    int32_t *nflag = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(order) + al((size_t)P * 4));
     p.out = out;
-    const int P = T * k;
-    const int mslots = (P + kPM - 1) / kPM + L->E + (p.has_shared ? (T + kPM - 1) / kPM : 0);
+    const bool delta = p.n_slots > 0;
+    p.order = delta ? order : sorted;
+    p.nflag = delta ? nflag : nullptr;
+    int rc;
+    if (delta) {
+        // a delta expert's gate-flagged pairs to the head of its run
+        hipLaunchKernelGGL(partition_kernel, dim3(L->E), dim3(256), 0, stream, p, order, nflag);
+        rc = check_launch("partition_kernel");
+        if (rc != MOET_OK) return rc;
+    }
+    const int mslots = (P + kPM - 1) / kPM + L->E + ((p.has_shared && !p.shared_fp4) ? (T + kPM - 1) / kPM : 0);
     p.n_mslots = mslots;
     const int ms8 = (mslots + 7) / 8 * 8;
+    // FP4 delta tiles: (N-tile, delta slot, 2 workgroups splitting the slot's tiles); NVFP4 shared
+    // expert: (N-tile, 128-token tile)
+    const dim3 dgrid1(L->I / 128, L->n_slots, 2), dgrid2(L->H / 256, L->n_slots, 2);
+    const dim3 sgrid1(L->I / 128, (T + kDM - 1) / kDM), sgrid2(L->H / 256, (T + kDM - 1) / kDM);
     p.n_ntiles = L->I / 128;
-    // tiles with FP4 work (delta rows, NVFP4 shared expert) go to the *_fp4 kernels
-    const bool fp4 = (p.n_slots > 0) || p.shared_fp4;
-    p.n_mslots4 = (P + kPM4 - 1) / kPM4 + L->E + (p.has_shared ? (T + kPM4 - 1) / kPM4 : 0);
-    const int ms8_4 = (p.n_mslots4 + 7) / 8 * 8;
     hipEvent_t ev0, ev1;
     if (timing_events(&ev0, &ev1))
         hipExtLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, ev0, ev1, 0, p);
     else
         hipLaunchKernelGGL(fc1_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
-    int rc = check_launch("fc1_prefill_kernel");
+    rc = check_launch("fc1_prefill_kernel");
     if (rc != MOET_OK) return rc;
-    if (fp4) {
-        hipLaunchKernelGGL(fc1_prefill_fp4_kernel, dim3(ms8_4 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
-        rc = check_launch("fc1_prefill_fp4_kernel");
+    if (delta) {
+        hipLaunchKernelGGL(fc1_prefill_delta_kernel<false>, dgrid1, dim3(64 * kPW), 0, stream, p);
+        rc = check_launch("fc1_prefill_delta_kernel");
+        if (rc != MOET_OK) return rc;
+    }
+    if (p.shared_fp4) {
+        hipLaunchKernelGGL(fc1_prefill_delta_kernel<true>, sgrid1, dim3(64 * kPW), 0, stream, p);
+        rc = check_launch("fc1_prefill_delta_kernel");
         if (rc != MOET_OK) return rc;
     }
     p.n_ntiles = L->H / 256;
     hipLaunchKernelGGL(fc2_prefill_kernel, dim3(ms8 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
     rc = check_launch("fc2_prefill_kernel");
     if (rc != MOET_OK) return rc;
-    if (fp4) {
-        hipLaunchKernelGGL(fc2_prefill_fp4_kernel, dim3(ms8_4 * p.n_ntiles), dim3(64 * kPW), 0, stream, p);
-        rc = check_launch("fc2_prefill_fp4_kernel");
+    if (delta) {
+        hipLaunchKernelGGL(fc2_prefill_delta_kernel<false>, dgrid2, dim3(64 * kPW), 0, stream, p);
+        rc = check_launch("fc2_prefill_delta_kernel");
+        if (rc != MOET_OK) return rc;
+    }
+    if (p.shared_fp4) {
+        hipLaunchKernelGGL(fc2_prefill_delta_kernel<true>, sgrid2, dim3(64 * kPW), 0, stream, p);
+        rc = check_launch("fc2_prefill_delta_kernel");
         if (rc != MOET_OK) return rc;
     }
     hipLaunchKernelGGL(combine_prefill_kernel, dim3((L->H + 1023) / 1024, T), dim3(256), 0, stream, p);

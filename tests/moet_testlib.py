@@ -189,6 +189,30 @@ def workspace_views(ws: torch.Tensor, T: int, k: int, H: int, I: int):
     return hb, y
 
 
+def partitioned_order(ids: np.ndarray, sorted_pairs: np.ndarray, offsets: np.ndarray, soe, gate_flags, resident=None):
+    """The pair order of the grouped-GEMM path with a gated delta: each expert's run of sorted pairs,
+    with the pairs of gate-flagged tokens first when the expert takes the delta (it holds a delta
+    slot no lower expert holds, and its 2-bit planes are resident); both parts keep their order.
+    Returns (order, flagged count per expert)."""
+    T, k = ids.shape
+    E = len(offsets) - 1
+    order = np.asarray(sorted_pairs, dtype=np.int64).copy()
+    nflag = np.zeros(E, dtype=np.int64)
+    seen = set()
+    for e in range(E):
+        run = order[offsets[e]:offsets[e + 1]].copy()
+        ds = int(soe[e]) if soe is not None else -1
+        takes = ds >= 0 and ds not in seen and (resident is None or resident[e])
+        if ds >= 0:
+            seen.add(ds)
+        if not takes:
+            continue
+        fl = np.asarray(gate_flags)[run // k] != 0
+        order[offsets[e]:offsets[e + 1]] = np.concatenate([run[fl], run[~fl]])
+        nflag[e] = int(fl.sum())
+    return order, nflag
+
+
 def mfma_path(T: int, k: int, H: int) -> bool:
     """Whether moet_moe_forward runs the grouped-GEMM kernels for this batch (else the GEMV kernels)."""
     return T * k > 1024 and H % 256 == 0
@@ -335,8 +359,23 @@ def check_pair_rows(ws: torch.Tensor, ol: "OracleLayer", x_bits, ids, sorted_pai
     hb = np_(hb).astype(np.uint16)
     y = np_(y)
     if mfma_path(T, k, H):
+        # h rows follow the pair order of the grouped GEMM: sorted, or with a gated delta the partitioned
+        # order, which the workspace also holds (compared here as index data, bit for bit)
+        rows_of = np.asarray(sorted_pairs, dtype=np.int64)
+        if gate_flags is not None and ol.soe is not None and (ol.soe >= 0).any():
+            E = len(ol.soe)
+            offsets = np.concatenate([[0], np.cumsum(np.bincount(ids.reshape(-1), minlength=E))])
+            exp_order, exp_nflag = partitioned_order(ids, sorted_pairs, offsets, ol.soe, gate_flags, resident)
+            P = T * k
+            off = _al256((P + T) * I * 2) + _al256((P + T) * H * 4)
+            got = np_(ws[off:off + P * 4].view(torch.int32))
+            off2 = off + _al256(P * 4)
+            got_nf = np_(ws[off2:off2 + E * 4].view(torch.int32))
+            assert (got == exp_order).all(), "partitioned pair order differs"
+            assert (got_nf == exp_nflag).all(), "flagged counts differ"
+            rows_of = exp_order
         row_of_pair = np.empty(T * k, dtype=np.int64)
-        row_of_pair[np.asarray(sorted_pairs, dtype=np.int64)] = np.arange(T * k)
+        row_of_pair[rows_of] = np.arange(T * k)
     else:
         row_of_pair = np.arange(T * k)
     keep = set(range(T)) if out_tokens is None else set(int(t) for t in out_tokens)

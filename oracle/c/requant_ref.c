@@ -32,6 +32,20 @@
  *    zeros of a block take alternating signs in k order, the first one +, and
  *    the source sign bit of a zero is ignored.  Zeros cost a^2 whatever their
  *    sign, so the block scale does not change;
+ *  - per-tensor codebook pick (same README, section "How it fits": the
+ *    sign-symmetric {-4,-1,1,4} is picked by nearly every tensor): a tensor
+ *    may instead use one of two other sign-symmetric four-level codebooks whose
+ *    levels are FP4 values.  Codebook c has magnitudes {lo_c, hi_c} times the
+ *    block scale and tensor scale 2^j_c * scale_2:
+ *        c = 0: {1, 4}, j = 1;   c = 1: {1/2, 3}, j = 1;   c = 2: {0, 2}, j = 2
+ *    (j_c is the smallest power of two with hi_c * 448 * 2^j_c >= 6 * 448, so
+ *    the largest NVFP4 value stays in range).  In units of u the two level
+ *    magnitudes of scale code t are LO = lo2_c * T9[t] << j_c and
+ *    HI = hi2_c * T9[t] << j_c with lo2/hi2 = 2 lo / 2 hi = (2, 8), (1, 6),
+ *    (0, 4); the block error is sum_i min((|Y_i| - LO)^2, (|Y_i| - HI)^2) and
+ *    an element takes HI iff 2|Y| > LO + HI.  Codebook 0 is the method's
+ *    default; the tensor-level pick (smallest exact total error, ties to the
+ *    lower c) is made by the caller from the per-block errors;
  *  - delta D = Y_nvfp4 - Y_2bit (exact integer in units of u), re-encoded as
  *    NVFP4 with the source scale_2: block-16 scale = e4m3 nearest (ties to the
  *    even code, saturating at 448) to max|D| / (6 * 2^10); element = e2m1
@@ -68,13 +82,22 @@ static inline int nib(const uint8_t *row, int64_t k)
     return (k & 1) ? (b >> 4) : (b & 15);
 }
 
-/* Returns 0 on success, -1 if a block scale byte is negative or NaN. */
+/* level magnitudes (doubled) and tensor-scale exponent of codebook c */
+static const int64_t CB_LO2[3] = {2, 1, 0}, CB_HI2[3] = {8, 6, 4};
+static const int CB_J[3] = {1, 1, 2};
+
+/* Returns 0 on success, -1 if a block scale byte is negative or NaN or the
+ * codebook index is not 0, 1 or 2. */
 int oracle_requant(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                   int64_t B, int balance, uint8_t *codes2, uint8_t *tau, int64_t *err_out)
+                   int64_t B, int balance, int cb, uint8_t *codes2, uint8_t *tau, int64_t *err_out)
 {
+    if (cb < 0 || cb > 2)
+        return -1;
     int64_t T9[127];
     for (int t = 0; t < 127; ++t)
         T9[t] = e4m3_x512(t);
+    const int64_t lo2 = CB_LO2[cb], hi2 = CB_HI2[cb];
+    const int j = CB_J[cb];
     int bad = 0;
     const int64_t nb = K / B;
 #pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
@@ -92,10 +115,10 @@ int oracle_requant(const uint8_t *codes, const uint8_t *scales, int64_t N, int64
             int best_t = 0;
             int64_t best_err = -1;
             for (int t = 0; t < 127; ++t) {
-                int64_t a = 4 * T9[t];
+                int64_t lo = (lo2 * T9[t]) << j, hi = (hi2 * T9[t]) << j;
                 int64_t e = 0;
                 for (int64_t i = 0; i < B; ++i) {
-                    int64_t d1 = y[i] - a, d4 = y[i] - 4 * a;
+                    int64_t d1 = y[i] - lo, d4 = y[i] - hi;
                     int64_t q1 = d1 * d1, q4 = d4 * d4;
                     e += q1 < q4 ? q1 : q4;
                 }
@@ -107,14 +130,14 @@ int oracle_requant(const uint8_t *codes, const uint8_t *scales, int64_t N, int64
             tau[n * nb + b] = (uint8_t)best_t;
             if (err_out)
                 err_out[n * nb + b] = best_err;
-            int64_t a = 4 * T9[best_t];
+            int64_t lo = (lo2 * T9[best_t]) << j, hi = (hi2 * T9[best_t]) << j;
             int zeros = 0;
             for (int64_t i = 0; i < B; ++i) {
                 int64_t k = b * B + i;
                 int s = (nib(crow, k) >> 3) & 1;
                 if (balance && y[i] == 0)
                     s = (zeros++) & 1;
-                int m = (2 * y[i] > 5 * a) ? 1 : 0;
+                int m = (2 * y[i] > lo + hi) ? 1 : 0;
                 codes2[n * K + k] = (uint8_t)((s << 1) | m);
             }
         }
@@ -123,10 +146,15 @@ int oracle_requant(const uint8_t *codes, const uint8_t *scales, int64_t N, int64
     return bad ? -1 : 0;
 }
 
-/* FP4 re-encoding of the exact residual; dcodes gets one 4-bit code per weight. */
-int oracle_delta(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K, int64_t B,
+/* FP4 re-encoding of the exact residual; dcodes gets one 4-bit code per weight.
+ * cb: the codebook the 2-bit codes use. */
+int oracle_delta(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K, int64_t B, int cb,
                  const uint8_t *codes2, const uint8_t *tau, uint8_t *dcodes, uint8_t *dscales)
 {
+    if (cb < 0 || cb > 2)
+        return -1;
+    const int64_t lo2 = CB_LO2[cb], hi2 = CB_HI2[cb];
+    const int j = CB_J[cb];
     int64_t T9[127];
     for (int t = 0; t < 127; ++t)
         T9[t] = e4m3_x512(t);
@@ -148,11 +176,11 @@ int oracle_delta(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t
                 if (c & 8)
                     y = -y;
                 int c2 = codes2[n * K + k];
-                int64_t a = 4 * T9[tau[n * (K / B) + k / B]];
-                int64_t lvl = (c2 & 1) ? 4 : 1;
+                int64_t T = T9[tau[n * (K / B) + k / B]];
+                int64_t lvl = ((c2 & 1) ? hi2 * T : lo2 * T) << j;   /* level magnitude in units of u */
                 if (c2 & 2)
                     lvl = -lvl;
-                D[i] = y - lvl * a;
+                D[i] = y - lvl;
                 int64_t ad = D[i] < 0 ? -D[i] : D[i];
                 if (ad > M)
                     M = ad;

@@ -171,16 +171,17 @@ __device__ __forceinline__ void slot_token(const DecodeParams &p, const SlotInfo
 }
 
 // ---------------------------------------------------------------------------
-// 2-bit decode constants: the and-mask lives in an SGPR, the or-constant in a VGPR
+// 2-bit decode constants: the and-mask lives in an SGPR, the or-constant (the
+// lane's codebook) in a VGPR
 struct W2Consts {
     uint32_t sm, vb;
 };
 
-__device__ __forceinline__ W2Consts w2_consts()
+__device__ __forceinline__ W2Consts w2_consts(uint32_t orc)
 {
     W2Consts c;
     c.sm = __builtin_amdgcn_readfirstlane(kW2Mask);
-    c.vb = kW2Or;
+    c.vb = orc;
     asm volatile("" : "+v"(c.vb));
     return c;
 }
@@ -228,6 +229,7 @@ struct LaneRow {
     const uint8_t *cb;    // wave-uniform: 2-bit codes of the wave's first matrix
     const uint8_t *sb;    // wave-uniform: its block scales
     uint32_t co, so;      // this lane's byte offsets (codes of 64-k chunk 0, scale dword of group 0)
+    uint32_t orc;         // or-constant of this lane's matrix's codebook
     const uint4 *dc4;     // FP4 delta codes (or null)
     const uint2 *ds8;     // FP4 delta scales
     int tile, rt;         // storage tile and row within it
@@ -383,7 +385,7 @@ template <int TT>
 __device__ __forceinline__ void w2_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
 {
     if (g0 >= g1) return;
-    const W2Consts kc = w2_consts();
+    const W2Consts kc = w2_consts(L.orc);
     const int wl = 8 * g1 - 1;
     W2Buf buf[kPF + 1];
     u32x8 xa[TT], xb[TT];
@@ -532,6 +534,7 @@ __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_D
     L.sb = W.scales + (size_t)m0 * I * H / 32;
     lane_offsets(L, mat, row >> 6, row & 63, I, H);
     const float s2 = (si.shared && p.shared_fp4) ? 0.f : W.scale2[m0 + mat];
+    L.orc = (si.shared && p.shared_fp4) ? kW2Or : w2_or_of(w2_codebook(W, m0 + mat));
     float ds2 = 0.f;
     L.dc4 = nullptr;
     L.ds8 = nullptr;
@@ -603,6 +606,7 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_D
     L.sb = W.scales + (size_t)m0 * H * I / 32;
     lane_offsets(L, 0, tile, lane, H, I);
     const float s2 = fp4_shared ? 0.f : W.scale2[m0];
+    L.orc = fp4_shared ? kW2Or : w2_or_of(w2_codebook(W, m0));
     float ds2 = 0.f;
     L.dc4 = nullptr;
     L.ds8 = nullptr;

@@ -26,6 +26,10 @@
 //    e2m1 image, four FP4 -> bf16 conversions give the levels, and a packed
 //    16-bit add of the scale's bf16 bits (less those of 1.0) multiplies by
 //    the e4m3 block scale; bf16(level * scale) is exact (4 significant bits).
+//    That add is a product only for levels +-1, +-4 (powers of two): a
+//    workgroup whose matrices use codebook 1 ({1/2, 3}) or 2 ({0, 2}) takes
+//    a second instantiation that converts e2m1 -> f32, multiplies by the scale
+//    and rounds to bf16, exact as well (at most 5 significant bits).
 //    The per-tensor scale2 is applied in the epilogue.
 //  * gate/up kernel: wave w owns 32 gate columns and the same 32 up columns,
 //    so SwiGLU is computed in registers and h = bf16(silu(g) * u) is written
@@ -182,10 +186,45 @@ __device__ __forceinline__ void block_consts(uint32_t scale_word, int byte, uint
     orc = b ? kW2Or : 0u;
 }
 
+// the same for any codebook (or-constant `cbor`): `sadd` carries the block scale as a float
+__device__ __forceinline__ void block_consts_gen(uint32_t scale_word, int byte, uint32_t cbor, uint32_t &mask,
+                                                 uint32_t &orc, uint32_t &sadd)
+{
+    const uint32_t b = (scale_word >> (8 * byte)) & 0xFFu;
+    sadd = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(b, 0));
+    mask = kW2Mask;
+    orc = cbor;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// e2m1 byte B of w (low nibble first) as two bf16 of value * sc (exact)
+template <int B>
+__device__ __forceinline__ void deq_fp4_pair(uint32_t w, float sc, bf16x8 &r)
+{
+    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+    r[2 * B] = (__bf16)(v.x * sc);
+    r[2 * B + 1] = (__bf16)(v.y * sc);
+}
+
+// 8 bf16 of one row for one MFMA k-step from 8 e2m1 codes, times `sc` (exact)
+__device__ __forceinline__ bf16x8 deq_fp4(uint32_t w, float sc)
+{
+    bf16x8 r;
+    deq_fp4_pair<0>(w, sc, r);
+    deq_fp4_pair<1>(w, sc, r);
+    deq_fp4_pair<2>(w, sc, r);
+    deq_fp4_pair<3>(w, sc, r);
+    return r;
+}
+
 // 8 bf16 of one row for one MFMA k-step: elements 8h .. 8h+7 of code word w
 // (sh = 2h selects the bit pair of each nibble), times the block scale
+template <bool GEN>
 __device__ __forceinline__ bf16x8 deq_frag(uint32_t w, uint32_t sh, uint32_t mask, uint32_t orc, uint32_t sadd)
 {
+    if constexpr (GEN) return deq_fp4(and_or_v(w << sh, mask, orc), __uint_as_float(sadd));
+
     const uint32_t f = and_or_v(w << sh, mask, orc);
     const u16x2 a = __builtin_bit_cast(u16x2, sadd);
     uint32_t q[4];
@@ -269,8 +308,10 @@ __device__ __forceinline__ void issue_stage(const PipeSrc &src, uint8_t *smem, i
 
 // Main loop shared by both kernels.  acc[mb][nb] += A(tile rows) x dequant(B row brow[nb]);
 // brow[nb] = index (0..255) of this lane's B row within the workgroup's 256 B-rows.
-template <int NMB>
-__device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2])
+// GEN: the generic dequant, with the or-constant cbor[nb] of B row brow[nb]'s codebook
+template <int NMB, bool GEN>
+__device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2],
+                                            const uint32_t cbor[2])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;                 // k half of the MFMA fragment
@@ -294,8 +335,13 @@ __device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, c
         for (int nb = 0; nb < 2; ++nb) {
             bw[nb] = *reinterpret_cast<const uint4 *>(bT + brow[nb] * 16);
             const uint32_t sw = *reinterpret_cast<const uint32_t *>(sT + brow[nb] * 4);
-            block_consts(sw, 2 * (s & 1) + 0, mask[nb][0], orc[nb][0], sadd[nb][0]);
-            block_consts(sw, 2 * (s & 1) + 1, mask[nb][1], orc[nb][1], sadd[nb][1]);
+            if constexpr (GEN) {
+                block_consts_gen(sw, 2 * (s & 1) + 0, cbor[nb], mask[nb][0], orc[nb][0], sadd[nb][0]);
+                block_consts_gen(sw, 2 * (s & 1) + 1, cbor[nb], mask[nb][1], orc[nb][1], sadd[nb][1]);
+            } else {
+                block_consts(sw, 2 * (s & 1) + 0, mask[nb][0], orc[nb][0], sadd[nb][0]);
+                block_consts(sw, 2 * (s & 1) + 1, mask[nb][1], orc[nb][1], sadd[nb][1]);
+            }
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {   // MFMA k-steps of 16
@@ -303,7 +349,7 @@ __device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, c
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
                 const uint32_t wv = (q == 0) ? bw[nb].x : (q == 1) ? bw[nb].y : (q == 2) ? bw[nb].z : bw[nb].w;
-                bfr[nb] = deq_frag(wv, sh, mask[nb][q >> 1], orc[nb][q >> 1], sadd[nb][q >> 1]);
+                bfr[nb] = deq_frag<GEN>(wv, sh, mask[nb][q >> 1], orc[nb][q >> 1], sadd[nb][q >> 1]);
             }
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
@@ -316,17 +362,27 @@ __device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, c
     }
 }
 
-// one instantiation per number of valid 32-row blocks, chosen once per workgroup
-__device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2],
-                                          int nmb)
+template <bool GEN>
+__device__ __forceinline__ void gemm_pipe_g(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2],
+                                            int nmb, const uint32_t cbor[2])
 {
     switch (nmb) {
-    case 1: gemm_pipe_n<1>(src, smem, brow, acc); break;
-    case 2: gemm_pipe_n<2>(src, smem, brow, acc); break;
-    case 3: gemm_pipe_n<3>(src, smem, brow, acc); break;
-    case 4: gemm_pipe_n<4>(src, smem, brow, acc); break;
-    default: gemm_pipe_n<5>(src, smem, brow, acc); break;
+    case 1: gemm_pipe_n<1, GEN>(src, smem, brow, acc, cbor); break;
+    case 2: gemm_pipe_n<2, GEN>(src, smem, brow, acc, cbor); break;
+    case 3: gemm_pipe_n<3, GEN>(src, smem, brow, acc, cbor); break;
+    case 4: gemm_pipe_n<4, GEN>(src, smem, brow, acc, cbor); break;
+    default: gemm_pipe_n<5, GEN>(src, smem, brow, acc, cbor); break;
     }
+}
+
+// one instantiation per number of valid 32-row blocks and dequant kind, chosen once per
+// workgroup; cb[nb]: codebook id of B row brow[nb]'s matrix
+__device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2],
+                                          int nmb, const uint32_t cb[2])
+{
+    const uint32_t cbor[2] = {w2_or_of(cb[0]), w2_or_of(cb[1])};
+    if ((cb[0] | cb[1]) == 0) gemm_pipe_g<false>(src, smem, brow, acc, nmb, cbor);
+    else gemm_pipe_g<true>(src, smem, brow, acc, nmb, cbor);
 }
 
 // ---------------------------------------------------------------------------
@@ -432,7 +488,8 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     const int tile = 2 * nt + (wave & 1);
     src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)mat * I * H / 16) + (size_t)tile * (H / 64) * 1024;
     src.ssrc = W.scales + (size_t)mat * I * H / 32 + (size_t)tile * (H / 128) * 256;
-    gemm_pipe(src, smem, brow, acc, nmb);
+    const uint32_t cb[2] = {w2_codebook(W, m0), w2_codebook(W, m0 + 1)};   // gate, up
+    gemm_pipe(src, smem, brow, acc, nmb, cb);
     const float sg = W.scale2[m0], su = W.scale2[m0 + 1];
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
 #pragma unroll
@@ -500,7 +557,8 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     const int m0 = (mt.e >= 0) ? ws : 0;
     src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
     src.ssrc = W.scales + (size_t)m0 * H * I / 32 + (size_t)tile * (I / 128) * 256;
-    gemm_pipe(src, smem, brow, acc, nmb);
+    const uint32_t cb[2] = {w2_codebook(W, m0), w2_codebook(W, m0)};
+    gemm_pipe(src, smem, brow, acc, nmb, cb);
     const float s2 = W.scale2[m0];
 #pragma unroll
     for (int mb = 0; mb < kPMB; ++mb) {
@@ -562,28 +620,6 @@ __device__ __forceinline__ void issue_dstage(const DeltaSrc &src, uint8_t *smem,
     dma16(src.b4 + ((size_t)(2 * s) * 64 + lane) * 16, base + kDOffB4 + wave * 2048);
     dma16(src.b4 + ((size_t)(2 * s + 1) * 64 + lane) * 16, base + kDOffB4 + wave * 2048 + 1024);
     dma4(src.s4 + ((size_t)(s >> 1) * 64 + lane) * 8 + (s & 1) * 4, base + kDOffS4 + wave * 256);
-}
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// e2m1 byte B of w (low nibble first) as two bf16 of value * sc (exact)
-template <int B>
-__device__ __forceinline__ void deq_fp4_pair(uint32_t w, float sc, bf16x8 &r)
-{
-    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
-    r[2 * B] = (__bf16)(v.x * sc);
-    r[2 * B + 1] = (__bf16)(v.y * sc);
-}
-
-// 8 bf16 of one row for one MFMA k-step from 8 e2m1 codes, times `sc` (exact)
-__device__ __forceinline__ bf16x8 deq_fp4(uint32_t w, float sc)
-{
-    bf16x8 r;
-    deq_fp4_pair<0>(w, sc, r);
-    deq_fp4_pair<1>(w, sc, r);
-    deq_fp4_pair<2>(w, sc, r);
-    deq_fp4_pair<3>(w, sc, r);
-    return r;
 }
 
 // block-16 scale byte Q of a scale dword as a float

@@ -50,7 +50,7 @@ int check_launch(const char *what)
 bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int launch_requant(const uint8_t *, const uint8_t *, const float *, int64_t, int, int, uint32_t *, uint8_t *, float *,
-                   const int32_t *, int64_t, uint8_t *, uint8_t *, float *, int, hipStream_t);
+                   uint8_t *, const int32_t *, int64_t, uint8_t *, uint8_t *, float *, int, int, hipStream_t);
 int launch_remap_mxfp4(const uint8_t *, const uint8_t *, int64_t, int, int, int, uint32_t *, uint8_t *, float *,
                        hipStream_t);
 int launch_pack_nvfp4(const uint8_t *, const uint8_t *, const float *, int64_t, int, int, uint8_t *, uint8_t *, float *,
@@ -68,7 +68,10 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I, int E);
 int launch_prefill(const moet_layer *, const uint16_t *, int, int, const int32_t *, const float *, const int32_t *,
                    const int32_t *, const uint8_t *, uint16_t *, int32_t *, void *, hipStream_t);
 
-static bool w2_ok(const moet_w2 &w) { return aligned16(w.codes) && aligned16(w.scales) && aligned16(w.scale2); }
+static bool w2_ok(const moet_w2 &w)
+{
+    return aligned16(w.codes) && aligned16(w.scales) && aligned16(w.scale2) && (!w.codebook || aligned16(w.codebook));
+}
 static bool fp4_ok(const moet_fp4 &w) { return aligned16(w.codes) && aligned16(w.scales) && aligned16(w.scale2); }
 
 static int check_layer(const moet_layer *L)
@@ -157,28 +160,33 @@ const char *moet_status_str(int s)
 
 const char *moet_last_error(void) { return g_err; }
 
-int moet_abi_version(void) { return 5; }
+int moet_abi_version(void) { return 6; }
 
-// shape checks shared by the load-time conversions
-static int check_stack(int64_t n_mat, int64_t N, int64_t K, uint32_t flags)
+// shape checks shared by the load-time conversions (`allowed`: the flags the entry point takes)
+static int check_stack(int64_t n_mat, int64_t N, int64_t K, uint32_t flags,
+                       uint32_t allowed = MOET_BALANCE_ZERO_SIGNS)
 {
     if (n_mat < 1) return fail(MOET_EINVAL, "n_mat (%lld) must be >= 1", (long long)n_mat);
     if (N < 64 || N % 64 || N > (1 << 24)) return fail(MOET_EINVAL, "N (%lld) must be a positive multiple of 64", (long long)N);
     if (K < 128 || K % 128 || K > (1 << 24)) return fail(MOET_EINVAL, "K (%lld) must be a positive multiple of 128", (long long)K);
     if ((unsigned long long)n_mat * N * (K / 32) >= (1ull << 40)) return fail(MOET_EINVAL, "stack too large");
     if ((unsigned long long)n_mat * N * (K / 32) / 256 >= (1ull << 31)) return fail(MOET_EINVAL, "stack too large for one launch");
-    if (flags & ~(uint32_t)MOET_BALANCE_ZERO_SIGNS) return fail(MOET_EINVAL, "unknown flags 0x%x", flags);
+    if (flags & ~allowed) return fail(MOET_EINVAL, "unknown flags 0x%x", flags);
     return MOET_OK;
 }
 
 int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
                  int64_t N, int64_t K, uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2,
-                 const int32_t *delta_sel, int64_t n_sel, uint8_t *d_codes, uint8_t *d_scales, float *d_scale2,
-                 uint32_t flags, void *stream)
+                 uint8_t *w2_codebook, const int32_t *delta_sel, int64_t n_sel, uint8_t *d_codes,
+                 uint8_t *d_scales, float *d_scale2, uint32_t flags, void *stream)
 {
     g_err[0] = 0;
-    int rc = check_stack(n_mat, N, K, flags);
+    int rc = check_stack(n_mat, N, K, flags, MOET_BALANCE_ZERO_SIGNS | MOET_PICK_CODEBOOK);
     if (rc != MOET_OK) return rc;
+    const bool pick = (flags & MOET_PICK_CODEBOOK) != 0;
+    if (pick && !aligned16(w2_codebook))
+        return fail(MOET_EINVAL, "MOET_PICK_CODEBOOK needs a non-NULL, 16-byte aligned w2_codebook");
+    if (w2_codebook && !aligned16(w2_codebook)) return fail(MOET_EINVAL, "w2_codebook must be 16-byte aligned");
     if (!aligned16(fp4_codes) || !aligned16(fp4_scales) || !aligned16(fp4_scale2) || !aligned16(w2_codes) ||
         !aligned16(w2_scales) || !aligned16(w2_scale2))
         return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
@@ -186,8 +194,8 @@ int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const floa
     if (n_sel > 0 && (!aligned16(delta_sel) || !aligned16(d_codes) || !aligned16(d_scales) || !aligned16(d_scale2)))
         return fail(MOET_EINVAL, "delta pointers must be non-NULL and 16-byte aligned when n_sel > 0");
     return launch_requant(fp4_codes, fp4_scales, fp4_scale2, n_mat, (int)N, (int)K, w2_codes, w2_scales, w2_scale2,
-                          delta_sel, n_sel, d_codes, d_scales, d_scale2, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
-                          (hipStream_t)stream);
+                          w2_codebook, delta_sel, n_sel, d_codes, d_scales, d_scale2,
+                          (int)(flags & MOET_BALANCE_ZERO_SIGNS), (int)pick, (hipStream_t)stream);
 }
 
 int moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,

@@ -47,12 +47,19 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)
 // 2-bit decode.  Nibble j of a code word holds element j in bits 2-3 and
 // element j + 8 in bits 0-1, each as (s, m) with m the lower bit.  Masking
 // one bit pair per nibble and or-ing 0b0010 into the rest gives an FP4 (e2m1)
-// nibble s|m|1|0 = +-1 (m = 0) or +-4 (m = 1), so one and-or turns eight
-// codes into eight e2m1 values, and the hardware FP4 -> bf16 conversion then
-// makes one bf16 pair per instruction.
+// nibble s|m|1|0 = +-1 (m = 0) or +-4 (m = 1) (codebook 0), so one and-or
+// turns eight codes into eight e2m1 values, and the hardware FP4 -> bf16
+// conversion then makes one bf16 pair per instruction.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kW2Mask = 0xCCCCCCCCu;   // bits 2-3 of every nibble
 constexpr uint32_t kW2Or = 0x22222222u;     // e2m1 exponent low bit
+
+// The other codebooks of the layout differ only in the or-constant: with
+// 0b0001 the e2m1 nibble s|m|0|1 is +-1/2 (m = 0) or +-3 (m = 1); with 0 it is
+// s|m|0|0 = +-0 or +-2.  Codebook id (0, 1, 2; larger reads as 2) -> or-constant.
+__device__ __forceinline__ uint32_t w2_or_of(uint32_t cb) { return cb == 0 ? kW2Or : cb == 1 ? 0x11111111u : 0u; }
+// codebook id of matrix m of a stack (0 when the stack carries no ids)
+__device__ __forceinline__ uint32_t w2_codebook(const moet_w2 &W, int m) { return W.codebook ? W.codebook[m] : 0u; }
 
 // v_and_or_b32 with the mask in an SGPR and the or-constant in a VGPR (gfx9 VOP3
 // takes no literal operands, and the compiler would otherwise emit and + or).

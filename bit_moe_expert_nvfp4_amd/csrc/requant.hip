@@ -21,9 +21,30 @@
 // One thread handles one 32-weight block; the 32 magnitudes collapse to at
 // most 16 distinct values (two 16-blocks x 8 e2m1 magnitudes), counted with
 // nibble SWAR tricks.
+//
+// Per-tensor codebook pick (README "How it fits": nearly every tensor picks
+// {-4,-1,1,4}): codebook c has level magnitudes {lo_c, hi_c} times the block
+// scale and tensor scale 2^j_c * scale_2 -- c = 0: {1, 4}, j = 1; c = 1:
+// {1/2, 3}, j = 1; c = 2: {0, 2}, j = 2 -- so in units of u the levels of
+// scale code t are LO = lo2_c * T << j_c and HI = hi2_c * T << j_c (T =
+// e4m3(t) * 2^9, lo2/hi2 = 2 lo / 2 hi), an element takes HI iff
+// 2|Y| > LO + HI, and the block error is exact in float64 as above.  With
+// MOET_PICK_CODEBOOK a first pass sums every block's smallest error per
+// codebook per matrix (exact integer sums: workgroup sums below 2^60, split
+// into 32-bit halves and added with 64-bit integer atomics into the head of
+// the matrix's output code plane, which the requant pass overwrites), a
+// second pass picks the codebook with the smallest total (ties to the lower
+// index), and the requant pass writes the codes of each matrix's codebook.
+// Codebook 0 keeps the search window above; codebooks 1 and 2 scan all 127
+// scale codes.
 #include "moet_common.h"
 
 namespace moet {
+
+constexpr int kNumCodebooks = 3;
+__device__ __forceinline__ int cb_lo2(int c) { return c == 0 ? 2 : c == 1 ? 1 : 0; }
+__device__ __forceinline__ int cb_hi2(int c) { return c == 0 ? 8 : c == 1 ? 6 : 4; }
+__device__ __forceinline__ int cb_j(int c) { return c == 2 ? 2 : 1; }
 
 __device__ __forceinline__ int e4m3_floor_code(int u)  // largest t with e4m3_x512(t) <= u, u >= 0
 {
@@ -56,11 +77,195 @@ __device__ __forceinline__ int mag2_of(int L)  // 2*|e2m1| for magnitude code L 
 }
 
 
+// The 32 magnitudes of one block as at most 14 distinct non-zero bins (value in
+// units of u, count) plus the zero count, and the largest magnitude.
+struct BlockBins {
+    int yv[14], cc[14], cy[14];
+    double y2;              // sum c*y^2 (< 2^49, exact)
+    int stot, ctot, nzero, amax;
+};
+
+__device__ __forceinline__ void block_bins(const uint32_t words[4], const int S9[2], BlockBins &bb)
+{
+    int cnt[2][8];
+    bb.amax = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t m0 = words[2 * h] & 0x77777777u, m1 = words[2 * h + 1] & 0x77777777u;
+#pragma unroll
+        for (int L = 1; L < 8; ++L) {
+            cnt[h][L] = count_nibbles_eq(m0, L) + count_nibbles_eq(m1, L);
+            if (cnt[h][L]) bb.amax = max(bb.amax, mag2_of(L) * S9[h]);
+        }
+        cnt[h][0] = 16;
+#pragma unroll
+        for (int L = 1; L < 8; ++L) cnt[h][0] -= cnt[h][L];
+    }
+    bb.y2 = 0.0;
+    bb.stot = bb.ctot = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int L = 1; L < 8; ++L) {
+            const int i = 7 * h + L - 1;
+            bb.yv[i] = mag2_of(L) * S9[h];                    // < 2^22
+            bb.cc[i] = cnt[h][L];
+            bb.cy[i] = bb.cc[i] * bb.yv[i];                   // < 2^27
+            bb.y2 = fma((double)bb.cy[i], (double)bb.yv[i], bb.y2);
+            bb.stot += bb.cy[i];
+            bb.ctot += bb.cc[i];
+        }
+    bb.nzero = cnt[0][0] + cnt[1][0];
+}
+
+// Err(LO, HI) with the bins split at the level boundary: a bin (value y, count
+// c) sits on LO iff 2y <= LO + HI (then (y-LO)^2 <= (y-HI)^2), so with S_lo,
+// C_lo the sums of c*y and c over the LO bins and S_hi, C_hi over the HI bins,
+//   Err = sum c*y^2 - 2 (LO S_lo + HI S_hi) + LO^2 (zeros + C_lo) + HI^2 C_hi,
+// the same exact integer as the per-bin sum (every product and partial sum is
+// an integer below 2^53, so float64 holds it exactly).
+__device__ __forceinline__ double block_err(const BlockBins &bb, int lo, int hi)
+{
+    int slo = 0, clo = 0;
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+        const bool l = 2 * bb.yv[i] <= lo + hi;
+        slo += l ? bb.cy[i] : 0;
+        clo += l ? bb.cc[i] : 0;
+    }
+    const double dl = (double)lo, dh = (double)hi;
+    const double lin = fma(dl, (double)slo, dh * (double)(bb.stot - slo));          // < 2^50
+    const double quad = fma(dl * dl, (double)(bb.nzero + clo), dh * dh * (double)(bb.ctot - clo));   // < 2^50
+    return bb.y2 - 2.0 * lin + quad;
+}
+
+// Smallest-error scale code of codebook c (ties: the smaller code) and its error.
+__device__ __forceinline__ int block_best(const BlockBins &bb, int c, double &best_err)
+{
+    best_err = 0.0;
+    if (bb.amax == 0) return 0;   // every level of scale 0 is exact
+    int t_lo = 0, t_hi = 126;
+    if (c == 0) {
+        t_lo = e4m3_floor_code(bb.amax / 512);
+        t_hi = e4m3_ceil_code((bb.amax + 3) / 4);
+    }
+    const int lo2 = cb_lo2(c), hi2 = cb_hi2(c), j = cb_j(c);
+    int best_t = t_lo;
+    best_err = -1.0;
+    for (int t = t_lo; t <= t_hi; ++t) {
+        const int T = e4m3_x512(t);
+        const double err = block_err(bb, (lo2 * T) << j, (hi2 * T) << j);
+        if (best_err < 0.0 || err < best_err) {   // ascending scan: ties keep the smaller scale
+            best_err = err;
+            best_t = t;
+        }
+    }
+    return best_t;
+}
+
+__device__ __forceinline__ void load_block(const uint8_t *codes, const uint8_t *scales, size_t mat, int N, int K, int n,
+                                           int b, uint32_t words[4], int S9[2])
+{
+    const uint4 cw = *reinterpret_cast<const uint4 *>(codes + (mat * N + n) * (size_t)(K / 2) + 16 * (size_t)b);
+    const uint32_t sw = *reinterpret_cast<const uint16_t *>(scales + (mat * N + n) * (size_t)(K / 16) + 2 * (size_t)b);
+    S9[0] = e4m3_x512(sw & 0x7F);
+    S9[1] = e4m3_x512((sw >> 8) & 0x7F);
+    words[0] = cw.x;
+    words[1] = cw.y;
+    words[2] = cw.z;
+    words[3] = cw.w;
+}
+
+// the per-matrix error sums of the pick, in the head of the matrix's output code plane:
+// [codebook][lo 32 bits, hi bits] as uint64
+__device__ __forceinline__ unsigned long long *pick_sums(uint32_t *wcodes, size_t mat, int N, int K)
+{
+    return reinterpret_cast<unsigned long long *>(wcodes + mat * (size_t)N * (K / 16));
+}
+
+__global__ __launch_bounds__(256) void pick_clear_kernel(uint32_t *__restrict__ wcodes, int64_t n_mat, int N, int K)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)n_mat * 2 * kNumCodebooks) return;
+    pick_sums(wcodes, i / (2 * kNumCodebooks), N, K)[i % (2 * kNumCodebooks)] = 0ull;
+}
+
+// every block's smallest error per codebook, summed per matrix (a workgroup's 256 blocks lie in
+// one matrix: N * K / 32 is a multiple of 256)
+__global__ __launch_bounds__(256) void pick_err_kernel(const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ scales, int64_t n_mat, int N, int K,
+                                                       uint32_t *__restrict__ wcodes)
+{
+    __shared__ unsigned long long part[4][kNumCodebooks];
+    const int nb = K / 32;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t total = (size_t)n_mat * N * nb;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned long long e[kNumCodebooks] = {0ull, 0ull, 0ull};
+    size_t mat = 0;
+    if (idx < total) {
+        const int b = (int)(idx % nb);
+        const size_t rg = idx / nb;
+        const int n = (int)(rg % N);
+        mat = rg / N;
+        uint32_t words[4];
+        int S9[2];
+        load_block(codes, scales, mat, N, K, n, b, words, S9);
+        BlockBins bb;
+        block_bins(words, S9, bb);
+#pragma unroll
+        for (int c = 0; c < kNumCodebooks; ++c) {
+            double err;
+            block_best(bb, c, err);
+            e[c] = (unsigned long long)err;   // exact integer < 2^51
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kNumCodebooks; ++c) {
+        unsigned long long v = e[c];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) part[wave][c] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < kNumCodebooks && (size_t)blockIdx.x * 256 < total) {
+        const int c = threadIdx.x;
+        const unsigned long long v = part[0][c] + part[1][c] + part[2][c] + part[3][c];   // < 2^59
+        const size_t m = ((size_t)blockIdx.x * 256) / nb / N;
+        unsigned long long *sum = pick_sums(wcodes, m, N, K);
+        atomicAdd(sum + 2 * c, v & 0xFFFFFFFFull);
+        atomicAdd(sum + 2 * c + 1, v >> 32);
+    }
+}
+
+// codebook of each matrix: the smallest total (sum = hi * 2^32 + lo, compared exactly), ties lower
+__global__ __launch_bounds__(256) void pick_choose_kernel(const uint32_t *__restrict__ wcodes, int64_t n_mat, int N,
+                                                          int K, uint8_t *__restrict__ cbook)
+{
+    const size_t m = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (m >= (size_t)n_mat) return;
+    const unsigned long long *sum =
+        reinterpret_cast<const unsigned long long *>(wcodes + m * (size_t)N * (K / 16));
+    int best = 0;
+    unsigned long long bhi = 0, blo = 0;
+    for (int c = 0; c < kNumCodebooks; ++c) {
+        // normalise lo < 2^32 (the carries of the lo sums into hi)
+        const unsigned long long lo = sum[2 * c] & 0xFFFFFFFFull, hi = sum[2 * c + 1] + (sum[2 * c] >> 32);
+        if (c == 0 || hi < bhi || (hi == bhi && lo < blo)) {
+            best = c;
+            bhi = hi;
+            blo = lo;
+        }
+    }
+    cbook[m] = (uint8_t)best;
+}
+
 __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales,
                                                       const float *__restrict__ s2in, int64_t n_mat, int N, int K,
                                                       uint32_t *__restrict__ wcodes, uint8_t *__restrict__ wscales,
-                                                      float *__restrict__ ws2, int balance)
+                                                      float *__restrict__ ws2, const uint8_t *__restrict__ cbook,
+                                                      int balance)
 {
     const int nb = K / 32;
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -70,77 +275,18 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict_
     const size_t rg = idx / nb;
     const int n = (int)(rg % N);
     const size_t mat = rg / N;
-    if (n == 0 && b == 0) ws2[mat] = 2.0f * s2in[mat];
+    const int c = cbook ? min((int)cbook[mat], kNumCodebooks - 1) : 0;
+    if (n == 0 && b == 0) ws2[mat] = (float)(1 << cb_j(c)) * s2in[mat];
 
-    const uint4 cw = *reinterpret_cast<const uint4 *>(codes + (mat * N + n) * (size_t)(K / 2) + 16 * (size_t)b);
-    const uint32_t sw = *reinterpret_cast<const uint16_t *>(scales + (mat * N + n) * (size_t)(K / 16) + 2 * (size_t)b);
-    const int S9[2] = {e4m3_x512(sw & 0x7F), e4m3_x512((sw >> 8) & 0x7F)};
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
-
-    // histogram of magnitudes per 16-half
-    int cnt[2][8];
-    int amax = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t m0 = words[2 * h] & 0x77777777u, m1 = words[2 * h + 1] & 0x77777777u;
-#pragma unroll
-        for (int L = 1; L < 8; ++L) {
-            cnt[h][L] = count_nibbles_eq(m0, L) + count_nibbles_eq(m1, L);
-            if (cnt[h][L]) amax = max(amax, mag2_of(L) * S9[h]);
-        }
-        cnt[h][0] = 16;
-#pragma unroll
-        for (int L = 1; L < 8; ++L) cnt[h][0] -= cnt[h][L];
-    }
-
-    // Err(a) with the bins split at the level boundary: a bin (value y, count
-    // c) sits on level 1 iff 2y <= 5a (then (y-a)^2 <= (y-4a)^2), so with
-    // S1, C1 the sums of c*y and c over level-1 bins and S4, C4 over level-4
-    // bins,
-    //   Err(a) = sum c*y^2 - 2a (S1 + 4 S4) + a^2 (zeros + C1 + 16 C4),
-    // the same exact integer as the per-bin sum (every product and partial
-    // sum is an integer below 2^53, so float64 holds it exactly).
-    int best_t = 0;
-    if (amax > 0) {
-        const int t_lo = e4m3_floor_code(amax / 512);
-        const int t_hi = e4m3_ceil_code((amax + 3) / 4);
-        int yv[14], cy[14], cc[14];
-        double y2 = 0.0;
-        int stot = 0, ctot = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int L = 1; L < 8; ++L) {
-                const int i = 7 * h + L - 1;
-                yv[i] = mag2_of(L) * S9[h];                    // < 2^22
-                cc[i] = cnt[h][L];
-                cy[i] = cc[i] * yv[i];                         // < 2^27
-                y2 = fma((double)cy[i], (double)yv[i], y2);    // < 2^49, exact
-                stot += cy[i];
-                ctot += cc[i];
-            }
-        const int nzero = cnt[0][0] + cnt[1][0];
-        double best_err = -1.0;
-        for (int t = t_lo; t <= t_hi; ++t) {
-            const int ai = 4 * e4m3_x512(t);                   // < 2^20
-            int s1 = 0, c1 = 0;
-#pragma unroll
-            for (int i = 0; i < 14; ++i) {
-                const bool l1 = 2 * yv[i] <= 5 * ai;
-                s1 += l1 ? cy[i] : 0;
-                c1 += l1 ? cc[i] : 0;
-            }
-            const int lin = s1 + 4 * (stot - s1);              // < 2^29
-            const int quad = nzero + c1 + 16 * (ctot - c1);    // <= 512
-            const double ad = (double)ai;
-            const double err = fma(ad * ad, (double)quad, fma(-2.0 * ad, (double)lin, y2));
-            if (best_err < 0.0 || err < best_err) {   // ascending scan: ties keep the smaller scale
-                best_err = err;
-                best_t = t;
-            }
-        }
-    }
-    const int a = 4 * e4m3_x512(best_t);
+    uint32_t words[4];
+    int S9[2];
+    load_block(codes, scales, mat, N, K, n, b, words, S9);
+    BlockBins bb;
+    block_bins(words, S9, bb);
+    double err;
+    const int best_t = block_best(bb, c, err);
+    const int T = e4m3_x512(best_t);
+    const int lo = (cb_lo2(c) * T) << cb_j(c), hi = (cb_hi2(c) * T) << cb_j(c);
 
     // element codes -> two output words (k = 32b .. 32b+31 = words 2b, 2b+1)
     uint32_t out[2] = {0, 0};
@@ -151,7 +297,7 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict_
         for (int e = 0; e < 16; ++e) {
             const uint32_t nib = (words[2 * half + (e >> 3)] >> (4 * (e & 7))) & 15u;
             const int y = mag2_of(nib & 7) * S9[half];
-            const uint32_t m = (2 * y > 5 * a) ? 1u : 0u;
+            const uint32_t m = (2 * y > lo + hi) ? 1u : 0u;
             const uint32_t s = (balance && y == 0) ? (uint32_t)(zeros++ & 1) : nib >> 3;
             out[half] |= (m << mbit(e)) | (s << sbit(e));
         }
@@ -165,6 +311,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint8_t *__restrict__ 
                                                     const float *__restrict__ s2in, int64_t n_mat, int N, int K,
                                                     const uint32_t *__restrict__ wcodes,
                                                     const uint8_t *__restrict__ wscales,
+                                                    const uint8_t *__restrict__ cbook,
                                                     const int32_t *__restrict__ sel, int64_t n_sel,
                                                     uint8_t *__restrict__ dcodes, uint8_t *__restrict__ dscales,
                                                     float *__restrict__ ds2)
@@ -189,7 +336,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint8_t *__restrict__ 
     const uint32_t w2w[2] = {wmat[(((size_t)tile * (K / 64) + (2 * b) / 4) * 64 + r) * 4 + (2 * b) % 4],
                              wmat[(((size_t)tile * (K / 64) + (2 * b + 1) / 4) * 64 + r) * 4 + (2 * b + 1) % 4]};
     const int tau = wscales[(size_t)mat * N * (K / 32) + (((size_t)tile * (K / 128) + b / 4) * 64 + r) * 4 + (b % 4)];
-    const int a = 4 * e4m3_x512(tau);
+    const int c = cbook ? min((int)cbook[mat], kNumCodebooks - 1) : 0;
+    const int lo = (cb_lo2(c) * e4m3_x512(tau)) << cb_j(c), hi = (cb_hi2(c) * e4m3_x512(tau)) << cb_j(c);
 
     uint32_t out[4] = {0, 0, 0, 0};
     uint32_t sbytes = 0;
@@ -205,7 +353,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint8_t *__restrict__ 
             if (nib & 8) y = -y;
             const uint32_t w = w2w[half];
             const int m = (w >> mbit(e)) & 1, s = (w >> sbit(e)) & 1;
-            int lvl = m ? 4 * a : a;
+            int lvl = m ? hi : lo;
             if (s) lvl = -lvl;
             D[e] = y - lvl;
             M = max(M, abs(D[e]));
@@ -243,20 +391,46 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint8_t *__restrict__ 
     *reinterpret_cast<uint16_t *>(smat + (((size_t)tile * (K / 128) + b / 4) * 64 + r) * 8 + 2 * (b % 4)) = (uint16_t)sbytes;
 }
 
+__global__ __launch_bounds__(256) void cbook_fill_kernel(uint8_t *__restrict__ cbook, int64_t n_mat)
+{
+    const size_t m = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (m < (size_t)n_mat) cbook[m] = 0;
+}
+
 int launch_requant(const uint8_t *codes, const uint8_t *scales, const float *s2, int64_t n_mat, int N, int K,
-                   uint32_t *wc, uint8_t *wsc, float *ws2, const int32_t *sel, int64_t n_sel, uint8_t *dc,
-                   uint8_t *ds, float *ds2, int balance, hipStream_t stream)
+                   uint32_t *wc, uint8_t *wsc, float *ws2, uint8_t *cbook, const int32_t *sel, int64_t n_sel,
+                   uint8_t *dc, uint8_t *ds, float *ds2, int balance, int pick, hipStream_t stream)
 {
     const size_t total = (size_t)n_mat * N * (K / 32);
     const size_t blocks = (total + 255) / 256;
+    int rc;
+    if (pick) {
+        const size_t nsum = (size_t)n_mat * 2 * kNumCodebooks;
+        hipLaunchKernelGGL(pick_clear_kernel, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0, stream, wc, n_mat, N, K);
+        rc = check_launch("pick_clear_kernel");
+        if (rc != MOET_OK) return rc;
+        hipLaunchKernelGGL(pick_err_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, n_mat, N, K, wc);
+        rc = check_launch("pick_err_kernel");
+        if (rc != MOET_OK) return rc;
+        hipLaunchKernelGGL(pick_choose_kernel, dim3((unsigned)((n_mat + 255) / 256)), dim3(256), 0, stream,
+                           (const uint32_t *)wc, n_mat, N, K, cbook);
+        rc = check_launch("pick_choose_kernel");
+        if (rc != MOET_OK) return rc;
+    } else if (cbook) {
+        // no pick: every matrix takes codebook 0
+        hipLaunchKernelGGL(cbook_fill_kernel, dim3((unsigned)((n_mat + 255) / 256)), dim3(256), 0, stream, cbook, n_mat);
+        rc = check_launch("cbook_fill_kernel");
+        if (rc != MOET_OK) return rc;
+    }
     hipLaunchKernelGGL(requant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, s2, n_mat, N, K,
-                       wc, wsc, ws2, balance);
-    int rc = check_launch("requant_kernel");
+                       wc, wsc, ws2, (const uint8_t *)(pick ? cbook : nullptr), balance);
+    rc = check_launch("requant_kernel");
     if (rc != MOET_OK || n_sel == 0) return rc;
     const size_t dtotal = (size_t)n_sel * N * (K / 32);
     const size_t dblocks = (dtotal + 255) / 256;
     hipLaunchKernelGGL(delta_kernel, dim3((unsigned)dblocks), dim3(256), 0, stream, codes, scales, s2, n_mat, N, K,
-                       (const uint32_t *)wc, (const uint8_t *)wsc, sel, n_sel, dc, ds, ds2);
+                       (const uint32_t *)wc, (const uint8_t *)wsc, (const uint8_t *)(pick ? cbook : nullptr), sel, n_sel,
+                       dc, ds, ds2);
     return check_launch("delta_kernel");
 }
 

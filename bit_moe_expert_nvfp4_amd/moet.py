@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_PKG, "libmoet.so")
 MOET_OK, MOET_EINVAL, MOET_EUNSUPPORTED, MOET_EWORKSPACE, MOET_EHIP = range(5)
 SOFTMAX, SIGMOID = 0, 1
 BALANCE_ZERO_SIGNS = 1
+PICK_CODEBOOK = 2
+ABI_VERSION = 6        # the moet.h this binding mirrors
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -28,7 +30,7 @@ _i64 = ctypes.c_int64
 
 
 class W2(ctypes.Structure):
-    _fields_ = [("codes", _vp), ("scales", _vp), ("scale2", _vp)]
+    _fields_ = [("codes", _vp), ("scales", _vp), ("scale2", _vp), ("codebook", _vp)]
 
 
 class FP4(ctypes.Structure):
@@ -64,7 +66,10 @@ def lib():
         L.moet_last_error.argtypes = []
         L.moet_last_error.restype = ctypes.c_char_p
         L.moet_abi_version.restype = ctypes.c_int
-        L.moet_requant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+        if L.moet_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.moet_abi_version()}, this binding needs "
+                               f"{ABI_VERSION}: rebuild it")
+        L.moet_requant.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                    ctypes.c_uint32, _vp]
         L.moet_requant.restype = ctypes.c_int
         L.moet_pack_nvfp4.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
@@ -134,9 +139,11 @@ class W2Planes:
     scale2: torch.Tensor   # float32 [n_mat]
     N: int
     K: int
+    codebook: Optional[torch.Tensor] = None   # uint8 [n_mat] codebook ids (None: codebook 0 everywhere)
 
     def c(self) -> W2:
-        return W2(self.codes.data_ptr(), self.scales.data_ptr(), self.scale2.data_ptr())
+        return W2(self.codes.data_ptr(), self.scales.data_ptr(), self.scale2.data_ptr(),
+                  self.codebook.data_ptr() if self.codebook is not None else None)
 
 
 @dataclass
@@ -159,9 +166,11 @@ def _new_w2(n: int, N: int, K: int, dev) -> W2Planes:
 
 
 def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
-            delta_sel: Optional[torch.Tensor] = None, balance_zero_signs: bool = False):
+            delta_sel: Optional[torch.Tensor] = None, balance_zero_signs: bool = False,
+            pick_codebook: bool = False):
     """NVFP4 stack (codes uint8 [n, N, K/2], scales uint8 [n, N, K/16], scale2 f32 [n]) ->
-    W2Planes (and FP4Planes of the matrices listed in delta_sel, int32)."""
+    W2Planes (and FP4Planes of the matrices listed in delta_sel, int32).  pick_codebook: each
+    matrix picks its codebook (W2Planes.codebook holds the ids); otherwise codebook 0."""
     _need(codes, torch.uint8, "codes")
     _need(scales, torch.uint8, "scales")
     _need(scale2, torch.float32, "scale2")
@@ -169,6 +178,8 @@ def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
     K = 2 * Kh
     dev = codes.device
     w = _new_w2(n, N, K, dev)
+    if pick_codebook:
+        w.codebook = torch.empty((n,), dtype=torch.uint8, device=dev)
     d = None
     n_sel = 0
     if delta_sel is not None:
@@ -178,11 +189,12 @@ def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
                       torch.empty((n_sel, N * K // 16), dtype=torch.uint8, device=dev),
                       torch.empty((n_sel,), dtype=torch.float32, device=dev), N, K)
     _check(lib().moet_requant(_ptr(codes), _ptr(scales), _ptr(scale2), n, N, K,
-                              _ptr(w.codes), _ptr(w.scales), _ptr(w.scale2),
+                              _ptr(w.codes), _ptr(w.scales), _ptr(w.scale2), _ptr(w.codebook),
                               _ptr(delta_sel) if n_sel else None, n_sel,
                               _ptr(d.codes) if d else None, _ptr(d.scales) if d else None,
                               _ptr(d.scale2) if d else None,
-                              BALANCE_ZERO_SIGNS if balance_zero_signs else 0, _stream()))
+                              (BALANCE_ZERO_SIGNS if balance_zero_signs else 0)
+                              | (PICK_CODEBOOK if pick_codebook else 0), _stream()))
     return (w, d) if delta_sel is not None else w
 
 
@@ -309,7 +321,7 @@ def expert_cache(layer: Layer, slot_of_expert) -> Layer:
 
     def pick(pl: W2Planes, idx) -> W2Planes:
         return W2Planes(pl.codes[idx].contiguous(), pl.scales[idx].contiguous(), pl.scale2[idx].contiguous(),
-                        pl.N, pl.K)
+                        pl.N, pl.K, pl.codebook[idx].contiguous() if pl.codebook is not None else None)
     return dataclasses.replace(layer, w13=pick(layer.w13, idx13), w2=pick(layer.w2, idx2),
                                base_slot_of_expert=soe.to(torch.int32).to(dev))
 
@@ -442,12 +454,13 @@ def set_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cu
 # Building a layer from NVFP4 sources
 # ---------------------------------------------------------------------------
 def layer_from_nvfp4(src, slot_of_expert: Optional[torch.Tensor] = None, swiglu_limit: float = 0.0,
-                     device="cuda", shared_nvfp4: bool = False) -> Layer:
+                     device="cuda", shared_nvfp4: bool = False, pick_codebook: bool = False) -> Layer:
     """Requantise an NVFP4 layer (synth.NVFP4Layer-like: w13/w2/shared13/shared2 tuples of
     (codes, scales, scale2)) on the GPU and build the library layer; experts with
     slot_of_expert >= 0 also get their FP4 delta.  shared_nvfp4 keeps the shared expert
-    in NVFP4 instead of requantising it."""
+    in NVFP4 instead of requantising it.  pick_codebook: every matrix picks its codebook."""
     cfg = src.cfg
+    pk = dict(pick_codebook=pick_codebook)
 
     def dev(t):
         return t.to(device, non_blocking=True).contiguous()
@@ -464,19 +477,19 @@ def layer_from_nvfp4(src, slot_of_expert: Optional[torch.Tensor] = None, swiglu_
                 res[soe[e]] = e
         sel13 = torch.stack([2 * res, 2 * res + 1], dim=1).reshape(-1).to(torch.int32).to(device)
         sel2 = res.to(torch.int32).to(device)
-        w13, d13 = requant(*w13_src, delta_sel=sel13)
-        w2, d2 = requant(*w2_src, delta_sel=sel2)
+        w13, d13 = requant(*w13_src, delta_sel=sel13, **pk)
+        w2, d2 = requant(*w2_src, delta_sel=sel2, **pk)
         slot_dev = slot_of_expert.to(torch.int32).to(device)
     else:
-        w13 = requant(*w13_src)
-        w2 = requant(*w2_src)
+        w13 = requant(*w13_src, **pk)
+        w2 = requant(*w2_src, **pk)
         slot_dev = None
     sh13 = sh2 = f13 = f2 = None
     if src.shared13 is not None and shared_nvfp4:
         f13 = pack_nvfp4(*(dev(t) for t in src.shared13))
         f2 = pack_nvfp4(*(dev(t) for t in src.shared2))
     elif src.shared13 is not None:
-        sh13 = requant(*(dev(t) for t in src.shared13))
-        sh2 = requant(*(dev(t) for t in src.shared2))
+        sh13 = requant(*(dev(t) for t in src.shared13), **pk)
+        sh2 = requant(*(dev(t) for t in src.shared2), **pk)
     return Layer(cfg.H, cfg.I, cfg.E, w13, w2, sh13, sh2, slot_dev, d13, d2, swiglu_limit,
                  shared13_fp4=f13, shared2_fp4=f2)

@@ -115,6 +115,29 @@ def make_nvfp4_stack(n_mat: int, N: int, K: int, seed: int, tag: str, device="cp
     return codes, scales, s2
 
 
+# e2m1 magnitude of each 3-bit magnitude code
+_E2M1_MAGS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def skew_magnitudes(codes: torch.Tensor, mats, targets, frac: float, seed: int, tag: str) -> torch.Tensor:
+    """A copy of an NVFP4 code stack [n, N, K/2] in which, in the matrices `mats`, a random fraction
+    `frac` of the codes take the nearer (by e2m1 value, ties to the first) of the two magnitude codes
+    `targets`, sign kept: weights concentrated on two magnitudes, the shape of a tensor that another
+    sign-symmetric four-level codebook than {-4,-1,1,4} fits better."""
+    out = codes.clone()
+    lut = torch.tensor([min(targets, key=lambda t: (abs(_E2M1_MAGS[t] - _E2M1_MAGS[m]), targets.index(t)))
+                        for m in range(8)], dtype=torch.uint8)
+    for i in mats:
+        g = _gen("cpu", seed, tag, "skew", i)
+        c = out[i].cpu()
+        nib = torch.stack([c & 15, c >> 4], dim=-1)                       # [N, K/2, 2]
+        pick = torch.rand(nib.shape, generator=g) < frac
+        moved = (nib & 8) | lut[(nib & 7).long()]
+        nib = torch.where(pick, moved, nib)
+        out[i] = (nib[..., 0] | (nib[..., 1] << 4)).to(out.device)
+    return out
+
+
 def mxfp4_export(W: torch.Tensor):
     """OCP microscaling FP4 export of one fp32 matrix [N, K]: per 32 weights along K
     the e8m0 scale is 2^(floor(log2(amax32)) - 2) (2 = the largest e2m1 exponent),

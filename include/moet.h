@@ -59,13 +59,16 @@
  *    128 x 128 block, [ceil(N/128)][K/128]; weight = e4m3 * scale.
  *  2-bit planes ("W2"): rows are grouped in tiles of 64;
  *    codes uint32 word index ((n/64 * K/64 + k/64) * 64 + n%64) * 4 + (k%64)/16;
- *    inside a word, element e = k%16 has code c = (s<<1)|m (levels 0:+1 1:+4
- *    2:-1 3:-4) with m at bit 4e+2 and s at bit 4e+3 for e < 8, and m at bit
- *    4(e-8), s at bit 4(e-8)+1 for e >= 8 (nibble j: element j in bits 2-3,
- *    element j+8 in bits 0-1);
+ *    inside a word, element e = k%16 has code c = (s<<1)|m with m at bit
+ *    4e+2 and s at bit 4e+3 for e < 8, and m at bit 4(e-8), s at bit
+ *    4(e-8)+1 for e >= 8 (nibble j: element j in bits 2-3, element j+8 in
+ *    bits 0-1);
  *    block scales e4m3fn, one per 32 along k, byte index
  *    ((n/64 * K/128 + k/128) * 64 + n%64) * 4 + (k%128)/32;
- *    per-tensor scale2 fp32.  Weight = level * e4m3(scale) * scale2.
+ *    per-tensor scale2 fp32; per-tensor codebook id (uint8, optional).
+ *    Weight = level * e4m3(scale) * scale2 with level (code 0, 1, 2, 3) =
+ *    codebook 0 (the default): +1, +4, -1, -4;  codebook 1: +1/2, +3, -1/2, -3;
+ *    codebook 2: +0, +2, -0, -2.
  *    Storage: 2.25 bits per weight.
  *  FP4 delta planes ("FP4"): NVFP4 values in the same row tiling;
  *    code byte index ((n/64 * K/32 + k/32) * 64 + n%64) * 16 + (k%32)/2, even k
@@ -102,6 +105,15 @@ enum { MOET_SOFTMAX = 0, MOET_SIGMOID = 1 };
  * layer).  Block scales are unaffected: a zero costs the same either way. */
 enum { MOET_BALANCE_ZERO_SIGNS = 1 };
 
+/* moet_requant only.  MOET_PICK_CODEBOOK: each matrix picks its codebook
+ * (README "Frontier MoE on consumer Blackwell (SM120)", section "How it fits
+ * — 2-bit experts at FP4 quality": a per-tensor pick, won by {-4,-1,1,4} for
+ * nearly every tensor).  The candidates are the three sign-symmetric
+ * four-level codebooks of the 2-bit layout (magnitudes {1, 4}, {1/2, 3},
+ * {0, 2}); the pick is the one whose requantisation has the smallest exact
+ * total L2 error over the matrix, ties to the lower id. */
+enum { MOET_PICK_CODEBOOK = 2 };
+
 /* Static string for a status code. */
 const char *moet_status_str(int status);
 /* Thread-local detail of the last failed call on this thread ("" if none). */
@@ -117,15 +129,21 @@ int moet_abi_version(void);
  * quality".)
  *
  * Per 32 consecutive weights along K the block scale is the e4m3fn value that
- * minimises the exact L2 error of the block against the codebook
- * {-4,-1,1,4} * scale * scale2 (ties -> the smaller scale), scale2 = 2 *
- * scale_2; each weight takes the nearest level (a tie keeps magnitude 1) and
- * its sign from the NVFP4 sign bit, zeros included.  The search is exact.
+ * minimises the exact L2 error of the block against the codebook levels
+ * * scale * scale2 (ties -> the smaller scale); each weight takes the nearest
+ * level (a tie keeps the smaller magnitude) and its sign from the NVFP4 sign
+ * bit, zeros included.  The search is exact.  Codebook 0 ({-4,-1,1,4}, scale2
+ * = 2 * scale_2) unless flags hold MOET_PICK_CODEBOOK: then each matrix takes
+ * the codebook of smallest total error (1: {-3,-1/2,1/2,3}, scale2 = 2 *
+ * scale_2; 2: {-2,-0,+0,2}, scale2 = 4 * scale_2), and its id is written to
+ * w2_codebook.
  *
  * Inputs: fp4_codes uint8 [n_mat][N][K/2], fp4_scales uint8 [n_mat][N][K/16]
  *   (finite, non-negative e4m3fn), fp4_scale2 fp32 [n_mat].
  * Outputs: w2_codes uint32 [n_mat][N*K/16], w2_scales uint8 [n_mat][N*K/32],
- *   w2_scale2 fp32 [n_mat], all in the 2-bit layout above.
+ *   w2_scale2 fp32 [n_mat], all in the 2-bit layout above; w2_codebook uint8
+ *   [n_mat] (required with MOET_PICK_CODEBOOK; without it may be NULL, else
+ *   it is filled with 0).
  * Delta (n_sel > 0): delta_sel int32 [n_sel] (device) lists matrix indices;
  *   the delta of matrix delta_sel[i] = W_nvfp4 - W_2bit, re-encoded as NVFP4
  *   with the source scale_2 (block-16 scale nearest to max|D|/6, ties to the
@@ -133,16 +151,19 @@ int moet_abi_version(void);
  *   keeps D's sign), is written at slot i of d_codes uint8 [n_sel][N*K/2],
  *   d_scales uint8 [n_sel][N*K/16], d_scale2 fp32 [n_sel] (FP4 layout).
  *   n_sel == 0: delta_sel and d_* may be NULL.
- * flags: 0 or MOET_BALANCE_ZERO_SIGNS (the delta then follows the balanced
- *   codes).
+ * flags: 0 or a combination of MOET_BALANCE_ZERO_SIGNS (the delta then
+ *   follows the balanced codes) and MOET_PICK_CODEBOOK (the delta is taken
+ *   against the picked codebook).  With the pick, the first 48 bytes of each
+ *   matrix's w2_codes hold its error sums until the requant pass overwrites
+ *   them.
  * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
- *   pointers, n_sel < 0 or n_sel > n_mat, unknown flags.  Out-of-range
- *   delta_sel entries are skipped by the kernel (their slots are left
- *   unwritten).
+ *   pointers, n_sel < 0 or n_sel > n_mat, unknown flags, NULL w2_codebook
+ *   with MOET_PICK_CODEBOOK.  Out-of-range delta_sel entries are skipped by
+ *   the kernel (their slots are left unwritten).
  */
 int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2,
                  int64_t n_mat, int64_t N, int64_t K,
-                 uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2,
+                 uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint8_t *w2_codebook,
                  const int32_t *delta_sel, int64_t n_sel,
                  uint8_t *d_codes, uint8_t *d_scales, float *d_scale2,
                  uint32_t flags, void *stream);
@@ -240,11 +261,15 @@ int moet_route(const float *logits, int32_t T, int32_t E, int32_t top_k, int32_t
                int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *sorted_pairs,
                void *stream);
 
-/* 2-bit planes of a stack of matrices (device pointers; layout above). */
+/* 2-bit planes of a stack of matrices (device pointers; layout above).
+ * codebook: uint8 [n_mat] codebook id of each matrix (0, 1 or 2, as
+ * moet_requant writes it; larger values read as 2), or NULL: every matrix
+ * uses codebook 0. */
 typedef struct {
     const uint32_t *codes;
     const uint8_t *scales;
     const float *scale2;
+    const uint8_t *codebook;
 } moet_w2;
 
 /* FP4 delta planes of a stack of matrices (device pointers; layout above). */

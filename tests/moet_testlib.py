@@ -18,15 +18,21 @@ def np_(t: torch.Tensor) -> np.ndarray:
 
 
 class OracleMatrix:
-    """Oracle requant (and optional delta) of one NVFP4 matrix, plus its packed layout."""
+    """Oracle requant (and optional delta) of one NVFP4 matrix, plus its packed layout.  pick: the
+    matrix picks its codebook (else codebook 0)."""
 
-    def __init__(self, codes: np.ndarray, scales: np.ndarray, scale_2: float, with_delta: bool = False):
+    def __init__(self, codes: np.ndarray, scales: np.ndarray, scale_2: float, with_delta: bool = False,
+                 pick: bool = False):
         self.codes, self.scales, self.scale_2 = codes, scales, float(scale_2)
-        self.c2, self.tau, self.s2 = OR.requant(codes, scales, scale_2)
+        if pick:
+            self.cb, self.c2, self.tau, self.s2, self.totals = OR.pick_codebook(codes, scales, scale_2)
+        else:
+            self.cb = 0
+            self.c2, self.tau, self.s2 = OR.requant(codes, scales, scale_2)
         self.N, self.K = self.c2.shape
         self.dc = self.ds = self.d2 = None
         if with_delta:
-            self.dc, self.ds, self.d2 = OR.delta(codes, scales, scale_2, self.c2, self.tau)
+            self.dc, self.ds, self.d2 = OR.delta(codes, scales, scale_2, self.c2, self.tau, codebook=self.cb)
 
     def packed_codes(self):
         return OL.pack_2bit_codes(self.c2)
@@ -38,7 +44,7 @@ class OracleMatrix:
         return OL.pack_fp4_codes(self.dc), OL.pack_fp4_scales(self.ds)
 
     def w2bit(self):
-        return OR.dequant_2bit(self.c2, self.tau, self.s2)
+        return OR.dequant_2bit(self.c2, self.tau, self.s2, codebook=self.cb)
 
     def wdelta(self):
         return OR.dequant_fp4_codes(self.dc, self.ds, self.d2)
@@ -79,11 +85,12 @@ class ExpertPrefetch:
 class OracleLayer:
     """Lazily requantises the experts the oracle needs, straight from the NVFP4 bytes."""
 
-    def __init__(self, src, slot_of_expert=None, shared_nvfp4=False):
+    def __init__(self, src, slot_of_expert=None, shared_nvfp4=False, pick_codebook=False):
         self.src = src
         self.cfg = src.cfg
         self.soe = None if slot_of_expert is None else np_(slot_of_expert)
         self.shared_nvfp4 = shared_nvfp4
+        self.pick = pick_codebook
         self._cache = {}
         self._prefetch = None
         # host copies of the NVFP4 stacks, made once (threads then slice them without the GPU)
@@ -107,7 +114,7 @@ class OracleLayer:
         key = (id(stack), i, with_delta)
         if key not in self._cache:
             c, s, s2 = self._host_stack(stack)
-            self._cache[key] = OracleMatrix(c[i], s[i], float(s2[i]), with_delta)
+            self._cache[key] = OracleMatrix(c[i], s[i], float(s2[i]), with_delta, pick=self.pick)
         return self._cache[key]
 
     def resident(self, e):

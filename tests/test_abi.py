@@ -44,22 +44,30 @@ def test_status_strings(L):
 
 def test_requant_rejects_bad_shapes(L):
     buf = ctypes.c_void_p(16)      # never dereferenced: checks fail first
-    args = [buf, buf, buf, 1, 64, 128, buf, buf, buf, None, 0, None, None, None, 0, None]
-    for i, bad in [(4, 63), (5, 96), (3, 0), (10, -1), (10, 2), (14, 2)]:
+    # codes, scales, scale2, n_mat, N, K, w2 codes/scales/scale2/codebook, sel, n_sel, d x3, flags, stream
+    args = [buf, buf, buf, 1, 64, 128, buf, buf, buf, None, None, 0, None, None, None, 0, None]
+    for i, bad in [(4, 63), (5, 96), (3, 0), (11, -1), (11, 2), (15, 4), (15, 0x80000000),
+                   (15, 2),                           # the codebook pick needs w2_codebook
+                   (9, ctypes.c_void_p(8))]:          # misaligned w2_codebook
         a = list(args)
         a[i] = bad
-        assert L.moet_requant(*a) == 1
+        assert L.moet_requant(*a) == 1, (i, bad)
     a = list(args)
     a[0] = ctypes.c_void_p(8)      # misaligned
     assert L.moet_requant(*a) == 1
     assert b"aligned" in L.moet_last_error()
+    a = list(args)
+    a[15] = 2
+    a[9] = ctypes.c_void_p(8)
+    assert L.moet_requant(*a) == 1
+    assert b"w2_codebook" in L.moet_last_error()
 
 
 def test_source_conversions_reject_bad_args(L):
     buf = ctypes.c_void_p(16)      # never dereferenced: checks fail first
     for fn in (L.moet_remap_mxfp4, L.moet_requant_fp8):
         args = [buf, buf, 1, 64, 128, buf, buf, buf, 0, None]
-        for i, bad in [(3, 63), (4, 96), (2, 0), (8, 2), (8, 0x80000000)]:
+        for i, bad in [(3, 63), (4, 96), (2, 0), (8, 2), (8, 4), (8, 0x80000000)]:   # no codebook pick here
             a = list(args)
             a[i] = bad
             assert fn(*a) == 1, (fn, i, bad)

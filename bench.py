@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--inputs", type=int, default=8, help="input sets in the rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
-    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps (1 GiB written between steps)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps (1 GiB read between steps)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk (T=4096) measurement")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the delta-cache and batched decode legs")
@@ -70,6 +70,47 @@ def calibrate_copy(reps=10):
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "torch.mul fp32", "read_bytes": COPY_BYTES, "write_bytes": COPY_BYTES,
                       "launches": reps}), flush=True)
+
+
+def achievable_refs(dev, reps=10):
+    """Measured achievable rates of this device, for the fractions beside the published peaks: a
+    streaming read of 1 GiB (moet_probe_read: 16-byte loads, grid-stride, the weight kernels' access
+    shape), a 1 GiB device copy (torch copy_: 1 GiB read + 1 GiB written) and a bf16 GEMM
+    8192 x 8192 x 8192 (torch.matmul, hipBLASLt); the median of `reps` launches of each, HIP events
+    around every launch."""
+    import numpy as np
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) / 1e3
+
+    buf = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(buf)
+    sink = torch.empty((moet.PROBE_SINK_WORDS,), dtype=torch.int32, device=dev)
+    rd = timed(lambda: moet.probe_read(buf, sink))
+    cp = timed(lambda: dst.copy_(buf))
+    del buf, dst
+    M = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    a = torch.randn((M, M), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((M, M), generator=g, device=dev).to(torch.bfloat16).contiguous()
+    mm = timed(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"read_GBps": round(COPY_BYTES / rd / 1e9, 1), "copy_GBps": round(2 * COPY_BYTES / cp / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2.0 * M ** 3 / mm / 1e12, 1),
+            "method": f"median of {reps} launches each: moet_probe_read over 1 GiB (read rate); torch copy_ "
+                      f"1 GiB -> 1 GiB (read + write bytes / time); torch.matmul bf16 {M}^3 (2 M^3 / time)"}
 
 
 def summarize_counters(path):
@@ -136,8 +177,32 @@ def step_bytes(cfg, ids_np, flags_np, soe_np, resident=None, shared_nvfp4=False)
     return total, fc1, n, nd
 
 
-def cpu_baseline(cfg, src, x, lg, seed):
-    """Time the float64 oracle (route + the layer output of every token) on the host cores."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _median_time(fn, runs=3):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(sorted(ts)[len(ts) // 2]), ts
+
+
+def cpu_baseline(cfg, src, x, lg, seed, cfg_prefill=None, x_prefill=None, lg_prefill=None, runs=3):
+    """Time the float64 oracle on the host cores (median of `runs` runs of each bounded sample):
+    the decode step (route + the layer output of every token), the load-time requant of two matrices
+    (scaled to a layer), and a prefill sample (route of the whole chunk, the expert FFN of every pair
+    routed to two experts; scaled to the chunk)."""
     import numpy as np
     from oracle import formats as OF
     from oracle import requant as OR
@@ -163,18 +228,65 @@ def cpu_baseline(cfg, src, x, lg, seed):
 
     def dq(p):
         return OR.dequant_2bit(*p)
-    t0 = time.perf_counter()
-    ids2, w2, _, _ = ORT.route(lg_np, cfg.k, cfg.score, cfg.renormalize)
-    OFF.moe_forward(xb, ids2, w2, lambda e: tuple(dq(p) for p in planes[e]),
-                    tuple(dq(p) for p in shared) if shared else None)
-    dt = time.perf_counter() - t0
+
+    def decode_step():
+        ids2, w2, _, _ = ORT.route(lg_np, cfg.k, cfg.score, cfg.renormalize)
+        OFF.moe_forward(xb, ids2, w2, lambda e: tuple(dq(p) for p in planes[e]),
+                        tuple(dq(p) for p in shared) if shared else None)
+    dt, dts = _median_time(decode_step, runs)
     n = len(experts) + (1 if cfg.shared else 0)
     nbytes = n * 3 * cfg.I * cfg.H * W2_BYTES_PER_WEIGHT + 2 * cfg.T * cfg.H * 2 + 4 * cfg.T * cfg.E
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
-            "sample": f"one full step of input set 0: routing and the layer output of all {cfg.T} tokens "
-                      f"({n} distinct experts incl. shared, {nbytes / 1e6:.1f} MB of 2-bit planes, dequantised "
-                      f"and applied in float64 numpy from the oracle's own requantised planes), {dt:.2f} s",
-            "seconds": dt}
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    res = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+           "cpu_model": _cpu_model(), "runs": runs, "run_seconds": [round(t, 3) for t in dts],
+           "sample": f"one full decode step of input set 0, median of {runs} runs: routing and the layer "
+                     f"output of all {cfg.T} tokens ({n} distinct experts incl. shared, {nbytes / 1e6:.1f} MB "
+                     f"of 2-bit planes, dequantised and applied in float64 numpy from the oracle's own "
+                     f"requantised planes), {dt:.2f} s"}
+
+    # load-time requant: two gate/up matrices of the layer, scaled to the layer's matrices
+    c13, s13, z13 = (npy(t[:2]) for t in src.w13)
+    rq_t, _ = _median_time(lambda: [OR.requant(c13[i], s13[i], float(z13[i])) for i in range(2)], runs)
+    n_mat = 3 * cfg.E + (3 if cfg.shared else 0)
+    res["requant"] = {"s_per_matrix": round(rq_t / 2, 3), "scaled_s_per_layer": round(rq_t / 2 * n_mat, 1),
+                      "threads": omp,
+                      "sample": f"oracle requant (C, exact 127-code scan, OpenMP over rows) of gate/up matrices "
+                                f"0 and 1 [{cfg.I}][{cfg.H}] of the layer, median of {runs} runs; scaled by "
+                                f"{n_mat} / 2 to the layer's {n_mat} equal-size matrices"}
+
+    if cfg_prefill is not None:
+        cp = cfg_prefill
+        lgp = npy(lg_prefill)
+        xpb = OF.bf16_rne_bits(npy(x_prefill.float()).astype(np.float64))
+        xpv = OF.bf16_bits_to_f64(xpb)
+        route_t, _ = _median_time(lambda: ORT.route(lgp, cp.k, cp.score, cp.renormalize), runs)
+        pids, _, offs, pairs = ORT.route(lgp, cp.k, cp.score, cp.renormalize)
+        rng = np.random.default_rng(seed)
+        sample_e = sorted(int(e) for e in rng.choice(cp.E, size=2, replace=False))
+        sp = {e: (rq(src.w13, 2 * e), rq(src.w13, 2 * e + 1), rq(src.w2, e)) for e in sample_e}
+        toks = {e: pairs[offs[e]:offs[e + 1]] // cp.k for e in sample_e}
+        n_pairs = sum(len(v) for v in toks.values())
+
+        def deq():
+            return {e: tuple(dq(p) for p in sp[e]) for e in sample_e}
+        deq_t, _ = _median_time(deq, runs)
+        W = deq()
+
+        def ffn():
+            for e in sample_e:
+                Wg, Wu, Wd = W[e]
+                OFF.expert_out(OFF.expert_hidden(xpv[toks[e]], Wg, Wu, cp.swiglu_limit), Wd)
+        ffn_t, _ = _median_time(ffn, runs)
+        chunk_s = route_t + deq_t / 2 * cp.E + ffn_t / max(n_pairs, 1) * cp.T * cp.k
+        res["prefill"] = {"value": round(cp.T / chunk_s, 2), "unit": "tokens/s",
+                          "scaled_s_per_chunk": round(chunk_s, 1),
+                          "sample": f"prefill chunk T={cp.T} (the GPU leg's logits and activations): oracle route "
+                                    f"of all {cp.T} tokens ({route_t:.2f} s), dequantisation of experts "
+                                    f"{sample_e} ({deq_t:.2f} s) and their expert FFN over all {n_pairs} routed "
+                                    f"pairs ({ffn_t:.2f} s), medians of {runs} runs; chunk time = route + "
+                                    f"dequant x {cp.E}/2 experts + FFN x {cp.T * cp.k}/{n_pairs} pairs (the "
+                                    f"weighted combine, {cp.T}x{cp.k}x{cp.H} multiply-adds, is left out)"}
+    return res
 
 
 def _blas_threads():
@@ -526,22 +638,26 @@ def main():
     step_us = np.array([marks[i].elapsed_time(marks[i + 1]) * 1e3 for i in range(K)])
     instrumented_us = marks[0].elapsed_time(marks[K]) / K * 1e3
 
-    # cold steps: 1 GiB written between steps evicts the caches; only the step is timed
+    # cold steps: a 1 GiB streaming read between steps evicts the caches (the 256 MB last-level cache
+    # and the L2s) without leaving dirty lines to write back during the step; only the step is timed
     cold = None
     if not args.no_cold:
-        scratch = torch.empty((1 << 28,), dtype=torch.float32, device=dev)
+        scratch = torch.ones((COPY_BYTES // 4,), dtype=torch.float32, device=dev)
+        sink = torch.empty((moet.PROBE_SINK_WORDS,), dtype=torch.int32, device=dev)
         nc = min(K, 50)
         ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nc)]
+        torch.cuda.synchronize()
         for i in range(nc):
-            scratch.fill_(float(i))
+            moet.probe_read(scratch, sink)
             ce[i][0].record()
             step(args.warmup + i)
             ce[i][1].record()
         torch.cuda.synchronize()
         cus = np.array([a.elapsed_time(b) * 1e3 for a, b in ce])
-        cold = {"steps": nc, "median_us": round(float(np.median(cus)), 2), "p10_us": round(float(np.percentile(cus, 10)), 2),
+        cold = {"steps": nc, "eviction": "1 GiB streaming read between steps",
+                "median_us": round(float(np.median(cus)), 2), "p10_us": round(float(np.percentile(cus, 10)), 2),
                 "p90_us": round(float(np.percentile(cus, 90)), 2)}
-        del scratch
+        del scratch, sink
         torch.cuda.empty_cache()
 
     # the same steps replayed from HIP graphs (one graph per layer/input combination)
@@ -570,7 +686,28 @@ def main():
         gms = g0.elapsed_time(g1) / K
         gbytes = sum(per_input[(args.warmup + i) % combos % args.inputs][0] for i in range(K)) / K
         graph = {"us_per_layer": round(gms * 1e3, 2), "GBps": round(gbytes / (gms / 1e3) / 1e9, 1),
-                 "pct_hbm_peak": round(100.0 * gbytes / (gms / 1e3) / 1e9 / HBM_PEAK_GBS, 1)}
+                 "pct_hbm_peak": round(100.0 * gbytes / (gms / 1e3) / 1e9 / HBM_PEAK_GBS, 1),
+                 "steps_per_graph": 1}
+        # one graph holding all `combos` steps back to back (a whole model's decode step is one graph
+        # in a serving loop): separates the per-graph-launch cost from the per-kernel-node cost
+        gm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gm, stream=cap):
+            for c in range(combos):
+                step(c)
+        torch.cuda.synchronize()
+        reps = max(1, K // combos)
+        for _ in range(2):
+            gm.replay()
+        torch.cuda.synchronize()
+        g0.record()
+        for _ in range(reps):
+            gm.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        mms = g0.elapsed_time(g1) / (reps * combos)
+        mbytes = sum(per_input[c % args.inputs][0] for c in range(combos)) / combos
+        graph["multi_step"] = {"steps_per_graph": combos, "replays": reps, "us_per_layer": round(mms * 1e3, 2),
+                               "GBps": round(mbytes / (mms / 1e3) / 1e9, 1)}
         # replayed graphs must reproduce the eager output bit for bit
         ref = out.clone()
         step(args.warmup + K - 1)
@@ -579,6 +716,9 @@ def main():
         torch.cuda.synchronize()
         graph["replay_matches_eager"] = bool(torch.equal(out, eager_last))
         del ref
+
+    print("[bench] measuring the achievable HBM read / copy and bf16 GEMM rates", file=sys.stderr, flush=True)
+    ach = achievable_refs(dev)
 
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / K
@@ -610,6 +750,8 @@ def main():
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.k},
         "us_per_layer": round(ms_per_step * 1e3, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "pct_hbm_achievable_read": round(100.0 * gbs / ach["read_GBps"], 1),
+        "achievable": ach,
         "tokens_per_s": round(cfg.T / (ms_per_step / 1e3), 1),
         "mean_experts_per_step": round(float(n_experts), 2),
         "algorithmic_bytes_per_step": round(tot_bytes / K),
@@ -629,6 +771,8 @@ def main():
             "unit": "GB/s",
             "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(),
+            "achievable_peak": ach["read_GBps"],
+            "frac_achievable": round(fc1_gbs / ach["read_GBps"], 4),
             "avg_launch_us": round(1e3 * float(np.mean(fc1_ms)), 2),
             "algorithmic_bytes_per_launch": round(fc1_bytes / K),
         },
@@ -638,24 +782,27 @@ def main():
         import dataclasses
         pl = dataclasses.replace(layers[0], shared13=None, shared2=None)
         result["prefill"] = prefill_leg(pl, synth.CONFIGS[5], args.prefill_steps, args.seed, dev)
+        # the same chunk with gate-flagged tokens on delta-cache experts, right after and with as many steps
+        print("[bench] timing the prefill chunk with the FP4 delta", file=sys.stderr, flush=True)
+        cfgd = dataclasses.replace(synth.CONFIGS[5], name="prefill_delta", n_resident=32, n_flagged=2048)
+        srcd = synth.make_layer(cfgd, seed=args.seed, device=dev)
+        soed = synth.slot_of_expert(cfgd, args.seed)
+        ld = moet.layer_from_nvfp4(srcd, soed)
+        del srcd
+        torch.cuda.empty_cache()
+        result["prefill_delta"] = prefill_leg(ld, cfgd, args.prefill_steps, args.seed, dev,
+                                              flags=synth.gate_flags(cfgd, args.seed).to(dev), soe=soed)
+        del ld
+        torch.cuda.empty_cache()
+        for key in ("prefill", "prefill_delta"):
+            rf = result[key]["roofline"]
+            rf["achievable_peak"] = ach["bf16_gemm_TFLOPs"]
+            rf["frac_achievable"] = round(rf["achieved"] / ach["bf16_gemm_TFLOPs"], 4)
     if not args.no_extra:
         print("[bench] timing the confidence gate", file=sys.stderr, flush=True)
         result["confidence_gate"] = gate_leg(args.seed, dev)
         print("[bench] timing the load-time conversions", file=sys.stderr, flush=True)
         result["load_conversions"] = conversion_leg(args.seed, dev)
-        if not args.no_prefill:
-            print("[bench] timing the prefill chunk with the FP4 delta", file=sys.stderr, flush=True)
-            import dataclasses
-            cfgd = dataclasses.replace(synth.CONFIGS[5], name="prefill_delta", n_resident=32, n_flagged=2048)
-            srcd = synth.make_layer(cfgd, seed=args.seed, device=dev)
-            soed = synth.slot_of_expert(cfgd, args.seed)
-            ld = moet.layer_from_nvfp4(srcd, soed)
-            del srcd
-            torch.cuda.empty_cache()
-            result["prefill_delta"] = prefill_leg(ld, cfgd, max(3, args.prefill_steps // 2), args.seed, dev,
-                                                  flags=synth.gate_flags(cfgd, args.seed).to(dev), soe=soed)
-            del ld
-            torch.cuda.empty_cache()
         del layers
         torch.cuda.empty_cache()
         result["other_decode"] = {}
@@ -670,8 +817,10 @@ def main():
                                                             shared_nvfp4=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        cb = cpu_baseline(cfg, srcs[0], xs[0], lgs[0], args.seed)
-        cb.pop("seconds", None)
+        c5 = synth.CONFIGS[5]
+        cb = cpu_baseline(cfg, srcs[0], xs[0], lgs[0], args.seed, cfg_prefill=c5,
+                          x_prefill=synth.make_activations(c5.T, c5.H, args.seed, tag="prefill_x", device=dev),
+                          lg_prefill=synth.make_logits(c5, args.seed, tag="prefill_logits", device=dev))
         cb["value"] = round(cb["value"], 4)
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)

@@ -96,6 +96,8 @@ def lib():
         L.moet_confidence_gate.restype = ctypes.c_int
         L.moet_set_timing_events.argtypes = [_vp, _vp]
         L.moet_set_timing_events.restype = ctypes.c_int
+        L.moet_probe_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+        L.moet_probe_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -448,6 +450,17 @@ def set_timing_events(start: Optional[torch.cuda.Event], stop: Optional[torch.cu
         _check(lib().moet_set_timing_events(None, None))
     else:
         _check(lib().moet_set_timing_events(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)))
+
+
+PROBE_SINK_WORDS = 8192
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Measurement reference (moet_probe_read): read every byte of the contiguous device tensor `buf`
+    once with the weight kernels' access shape; `sink` is an int32 device tensor of PROBE_SINK_WORDS."""
+    if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < PROBE_SINK_WORDS:
+        raise ValueError("probe_read needs a contiguous buffer and an int32 sink of PROBE_SINK_WORDS words")
+    _check(lib().moet_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream()))
 
 
 # ---------------------------------------------------------------------------

@@ -6,6 +6,9 @@
 #ifndef MOET_INSTRUMENT_H
 #define MOET_INSTRUMENT_H
 
+#include <stddef.h>
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -20,6 +23,22 @@ extern "C" {
  * pass NULL, NULL to disable.  Returns MOET_EINVAL if only one is NULL.
  */
 int moet_set_timing_events(void *start, void *stop);
+
+/* Words of the sink array moet_probe_read writes. */
+#define MOET_PROBE_SINK_WORDS 8192
+
+/*
+ * moet_probe_read - measurement reference: reads every byte of `src` once
+ * with 16-byte loads in a grid-stride loop over 1024 workgroups of 4 waves
+ * (the fastest streaming-read shape measured on MI355X), and writes one xor
+ * word per wave to `sink` (uint32 [MOET_PROBE_SINK_WORDS], device) so that
+ * no load can be dropped.  Timing it gives the achievable HBM read rate
+ * on the running device; it also evicts the caches without dirtying them.
+ * src: device memory, `bytes` long (a positive multiple of 16).  Enqueued on
+ * `stream`.  Returns MOET_EINVAL for NULL or misaligned pointers or a bad
+ * size, MOET_EHIP if the launch fails.
+ */
+int moet_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

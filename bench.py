@@ -445,6 +445,8 @@ def conversion_leg(seed, dev, n_mat=16, N=2048, K=7168, steps=5):
     f8 = synth.make_fp8_stack(n_mat, N, K, seed, "conv_fp8", device=dev)
     out_bytes = n_mat * (N * K // 4 + N * K // 32)
     legs = (("nvfp4_requant", lambda: moet.requant(*nv), n_mat * (N * K // 2 + N * K // 16)),
+            ("nvfp4_requant_codebook_pick", lambda: moet.requant(*nv, pick_codebook=True),
+             n_mat * (N * K // 2 + N * K // 16)),
             ("mxfp4_remap", lambda: moet.remap_mxfp4(*mx), n_mat * (N * K // 2 + N * K // 32)),
             ("fp8_requant", lambda: moet.requant_fp8(*f8), n_mat * (N * K + 4 * ((N + 127) // 128) * (K // 128))))
     res = {}

@@ -35,8 +35,16 @@
 // the matrix's output code plane, which the requant pass overwrites), a
 // second pass picks the codebook with the smallest total (ties to the lower
 // index), and the requant pass writes the codes of each matrix's codebook.
-// Codebook 0 keeps the search window above; codebooks 1 and 2 scan all 127
-// scale codes.
+// Each codebook has its own search window, by the argument above: below the
+// window the largest element's slope, -2 hi (amax - HI) in units of the
+// scale, outweighs the at most 31 max(2 lo^2, hi (hi - lo)) of the others
+// (codebook 0: below amax/50; 1: amax/41; 2: amax/33, taken with margin as
+// the code with a <= amax/128, amax/64, amax/64, a = 4 T, 4 T, 8 T), so Err
+// falls there; above it every element sits on LO and Err rises (LO >= amax,
+// codebooks 0 and 1) or is constant at sum y^2 (HI >= 2 amax, codebook 2,
+// whose LO is 0), which the smallest-scale tie rule settles at the window's
+// end.  Windows in T: [amax/512, amax/4], [amax/256, amax/2], [amax/512,
+// amax/8].
 #include "moet_common.h"
 
 namespace moet {
@@ -144,10 +152,16 @@ __device__ __forceinline__ int block_best(const BlockBins &bb, int c, double &be
 {
     best_err = 0.0;
     if (bb.amax == 0) return 0;   // every level of scale 0 is exact
-    int t_lo = 0, t_hi = 126;
+    int t_lo, t_hi;
     if (c == 0) {
         t_lo = e4m3_floor_code(bb.amax / 512);
         t_hi = e4m3_ceil_code((bb.amax + 3) / 4);
+    } else if (c == 1) {
+        t_lo = e4m3_floor_code(bb.amax / 256);
+        t_hi = e4m3_ceil_code((bb.amax + 1) / 2);
+    } else {
+        t_lo = e4m3_floor_code(bb.amax / 512);
+        t_hi = e4m3_ceil_code((bb.amax + 7) / 8);
     }
     const int lo2 = cb_lo2(c), hi2 = cb_hi2(c), j = cb_j(c);
     int best_t = t_lo;

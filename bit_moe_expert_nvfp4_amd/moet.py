@@ -98,6 +98,8 @@ def lib():
         L.moet_set_timing_events.restype = ctypes.c_int
         L.moet_probe_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
         L.moet_probe_read.restype = ctypes.c_int
+        L.moet_probe_peak.argtypes = [ctypes.c_int, _i32, _vp, _vp]
+        L.moet_probe_peak.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -461,6 +463,19 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
     if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < PROBE_SINK_WORDS:
         raise ValueError("probe_read needs a contiguous buffer and an int32 sink of PROBE_SINK_WORDS words")
     _check(lib().moet_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream()))
+
+
+PROBE_MFMA_BF16, PROBE_DOT2_BF16 = 0, 1
+PROBE_PEAK_WAVES = 4096   # waves of one moet_probe_peak launch
+
+
+def probe_peak(kind: int, iters: int, sink: torch.Tensor) -> None:
+    """Measurement reference (moet_probe_peak): a tight loop of bf16 MFMAs (PROBE_MFMA_BF16: 4 x 32,768
+    flops per round per wave) or dot2 instructions (PROBE_DOT2_BF16: 8 per round per wave) over
+    PROBE_PEAK_WAVES waves; `sink` is an int32 device tensor of PROBE_SINK_WORDS."""
+    if sink.dtype != torch.int32 or sink.numel() < PROBE_SINK_WORDS:
+        raise ValueError("probe_peak needs an int32 sink of PROBE_SINK_WORDS words")
+    _check(lib().moet_probe_peak(int(kind), int(iters), _ptr(sink), _stream()))
 
 
 # ---------------------------------------------------------------------------

@@ -40,6 +40,25 @@ int moet_set_timing_events(void *start, void *stop);
  */
 int moet_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
+enum { MOET_PROBE_MFMA_BF16 = 0, MOET_PROBE_DOT2_BF16 = 1 };
+
+/*
+ * moet_probe_peak - measurement reference: the sustained issue rate of one
+ * instruction with no memory traffic, over 1024 workgroups of 4 waves (4 per
+ * CU).  Each wave runs `iters` rounds of 4 (MFMA) or 8 (dot2) independent
+ * accumulation chains and writes one word to `sink` (uint32
+ * [MOET_PROBE_SINK_WORDS], device) so that nothing can be dropped.
+ *   MOET_PROBE_MFMA_BF16: v_mfma_f32_32x32x16_bf16, 32,768 flops each, 4 per
+ *     round per wave: flops = 1024 * 4 * 4 * iters * 32768.
+ *   MOET_PROBE_DOT2_BF16: v_dot2_f32_bf16, 8 per round per wave:
+ *     wave instructions = 1024 * 4 * 8 * iters.
+ * Timing it gives the matrix-core and vector-ALU peaks the running device
+ * sustains (its clock under that load included).  Returns MOET_EINVAL for a
+ * NULL or misaligned sink, iters < 1 or an unknown kind, MOET_EHIP if the
+ * launch fails.
+ */
+int moet_probe_peak(int kind, int32_t iters, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

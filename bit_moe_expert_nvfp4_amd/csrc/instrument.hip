@@ -80,27 +80,29 @@ __global__ __launch_bounds__(256) void probe_dot2_kernel(int iters, uint32_t *__
 
 using namespace moet;
 
-extern "C" int moet_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream)
+extern "C" moet_status moet_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream)
 {
     set_error("%s", "");
-    if (!aligned16(src) || !aligned16(sink)) return fail(MOET_EINVAL, "src and sink must be non-NULL and 16-byte aligned");
-    if (bytes == 0 || bytes % 16) return fail(MOET_EINVAL, "bytes (%zu) must be a positive multiple of 16", bytes);
+    if (!aligned16(src) || !aligned16(sink))
+        return (moet_status)(fail(MOET_EINVAL, "src and sink must be non-NULL and 16-byte aligned"));
+    if (bytes == 0 || bytes % 16)
+        return (moet_status)(fail(MOET_EINVAL, "bytes (%zu) must be a positive multiple of 16", bytes));
     hipLaunchKernelGGL(probe_read_kernel, dim3(kProbeBlocks), dim3(256), 0, (hipStream_t)stream,
                        (const uint4 *)src, bytes / 16, sink);
-    return check_launch("probe_read_kernel");
+    return (moet_status)(check_launch("probe_read_kernel"));
 }
 
-extern "C" int moet_probe_peak(int kind, int32_t iters, uint32_t *sink, void *stream)
+extern "C" moet_status moet_probe_peak(int kind, int32_t iters, uint32_t *sink, void *stream)
 {
     set_error("%s", "");
-    if (!aligned16(sink)) return fail(MOET_EINVAL, "sink must be non-NULL and 16-byte aligned");
-    if (iters < 1) return fail(MOET_EINVAL, "iters (%d) must be >= 1", iters);
+    if (!aligned16(sink)) return (moet_status)(fail(MOET_EINVAL, "sink must be non-NULL and 16-byte aligned"));
+    if (iters < 1) return (moet_status)(fail(MOET_EINVAL, "iters (%d) must be >= 1", iters));
     static_assert(kPeakBlocks * 4 <= MOET_PROBE_SINK_WORDS, "sink too small");
     if (kind == MOET_PROBE_MFMA_BF16)
         hipLaunchKernelGGL(probe_mfma_kernel, dim3(kPeakBlocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
     else if (kind == MOET_PROBE_DOT2_BF16)
         hipLaunchKernelGGL(probe_dot2_kernel, dim3(kPeakBlocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
     else
-        return fail(MOET_EINVAL, "unknown probe kind %d", kind);
-    return check_launch("probe peak kernel");
+        return (moet_status)(fail(MOET_EINVAL, "unknown probe kind %d", kind));
+    return (moet_status)(check_launch("probe peak kernel"));
 }

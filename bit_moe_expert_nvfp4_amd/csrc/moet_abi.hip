@@ -146,7 +146,7 @@ using namespace moet;
 
 extern "C" {
 
-const char *moet_status_str(int s)
+const char *moet_status_str(moet_status s)
 {
     switch (s) {
     case MOET_OK: return "MOET_OK";
@@ -175,83 +175,87 @@ static int check_stack(int64_t n_mat, int64_t N, int64_t K, uint32_t flags,
     return MOET_OK;
 }
 
-int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
+moet_status moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
                  int64_t N, int64_t K, uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2,
                  uint8_t *w2_codebook, const int32_t *delta_sel, int64_t n_sel, uint8_t *d_codes,
                  uint8_t *d_scales, float *d_scale2, uint32_t flags, void *stream)
 {
     g_err[0] = 0;
     int rc = check_stack(n_mat, N, K, flags, MOET_BALANCE_ZERO_SIGNS | MOET_PICK_CODEBOOK);
-    if (rc != MOET_OK) return rc;
+    if (rc != MOET_OK) return (moet_status)(rc);
     const bool pick = (flags & MOET_PICK_CODEBOOK) != 0;
     if (pick && !aligned16(w2_codebook))
-        return fail(MOET_EINVAL, "MOET_PICK_CODEBOOK needs a non-NULL, 16-byte aligned w2_codebook");
-    if (w2_codebook && !aligned16(w2_codebook)) return fail(MOET_EINVAL, "w2_codebook must be 16-byte aligned");
+        return (moet_status)(fail(MOET_EINVAL, "MOET_PICK_CODEBOOK needs a non-NULL, 16-byte aligned w2_codebook"));
+    if (w2_codebook && !aligned16(w2_codebook))
+        return (moet_status)(fail(MOET_EINVAL, "w2_codebook must be 16-byte aligned"));
     if (!aligned16(fp4_codes) || !aligned16(fp4_scales) || !aligned16(fp4_scale2) || !aligned16(w2_codes) ||
         !aligned16(w2_scales) || !aligned16(w2_scale2))
-        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
-    if (n_sel < 0 || n_sel > n_mat) return fail(MOET_EINVAL, "n_sel (%lld) must be in [0, n_mat]", (long long)n_sel);
+        return (moet_status)(fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned"));
+    if (n_sel < 0 || n_sel > n_mat)
+        return (moet_status)(fail(MOET_EINVAL, "n_sel (%lld) must be in [0, n_mat]", (long long)n_sel));
     if (n_sel > 0 && (!aligned16(delta_sel) || !aligned16(d_codes) || !aligned16(d_scales) || !aligned16(d_scale2)))
-        return fail(MOET_EINVAL, "delta pointers must be non-NULL and 16-byte aligned when n_sel > 0");
-    return launch_requant(fp4_codes, fp4_scales, fp4_scale2, n_mat, (int)N, (int)K, w2_codes, w2_scales, w2_scale2,
-                          w2_codebook, delta_sel, n_sel, d_codes, d_scales, d_scale2,
-                          (int)(flags & MOET_BALANCE_ZERO_SIGNS), (int)pick, (hipStream_t)stream);
+        return (moet_status)(fail(MOET_EINVAL, "delta pointers must be non-NULL and 16-byte aligned when n_sel > 0"));
+    return (moet_status)launch_requant(fp4_codes, fp4_scales, fp4_scale2, n_mat, (int)N, (int)K, w2_codes, w2_scales, w2_scale2,
+                                       w2_codebook, delta_sel, n_sel, d_codes, d_scales, d_scale2,
+                                       (int)(flags & MOET_BALANCE_ZERO_SIGNS), (int)pick, (hipStream_t)stream);
 }
 
-int moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
+moet_status moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2, int64_t n_mat,
                     int64_t N, int64_t K, uint8_t *d_codes, uint8_t *d_scales, float *d_scale2, void *stream)
 {
     g_err[0] = 0;
     int rc = check_stack(n_mat, N, K, 0);
-    if (rc != MOET_OK) return rc;
+    if (rc != MOET_OK) return (moet_status)(rc);
     if (!aligned16(fp4_codes) || !aligned16(fp4_scales) || !aligned16(fp4_scale2) || !aligned16(d_codes) ||
         !aligned16(d_scales) || !aligned16(d_scale2))
-        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
-    return launch_pack_nvfp4(fp4_codes, fp4_scales, fp4_scale2, n_mat, (int)N, (int)K, d_codes, d_scales, d_scale2,
-                             (hipStream_t)stream);
+        return (moet_status)(fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned"));
+    return (moet_status)launch_pack_nvfp4(fp4_codes, fp4_scales, fp4_scale2, n_mat, (int)N, (int)K, d_codes, d_scales, d_scale2,
+                                          (hipStream_t)stream);
 }
 
-int moet_remap_mxfp4(const uint8_t *mx_codes, const uint8_t *mx_scales, int64_t n_mat, int64_t N, int64_t K,
+moet_status moet_remap_mxfp4(const uint8_t *mx_codes, const uint8_t *mx_scales, int64_t n_mat, int64_t N, int64_t K,
                      uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint32_t flags, void *stream)
 {
     g_err[0] = 0;
     int rc = check_stack(n_mat, N, K, flags);
-    if (rc != MOET_OK) return rc;
+    if (rc != MOET_OK) return (moet_status)(rc);
     if (!aligned16(mx_codes) || !aligned16(mx_scales) || !aligned16(w2_codes) || !aligned16(w2_scales) ||
         !aligned16(w2_scale2))
-        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
-    return launch_remap_mxfp4(mx_codes, mx_scales, n_mat, (int)N, (int)K, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
-                              w2_codes, w2_scales, w2_scale2, (hipStream_t)stream);
+        return (moet_status)(fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned"));
+    return (moet_status)launch_remap_mxfp4(mx_codes, mx_scales, n_mat, (int)N, (int)K, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
+                                           w2_codes, w2_scales, w2_scale2, (hipStream_t)stream);
 }
 
-int moet_requant_fp8(const uint8_t *fp8_w, const float *fp8_scales, int64_t n_mat, int64_t N, int64_t K,
+moet_status moet_requant_fp8(const uint8_t *fp8_w, const float *fp8_scales, int64_t n_mat, int64_t N, int64_t K,
                      uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint32_t flags, void *stream)
 {
     g_err[0] = 0;
     int rc = check_stack(n_mat, N, K, flags);
-    if (rc != MOET_OK) return rc;
+    if (rc != MOET_OK) return (moet_status)(rc);
     if (!aligned16(fp8_w) || !aligned16(fp8_scales) || !aligned16(w2_codes) || !aligned16(w2_scales) ||
         !aligned16(w2_scale2))
-        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
-    return launch_requant_fp8(fp8_w, fp8_scales, n_mat, (int)N, (int)K, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
-                              w2_codes, w2_scales, w2_scale2, (hipStream_t)stream);
+        return (moet_status)(fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned"));
+    return (moet_status)launch_requant_fp8(fp8_w, fp8_scales, n_mat, (int)N, (int)K, (int)(flags & MOET_BALANCE_ZERO_SIGNS),
+                                           w2_codes, w2_scales, w2_scale2, (hipStream_t)stream);
 }
 
-int moet_route(const float *logits, int32_t T, int32_t E, int32_t top_k, int32_t score_fn, int32_t renormalize,
+moet_status moet_route(const float *logits, int32_t T, int32_t E, int32_t top_k, int32_t score_fn, int32_t renormalize,
                float route_scale, int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *sorted_pairs,
                void *stream)
 {
     g_err[0] = 0;
-    if (T < 1 || T > 65536) return fail(MOET_EINVAL, "T (%d) must be in [1, 65536]", T);
-    if (E < 1 || E > 1024) return fail(MOET_EINVAL, "E (%d) must be in [1, 1024]", E);
-    if (top_k < 1 || top_k > E || top_k > 16) return fail(MOET_EINVAL, "top_k (%d) must be in [1, min(E, 16)]", top_k);
-    if (score_fn != MOET_SOFTMAX && score_fn != MOET_SIGMOID) return fail(MOET_EINVAL, "unknown score_fn %d", score_fn);
-    if (!(route_scale == route_scale)) return fail(MOET_EINVAL, "route_scale is NaN");
+    if (T < 1 || T > 65536) return (moet_status)(fail(MOET_EINVAL, "T (%d) must be in [1, 65536]", T));
+    if (E < 1 || E > 1024) return (moet_status)(fail(MOET_EINVAL, "E (%d) must be in [1, 1024]", E));
+    if (top_k < 1 || top_k > E || top_k > 16)
+        return (moet_status)(fail(MOET_EINVAL, "top_k (%d) must be in [1, min(E, 16)]", top_k));
+    if (score_fn != MOET_SOFTMAX && score_fn != MOET_SIGMOID)
+        return (moet_status)(fail(MOET_EINVAL, "unknown score_fn %d", score_fn));
+    if (!(route_scale == route_scale)) return (moet_status)(fail(MOET_EINVAL, "route_scale is NaN"));
     if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(expert_offsets) ||
         !aligned16(sorted_pairs))
-        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
-    return launch_route(logits, T, E, top_k, score_fn, renormalize, route_scale, topk_ids, topk_w, expert_offsets,
-                        sorted_pairs, (hipStream_t)stream);
+        return (moet_status)(fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned"));
+    return (moet_status)launch_route(logits, T, E, top_k, score_fn, renormalize, route_scale, topk_ids, topk_w, expert_offsets,
+                                     sorted_pairs, (hipStream_t)stream);
 }
 
 size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k)
@@ -259,41 +263,42 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k)
     return forward_workspace_bytes(L, T, top_k);
 }
 
-int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k, const int32_t *topk_ids,
+moet_status moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k, const int32_t *topk_ids,
                      const float *topk_w, const int32_t *expert_offsets, const int32_t *sorted_pairs,
                      const uint8_t *gate_flags, uint16_t *out, int32_t *miss_count, void *workspace,
                      size_t workspace_bytes, void *stream)
 {
     g_err[0] = 0;
     int rc = check_forward(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count);
-    if (rc != MOET_OK) return rc;
-    return dispatch_forward(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out,
-                            miss_count, workspace, workspace_bytes, (hipStream_t)stream);
+    if (rc != MOET_OK) return (moet_status)(rc);
+    return (moet_status)dispatch_forward(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out,
+                                         miss_count, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
-int moet_set_timing_events(void *start, void *stop)
+moet_status moet_set_timing_events(void *start, void *stop)
 {
     g_err[0] = 0;
-    if ((start == nullptr) != (stop == nullptr)) return fail(MOET_EINVAL, "set both timing events or neither");
+    if ((start == nullptr) != (stop == nullptr))
+        return (moet_status)(fail(MOET_EINVAL, "set both timing events or neither"));
     g_ev_start = (hipEvent_t)start;
     g_ev_stop = (hipEvent_t)stop;
-    return MOET_OK;
+    return (moet_status)(MOET_OK);
 }
 
-int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K, const uint16_t *act,
+moet_status moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K, const uint16_t *act,
                        const int32_t *row_slot, int32_t R, float *acc, void *stream)
 {
     g_err[0] = 0;
-    if (!D) return fail(MOET_EINVAL, "D is NULL");
-    if (n_slots < 1) return fail(MOET_EINVAL, "n_slots (%d) must be >= 1", n_slots);
-    if (N < 64 || N % 64) return fail(MOET_EINVAL, "N (%d) must be a positive multiple of 64", N);
-    if (K < 128 || K % 128) return fail(MOET_EINVAL, "K (%d) must be a positive multiple of 128", K);
-    if (R < 0 || R > 65535) return fail(MOET_EINVAL, "R (%d) must be in [0, 65535]", R);
-    if (R == 0) return MOET_OK;
+    if (!D) return (moet_status)(fail(MOET_EINVAL, "D is NULL"));
+    if (n_slots < 1) return (moet_status)(fail(MOET_EINVAL, "n_slots (%d) must be >= 1", n_slots));
+    if (N < 64 || N % 64) return (moet_status)(fail(MOET_EINVAL, "N (%d) must be a positive multiple of 64", N));
+    if (K < 128 || K % 128) return (moet_status)(fail(MOET_EINVAL, "K (%d) must be a positive multiple of 128", K));
+    if (R < 0 || R > 65535) return (moet_status)(fail(MOET_EINVAL, "R (%d) must be in [0, 65535]", R));
+    if (R == 0) return (moet_status)(MOET_OK);
     if (!aligned16(D->codes) || !aligned16(D->scales) || !aligned16(D->scale2) || !aligned16(act) ||
         !aligned16(row_slot) || !aligned16(acc))
-        return fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned");
-    return launch_delta(D, n_slots, N, K, act, row_slot, R, acc, (hipStream_t)stream);
+        return (moet_status)(fail(MOET_EINVAL, "pointers must be non-NULL and 16-byte aligned"));
+    return (moet_status)launch_delta(D, n_slots, N, K, act, row_slot, R, acc, (hipStream_t)stream);
 }
 
 size_t moet_gate_workspace_bytes(int32_t T, int32_t V)
@@ -302,21 +307,22 @@ size_t moet_gate_workspace_bytes(int32_t T, int32_t V)
     return gate_workspace_bytes(T, V);
 }
 
-int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
+moet_status moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
                          float *confidence_out, void *workspace, size_t workspace_bytes, void *stream)
 {
     g_err[0] = 0;
-    if (T < 1 || T > 65535) return fail(MOET_EINVAL, "T (%d) must be in [1, 65535]", T);
-    if (V < 1) return fail(MOET_EINVAL, "V (%d) must be >= 1", V);
-    if (!(tau == tau) || tau > 3.4e38f || tau < -3.4e38f) return fail(MOET_EINVAL, "tau must be finite");
-    if (!aligned16(logits) || !gate_flags) return fail(MOET_EINVAL, "logits (16-byte aligned) and gate_flags must be non-NULL");
+    if (T < 1 || T > 65535) return (moet_status)(fail(MOET_EINVAL, "T (%d) must be in [1, 65535]", T));
+    if (V < 1) return (moet_status)(fail(MOET_EINVAL, "V (%d) must be >= 1", V));
+    if (!(tau == tau) || tau > 3.4e38f || tau < -3.4e38f) return (moet_status)(fail(MOET_EINVAL, "tau must be finite"));
+    if (!aligned16(logits) || !gate_flags)
+        return (moet_status)(fail(MOET_EINVAL, "logits (16-byte aligned) and gate_flags must be non-NULL"));
     if (confidence_out && (reinterpret_cast<uintptr_t>(confidence_out) & 3u))
-        return fail(MOET_EINVAL, "confidence_out must be 4-byte aligned");
+        return (moet_status)(fail(MOET_EINVAL, "confidence_out must be 4-byte aligned"));
     const size_t need = gate_workspace_bytes(T, V);
     if (need && (!workspace || workspace_bytes < need))
-        return fail(MOET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-    if (need && !aligned16(workspace)) return fail(MOET_EINVAL, "workspace must be 16-byte aligned");
-    return launch_gate(logits, T, V, tau, gate_flags, confidence_out, workspace, (hipStream_t)stream);
+        return (moet_status)(fail(MOET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes));
+    if (need && !aligned16(workspace)) return (moet_status)(fail(MOET_EINVAL, "workspace must be 16-byte aligned"));
+    return (moet_status)launch_gate(logits, T, V, tau, gate_flags, confidence_out, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -50,24 +50,25 @@ using namespace moet;
 
 extern "C" {
 
-int moet_moe_forward_noalloc(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
+moet_status moet_moe_forward_noalloc(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
                              const int32_t *topk_ids, const float *topk_w, const int32_t *expert_offsets,
                              const int32_t *sorted_pairs, const uint8_t *gate_flags, uint16_t *out,
                              int32_t *miss_count, void *stream)
 {
     set_error("%s", "");
     int rc = check_forward(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out, miss_count);
-    if (rc != MOET_OK) return rc;
+    if (rc != MOET_OK) return (moet_status)(rc);
     const size_t need = forward_workspace_bytes(L, T, top_k);
     if (need > kNoallocScratchBytes)
-        return fail(MOET_EWORKSPACE, "this batch needs %zu bytes of scratch; the static scratch of "
-                                     "moet_moe_forward_noalloc holds %zu (use moet_moe_forward with a workspace)",
-                    need, kNoallocScratchBytes);
+        return (moet_status)fail(MOET_EWORKSPACE, "this batch needs %zu bytes of scratch; the static scratch of "
+                                 "moet_moe_forward_noalloc holds %zu (use moet_moe_forward with a "
+                                 "workspace)",
+                                 need, kNoallocScratchBytes);
     void *ws = nullptr;
     rc = device_scratch(&ws);
-    if (rc != MOET_OK) return rc;
-    return dispatch_forward(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out,
-                            miss_count, ws, kNoallocScratchBytes, (hipStream_t)stream);
+    if (rc != MOET_OK) return (moet_status)(rc);
+    return (moet_status)dispatch_forward(L, x, T, top_k, topk_ids, topk_w, expert_offsets, sorted_pairs, gate_flags, out,
+                                         miss_count, ws, kNoallocScratchBytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

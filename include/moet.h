@@ -115,7 +115,7 @@ enum { MOET_BALANCE_ZERO_SIGNS = 1 };
 enum { MOET_PICK_CODEBOOK = 2 };
 
 /* Static string for a status code. */
-const char *moet_status_str(int status);
+const char *moet_status_str(moet_status status);
 /* Thread-local detail of the last failed call on this thread ("" if none). */
 const char *moet_last_error(void);
 /* ABI version (bumped on any incompatible change). */
@@ -161,7 +161,7 @@ int moet_abi_version(void);
  *   with MOET_PICK_CODEBOOK.  Out-of-range delta_sel entries are skipped by
  *   the kernel (their slots are left unwritten).
  */
-int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2,
+moet_status moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2,
                  int64_t n_mat, int64_t N, int64_t K,
                  uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint8_t *w2_codebook,
                  const int32_t *delta_sel, int64_t n_sel,
@@ -183,7 +183,7 @@ int moet_requant(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const floa
  * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
  *   pointers.
  */
-int moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2,
+moet_status moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const float *fp4_scale2,
                     int64_t n_mat, int64_t N, int64_t K,
                     uint8_t *d_codes, uint8_t *d_scales, float *d_scale2, void *stream);
 
@@ -211,7 +211,7 @@ int moet_pack_nvfp4(const uint8_t *fp4_codes, const uint8_t *fp4_scales, const f
  * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
  *   pointers, unknown flags.
  */
-int moet_remap_mxfp4(const uint8_t *mx_codes, const uint8_t *mx_scales, int64_t n_mat, int64_t N, int64_t K,
+moet_status moet_remap_mxfp4(const uint8_t *mx_codes, const uint8_t *mx_scales, int64_t n_mat, int64_t N, int64_t K,
                      uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint32_t flags, void *stream);
 
 /*
@@ -236,7 +236,7 @@ int moet_remap_mxfp4(const uint8_t *mx_codes, const uint8_t *mx_scales, int64_t 
  * Errors: MOET_EINVAL for n_mat < 1, N % 64, K % 128, NULL or misaligned
  *   pointers, unknown flags.
  */
-int moet_requant_fp8(const uint8_t *fp8_w, const float *fp8_scales, int64_t n_mat, int64_t N, int64_t K,
+moet_status moet_requant_fp8(const uint8_t *fp8_w, const float *fp8_scales, int64_t n_mat, int64_t N, int64_t K,
                      uint32_t *w2_codes, uint8_t *w2_scales, float *w2_scale2, uint32_t flags, void *stream);
 
 /*
@@ -256,7 +256,7 @@ int moet_requant_fp8(const uint8_t *fp8_w, const float *fp8_scales, int64_t n_ma
  * Limits: 1 <= T <= 65536, 1 <= E <= 1024, 1 <= top_k <= min(E, 16).
  * Errors: MOET_EINVAL on any limit, NULL or misaligned pointer, bad score_fn.
  */
-int moet_route(const float *logits, int32_t T, int32_t E, int32_t top_k, int32_t score_fn,
+moet_status moet_route(const float *logits, int32_t T, int32_t E, int32_t top_k, int32_t score_fn,
                int32_t renormalize, float route_scale,
                int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *sorted_pairs,
                void *stream);
@@ -348,7 +348,7 @@ size_t moet_moe_workspace_bytes(const moet_layer *L, int32_t T, int32_t top_k);
  * 1 <= top_k <= min(E, 16); 1 <= T <= 65536), NULL or misaligned pointers, a
  * delta cache with NULL members; MOET_EWORKSPACE if the workspace is short.
  */
-int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
+moet_status moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
                      const int32_t *topk_ids, const float *topk_w,
                      const int32_t *expert_offsets, const int32_t *sorted_pairs,
                      const uint8_t *gate_flags, uint16_t *out, int32_t *miss_count,
@@ -371,7 +371,7 @@ int moet_moe_forward(const moet_layer *L, const uint16_t *x, int32_t T, int32_t 
  * device looks up the array's device address (hipGetSymbolAddress).
  */
 #define MOET_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
-int moet_moe_forward_noalloc(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
+moet_status moet_moe_forward_noalloc(const moet_layer *L, const uint16_t *x, int32_t T, int32_t top_k,
                              const int32_t *topk_ids, const float *topk_w,
                              const int32_t *expert_offsets, const int32_t *sorted_pairs,
                              const uint8_t *gate_flags, uint16_t *out, int32_t *miss_count,
@@ -388,7 +388,7 @@ int moet_moe_forward_noalloc(const moet_layer *L, const uint16_t *x, int32_t T, 
  * Errors: MOET_EINVAL for n_slots < 1, N % 64, K % 128, R < 0, NULL or
  * misaligned pointers.
  */
-int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
+moet_status moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
                        const uint16_t *act, const int32_t *row_slot, int32_t R, float *acc,
                        void *stream);
 
@@ -415,7 +415,7 @@ int moet_delta_forward(const moet_fp4 *D, int32_t n_slots, int32_t N, int32_t K,
  * workspace is missing or short.
  */
 size_t moet_gate_workspace_bytes(int32_t T, int32_t V);
-int moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
+moet_status moet_confidence_gate(const float *logits, int32_t T, int32_t V, float tau, uint8_t *gate_flags,
                          float *confidence_out, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus

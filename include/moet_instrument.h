@@ -9,6 +9,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moet.h"   /* moet_status */
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -22,7 +24,7 @@ extern "C" {
  * hipEventElapsedTime.  `start` / `stop` are caller-owned hipEvent_t handles;
  * pass NULL, NULL to disable.  Returns MOET_EINVAL if only one is NULL.
  */
-int moet_set_timing_events(void *start, void *stop);
+moet_status moet_set_timing_events(void *start, void *stop);
 
 /* Words of the sink array moet_probe_read writes. */
 #define MOET_PROBE_SINK_WORDS 8192
@@ -38,7 +40,7 @@ int moet_set_timing_events(void *start, void *stop);
  * `stream`.  Returns MOET_EINVAL for NULL or misaligned pointers or a bad
  * size, MOET_EHIP if the launch fails.
  */
-int moet_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+moet_status moet_probe_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 enum { MOET_PROBE_MFMA_BF16 = 0, MOET_PROBE_DOT2_BF16 = 1 };
 
@@ -57,7 +59,7 @@ enum { MOET_PROBE_MFMA_BF16 = 0, MOET_PROBE_DOT2_BF16 = 1 };
  * NULL or misaligned sink, iters < 1 or an unknown kind, MOET_EHIP if the
  * launch fails.
  */
-int moet_probe_peak(int kind, int32_t iters, uint32_t *sink, void *stream);
+moet_status moet_probe_peak(int kind, int32_t iters, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

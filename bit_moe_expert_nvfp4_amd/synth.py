@@ -125,16 +125,17 @@ def skew_magnitudes(codes: torch.Tensor, mats, targets, frac: float, seed: int, 
     `targets`, sign kept: weights concentrated on two magnitudes, the shape of a tensor that another
     sign-symmetric four-level codebook than {-4,-1,1,4} fits better."""
     out = codes.clone()
+    dev = out.device
     lut = torch.tensor([min(targets, key=lambda t: (abs(_E2M1_MAGS[t] - _E2M1_MAGS[m]), targets.index(t)))
-                        for m in range(8)], dtype=torch.uint8)
+                        for m in range(8)], dtype=torch.uint8, device=dev)
     for i in mats:
-        g = _gen("cpu", seed, tag, "skew", i)
-        c = out[i].cpu()
+        g = _gen(dev, seed, tag, "skew", i)        # the stream depends on the device, as for the weights
+        c = out[i]
         nib = torch.stack([c & 15, c >> 4], dim=-1)                       # [N, K/2, 2]
-        pick = torch.rand(nib.shape, generator=g) < frac
+        pick = torch.rand(nib.shape, generator=g, device=dev) < frac
         moved = (nib & 8) | lut[(nib & 7).long()]
         nib = torch.where(pick, moved, nib)
-        out[i] = (nib[..., 0] | (nib[..., 1] << 4)).to(out.device)
+        out[i] = nib[..., 0] | (nib[..., 1] << 4)
     return out
 
 

@@ -50,6 +50,33 @@ class OracleMatrix:
         return OR.dequant_fp4_codes(self.dc, self.ds, self.d2)
 
 
+#: e2m1 magnitude codes of 1/2 and 3 (codebook 1's levels) and of 0 and 2 (codebook 2's)
+C1_MAGS = (1, 5)
+C2_MAGS = (0, 4)
+
+
+def mixed_codebook_layer(src, seed):
+    """The synthetic layer `src` with some matrices moved towards codebook 1 or 2
+    (synth.skew_magnitudes): expert e's gate for e % 3 == 1, its up for e % 3 == 2, both (gate 1,
+    up 2) for e % 4 == 3; its down to 1 for odd e and to 2 for e % 6 == 0; the shared expert's gate
+    to 2 and its down to 1."""
+    from bit_moe_expert_nvfp4_amd import synth
+    E = src.cfg.E
+    g1 = [2 * e for e in range(E) if e % 3 == 1 or e % 4 == 3]
+    u2 = [2 * e + 1 for e in range(E) if e % 3 == 2 or e % 4 == 3]
+    c13 = synth.skew_magnitudes(src.w13[0], g1, C1_MAGS, 0.9, seed, "w13c1")
+    c13 = synth.skew_magnitudes(c13, u2, C2_MAGS, 0.95, seed, "w13c2")
+    d1 = [e for e in range(E) if e % 2 == 1]
+    d2 = [e for e in range(E) if e % 6 == 0]
+    c2 = synth.skew_magnitudes(src.w2[0], d1, C1_MAGS, 0.9, seed, "w2c1")
+    c2 = synth.skew_magnitudes(c2, d2, C2_MAGS, 0.95, seed, "w2c2")
+    sh13, sh2 = src.shared13, src.shared2
+    if sh13 is not None:
+        sh13 = (synth.skew_magnitudes(sh13[0], [0], C2_MAGS, 0.95, seed, "sh13"),) + tuple(sh13[1:])
+        sh2 = (synth.skew_magnitudes(sh2[0], [0], C1_MAGS, 0.9, seed, "sh2"),) + tuple(sh2[1:])
+    return synth.NVFP4Layer(src.cfg, (c13,) + tuple(src.w13[1:]), (c2,) + tuple(src.w2[1:]), sh13, sh2)
+
+
 class ExpertPrefetch:
     """Calls fn(e) for the experts of `order` on a thread pool, up to `window` experts ahead of the
     caller, who then asks for them in that order (the oracle's C requantisation and numpy's large

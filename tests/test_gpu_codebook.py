@@ -18,14 +18,13 @@ import pytest
 import torch
 
 from bit_moe_expert_nvfp4_amd import moet, synth
-from moet_testlib import (OracleLayer, OracleMatrix, assert_elementwise, bf16_bits, check_out_rows,
-                          check_pair_rows, np_, oracle_route, rel_l2, REL_L2_BAR, alarm_rel_l2)
+from moet_testlib import (C1_MAGS, C2_MAGS, OracleLayer, OracleMatrix, assert_elementwise, bf16_bits,
+                          check_out_rows, check_pair_rows, mixed_codebook_layer, np_, oracle_route, rel_l2,
+                          REL_L2_BAR, alarm_rel_l2)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
-C1_MAGS = (1, 5)   # e2m1 magnitude codes of 1/2 and 3
-C2_MAGS = (0, 4)   # e2m1 magnitude codes of 0 and 2
 
 
 def _print_case(name):
@@ -117,27 +116,6 @@ def test_pick_full_size_matrices():
 # ---------------------------------------------------------------------------
 # forward over a mixed-codebook layer
 # ---------------------------------------------------------------------------
-def _mixed_layer(cfg, seed):
-    """The synthetic layer with some matrices moved towards codebook 1 or 2: expert e's gate for
-    e % 3 == 1, its up for e % 3 == 2, both (gate 1, up 2) for e % 4 == 3; down 1 for odd e, 2 for
-    e % 3 == 0; the shared expert's gate 2 and down 1."""
-    src = synth.make_layer(cfg, seed=seed)
-    E = cfg.E
-    g1 = [2 * e for e in range(E) if e % 3 == 1 or e % 4 == 3]
-    u2 = [2 * e + 1 for e in range(E) if e % 3 == 2 or e % 4 == 3]
-    c13 = synth.skew_magnitudes(src.w13[0], g1, C1_MAGS, 0.9, seed, "w13c1")
-    c13 = synth.skew_magnitudes(c13, u2, C2_MAGS, 0.95, seed, "w13c2")
-    d1 = [e for e in range(E) if e % 2 == 1]
-    d2 = [e for e in range(E) if e % 3 == 0 and e % 2 == 0]
-    c2 = synth.skew_magnitudes(src.w2[0], d1, C1_MAGS, 0.9, seed, "w2c1")
-    c2 = synth.skew_magnitudes(c2, d2, C2_MAGS, 0.95, seed, "w2c2")
-    sh13, sh2 = src.shared13, src.shared2
-    if sh13 is not None:
-        sh13 = (synth.skew_magnitudes(sh13[0], [0], C2_MAGS, 0.95, seed, "sh13"),) + tuple(sh13[1:])
-        sh2 = (synth.skew_magnitudes(sh2[0], [0], C1_MAGS, 0.9, seed, "sh2"),) + tuple(sh2[1:])
-    return synth.NVFP4Layer(cfg, (c13,) + tuple(src.w13[1:]), (c2,) + tuple(src.w2[1:]), sh13, sh2)
-
-
 def _small_cfg(**kw):
     base = dict(name="mixed", T=4, H=256, I=128, E=8, k=2, score=synth.SIGMOID)
     base.update(kw)
@@ -156,7 +134,7 @@ def test_forward_mixed_codebooks(case):
     cfg = _small_cfg(**case)
     _print_case(f"forward mixed codebooks {case}")
     seed = zlib.crc32(str(sorted(case.items())).encode()) & 0xFFFF
-    src = _mixed_layer(cfg, seed)
+    src = mixed_codebook_layer(synth.make_layer(cfg, seed=seed), seed)
     soe = synth.slot_of_expert(cfg, seed) if cfg.n_resident else None
     layer = moet.layer_from_nvfp4(src, soe, swiglu_limit=cfg.swiglu_limit, pick_codebook=True)
     ol = OracleLayer(src, soe, pick_codebook=True)

@@ -22,7 +22,7 @@ import torch
 
 from bit_moe_expert_nvfp4_amd import moet, synth
 from moet_testlib import (OracleLayer, REL_L2_BAR, assert_elementwise, bf16_bits, check_out_rows, check_pair_rows,
-                          np_, oracle_route, rel_l2)
+                          mixed_codebook_layer, np_, oracle_route, rel_l2)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -36,7 +36,8 @@ def _u32(t):
 
 def _variant(cfg_id, variant):
     """The benchmark's other full-size workloads: the prefill chunk with a gated FP4 delta,
-    the decode layer with an NVFP4 shared expert, one GPU's share of a TP4 layer."""
+    the decode layer with an NVFP4 shared expert, one GPU's share of a TP4 layer; and the decode
+    layer with a delta cache whose matrices pick different codebooks."""
     cfg = synth.CONFIGS[cfg_id]
     if variant == "prefill_delta":
         cfg = dataclasses.replace(cfg, name="prefill_delta", n_resident=32, n_flagged=2048)
@@ -75,15 +76,18 @@ def _choose_tokens(ids: np.ndarray, n_tok: int, flags=None, soe=None):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg_id,variant", [(2, None), (3, None), (4, None), (5, None), (5, "prefill_delta"),
-                                            (2, "nvfp4_shared"), (2, "tp4_shard")])
+                                            (2, "nvfp4_shared"), (2, "tp4_shard"), (3, "mixed_codebooks")])
 def test_full_size_forward(cfg_id, variant):
     cfg = _variant(cfg_id, variant)
     shared_nvfp4 = variant == "nvfp4_shared"
+    pick = variant == "mixed_codebooks"
     print(f"[case] full-size config {cfg.name} T={cfg.T} E={cfg.E} I={cfg.I} variant={variant}", flush=True)
     t0 = time.time()
     src = synth.make_layer(cfg, seed=SEED, device=DEV)
+    if pick:
+        src = mixed_codebook_layer(src, SEED)
     soe = synth.slot_of_expert(cfg, SEED) if cfg.n_resident else None
-    layer = moet.layer_from_nvfp4(src, soe, shared_nvfp4=shared_nvfp4)
+    layer = moet.layer_from_nvfp4(src, soe, shared_nvfp4=shared_nvfp4, pick_codebook=pick)
     x = synth.make_activations(cfg.T, cfg.H, SEED, device=DEV)
     lg = synth.make_logits(cfg, SEED, device=DEV)
     flags = synth.gate_flags(cfg, SEED).to(DEV) if cfg.n_flagged else None
@@ -111,7 +115,7 @@ def test_full_size_forward(cfg_id, variant):
         assert len(toks) == 64 and len(experts) >= 32
         assert set(two_tile) <= experts
         print(f"{len(toks)} tokens over {len(experts)} experts; experts spanning two M-tiles: {two_tile}", flush=True)
-    ol = OracleLayer(src, soe, shared_nvfp4=shared_nvfp4)
+    ol = OracleLayer(src, soe, shared_nvfp4=shared_nvfp4, pick_codebook=pick)
     ol.prefetch(set(o_ids[toks].reshape(-1).tolist()))
     ref = ol.forward(bf16_bits(x), o_ids, o_w, gate_flags=fl, tokens=toks)
     print(f"oracle outputs done ({time.time() - t0:.0f} s)", flush=True)
@@ -159,6 +163,16 @@ def test_full_size_forward(cfg_id, variant):
             continue
         jobs.append((om, h(planes.codes)[i].view(np.uint32), h(planes.scales)[i],
                      None if dslot is None else (h(dpl.codes)[dslot], h(dpl.scales)[dslot])))
+
+    if pick:     # the oracle's picks: every codebook among the touched matrices, and the layer's ids equal them
+        cbs = {}
+        for (sid, i, _), om in ol._cache.items():
+            stack = {id(src.w13): layer.w13, id(src.w2): layer.w2, id(src.shared13): layer.shared13,
+                     id(src.shared2): layer.shared2}[sid]
+            assert int(h(stack.codebook)[i]) == om.cb, f"codebook of matrix {i}"
+            cbs[om.cb] = cbs.get(om.cb, 0) + 1
+        print(f"codebooks of the touched matrices: {cbs}", flush=True)
+        assert set(cbs) == {0, 1, 2}
 
     def same(job):
         om, codes, scales, delta = job

@@ -126,55 +126,66 @@ __device__ __forceinline__ void block_bins(const uint32_t words[4], const int S9
     bb.nzero = cnt[0][0] + cnt[1][0];
 }
 
-// Err(LO, HI) with the bins split at the level boundary: a bin (value y, count
-// c) sits on LO iff 2y <= LO + HI (then (y-LO)^2 <= (y-HI)^2), so with S_lo,
-// C_lo the sums of c*y and c over the LO bins and S_hi, C_hi over the HI bins,
-//   Err = sum c*y^2 - 2 (LO S_lo + HI S_hi) + LO^2 (zeros + C_lo) + HI^2 C_hi,
-// the same exact integer as the per-bin sum (every product and partial sum is
-// an integer below 2^53, so float64 holds it exactly).
-__device__ __forceinline__ double block_err(const BlockBins &bb, int lo, int hi)
+// Err for levels LO = lo2 a, HI = hi2 a (a = T << j) with the bins split at the
+// level boundary: a bin (value y, count c) sits on LO iff 2y <= LO + HI (then
+// (y-LO)^2 <= (y-HI)^2), so with S_lo, C_lo the sums of c*y and c over the LO
+// bins and S_hi, C_hi over the HI bins,
+//   Err = sum c*y^2 - 2a (lo2 S_lo + hi2 S_hi) + a^2 (lo2^2 (zeros + C_lo) + hi2^2 C_hi),
+// the same exact integer as the per-bin sum: the two bracketed sums are
+// integers (< 2^30 and <= 2048) and every product and partial sum is an
+// integer below 2^53, so float64 holds it exactly.
+template <int C>
+__device__ __forceinline__ double block_err(const BlockBins &bb, int a)
 {
+    constexpr int lo2 = C == 0 ? 2 : C == 1 ? 1 : 0, hi2 = C == 0 ? 8 : C == 1 ? 6 : 4;
     int slo = 0, clo = 0;
 #pragma unroll
     for (int i = 0; i < 14; ++i) {
-        const bool l = 2 * bb.yv[i] <= lo + hi;
+        const bool l = 2 * bb.yv[i] <= (lo2 + hi2) * a;
         slo += l ? bb.cy[i] : 0;
         clo += l ? bb.cc[i] : 0;
     }
-    const double dl = (double)lo, dh = (double)hi;
-    const double lin = fma(dl, (double)slo, dh * (double)(bb.stot - slo));          // < 2^50
-    const double quad = fma(dl * dl, (double)(bb.nzero + clo), dh * dh * (double)(bb.ctot - clo));   // < 2^50
-    return bb.y2 - 2.0 * lin + quad;
+    const int lin = lo2 * slo + hi2 * (bb.stot - slo);                                  // < 2^30
+    const int quad = lo2 * lo2 * (bb.nzero + clo) + hi2 * hi2 * (bb.ctot - clo);        // <= 2048
+    const double ad = (double)a;                                                        // < 2^20
+    return fma(ad * ad, (double)quad, fma(-2.0 * ad, (double)lin, bb.y2));
 }
 
-// Smallest-error scale code of codebook c (ties: the smaller code) and its error.
-__device__ __forceinline__ int block_best(const BlockBins &bb, int c, double &best_err)
+// Smallest-error scale code of codebook C (ties: the smaller code) and its error.
+template <int C>
+__device__ __forceinline__ int block_best(const BlockBins &bb, double &best_err)
 {
     best_err = 0.0;
     if (bb.amax == 0) return 0;   // every level of scale 0 is exact
     int t_lo, t_hi;
-    if (c == 0) {
+    if constexpr (C == 0) {
         t_lo = e4m3_floor_code(bb.amax / 512);
         t_hi = e4m3_ceil_code((bb.amax + 3) / 4);
-    } else if (c == 1) {
+    } else if constexpr (C == 1) {
         t_lo = e4m3_floor_code(bb.amax / 256);
         t_hi = e4m3_ceil_code((bb.amax + 1) / 2);
     } else {
         t_lo = e4m3_floor_code(bb.amax / 512);
         t_hi = e4m3_ceil_code((bb.amax + 7) / 8);
     }
-    const int lo2 = cb_lo2(c), hi2 = cb_hi2(c), j = cb_j(c);
+    constexpr int j = C == 2 ? 2 : 1;
     int best_t = t_lo;
     best_err = -1.0;
     for (int t = t_lo; t <= t_hi; ++t) {
-        const int T = e4m3_x512(t);
-        const double err = block_err(bb, (lo2 * T) << j, (hi2 * T) << j);
+        const double err = block_err<C>(bb, e4m3_x512(t) << j);
         if (best_err < 0.0 || err < best_err) {   // ascending scan: ties keep the smaller scale
             best_err = err;
             best_t = t;
         }
     }
     return best_t;
+}
+
+__device__ __forceinline__ int block_best_of(const BlockBins &bb, int c, double &err)
+{
+    if (c == 0) return block_best<0>(bb, err);
+    if (c == 1) return block_best<1>(bb, err);
+    return block_best<2>(bb, err);
 }
 
 __device__ __forceinline__ void load_block(const uint8_t *codes, const uint8_t *scales, size_t mat, int N, int K, int n,
@@ -227,12 +238,13 @@ __global__ __launch_bounds__(256) void pick_err_kernel(const uint8_t *__restrict
         load_block(codes, scales, mat, N, K, n, b, words, S9);
         BlockBins bb;
         block_bins(words, S9, bb);
-#pragma unroll
-        for (int c = 0; c < kNumCodebooks; ++c) {
-            double err;
-            block_best(bb, c, err);
-            e[c] = (unsigned long long)err;   // exact integer < 2^51
-        }
+        double err;
+        block_best<0>(bb, err);
+        e[0] = (unsigned long long)err;   // exact integers < 2^51
+        block_best<1>(bb, err);
+        e[1] = (unsigned long long)err;
+        block_best<2>(bb, err);
+        e[2] = (unsigned long long)err;
     }
 #pragma unroll
     for (int c = 0; c < kNumCodebooks; ++c) {
@@ -274,6 +286,8 @@ __global__ __launch_bounds__(256) void pick_choose_kernel(const uint32_t *__rest
     cbook[m] = (uint8_t)best;
 }
 
+// PICK: each matrix's codebook comes from cbook (else codebook 0 everywhere)
+template <bool PICK>
 __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales,
                                                       const float *__restrict__ s2in, int64_t n_mat, int N, int K,
@@ -289,7 +303,7 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict_
     const size_t rg = idx / nb;
     const int n = (int)(rg % N);
     const size_t mat = rg / N;
-    const int c = cbook ? min((int)cbook[mat], kNumCodebooks - 1) : 0;
+    const int c = PICK ? min((int)cbook[mat], kNumCodebooks - 1) : 0;
     if (n == 0 && b == 0) ws2[mat] = (float)(1 << cb_j(c)) * s2in[mat];
 
     uint32_t words[4];
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t *__restrict_
     BlockBins bb;
     block_bins(words, S9, bb);
     double err;
-    const int best_t = block_best(bb, c, err);
+    const int best_t = PICK ? block_best_of(bb, c, err) : block_best<0>(bb, err);
     const int T = e4m3_x512(best_t);
     const int lo = (cb_lo2(c) * T) << cb_j(c), hi = (cb_hi2(c) * T) << cb_j(c);
 
@@ -436,8 +450,12 @@ int launch_requant(const uint8_t *codes, const uint8_t *scales, const float *s2,
         rc = check_launch("cbook_fill_kernel");
         if (rc != MOET_OK) return rc;
     }
-    hipLaunchKernelGGL(requant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, s2, n_mat, N, K,
-                       wc, wsc, ws2, (const uint8_t *)(pick ? cbook : nullptr), balance);
+    if (pick)
+        hipLaunchKernelGGL(requant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, s2, n_mat,
+                           N, K, wc, wsc, ws2, (const uint8_t *)cbook, balance);
+    else
+        hipLaunchKernelGGL(requant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, s2, n_mat,
+                           N, K, wc, wsc, ws2, (const uint8_t *)nullptr, balance);
     rc = check_launch("requant_kernel");
     if (rc != MOET_OK || n_sel == 0) return rc;
     const size_t dtotal = (size_t)n_sel * N * (K / 32);

@@ -238,3 +238,13 @@ def test_moe_forward_binding_checks_shapes():
     # right shapes on CPU tensors: rejected as not on the GPU, before any library call
     with pytest.raises(TypeError):
         moet.moe_forward(layer, **good)
+
+
+def test_probes_reject_bad_args(L):
+    """The measurement references validate on the host (no GPU needed for the rejections)."""
+    buf = ctypes.c_void_p(16)      # never dereferenced: checks fail first
+    for args in [(None, 16, buf, None), (buf, 0, buf, None), (buf, 24, buf, None), (buf, 16, None, None),
+                 (ctypes.c_void_p(8), 16, buf, None)]:
+        assert L.moet_probe_read(*args) == 1, args
+    for args in [(7, 1, buf, None), (0, 0, buf, None), (1, -3, buf, None), (0, 1, None, None)]:
+        assert L.moet_probe_peak(*args) == 1, args

@@ -362,6 +362,10 @@ def _check_forward_args(layer: Layer, x, topk_ids, topk_w, expert_offsets, sorte
         spec.append((miss_count, torch.int32, (1,), "miss_count"))
     if workspace is not None:
         spec.append((workspace, torch.uint8, (workspace.numel(),), "workspace"))
+    for name in ("w13", "w2", "shared13", "shared2"):     # per-matrix codebook ids: one per matrix of the stack
+        pl = getattr(layer, name)
+        if pl is not None and pl.codebook is not None:
+            spec.append((pl.codebook, torch.uint8, (pl.scale2.numel(),), f"{name}.codebook"))
     for t, dt, shape, name in spec:        # every shape first, so a mismatch is reported as such
         _need_shape(t, dt, shape, name, device_check=False)
     for t, dt, _, name in spec:

@@ -238,6 +238,12 @@ def test_moe_forward_binding_checks_shapes():
     # right shapes on CPU tensors: rejected as not on the GPU, before any library call
     with pytest.raises(TypeError):
         moet.moe_forward(layer, **good)
+    # per-matrix codebook ids: one uint8 per matrix of the stack
+    import dataclasses
+    for cb in (torch.zeros(2, dtype=torch.uint8), torch.zeros(1, dtype=torch.int32)):
+        zc = dataclasses.replace(z, codebook=cb)
+        with pytest.raises(ValueError):
+            moet.moe_forward(moet.Layer(256, 128, 8, zc, z), **good)
 
 
 def test_probes_reject_bad_args(L):

@@ -166,3 +166,26 @@ def test_forward_mixed_codebooks(case):
     print(f"rel_l2={err:.3e}", flush=True)
     assert err <= REL_L2_BAR
     assert err <= alarm_rel_l2(cfg.H)
+
+
+def test_pick_with_balanced_zero_signs():
+    """Both load flags at once (MOET_PICK_CODEBOOK | MOET_BALANCE_ZERO_SIGNS) on a +0-only export
+    (every zero written as +0), skewed so that each codebook is picked: ids, codes, scales and scale2
+    equal the oracle's pick with balanced zeros."""
+    from oracle import layout as OL
+    from oracle import requant as OR
+    _print_case("codebook pick + balanced zero signs n=4 N=128 K=256")
+    c, s, z = synth.make_nvfp4_stack(4, 128, 256, 24, "balanced", plus_zeros=True)
+    c = synth.skew_magnitudes(c, [1], C1_MAGS, 0.9, 24, "c1")
+    c = synth.skew_magnitudes(c, [2, 3], C2_MAGS, 0.95, 24, "c2")
+    w = moet.requant(c.to(DEV), s.to(DEV), z.to(DEV), balance_zero_signs=True, pick_codebook=True)
+    torch.cuda.synchronize()
+    picks = []
+    for m in range(4):
+        cb, c2, tau, s2, _ = OR.pick_codebook(np_(c)[m], np_(s)[m], float(z[m]), balance_zero_signs=True)
+        picks.append(cb)
+        assert int(np_(w.codebook)[m]) == cb
+        assert (_u32(w.codes[m]) == OL.pack_2bit_codes(c2)).all(), f"codes of matrix {m}"
+        assert (np_(w.scales[m]) == OL.pack_2bit_scales(tau)).all(), f"scales of matrix {m}"
+        assert np_(w.scale2)[m] == s2
+    assert set(picks) == {0, 1, 2}, picks

@@ -169,17 +169,31 @@ def _new_w2(n: int, N: int, K: int, dev) -> W2Planes:
                     torch.empty((n,), dtype=torch.float32, device=dev), N, K)
 
 
+def _nvfp4_stack_dims(codes, scales, scale2, scale_group=16):
+    """(n, N, K) of a stack of [N][K] matrices (codes uint8 [n, N, K/2], block scales uint8
+    [n, N, K/scale_group], optional scale2 f32 [n]); ValueError on any mismatch (the kernels index the
+    scales with the dimensions taken from the codes)."""
+    if codes.dim() != 3:
+        raise ValueError(f"codes must be [n, N, K/2], got {tuple(codes.shape)}")
+    n, N, Kh = (int(v) for v in codes.shape)
+    K = 2 * Kh
+    if tuple(scales.shape) != (n, N, K // scale_group) or K % scale_group:
+        raise ValueError(f"scales must be [{n}, {N}, {K // scale_group}], got {tuple(scales.shape)}")
+    if scale2 is not None and tuple(scale2.shape) != (n,):
+        raise ValueError(f"scale2 must be [{n}], got {tuple(scale2.shape)}")
+    return n, N, K
+
+
 def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
             delta_sel: Optional[torch.Tensor] = None, balance_zero_signs: bool = False,
             pick_codebook: bool = False):
     """NVFP4 stack (codes uint8 [n, N, K/2], scales uint8 [n, N, K/16], scale2 f32 [n]) ->
     W2Planes (and FP4Planes of the matrices listed in delta_sel, int32).  pick_codebook: each
     matrix picks its codebook (W2Planes.codebook holds the ids); otherwise codebook 0."""
+    n, N, K = _nvfp4_stack_dims(codes, scales, scale2)
     _need(codes, torch.uint8, "codes")
     _need(scales, torch.uint8, "scales")
     _need(scale2, torch.float32, "scale2")
-    n, N, Kh = codes.shape
-    K = 2 * Kh
     dev = codes.device
     w = _new_w2(n, N, K, dev)
     if pick_codebook:
@@ -205,11 +219,10 @@ def requant(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor,
 def pack_nvfp4(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor) -> FP4Planes:
     """NVFP4 stack (codes uint8 [n, N, K/2], scales uint8 [n, N, K/16], scale2 f32 [n]) in the FP4
     layout, values unchanged (the form of an NVFP4 shared expert)."""
+    n, N, K = _nvfp4_stack_dims(codes, scales, scale2)
     _need(codes, torch.uint8, "codes")
     _need(scales, torch.uint8, "scales")
     _need(scale2, torch.float32, "scale2")
-    n, N, Kh = codes.shape
-    K = 2 * Kh
     dev = codes.device
     d = FP4Planes(torch.empty((n, N * K // 2), dtype=torch.uint8, device=dev),
                   torch.empty((n, N * K // 16), dtype=torch.uint8, device=dev),
@@ -221,10 +234,9 @@ def pack_nvfp4(codes: torch.Tensor, scales: torch.Tensor, scale2: torch.Tensor) 
 
 def remap_mxfp4(codes: torch.Tensor, scales: torch.Tensor, balance_zero_signs: bool = False) -> W2Planes:
     """MXFP4 stack (codes uint8 [n, N, K/2], e8m0 scales uint8 [n, N, K/32]) -> W2Planes."""
+    n, N, K = _nvfp4_stack_dims(codes, scales, None, scale_group=32)
     _need(codes, torch.uint8, "codes")
     _need(scales, torch.uint8, "scales")
-    n, N, Kh = codes.shape
-    K = 2 * Kh
     w = _new_w2(n, N, K, codes.device)
     _check(lib().moet_remap_mxfp4(_ptr(codes), _ptr(scales), n, N, K, _ptr(w.codes), _ptr(w.scales),
                                   _ptr(w.scale2), BALANCE_ZERO_SIGNS if balance_zero_signs else 0, _stream()))
@@ -233,11 +245,13 @@ def remap_mxfp4(codes: torch.Tensor, scales: torch.Tensor, balance_zero_signs: b
 
 def requant_fp8(weights: torch.Tensor, block_scales: torch.Tensor, balance_zero_signs: bool = False) -> W2Planes:
     """FP8 block-quant stack (e4m3fn bytes uint8 [n, N, K], fp32 scales [n, ceil(N/128), K/128]) -> W2Planes."""
-    _need(weights, torch.uint8, "weights")
-    _need(block_scales, torch.float32, "block_scales")
-    n, N, K = weights.shape
+    if weights.dim() != 3:
+        raise ValueError(f"weights must be [n, N, K], got {tuple(weights.shape)}")
+    n, N, K = (int(v) for v in weights.shape)
     if tuple(block_scales.shape) != (n, (N + 127) // 128, K // 128):
         raise ValueError(f"block_scales must be [{n}, {(N + 127) // 128}, {K // 128}], got {tuple(block_scales.shape)}")
+    _need(weights, torch.uint8, "weights")
+    _need(block_scales, torch.float32, "block_scales")
     w = _new_w2(n, N, K, weights.device)
     _check(lib().moet_requant_fp8(_ptr(weights), _ptr(block_scales), n, N, K, _ptr(w.codes), _ptr(w.scales),
                                   _ptr(w.scale2), BALANCE_ZERO_SIGNS if balance_zero_signs else 0, _stream()))
@@ -250,14 +264,21 @@ def requant_fp8(weights: torch.Tensor, block_scales: torch.Tensor, balance_zero_
 def route(logits: torch.Tensor, top_k: int, score_fn: int = SIGMOID, renormalize: bool = True,
           route_scale: float = 1.0, out=None):
     """Returns (topk_ids int32 [T,k], topk_w f32 [T,k], expert_offsets int32 [E+1], sorted_pairs int32 [T*k])."""
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [T, E], got {tuple(logits.shape)}")
     _need(logits, torch.float32, "logits")
-    T, E = logits.shape
+    T, E = (int(v) for v in logits.shape)
     dev = logits.device
     if out is None:
         out = (torch.empty((T, top_k), dtype=torch.int32, device=dev),
                torch.empty((T, top_k), dtype=torch.float32, device=dev),
                torch.empty((E + 1,), dtype=torch.int32, device=dev),
                torch.empty((T * top_k,), dtype=torch.int32, device=dev))
+    else:
+        for t, dt, shape, name in zip(out, (torch.int32, torch.float32, torch.int32, torch.int32),
+                                      ((T, top_k), (T, top_k), (E + 1,), (T * top_k,)),
+                                      ("topk_ids", "topk_w", "expert_offsets", "sorted_pairs")):
+            _need_shape(t, dt, shape, name)
     ids, w, offs, pairs = out
     _check(lib().moet_route(_ptr(logits), T, E, top_k, score_fn, int(bool(renormalize)), float(route_scale),
                             _ptr(ids), _ptr(w), _ptr(offs), _ptr(pairs), _stream()))
@@ -466,6 +487,8 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
     once with the weight kernels' access shape; `sink` is an int32 device tensor of PROBE_SINK_WORDS."""
     if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < PROBE_SINK_WORDS:
         raise ValueError("probe_read needs a contiguous buffer and an int32 sink of PROBE_SINK_WORDS words")
+    if not buf.is_cuda or not sink.is_cuda or not sink.is_contiguous():
+        raise TypeError("probe_read needs device tensors")
     _check(lib().moet_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream()))
 
 
@@ -479,6 +502,8 @@ def probe_peak(kind: int, iters: int, sink: torch.Tensor) -> None:
     PROBE_PEAK_WAVES waves; `sink` is an int32 device tensor of PROBE_SINK_WORDS."""
     if sink.dtype != torch.int32 or sink.numel() < PROBE_SINK_WORDS:
         raise ValueError("probe_peak needs an int32 sink of PROBE_SINK_WORDS words")
+    if not sink.is_cuda or not sink.is_contiguous():
+        raise TypeError("probe_peak needs a contiguous device sink")
     _check(lib().moet_probe_peak(int(kind), int(iters), _ptr(sink), _stream()))
 
 

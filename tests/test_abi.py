@@ -254,3 +254,38 @@ def test_probes_reject_bad_args(L):
         assert L.moet_probe_read(*args) == 1, args
     for args in [(7, 1, buf, None), (0, 0, buf, None), (1, -3, buf, None), (0, 1, None, None)]:
         assert L.moet_probe_peak(*args) == 1, args
+
+
+def test_probe_bindings_reject_host_tensors():
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet
+    sink = torch.zeros(moet.PROBE_SINK_WORDS, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        moet.probe_read(torch.zeros(1024, dtype=torch.int32), sink)
+    with pytest.raises(TypeError):
+        moet.probe_peak(moet.PROBE_MFMA_BF16, 4, sink)
+    with pytest.raises(ValueError):
+        moet.probe_peak(moet.PROBE_DOT2_BF16, 4, torch.zeros(16, dtype=torch.int32))
+
+
+def test_conversion_bindings_check_shapes():
+    """Mismatched scale or scale2 shapes raise ValueError before any device check or library call (the
+    kernels would index the scales with the dimensions of the codes)."""
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet
+    c = torch.zeros(2, 64, 64, dtype=torch.uint8)
+    for s, z in [(torch.zeros(2, 64, 7, dtype=torch.uint8), torch.zeros(2)),
+                 (torch.zeros(2, 64, 8, dtype=torch.uint8), torch.zeros(3)),
+                 (torch.zeros(1, 64, 8, dtype=torch.uint8), torch.zeros(2))]:
+        with pytest.raises(ValueError):
+            moet.requant(c, s, z)
+        with pytest.raises(ValueError):
+            moet.pack_nvfp4(c, s, z)
+    with pytest.raises(ValueError):
+        moet.remap_mxfp4(c, torch.zeros(2, 64, 8, dtype=torch.uint8))     # MXFP4 scales are per 32
+    with pytest.raises(ValueError):
+        moet.requant(torch.zeros(64, 64, dtype=torch.uint8), torch.zeros(64, 8, dtype=torch.uint8), torch.zeros(1))
+    with pytest.raises(ValueError):
+        moet.route(torch.zeros(4, 8, 2), 2)
+    with pytest.raises(TypeError):      # right shapes, host tensors
+        moet.requant(c, torch.zeros(2, 64, 8, dtype=torch.uint8), torch.zeros(2))

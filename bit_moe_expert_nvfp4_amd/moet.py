@@ -434,10 +434,15 @@ def moe_forward_noalloc(layer: Layer, x: torch.Tensor, topk_ids, topk_w, expert_
 # ---------------------------------------------------------------------------
 def delta_forward(D: FP4Planes, act: torch.Tensor, row_slot: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
     """acc[r] += D[row_slot[r]] @ act[r] (in place) for rows with a valid slot."""
+    if not isinstance(act, torch.Tensor) or act.dim() != 2 or act.shape[1] != D.K:
+        raise ValueError(f"act must be [R, {D.K}] (the planes' K), got {tuple(getattr(act, 'shape', ()))}")
+    R, K = (int(v) for v in act.shape)
+    for t, dt, shape, name in ((act, torch.bfloat16, (R, K), "act"), (row_slot, torch.int32, (R,), "row_slot"),
+                               (acc, torch.float32, (R, D.N), "acc")):
+        _need_shape(t, dt, shape, name, device_check=False)
     _need(act, torch.bfloat16, "act")
     _need(row_slot, torch.int32, "row_slot")
     _need(acc, torch.float32, "acc")
-    R, K = act.shape
     Dc = D.c()
     _check(lib().moet_delta_forward(ctypes.byref(Dc), int(D.scale2.numel()), D.N, K, _ptr(act), _ptr(row_slot), R,
                                     _ptr(acc), _stream()))
@@ -454,8 +459,14 @@ def confidence_gate(logits: torch.Tensor, tau: float = 0.60, flags: Optional[tor
     """moet_confidence_gate: uint8 [T] flags (1 = largest next-token probability below tau) from fp32
     logits [T, V]; optionally the confidence itself into an fp32 [T] tensor.  The workspace (uint8,
     gate_workspace_bytes(T, V) bytes) is allocated per call unless given.  Returns the flags."""
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError(f"logits must be [T, V], got {tuple(getattr(logits, 'shape', ()))}")
+    T, V = (int(v) for v in logits.shape)
+    if flags is not None:
+        _need_shape(flags, torch.uint8, (T,), "flags", device_check=False)
+    if confidence is not None:
+        _need_shape(confidence, torch.float32, (T,), "confidence", device_check=False)
     _need(logits, torch.float32, "logits")
-    T, V = logits.shape
     if flags is None:
         flags = torch.empty((T,), dtype=torch.uint8, device=logits.device)
     _need(flags, torch.uint8, "flags")

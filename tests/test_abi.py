@@ -289,3 +289,26 @@ def test_conversion_bindings_check_shapes():
         moet.route(torch.zeros(4, 8, 2), 2)
     with pytest.raises(TypeError):      # right shapes, host tensors
         moet.requant(c, torch.zeros(2, 64, 8, dtype=torch.uint8), torch.zeros(2))
+
+
+def test_delta_and_gate_bindings_check_shapes():
+    import torch
+    from bit_moe_expert_nvfp4_amd import moet
+    D = moet.FP4Planes(torch.zeros(1, 64 * 128 // 2, dtype=torch.uint8), torch.zeros(1, 64 * 128 // 16, dtype=torch.uint8),
+                       torch.zeros(1), 64, 128)
+    R = 3
+    good = dict(act=torch.zeros(R, 128, dtype=torch.bfloat16), row_slot=torch.zeros(R, dtype=torch.int32),
+                acc=torch.zeros(R, 64))
+    for b in [dict(act=torch.zeros(R, 256, dtype=torch.bfloat16)), dict(row_slot=torch.zeros(R + 1, dtype=torch.int32)),
+              dict(acc=torch.zeros(R, 128)), dict(acc=torch.zeros(R, 64, dtype=torch.float64))]:
+        with pytest.raises(ValueError):
+            moet.delta_forward(D, **dict(good, **b))
+    with pytest.raises(TypeError):
+        moet.delta_forward(D, **good)
+    lg = torch.zeros(4, 100)
+    with pytest.raises(ValueError):
+        moet.confidence_gate(lg, flags=torch.zeros(5, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        moet.confidence_gate(lg, confidence=torch.zeros(3))
+    with pytest.raises(ValueError):
+        moet.confidence_gate(torch.zeros(100))

@@ -559,7 +559,7 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not sharded in this build.",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not sharded across GPUs.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np

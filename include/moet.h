@@ -89,7 +89,7 @@ extern "C" {
 typedef enum {
     MOET_OK = 0,
     MOET_EINVAL = 1,       /* bad shape, pointer, alignment or enum value */
-    MOET_EUNSUPPORTED = 2, /* a valid request this build does not implement */
+    MOET_EUNSUPPORTED = 2, /* a valid request this library does not implement */
     MOET_EWORKSPACE = 3,   /* workspace missing or too small */
     MOET_EHIP = 4          /* a HIP launch or runtime call failed */
 } moet_status;

@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="synthetic layer config (2: MTP decode)")
+    ap.add_argument("--config", default="decode_mtp", help="synthetic decode layer (a key of synth.CONFIGS)")
     ap.add_argument("--layers", type=int, default=4, help="layers in the rotating pool")
     ap.add_argument("--inputs", type=int, default=8, help="input sets in the rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -309,7 +309,7 @@ def _blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_fraction=None, tp=1,
+def decode_leg(cfg_name, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_fraction=None, tp=1,
                shared_nvfp4=False):
     """Route + forward of another decode configuration (FP4 delta cache, batched streams, one GPU's
     share of a tensor-parallel layer), timed like the main step over its own pool of layers and input sets."""
@@ -318,7 +318,7 @@ def decode_leg(cfg_no, steps, warmup, seed, dev, n_layers=2, n_inputs=8, cache_f
     import torch
     from bit_moe_expert_nvfp4_amd import moet, synth
 
-    cfg = synth.CONFIGS[cfg_no]
+    cfg = synth.CONFIGS[cfg_name]
     if tp > 1:                         # rows I/tp of gate/up and columns I/tp of down per GPU
         cfg = dataclasses.replace(cfg, name=f"{cfg.name}_tp{tp}_shard", I=cfg.I // tp)
     soe = synth.slot_of_expert(cfg, seed) if cfg.n_resident else None
@@ -791,10 +791,10 @@ def main():
         print("[bench] timing the prefill chunk", file=sys.stderr, flush=True)
         import dataclasses
         pl = dataclasses.replace(layers[0], shared13=None, shared2=None)
-        result["prefill"] = prefill_leg(pl, synth.CONFIGS[5], args.prefill_steps, args.seed, dev)
+        result["prefill"] = prefill_leg(pl, synth.CONFIGS["prefill"], args.prefill_steps, args.seed, dev)
         # the same chunk with gate-flagged tokens on delta-cache experts, right after and with as many steps
         print("[bench] timing the prefill chunk with the FP4 delta", file=sys.stderr, flush=True)
-        cfgd = dataclasses.replace(synth.CONFIGS[5], name="prefill_delta", n_resident=32, n_flagged=2048)
+        cfgd = dataclasses.replace(synth.CONFIGS["prefill"], name="prefill_delta", n_resident=32, n_flagged=2048)
         srcd = synth.make_layer(cfgd, seed=args.seed, device=dev)
         soed = synth.slot_of_expert(cfgd, args.seed)
         ld = moet.layer_from_nvfp4(srcd, soed)
@@ -817,18 +817,20 @@ def main():
         del layers
         torch.cuda.empty_cache()
         result["other_decode"] = {}
-        for cno, key, frac, tp in ((3, "delta_cache", None, 1), (4, "batched", None, 1),
-                                   (2, "expert_cache_half", 0.5, 1), (2, "tp2_shard", None, 2),
-                                   (2, "tp4_shard", None, 4)):
+        for cname, key, frac, tp in (("decode_mtp_delta", "delta_cache", None, 1),
+                                     ("batched_decode", "batched", None, 1),
+                                     ("decode_mtp", "expert_cache_half", 0.5, 1),
+                                     ("decode_mtp", "tp2_shard", None, 2),
+                                     ("decode_mtp", "tp4_shard", None, 4)):
             print(f"[bench] timing decode config {key}", file=sys.stderr, flush=True)
-            result["other_decode"][key] = decode_leg(cno, args.extra_steps, 10, args.seed, dev,
+            result["other_decode"][key] = decode_leg(cname, args.extra_steps, 10, args.seed, dev,
                                                      cache_fraction=frac, tp=tp)
         print("[bench] timing decode with an NVFP4 shared expert", file=sys.stderr, flush=True)
-        result["other_decode"]["nvfp4_shared"] = decode_leg(2, args.extra_steps, 10, args.seed, dev,
+        result["other_decode"]["nvfp4_shared"] = decode_leg("decode_mtp", args.extra_steps, 10, args.seed, dev,
                                                             shared_nvfp4=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        c5 = synth.CONFIGS[5]
+        c5 = synth.CONFIGS["prefill"]
         cb = cpu_baseline(cfg, srcs[0], xs[0], lgs[0], args.seed, cfg_prefill=c5,
                           x_prefill=synth.make_activations(c5.T, c5.H, args.seed, tag="prefill_x", device=dev),
                           lg_prefill=synth.make_logits(c5, args.seed, tag="prefill_logits", device=dev))

@@ -49,16 +49,16 @@ class LayerConfig:
 
 
 CONFIGS = {
-    1: LayerConfig("tiny", T=4, H=256, I=128, E=8, k=2, score=SOFTMAX,
+    "tiny": LayerConfig("tiny", T=4, H=256, I=128, E=8, k=2, score=SOFTMAX,
                    notes="parity config"),
-    2: LayerConfig("decode_mtp", T=3, H=7168, I=2048, E=256, k=8, score=SIGMOID, shared=True,
+    "decode_mtp": LayerConfig("decode_mtp", T=3, H=7168, I=2048, E=256, k=8, score=SIGMOID, shared=True,
                    notes="single-stream MTP decode, 1 + 2 tokens, 2-bit base only"),
-    3: LayerConfig("decode_mtp_delta", T=3, H=7168, I=2048, E=256, k=8, score=SIGMOID, shared=True,
+    "decode_mtp_delta": LayerConfig("decode_mtp_delta", T=3, H=7168, I=2048, E=256, k=8, score=SIGMOID, shared=True,
                    n_resident=32, n_flagged=2, notes="decode + FP4 delta for 32 experts, 2 of 3 tokens gated"),
-    4: LayerConfig("batched_decode", T=24, H=7168, I=2048, E=384, k=8, score=SIGMOID,
+    "batched_decode": LayerConfig("batched_decode", T=24, H=7168, I=2048, E=384, k=8, score=SIGMOID,
                    n_resident=64, n_flagged=12, logits="zipf",
                    notes="8 streams x 3 tokens, Zipf(1.1) expert popularity"),
-    5: LayerConfig("prefill", T=4096, H=7168, I=2048, E=256, k=8, score=SIGMOID,
+    "prefill": LayerConfig("prefill", T=4096, H=7168, I=2048, E=256, k=8, score=SIGMOID,
                    notes="prefill chunk, MFMA grouped GEMM"),
 }
 

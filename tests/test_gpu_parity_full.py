@@ -34,11 +34,11 @@ def _u32(t):
     return np_(t).view(np.uint32)
 
 
-def _variant(cfg_id, variant):
+def _variant(cfg_name, variant):
     """The benchmark's other full-size workloads: the prefill chunk with a gated FP4 delta,
     the decode layer with an NVFP4 shared expert, one GPU's share of a TP4 layer; and the decode
     layer with a delta cache whose matrices pick different codebooks."""
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = synth.CONFIGS[cfg_name]
     if variant == "prefill_delta":
         cfg = dataclasses.replace(cfg, name="prefill_delta", n_resident=32, n_flagged=2048)
     elif variant == "tp4_shard":
@@ -75,10 +75,12 @@ def _choose_tokens(ids: np.ndarray, n_tok: int, flags=None, soe=None):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg_id,variant", [(2, None), (3, None), (4, None), (5, None), (5, "prefill_delta"),
-                                            (2, "nvfp4_shared"), (2, "tp4_shard"), (3, "mixed_codebooks")])
-def test_full_size_forward(cfg_id, variant):
-    cfg = _variant(cfg_id, variant)
+@pytest.mark.parametrize("cfg_name,variant", [("decode_mtp", None), ("decode_mtp_delta", None), ("batched_decode", None),
+                                              ("prefill", None), ("prefill", "prefill_delta"),
+                                              ("decode_mtp", "nvfp4_shared"), ("decode_mtp", "tp4_shard"),
+                                              ("decode_mtp_delta", "mixed_codebooks")])
+def test_full_size_forward(cfg_name, variant):
+    cfg = _variant(cfg_name, variant)
     shared_nvfp4 = variant == "nvfp4_shared"
     pick = variant == "mixed_codebooks"
     print(f"[case] full-size config {cfg.name} T={cfg.T} E={cfg.E} I={cfg.I} variant={variant}", flush=True)

@@ -77,7 +77,7 @@ def test_requant_random_bytes_bitexact():
 
 def test_requant_synthetic_layer_bitexact():
     _print_case("requant tiny synthetic layer (24 matrices)")
-    src = synth.make_layer(synth.CONFIGS[1], seed=1)
+    src = synth.make_layer(synth.CONFIGS["tiny"], seed=1)
     for stack in (src.w13, src.w2):
         codes, scales, s2 = (np_(t) for t in stack)
         w = _gpu_requant(codes, scales, s2)

@@ -626,24 +626,42 @@ __device__ __forceinline__ void issue_dstage(const DeltaSrc &src, uint8_t *smem,
 template <int Q>
 __device__ __forceinline__ float fp8_byte(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8(w, Q); }
 
-// one MFMA k-step (16 k = one FP4 block)
+// The B words of one pipeline step for B row offset `bo`: k-steps Q = 0..3 (one FP4
+// block-16 each) sit at byte offsets (Q / 2) * 1024 + (Q % 2) * 8
+__device__ __forceinline__ void fp4_words(const uint8_t *stg, int bo, uint32_t w[4])
+{
+    const uint8_t *b = stg + kDOffB4 + bo;
+    w[0] = *reinterpret_cast<const uint32_t *>(b);
+    w[1] = *reinterpret_cast<const uint32_t *>(b + 8);
+    w[2] = *reinterpret_cast<const uint32_t *>(b + 1024);
+    w[3] = *reinterpret_cast<const uint32_t *>(b + 1032);
+}
+
+// k-step Q of a pipeline step, software-pipelined: the MFMAs of k-step Q use
+// the A fragments and dequantised B fragments made during k-step Q - 1, while
+// this k-step loads the A fragments and dequantises the B of k-step Q + 1
 template <int NMB, int Q>
-__device__ __forceinline__ void fp4_kstep(const uint8_t *stg, const int boff[2], const uint32_t sw4[2],
-                                          f32x16 acc[kDMB][2])
+__device__ __forceinline__ void fp4_kstep(const uint8_t *stg, const uint32_t w4[2][4], const uint32_t sw4[2],
+                                          bf16x8 afr[kDMB], bf16x8 bq[2], f32x16 acc[kDMB][2])
 {
     const int lane = threadIdx.x & 63, h = lane >> 5;
-    bf16x8 b4[2];
+    bf16x8 an[kDMB], bn[2];
+    if constexpr (Q < 3) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const uint32_t w4 = *reinterpret_cast<const uint32_t *>(stg + kDOffB4 + boff[nb] + (Q >> 1) * 1024 + (Q & 1) * 8);
-        b4[nb] = deq_fp4(w4, fp8_byte<Q>(sw4[nb]));
+        for (int mb = 0; mb < NMB; ++mb) an[mb] = a_frag(stg, 32 * mb + (lane & 31), 2 * (Q + 1) + h);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bn[nb] = deq_fp4(w4[nb][Q + 1], fp8_byte<Q + 1>(sw4[nb]));
     }
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-        const bf16x8 afr = a_frag(stg, 32 * mb + (lane & 31), 2 * Q + h);
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, b4[nb], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[mb], bq[nb], acc[mb][nb], 0, 0, 0);
+    if constexpr (Q < 3) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) afr[mb] = an[mb];
+        bq[0] = bn[0];
+        bq[1] = bn[1];
     }
 }
 
@@ -666,13 +684,22 @@ __device__ __forceinline__ void fp4_pipe_n(const DeltaSrc &src, uint8_t *smem, c
         else wait_barrier<0>();
         if (s + kPS - 1 < nsteps) issue_dstage<NMB>(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
         const uint8_t *stg = smem + (s % kPS) * kDStage;
-        uint32_t sw4[2];
+        // every B word and scale of the step first, so one LDS round trip covers them
+        uint32_t w4[2][4], sw4[2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) sw4[nb] = *reinterpret_cast<const uint32_t *>(stg + kDOffS4 + brow[nb] * 4);
-        fp4_kstep<NMB, 0>(stg, boff, sw4, acc);
-        fp4_kstep<NMB, 1>(stg, boff, sw4, acc);
-        fp4_kstep<NMB, 2>(stg, boff, sw4, acc);
-        fp4_kstep<NMB, 3>(stg, boff, sw4, acc);
+        for (int nb = 0; nb < 2; ++nb) {
+            fp4_words(stg, boff[nb], w4[nb]);
+            sw4[nb] = *reinterpret_cast<const uint32_t *>(stg + kDOffS4 + brow[nb] * 4);
+        }
+        bf16x8 afr[kDMB], bq[2];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) afr[mb] = a_frag(stg, 32 * mb + (lane & 31), h);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bq[nb] = deq_fp4(w4[nb][0], fp8_byte<0>(sw4[nb]));
+        fp4_kstep<NMB, 0>(stg, w4, sw4, afr, bq, acc);
+        fp4_kstep<NMB, 1>(stg, w4, sw4, afr, bq, acc);
+        fp4_kstep<NMB, 2>(stg, w4, sw4, afr, bq, acc);
+        fp4_kstep<NMB, 3>(stg, w4, sw4, afr, bq, acc);
     }
 }
 

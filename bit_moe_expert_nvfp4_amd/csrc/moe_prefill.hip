@@ -55,9 +55,11 @@ namespace moet {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPM = 160;    // rows per M-tile
-constexpr int kPMB = 5;     // 32-row MFMA blocks per M-tile
+constexpr int kPMB = 5;     // 32-row blocks per M-tile (A staging granularity)
+constexpr int kPB = kPM / 16;     // 16-row MFMA blocks per M-tile (2-bit kernels)
 constexpr int kASeg = kPM / 32;   // 8-row A segments each wavefront stages per step
 constexpr int kPK = 64;     // k per pipeline step
 constexpr int kPW = 4;      // wavefronts per workgroup
@@ -306,83 +308,91 @@ __device__ __forceinline__ void issue_stage(const PipeSrc &src, uint8_t *smem, i
     dma4(src.ssrc + ((size_t)(s >> 1) * 64 + lane) * 4, base + kStageA + kStageB + wave * 256);
 }
 
-// Main loop shared by both kernels.  acc[mb][nb] += A(tile rows) x dequant(B row brow[nb]);
-// brow[nb] = index (0..255) of this lane's B row within the workgroup's 256 B-rows.
+// Main loop shared by both 2-bit kernels, on v_mfma_f32_16x16x32_bf16 so that an
+// M-tile costs MFMAs for ceil(rows / 16) blocks of 16 rows.  acc[mb][nb] += A(rows
+// 16 mb .. +15) x dequant(B rows brow[nb]); brow[nb] = index (0..255) of this lane's
+// B row within the workgroup's 256 B-rows (lane l holds B column l % 16 of each of
+// its four 16-column blocks).  The 32 k of one MFMA are split over the lane groups
+// g = l / 16 so that lane group g always reads the same pair of 16-k code words of
+// a 64-k step (words 2 (g / 2) and 2 (g / 2) + 1, i.e. one 32-k scale block): MFMA
+// kc of the step takes word 2 (g / 2) + kc, elements 8 (g % 2) .. + 7, and the A
+// fragment of the same 8 k.  NB = valid 16-row blocks; the tile's ceil(NB / 2)
+// 32-row blocks are staged.
 // GEN: the generic dequant, with the or-constant cbor[nb] of B row brow[nb]'s codebook
-template <int NMB, bool GEN>
-__device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2],
-                                            const uint32_t cbor[2])
+template <int NB, bool GEN>
+__device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, const int brow[4], f32x4 acc[kPB][4],
+                                            const uint32_t cbor[4])
 {
+    constexpr int NSEG = (NB + 1) / 2;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = lane >> 5;                 // k half of the MFMA fragment
-    const uint32_t sh = 2 * h;               // selects elements 8h .. 8h+7 of a code word
+    const int g = lane >> 4;                 // k group of the MFMA fragment
+    const int wsel = g >> 1;                 // this lane's word pair / scale block of a step
+    const uint32_t sh = 2 * (g & 1);         // selects elements 8 (g % 2) .. + 7 of a code word
     const int nsteps = src.K / kPK;
 #pragma unroll
     for (int st = 0; st < kPS - 1; ++st)
-        if (st < nsteps) issue_stage<NMB>(src, smem, st, st, wave, lane);
+        if (st < nsteps) issue_stage<NSEG>(src, smem, st, st, wave, lane);
     for (int s = 0; s < nsteps; ++s) {
-        // stages issued after s: min(kPS - 2, nsteps - 1 - s), NMB + 2 DMAs each
-        if (s + 1 < nsteps) wait_barrier<(NMB + 2) * (kPS - 2)>();
+        // stages issued after s: min(kPS - 2, nsteps - 1 - s), NSEG + 2 DMAs each
+        if (s + 1 < nsteps) wait_barrier<(NSEG + 2) * (kPS - 2)>();
         else wait_barrier<0>();
-        if (s + kPS - 1 < nsteps) issue_stage<NMB>(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
+        if (s + kPS - 1 < nsteps) issue_stage<NSEG>(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
         const uint8_t *stg = smem + (s % kPS) * kStage;
         const uint8_t *aT = stg;
         const uint8_t *bT = stg + kStageA;
         const uint8_t *sT = stg + kStageA + kStageB;
-        uint4 bw[2];
-        uint32_t mask[2][2], orc[2][2], sadd[2][2];
+        uint2 bw[4];
+        uint32_t mask[4], orc[4], sadd[4];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            bw[nb] = *reinterpret_cast<const uint4 *>(bT + brow[nb] * 16);
+        for (int nb = 0; nb < 4; ++nb) {
+            bw[nb] = *reinterpret_cast<const uint2 *>(bT + brow[nb] * 16 + 8 * wsel);
             const uint32_t sw = *reinterpret_cast<const uint32_t *>(sT + brow[nb] * 4);
-            if constexpr (GEN) {
-                block_consts_gen(sw, 2 * (s & 1) + 0, cbor[nb], mask[nb][0], orc[nb][0], sadd[nb][0]);
-                block_consts_gen(sw, 2 * (s & 1) + 1, cbor[nb], mask[nb][1], orc[nb][1], sadd[nb][1]);
-            } else {
-                block_consts(sw, 2 * (s & 1) + 0, mask[nb][0], orc[nb][0], sadd[nb][0]);
-                block_consts(sw, 2 * (s & 1) + 1, mask[nb][1], orc[nb][1], sadd[nb][1]);
-            }
+            if constexpr (GEN) block_consts_gen(sw, 2 * (s & 1) + wsel, cbor[nb], mask[nb], orc[nb], sadd[nb]);
+            else block_consts(sw, 2 * (s & 1) + wsel, mask[nb], orc[nb], sadd[nb]);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {   // MFMA k-steps of 16
-            bf16x8 bfr[2];
+        for (int kc = 0; kc < 2; ++kc) {
+            bf16x8 bfr[4];
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const uint32_t wv = (q == 0) ? bw[nb].x : (q == 1) ? bw[nb].y : (q == 2) ? bw[nb].z : bw[nb].w;
-                bfr[nb] = deq_frag<GEN>(wv, sh, mask[nb][q >> 1], orc[nb][q >> 1], sadd[nb][q >> 1]);
-            }
+            for (int nb = 0; nb < 4; ++nb)
+                bfr[nb] = deq_frag<GEN>(kc ? bw[nb].y : bw[nb].x, sh, mask[nb], orc[nb], sadd[nb]);
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                const bf16x8 afr = a_frag(aT, 32 * mb + (lane & 31), 2 * q + h);
+            for (int mb = 0; mb < NB; ++mb) {
+                const bf16x8 afr = a_frag(aT, 16 * mb + (lane & 15), 4 * wsel + 2 * kc + (g & 1));
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[nb], acc[mb][nb], 0, 0, 0);
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[nb], acc[mb][nb], 0, 0, 0);
             }
         }
     }
 }
 
 template <bool GEN>
-__device__ __forceinline__ void gemm_pipe_g(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2],
-                                            int nmb, const uint32_t cbor[2])
+__device__ __forceinline__ void gemm_pipe_g(const PipeSrc &src, uint8_t *smem, const int brow[4], f32x4 acc[kPB][4],
+                                            int nb16, const uint32_t cbor[4])
 {
-    switch (nmb) {
+    switch (nb16) {
     case 1: gemm_pipe_n<1, GEN>(src, smem, brow, acc, cbor); break;
     case 2: gemm_pipe_n<2, GEN>(src, smem, brow, acc, cbor); break;
     case 3: gemm_pipe_n<3, GEN>(src, smem, brow, acc, cbor); break;
     case 4: gemm_pipe_n<4, GEN>(src, smem, brow, acc, cbor); break;
-    default: gemm_pipe_n<5, GEN>(src, smem, brow, acc, cbor); break;
+    case 5: gemm_pipe_n<5, GEN>(src, smem, brow, acc, cbor); break;
+    case 6: gemm_pipe_n<6, GEN>(src, smem, brow, acc, cbor); break;
+    case 7: gemm_pipe_n<7, GEN>(src, smem, brow, acc, cbor); break;
+    case 8: gemm_pipe_n<8, GEN>(src, smem, brow, acc, cbor); break;
+    case 9: gemm_pipe_n<9, GEN>(src, smem, brow, acc, cbor); break;
+    default: gemm_pipe_n<10, GEN>(src, smem, brow, acc, cbor); break;
     }
 }
 
-// one instantiation per number of valid 32-row blocks and dequant kind, chosen once per
+// one instantiation per number of valid 16-row blocks and dequant kind, chosen once per
 // workgroup; cb[nb]: codebook id of B row brow[nb]'s matrix
-__device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kPMB][2],
-                                          int nmb, const uint32_t cb[2])
+__device__ __forceinline__ void gemm_pipe(const PipeSrc &src, uint8_t *smem, const int brow[4], f32x4 acc[kPB][4],
+                                          int nb16, const uint32_t cb[4])
 {
-    const uint32_t cbor[2] = {w2_or_of(cb[0]), w2_or_of(cb[1])};
-    if ((cb[0] | cb[1]) == 0) gemm_pipe_g<false>(src, smem, brow, acc, nmb, cbor);
-    else gemm_pipe_g<true>(src, smem, brow, acc, nmb, cbor);
+    const uint32_t cbor[4] = {w2_or_of(cb[0]), w2_or_of(cb[1]), w2_or_of(cb[2]), w2_or_of(cb[3])};
+    if ((cb[0] | cb[1] | cb[2] | cb[3]) == 0) gemm_pipe_g<false>(src, smem, brow, acc, nb16, cbor);
+    else gemm_pipe_g<true>(src, smem, brow, acc, nb16, cbor);
 }
 
 // ---------------------------------------------------------------------------
@@ -454,7 +464,8 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     if (ms >= p.n_mslots) return;
     MTile mt;
     if (!locate_mtile<kPM>(p, ms, mt)) return;
-    const int nmb = (mt.rows + 31) / 32;
+    const int nb16 = (mt.rows + 15) / 16;
+    const int nmb = (nb16 + 1) / 2;   // staged 32-row blocks
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
     // A rows fetched by this lane: segment i of wave w holds rows 8(nmb w + i) .. +7; lane -> row + lane/8
@@ -472,45 +483,49 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     // B: 256 rows = gate rows [128 nt, +128) then up rows [128 nt, +128); wave w fetches storage tile w
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
     if (ws < 0) return;   // missing expert: no work, the combine skips its routings
-    const int jl = 32 * wave + (lane & 31);          // h column within the tile
-    const int j = 128 * nt + jl;
-    const int brow[2] = {jl, 128 + jl};               // gate row, up row in the stage
-    f32x16 acc[kPMB][2];
+    // this lane's h columns within the tile: jl + 16 c (c = 0, 1); B rows: gate jl + 16 c, up 128 + jl + 16 c
+    const int jl = 32 * wave + (lane & 15);
+    const int brow[4] = {jl, jl + 16, 128 + jl, 128 + jl + 16};
+    f32x4 acc[kPB][4];
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb)
+    for (int mb = 0; mb < kPB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+            for (int v = 0; v < 4; ++v) acc[mb][nb][v] = 0.f;
     const moet_w2 &W = (mt.e >= 0) ? p.w13 : p.sh13;
     const int m0 = (mt.e >= 0) ? 2 * ws : 0;
     const int mat = m0 + (wave >> 1);
     const int tile = 2 * nt + (wave & 1);
     src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)mat * I * H / 16) + (size_t)tile * (H / 64) * 1024;
     src.ssrc = W.scales + (size_t)mat * I * H / 32 + (size_t)tile * (H / 128) * 256;
-    const uint32_t cb[2] = {w2_codebook(W, m0), w2_codebook(W, m0 + 1)};   // gate, up
-    gemm_pipe(src, smem, brow, acc, nmb, cb);
+    const uint32_t cbg = w2_codebook(W, m0), cbu = w2_codebook(W, m0 + 1);
+    const uint32_t cb[4] = {cbg, cbg, cbu, cbu};   // gate, gate, up, up
+    gemm_pipe(src, smem, brow, acc, nb16, cb);
     const float sg = W.scale2[m0], su = W.scale2[m0 + 1];
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
+#pragma clang loop unroll(full)
+    for (int mb = 0; mb < kPB; ++mb) {
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb) {
-        if (mb >= nmb) break;
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * mb + 4 * (lane >> 4) + v;
+            if (mb < nb16 && r < mt.rows) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (r < mt.rows) {
-                float g = acc[mb][0][v] * sg, u = acc[mb][1][v] * su;
-                if (rowbase + r < mt.fl_end) {   // flagged row: the FP4 kernel adds its delta, then SwiGLU
-                    float *pre = p.pre + (size_t)(rowbase + r) * (2 * I) + j;
-                    pre[0] = g;
-                    pre[I] = u;
-                    continue;
+                for (int c = 0; c < 2; ++c) {
+                    const int j = 128 * nt + jl + 16 * c;
+                    float g = acc[mb][c][v] * sg, u = acc[mb][2 + c][v] * su;
+                    if (rowbase + r < mt.fl_end) {   // flagged row: the FP4 kernel adds its delta, then SwiGLU
+                        float *pre = p.pre + (size_t)(rowbase + r) * (2 * I) + j;
+                        pre[0] = g;
+                        pre[I] = u;
+                        continue;
+                    }
+                    if (p.swiglu_limit > 0.f) {
+                        g = fminf(g, p.swiglu_limit);
+                        u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+                    }
+                    p.h[(size_t)(rowbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
                 }
-                if (p.swiglu_limit > 0.f) {
-                    g = fminf(g, p.swiglu_limit);
-                    u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
-                }
-                p.h[(size_t)(rowbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
             }
         }
     }
@@ -531,7 +546,8 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     if (ms >= p.n_mslots) return;
     MTile mt;
     if (!locate_mtile<kPM>(p, ms, mt)) return;
-    const int nmb = (mt.rows + 31) / 32;
+    const int nb16 = (mt.rows + 15) / 16;
+    const int nmb = (nb16 + 1) / 2;   // staged 32-row blocks
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k;
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;
@@ -545,31 +561,32 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
     if (ws < 0) return;
     const int tile = 4 * nt + wave;
-    const int brow[2] = {64 * wave + (lane & 31), 64 * wave + 32 + (lane & 31)};
-    f32x16 acc[kPMB][2];
+    const int bl = 64 * wave + (lane & 15);
+    const int brow[4] = {bl, bl + 16, bl + 32, bl + 48};
+    f32x4 acc[kPB][4];
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb)
+    for (int mb = 0; mb < kPB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+            for (int v = 0; v < 4; ++v) acc[mb][nb][v] = 0.f;
     const moet_w2 &W = (mt.e >= 0) ? p.w2 : p.sh2;
     const int m0 = (mt.e >= 0) ? ws : 0;
     src.bsrc = reinterpret_cast<const uint8_t *>(W.codes + (size_t)m0 * H * I / 16) + (size_t)tile * (I / 64) * 1024;
     src.ssrc = W.scales + (size_t)m0 * H * I / 32 + (size_t)tile * (I / 128) * 256;
-    const uint32_t cb[2] = {w2_codebook(W, m0), w2_codebook(W, m0)};
-    gemm_pipe(src, smem, brow, acc, nmb, cb);
+    const uint32_t cbw = w2_codebook(W, m0);
+    const uint32_t cb[4] = {cbw, cbw, cbw, cbw};
+    gemm_pipe(src, smem, brow, acc, nb16, cb);
     const float s2 = W.scale2[m0];
+#pragma clang loop unroll(full)
+    for (int mb = 0; mb < kPB; ++mb) {
 #pragma unroll
-    for (int mb = 0; mb < kPMB; ++mb) {
-        if (mb >= nmb) break;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (r < mt.rows) {
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * mb + 4 * (lane >> 4) + v;
+            if (mb < nb16 && r < mt.rows) {
                 const int prow = (mt.e >= 0) ? min(max(p.order[mt.row0 + r], 0), P - 1) : P + mt.row0 + r;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) p.ypart[(size_t)prow * H + 256 * nt + brow[nb]] = acc[mb][nb][v] * s2;
+                for (int nb = 0; nb < 4; ++nb) p.ypart[(size_t)prow * H + 256 * nt + brow[nb]] = acc[mb][nb][v] * s2;
             }
         }
     }

@@ -483,9 +483,13 @@ def prefill_leg(layer, cfg5, steps, seed, dev, flags=None, soe=None):
     import torch
     from bit_moe_expert_nvfp4_amd import moet, synth
 
+    import dataclasses
     T, k = cfg5.T, cfg5.k
+    # activations and router logits of the plain chunk in every leg, so that a leg with the delta
+    # routes exactly the same pairs and differs from the plain one only by the delta's work
+    base = dataclasses.replace(cfg5, name=synth.CONFIGS["prefill"].name)
     x = synth.make_activations(T, cfg5.H, seed, tag="prefill_x", device=dev)
-    lg = synth.make_logits(cfg5, seed, tag="prefill_logits", device=dev)
+    lg = synth.make_logits(base, seed, tag="prefill_logits", device=dev)
     ws = moet.alloc_workspace(layer, T, k, dev)
     out = torch.empty((T, cfg5.H), dtype=torch.bfloat16, device=dev)
     ro = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),

@@ -54,7 +54,6 @@
 namespace moet {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPM = 160;    // rows per M-tile
@@ -611,7 +610,7 @@ __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2))) v
 #define MOET_FP4_TILE 128
 #endif
 constexpr int kDM = MOET_FP4_TILE;            // rows per FP4 M-tile (64 or 128)
-constexpr int kDMB = kDM / 32;                // MFMA row blocks
+constexpr int kDB = kDM / 16;                 // 16-row MFMA blocks
 constexpr int kDSeg = kDM / 32;               // 8-row A segments per wavefront (4 waves x kDSeg x 8 = kDM rows)
 constexpr int kDStageA = kDM * 128;
 constexpr int kDOffB4 = kDStageA;
@@ -643,95 +642,82 @@ __device__ __forceinline__ void issue_dstage(const DeltaSrc &src, uint8_t *smem,
 template <int Q>
 __device__ __forceinline__ float fp8_byte(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8(w, Q); }
 
-// The B words of one pipeline step for B row offset `bo`: k-steps Q = 0..3 (one FP4
-// block-16 each) sit at byte offsets (Q / 2) * 1024 + (Q % 2) * 8
-__device__ __forceinline__ void fp4_words(const uint8_t *stg, int bo, uint32_t w[4])
+// acc[mb][nb] += A(tile rows 16 mb .. +15) x dequantFP4(B row brow[nb]) on
+// v_mfma_f32_16x16x32_bf16 (lane l holds B column l % 16 of each of its four
+// 16-column blocks).  MFMA kc of a 64-k step covers the step's 32-k FP4 chunk kc,
+// lane group g = l / 16 taking its code dword g (8 k) and the A fragment of the
+// same 8 k; that dword lies in block-16 2 kc + g / 2 of the row's scale dword.
+// NB = valid 16-row blocks; ceil(NB / 2) 32-row blocks of A are staged.  The B of
+// MFMA 1 is dequantised while the MFMAs of MFMA 0 run.
+template <int NB>
+__device__ __forceinline__ void fp4_pipe_n(const DeltaSrc &src, uint8_t *smem, const int brow[4], f32x4 acc[kDB][4])
 {
-    const uint8_t *b = stg + kDOffB4 + bo;
-    w[0] = *reinterpret_cast<const uint32_t *>(b);
-    w[1] = *reinterpret_cast<const uint32_t *>(b + 8);
-    w[2] = *reinterpret_cast<const uint32_t *>(b + 1024);
-    w[3] = *reinterpret_cast<const uint32_t *>(b + 1032);
-}
-
-// k-step Q of a pipeline step, software-pipelined: the MFMAs of k-step Q use
-// the A fragments and dequantised B fragments made during k-step Q - 1, while
-// this k-step loads the A fragments and dequantises the B of k-step Q + 1
-template <int NMB, int Q>
-__device__ __forceinline__ void fp4_kstep(const uint8_t *stg, const uint32_t w4[2][4], const uint32_t sw4[2],
-                                          bf16x8 afr[kDMB], bf16x8 bq[2], f32x16 acc[kDMB][2])
-{
-    const int lane = threadIdx.x & 63, h = lane >> 5;
-    bf16x8 an[kDMB], bn[2];
-    if constexpr (Q < 3) {
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) an[mb] = a_frag(stg, 32 * mb + (lane & 31), 2 * (Q + 1) + h);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bn[nb] = deq_fp4(w4[nb][Q + 1], fp8_byte<Q + 1>(sw4[nb]));
-    }
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[mb], bq[nb], acc[mb][nb], 0, 0, 0);
-    if constexpr (Q < 3) {
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) afr[mb] = an[mb];
-        bq[0] = bn[0];
-        bq[1] = bn[1];
-    }
-}
-
-// acc[mb][nb] += A(tile rows) x dequantFP4(B row brow[nb])
-template <int NMB>
-__device__ __forceinline__ void fp4_pipe_n(const DeltaSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kDMB][2])
-{
-    constexpr int kDma = NMB + 3;     // DMA instructions per wave per stage
+    constexpr int NSEG = (NB + 1) / 2;
+    constexpr int kDma = NSEG + 3;    // DMA instructions per wave per stage
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = lane >> 5;
+    const int g = lane >> 4;
     const int nsteps = src.K / kPK;
-    int boff[2];
+    int boff[4];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) boff[nb] = (brow[nb] >> 6) * 2048 + (brow[nb] & 63) * 16 + 4 * h;
+    for (int nb = 0; nb < 4; ++nb) boff[nb] = kDOffB4 + (brow[nb] >> 6) * 2048 + (brow[nb] & 63) * 16 + 4 * g;
 #pragma unroll
     for (int st = 0; st < kPS - 1; ++st)
-        if (st < nsteps) issue_dstage<NMB>(src, smem, st, st, wave, lane);
+        if (st < nsteps) issue_dstage<NSEG>(src, smem, st, st, wave, lane);
     for (int s = 0; s < nsteps; ++s) {
         if (s + 1 < nsteps) wait_barrier<kDma * (kPS - 2)>();
         else wait_barrier<0>();
-        if (s + kPS - 1 < nsteps) issue_dstage<NMB>(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
+        if (s + kPS - 1 < nsteps) issue_dstage<NSEG>(src, smem, (s + kPS - 1) % kPS, s + kPS - 1, wave, lane);
         const uint8_t *stg = smem + (s % kPS) * kDStage;
         // every B word and scale of the step first, so one LDS round trip covers them
-        uint32_t w4[2][4], sw4[2];
+        uint32_t w0[4], w1[4], sw[4];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            fp4_words(stg, boff[nb], w4[nb]);
-            sw4[nb] = *reinterpret_cast<const uint32_t *>(stg + kDOffS4 + brow[nb] * 4);
+        for (int nb = 0; nb < 4; ++nb) {
+            w0[nb] = *reinterpret_cast<const uint32_t *>(stg + boff[nb]);
+            w1[nb] = *reinterpret_cast<const uint32_t *>(stg + boff[nb] + 1024);
+            sw[nb] = *reinterpret_cast<const uint32_t *>(stg + kDOffS4 + brow[nb] * 4) >> (8 * (g >> 1));
         }
-        bf16x8 afr[kDMB], bq[2];
+        bf16x8 b0[4], b1[4];
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) afr[mb] = a_frag(stg, 32 * mb + (lane & 31), h);
+        for (int nb = 0; nb < 4; ++nb) b0[nb] = deq_fp4(w0[nb], fp8_byte<0>(sw[nb]));
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bq[nb] = deq_fp4(w4[nb][0], fp8_byte<0>(sw4[nb]));
-        fp4_kstep<NMB, 0>(stg, w4, sw4, afr, bq, acc);
-        fp4_kstep<NMB, 1>(stg, w4, sw4, afr, bq, acc);
-        fp4_kstep<NMB, 2>(stg, w4, sw4, afr, bq, acc);
-        fp4_kstep<NMB, 3>(stg, w4, sw4, afr, bq, acc);
+        for (int nb = 0; nb < 4; ++nb) b1[nb] = deq_fp4(w1[nb], fp8_byte<2>(sw[nb]));
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb) {
+            const bf16x8 afr = a_frag(stg, 16 * mb + (lane & 15), g);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, b0[nb], acc[mb][nb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb) {
+            const bf16x8 afr = a_frag(stg, 16 * mb + (lane & 15), 4 + g);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, b1[nb], acc[mb][nb], 0, 0, 0);
+        }
     }
 }
 
-__device__ __forceinline__ void fp4_pipe(const DeltaSrc &src, uint8_t *smem, const int brow[2], f32x16 acc[kDMB][2],
-                                         int nmb)
+__device__ __forceinline__ void fp4_pipe(const DeltaSrc &src, uint8_t *smem, const int brow[4], f32x4 acc[kDB][4],
+                                         int nb16)
 {
-    if constexpr (kDMB == 2) {
-        if (nmb == 1) fp4_pipe_n<1>(src, smem, brow, acc);
-        else fp4_pipe_n<2>(src, smem, brow, acc);
-    } else {
-        switch (nmb) {
+    if constexpr (kDB == 4) {
+        switch (nb16) {
         case 1: fp4_pipe_n<1>(src, smem, brow, acc); break;
         case 2: fp4_pipe_n<2>(src, smem, brow, acc); break;
         case 3: fp4_pipe_n<3>(src, smem, brow, acc); break;
         default: fp4_pipe_n<4>(src, smem, brow, acc); break;
+        }
+    } else {
+        switch (nb16) {
+        case 1: fp4_pipe_n<1>(src, smem, brow, acc); break;
+        case 2: fp4_pipe_n<2>(src, smem, brow, acc); break;
+        case 3: fp4_pipe_n<3>(src, smem, brow, acc); break;
+        case 4: fp4_pipe_n<4>(src, smem, brow, acc); break;
+        case 5: fp4_pipe_n<5>(src, smem, brow, acc); break;
+        case 6: fp4_pipe_n<6>(src, smem, brow, acc); break;
+        case 7: fp4_pipe_n<7>(src, smem, brow, acc); break;
+        default: fp4_pipe_n<8>(src, smem, brow, acc); break;
         }
     }
 }
@@ -778,8 +764,9 @@ __device__ __forceinline__ void fc1_delta_body(const PrefillParams &p, uint8_t *
     if (!delta_tiles<SHARED>(p, dt)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k, nt = blockIdx.x;
-    const int jl = 32 * wave + (lane & 31), j = 128 * nt + jl;
-    const int brow[2] = {jl, 128 + jl};
+    // this lane's h columns within the tile: jl + 16 c (c = 0, 1); B rows: gate jl + 16 c, up 128 + jl + 16 c
+    const int jl = 32 * wave + (lane & 15);
+    const int brow[4] = {jl, jl + 16, 128 + jl, 128 + jl + 16};
     const moet_fp4 &F = SHARED ? p.shf13 : p.d13;
     const int fm0 = SHARED ? 0 : 2 * dt.ds;
     const int mat = wave >> 1, tile = 2 * nt + (wave & 1);
@@ -791,40 +778,44 @@ __device__ __forceinline__ void fc1_delta_body(const PrefillParams &p, uint8_t *
     const int ntile = (dt.count + kDM - 1) / kDM;
     for (int it = SHARED ? 0 : (int)blockIdx.z; it < ntile; it += SHARED ? 1 : (int)gridDim.z) {
         const int r0 = dt.row0 + kDM * it, rows = min(kDM, dt.count - kDM * it);
-        const int nmb = (rows + 31) / 32;
+        const int nb16 = (rows + 15) / 16;
+        const int nmb = (nb16 + 1) / 2;   // staged 32-row blocks
 #pragma unroll
         for (int i = 0; i < kDSeg; ++i) {
             const int r = min(8 * (nmb * wave + i) + (lane >> 3), rows - 1);
             const int tok = SHARED ? r0 + r : min(max(p.order[r0 + r], 0), P - 1) / p.k;
             src.arow[i] = reinterpret_cast<const uint8_t *>(p.x + (size_t)tok * H);
         }
-        f32x16 acc[kDMB][2];
+        f32x4 acc[kDB][4];
 #pragma unroll
-        for (int mb = 0; mb < kDMB; ++mb)
+        for (int mb = 0; mb < kDB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-        fp4_pipe(src, smem, brow, acc, nmb);
+                for (int v = 0; v < 4; ++v) acc[mb][nb][v] = 0.f;
+        fp4_pipe(src, smem, brow, acc, nb16);
         const int hbase = SHARED ? P + r0 : r0;
+#pragma clang loop unroll(full)
+        for (int mb = 0; mb < kDB; ++mb) {
 #pragma unroll
-        for (int mb = 0; mb < kDMB; ++mb) {
-            if (mb >= nmb) break;
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * mb + 4 * (lane >> 4) + v;
+                if (mb < nb16 && r < rows) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (r < rows) {
-                    float g = acc[mb][0][v] * dsg, u = acc[mb][1][v] * dsu;
-                    if (!SHARED) {   // plus the 2-bit pre-activations of this row
-                        const float *pre = p.pre + (size_t)(r0 + r) * (2 * I) + j;
-                        g += pre[0];
-                        u += pre[I];
+                    for (int c = 0; c < 2; ++c) {
+                        const int j = 128 * nt + jl + 16 * c;
+                        float g = acc[mb][c][v] * dsg, u = acc[mb][2 + c][v] * dsu;
+                        if (!SHARED) {   // plus the 2-bit pre-activations of this row
+                            const float *pre = p.pre + (size_t)(r0 + r) * (2 * I) + j;
+                            g += pre[0];
+                            u += pre[I];
+                        }
+                        if (p.swiglu_limit > 0.f) {
+                            g = fminf(g, p.swiglu_limit);
+                            u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
+                        }
+                        p.h[(size_t)(hbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
                     }
-                    if (p.swiglu_limit > 0.f) {
-                        g = fminf(g, p.swiglu_limit);
-                        u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
-                    }
-                    p.h[(size_t)(hbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
                 }
             }
         }
@@ -839,7 +830,8 @@ __device__ __forceinline__ void fc2_delta_body(const PrefillParams &p, uint8_t *
     if (!delta_tiles<SHARED>(p, dt)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k, nt = blockIdx.x;
-    const int brow[2] = {64 * wave + (lane & 31), 64 * wave + 32 + (lane & 31)};
+    const int bl = 64 * wave + (lane & 15);
+    const int brow[4] = {bl, bl + 16, bl + 32, bl + 48};
     const moet_fp4 &F = SHARED ? p.shf2 : p.d2;
     const int fm = SHARED ? 0 : dt.ds;
     const int tile = 4 * nt + wave;
@@ -851,7 +843,8 @@ __device__ __forceinline__ void fc2_delta_body(const PrefillParams &p, uint8_t *
     const int ntile = (dt.count + kDM - 1) / kDM;
     for (int it = SHARED ? 0 : (int)blockIdx.z; it < ntile; it += SHARED ? 1 : (int)gridDim.z) {
         const int r0 = dt.row0 + kDM * it, rows = min(kDM, dt.count - kDM * it);
-        const int nmb = (rows + 31) / 32;
+        const int nb16 = (rows + 15) / 16;
+        const int nmb = (nb16 + 1) / 2;   // staged 32-row blocks
         const int hbase = SHARED ? P + r0 : r0;
 #pragma unroll
         for (int i = 0; i < kDSeg; ++i) {
@@ -861,24 +854,23 @@ __device__ __forceinline__ void fc2_delta_body(const PrefillParams &p, uint8_t *
         // y row (pair id) of each tile row, staged once for the epilogue
         if (tid < rows) s_prow[tid] = SHARED ? P + r0 + tid : min(max(p.order[r0 + tid], 0), P - 1);
         __syncthreads();
-        f32x16 acc[kDMB][2];
+        f32x4 acc[kDB][4];
 #pragma unroll
-        for (int mb = 0; mb < kDMB; ++mb)
+        for (int mb = 0; mb < kDB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-        fp4_pipe(src, smem, brow, acc, nmb);
+                for (int v = 0; v < 4; ++v) acc[mb][nb][v] = 0.f;
+        fp4_pipe(src, smem, brow, acc, nb16);
+#pragma clang loop unroll(full)
+        for (int mb = 0; mb < kDB; ++mb) {
 #pragma unroll
-        for (int mb = 0; mb < kDMB; ++mb) {
-            if (mb >= nmb) break;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (r < rows) {
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * mb + 4 * (lane >> 4) + v;
+                if (mb < nb16 && r < rows) {
                     const int prow = s_prow[r];
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
+                    for (int nb = 0; nb < 4; ++nb) {
                         float *y = p.ypart + (size_t)prow * H + 256 * nt + brow[nb];
                         const float d = acc[mb][nb][v] * ds2;
                         *y = SHARED ? d : *y + d;   // delta: added to the 2-bit y

@@ -308,10 +308,13 @@ __device__ __forceinline__ void issue_stage(const PipeSrc &src, uint8_t *smem, i
 }
 
 // Main loop shared by both 2-bit kernels, on v_mfma_f32_16x16x32_bf16 so that an
-// M-tile costs MFMAs for ceil(rows / 16) blocks of 16 rows.  acc[mb][nb] += A(rows
-// 16 mb .. +15) x dequant(B rows brow[nb]); brow[nb] = index (0..255) of this lane's
-// B row within the workgroup's 256 B-rows (lane l holds B column l % 16 of each of
-// its four 16-column blocks).  The 32 k of one MFMA are split over the lane groups
+// M-tile costs MFMAs for ceil(rows / 16) blocks of 16 rows.  acc[mb][nb] accumulates
+// the 16 x 16 product of A rows 16 mb .. +15 and the dequantised B block nb, with the
+// B fragment as the MFMA's first operand so that the result comes out transposed:
+// lane l holds features 4 (l / 16) .. + 3 of tile row 16 mb + l % 16, which the
+// epilogues store as one 16-byte (y) or 8-byte (h) write.  brow[nb] = index (0..255)
+// of this lane's B row within the workgroup's 256 B-rows (lane l loads the fragment
+// of feature l % 16 of each of its four 16-feature blocks).  The 32 k of one MFMA are split over the lane groups
 // g = l / 16 so that lane group g always reads the same pair of 16-k code words of
 // a 64-k step (words 2 (g / 2) and 2 (g / 2) + 1, i.e. one 32-k scale block): MFMA
 // kc of the step takes word 2 (g / 2) + kc, elements 8 (g % 2) .. + 7, and the A
@@ -360,7 +363,7 @@ __device__ __forceinline__ void gemm_pipe_n(const PipeSrc &src, uint8_t *smem, c
                 const bf16x8 afr = a_frag(aT, 16 * mb + (lane & 15), 4 * wsel + 2 * kc + (g & 1));
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[nb], acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nb], afr, acc[mb][nb], 0, 0, 0);
             }
         }
     }
@@ -482,7 +485,7 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     // B: 256 rows = gate rows [128 nt, +128) then up rows [128 nt, +128); wave w fetches storage tile w
     const int ws = (mt.e >= 0) ? weight_slot(p, mt.e) : 0;
     if (ws < 0) return;   // missing expert: no work, the combine skips its routings
-    // this lane's h columns within the tile: jl + 16 c (c = 0, 1); B rows: gate jl + 16 c, up 128 + jl + 16 c
+    // B rows of this lane's fragments: gate jl + 16 c, up 128 + jl + 16 c (c = 0, 1)
     const int jl = 32 * wave + (lane & 15);
     const int brow[4] = {jl, jl + 16, 128 + jl, 128 + jl + 16};
     f32x4 acc[kPB][4];
@@ -503,28 +506,38 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     gemm_pipe(src, smem, brow, acc, nb16, cb);
     const float sg = W.scale2[m0], su = W.scale2[m0 + 1];
     const int rowbase = (mt.e >= 0) ? mt.row0 : P + mt.row0;   // h row of tile row 0
+    // acc[mb][nb][v]: tile row 16 mb + lane % 16, feature 4 (lane / 16) + v of B block nb
+    const int r0 = lane & 15, f0 = 4 * (lane >> 4);
 #pragma clang loop unroll(full)
     for (int mb = 0; mb < kPB; ++mb) {
+        const int r = 16 * mb + r0;
+        if (mb < nb16 && r < mt.rows) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = 16 * mb + 4 * (lane >> 4) + v;
-            if (mb < nb16 && r < mt.rows) {
+            for (int c = 0; c < 2; ++c) {
+                const int j = 128 * nt + 32 * wave + 16 * c + f0;   // h columns j .. j + 3
+                float g[4], u[4];
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int j = 128 * nt + jl + 16 * c;
-                    float g = acc[mb][c][v] * sg, u = acc[mb][2 + c][v] * su;
-                    if (rowbase + r < mt.fl_end) {   // flagged row: the FP4 kernel adds its delta, then SwiGLU
-                        float *pre = p.pre + (size_t)(rowbase + r) * (2 * I) + j;
-                        pre[0] = g;
-                        pre[I] = u;
-                        continue;
-                    }
-                    if (p.swiglu_limit > 0.f) {
-                        g = fminf(g, p.swiglu_limit);
-                        u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
-                    }
-                    p.h[(size_t)(rowbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
+                for (int v = 0; v < 4; ++v) {
+                    g[v] = acc[mb][c][v] * sg;
+                    u[v] = acc[mb][2 + c][v] * su;
                 }
+                if (rowbase + r < mt.fl_end) {   // flagged row: the FP4 kernel adds its delta, then SwiGLU
+                    float *pre = p.pre + (size_t)(rowbase + r) * (2 * I) + j;
+                    *reinterpret_cast<float4 *>(pre) = make_float4(g[0], g[1], g[2], g[3]);
+                    *reinterpret_cast<float4 *>(pre + I) = make_float4(u[0], u[1], u[2], u[3]);
+                    continue;
+                }
+                uint32_t hv[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    if (p.swiglu_limit > 0.f) {
+                        g[v] = fminf(g[v], p.swiglu_limit);
+                        u[v] = fminf(fmaxf(u[v], -p.swiglu_limit), p.swiglu_limit);
+                    }
+                    hv[v] = f32_to_bf16_rne(silu_f32(g[v]) * u[v]);
+                }
+                *reinterpret_cast<uint2 *>(p.h + (size_t)(rowbase + r) * I + j) =
+                    make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
             }
         }
     }
@@ -577,16 +590,18 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     const uint32_t cb[4] = {cbw, cbw, cbw, cbw};
     gemm_pipe(src, smem, brow, acc, nb16, cb);
     const float s2 = W.scale2[m0];
+    // acc[mb][nb][v]: tile row 16 mb + lane % 16, output feature 64 wave + 16 nb + 4 (lane / 16) + v
+    const int r0 = lane & 15, f0 = 64 * wave + 4 * (lane >> 4);
 #pragma clang loop unroll(full)
     for (int mb = 0; mb < kPB; ++mb) {
+        const int r = 16 * mb + r0;
+        if (mb < nb16 && r < mt.rows) {
+            const int prow = (mt.e >= 0) ? min(max(p.order[mt.row0 + r], 0), P - 1) : P + mt.row0 + r;
+            float *y = p.ypart + (size_t)prow * H + 256 * nt + f0;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = 16 * mb + 4 * (lane >> 4) + v;
-            if (mb < nb16 && r < mt.rows) {
-                const int prow = (mt.e >= 0) ? min(max(p.order[mt.row0 + r], 0), P - 1) : P + mt.row0 + r;
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) p.ypart[(size_t)prow * H + 256 * nt + brow[nb]] = acc[mb][nb][v] * s2;
-            }
+            for (int nb = 0; nb < 4; ++nb)
+                *reinterpret_cast<float4 *>(y + 16 * nb) =
+                    make_float4(acc[mb][nb][0] * s2, acc[mb][nb][1] * s2, acc[mb][nb][2] * s2, acc[mb][nb][3] * s2);
         }
     }
 }
@@ -642,9 +657,10 @@ __device__ __forceinline__ void issue_dstage(const DeltaSrc &src, uint8_t *smem,
 template <int Q>
 __device__ __forceinline__ float fp8_byte(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8(w, Q); }
 
-// acc[mb][nb] += A(tile rows 16 mb .. +15) x dequantFP4(B row brow[nb]) on
-// v_mfma_f32_16x16x32_bf16 (lane l holds B column l % 16 of each of its four
-// 16-column blocks).  MFMA kc of a 64-k step covers the step's 32-k FP4 chunk kc,
+// acc[mb][nb] accumulates the product of A rows 16 mb .. +15 and the dequantised
+// FP4 B block nb on v_mfma_f32_16x16x32_bf16, transposed as in the 2-bit kernels
+// (lane l loads the fragment of feature l % 16 of each of its four 16-feature
+// blocks and holds features 4 (l / 16) .. + 3 of row 16 mb + l % 16).  MFMA kc of a 64-k step covers the step's 32-k FP4 chunk kc,
 // lane group g = l / 16 taking its code dword g (8 k) and the A fragment of the
 // same 8 k; that dword lies in block-16 2 kc + g / 2 of the row's scale dword.
 // NB = valid 16-row blocks; ceil(NB / 2) 32-row blocks of A are staged.  The B of
@@ -686,14 +702,14 @@ __device__ __forceinline__ void fp4_pipe_n(const DeltaSrc &src, uint8_t *smem, c
             const bf16x8 afr = a_frag(stg, 16 * mb + (lane & 15), g);
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, b0[nb], acc[mb][nb], 0, 0, 0);
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[nb], afr, acc[mb][nb], 0, 0, 0);
         }
 #pragma unroll
         for (int mb = 0; mb < NB; ++mb) {
             const bf16x8 afr = a_frag(stg, 16 * mb + (lane & 15), 4 + g);
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, b1[nb], acc[mb][nb], 0, 0, 0);
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[nb], afr, acc[mb][nb], 0, 0, 0);
         }
     }
 }
@@ -764,7 +780,7 @@ __device__ __forceinline__ void fc1_delta_body(const PrefillParams &p, uint8_t *
     if (!delta_tiles<SHARED>(p, dt)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, P = p.T * p.k, nt = blockIdx.x;
-    // this lane's h columns within the tile: jl + 16 c (c = 0, 1); B rows: gate jl + 16 c, up 128 + jl + 16 c
+    // B rows of this lane's fragments: gate jl + 16 c, up 128 + jl + 16 c (c = 0, 1)
     const int jl = 32 * wave + (lane & 15);
     const int brow[4] = {jl, jl + 16, 128 + jl, 128 + jl + 16};
     const moet_fp4 &F = SHARED ? p.shf13 : p.d13;
@@ -795,27 +811,39 @@ __device__ __forceinline__ void fc1_delta_body(const PrefillParams &p, uint8_t *
                 for (int v = 0; v < 4; ++v) acc[mb][nb][v] = 0.f;
         fp4_pipe(src, smem, brow, acc, nb16);
         const int hbase = SHARED ? P + r0 : r0;
+        // acc[mb][nb][v]: tile row 16 mb + lane % 16, feature 4 (lane / 16) + v of B block nb
+        const int rl = lane & 15, f0 = 4 * (lane >> 4);
 #pragma clang loop unroll(full)
         for (int mb = 0; mb < kDB; ++mb) {
+            const int r = 16 * mb + rl;
+            if (mb < nb16 && r < rows) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * mb + 4 * (lane >> 4) + v;
-                if (mb < nb16 && r < rows) {
+                for (int c = 0; c < 2; ++c) {
+                    const int j = 128 * nt + 32 * wave + 16 * c + f0;   // h columns j .. j + 3
+                    float g[4], u[4];
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        const int j = 128 * nt + jl + 16 * c;
-                        float g = acc[mb][c][v] * dsg, u = acc[mb][2 + c][v] * dsu;
-                        if (!SHARED) {   // plus the 2-bit pre-activations of this row
-                            const float *pre = p.pre + (size_t)(r0 + r) * (2 * I) + j;
-                            g += pre[0];
-                            u += pre[I];
-                        }
-                        if (p.swiglu_limit > 0.f) {
-                            g = fminf(g, p.swiglu_limit);
-                            u = fminf(fmaxf(u, -p.swiglu_limit), p.swiglu_limit);
-                        }
-                        p.h[(size_t)(hbase + r) * I + j] = (uint16_t)f32_to_bf16_rne(silu_f32(g) * u);
+                    for (int v = 0; v < 4; ++v) {
+                        g[v] = acc[mb][c][v] * dsg;
+                        u[v] = acc[mb][2 + c][v] * dsu;
                     }
+                    if (!SHARED) {   // plus the 2-bit pre-activations of this row
+                        const float *pre = p.pre + (size_t)(r0 + r) * (2 * I) + j;
+                        const float4 pg = *reinterpret_cast<const float4 *>(pre);
+                        const float4 pu = *reinterpret_cast<const float4 *>(pre + I);
+                        g[0] += pg.x; g[1] += pg.y; g[2] += pg.z; g[3] += pg.w;
+                        u[0] += pu.x; u[1] += pu.y; u[2] += pu.z; u[3] += pu.w;
+                    }
+                    uint32_t hv[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        if (p.swiglu_limit > 0.f) {
+                            g[v] = fminf(g[v], p.swiglu_limit);
+                            u[v] = fminf(fmaxf(u[v], -p.swiglu_limit), p.swiglu_limit);
+                        }
+                        hv[v] = f32_to_bf16_rne(silu_f32(g[v]) * u[v]);
+                    }
+                    *reinterpret_cast<uint2 *>(p.h + (size_t)(hbase + r) * I + j) =
+                        make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
                 }
             }
         }
@@ -862,19 +890,22 @@ __device__ __forceinline__ void fc2_delta_body(const PrefillParams &p, uint8_t *
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[mb][nb][v] = 0.f;
         fp4_pipe(src, smem, brow, acc, nb16);
+        // acc[mb][nb][v]: tile row 16 mb + lane % 16, output feature 64 wave + 16 nb + 4 (lane / 16) + v
+        const int rl = lane & 15, f0 = 64 * wave + 4 * (lane >> 4);
 #pragma clang loop unroll(full)
         for (int mb = 0; mb < kDB; ++mb) {
+            const int r = 16 * mb + rl;
+            if (mb < nb16 && r < rows) {
+                float *y = p.ypart + (size_t)s_prow[r] * H + 256 * nt + f0;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * mb + 4 * (lane >> 4) + v;
-                if (mb < nb16 && r < rows) {
-                    const int prow = s_prow[r];
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        float *y = p.ypart + (size_t)prow * H + 256 * nt + brow[nb];
-                        const float d = acc[mb][nb][v] * ds2;
-                        *y = SHARED ? d : *y + d;   // delta: added to the 2-bit y
+                for (int nb = 0; nb < 4; ++nb) {
+                    float4 d = make_float4(acc[mb][nb][0] * ds2, acc[mb][nb][1] * ds2, acc[mb][nb][2] * ds2,
+                                           acc[mb][nb][3] * ds2);
+                    if (!SHARED) {   // delta: added to the 2-bit y
+                        const float4 y2 = *reinterpret_cast<const float4 *>(y + 16 * nb);
+                        d = make_float4(y2.x + d.x, y2.y + d.y, y2.z + d.z, y2.w + d.w);
                     }
+                    *reinterpret_cast<float4 *>(y + 16 * nb) = d;
                 }
             }
         }

@@ -6,21 +6,24 @@
 // prefill GEMM is limited by how fast operands are fed to the matrix units
 // (one wide load per operand fragment), not by DRAM.
 //
-// MI355X design (bf16 v_mfma_f32_32x32x16, fp32 accumulation):
+// MI355X design (bf16 v_mfma_f32_16x16x32, fp32 accumulation):
 //  * Work item = (M-tile of up to 160 consecutive sorted pairs of one expert,
-//    N-tile).  160 rows (5 MFMA blocks) hold a whole expert at the usual
-//    prefill load (T*k/E ~ 128 +- 11 rows), so the weights are staged and
-//    dequantised once per expert instead of twice for about half of them.  M-tiles are numbered per expert from expert_offsets, so the
-//    routing never round-trips to the host.  Linear workgroup ids are mapped
-//    so that every N-tile of one M-tile lands on the same XCD (workgroups are
-//    dispatched round-robin over the 8 XCDs): the gathered activation rows
-//    are then read from that XCD's L2 by all of them.
-//  * A (activations): 160 rows x 64 k bf16 per step, gathered by token
-//    (gate/up) or read from h in sorted order (down), staged in LDS with an
-//    XOR swizzle of the 16-byte columns (by row / 2) so each MFMA A fragment
-//    is one conflict-free ds_read_b128 (16-lane phases over 64 banks).  A, B codes and B scales of each 64-k step
-//    travel by LDS-DMA into a 3-stage ring, so two steps are in flight while
-//    one is computed and no registers are spent on prefetching.
+//    N-tile).  160 rows hold a whole expert at the usual prefill load
+//    (T*k/E ~ 128 +- 11 rows), so the weights are staged and dequantised once
+//    per expert instead of twice for about half of them; MFMAs are issued per
+//    16-row block, so a tile pays for ceil(rows / 16) blocks.  M-tiles are
+//    numbered per expert from expert_offsets, so the routing never
+//    round-trips to the host.  Linear workgroup ids are mapped so that every
+//    N-tile of one M-tile lands on the same XCD (workgroups are dispatched
+//    round-robin over the 8 XCDs): the gathered activation rows are then read
+//    from that XCD's L2 by all of them.
+//  * A (activations): up to 160 rows x 64 k bf16 per step (the tile's valid
+//    32-row blocks), gathered by token (gate/up) or read from h in sorted
+//    order (down), staged in LDS with an XOR swizzle of the 16-byte columns
+//    (by row / 2) so each MFMA A fragment is one conflict-free ds_read_b128
+//    (16-lane phases over 64 banks).  A, B codes and B scales of each 64-k
+//    step travel by LDS-DMA into a 3-stage ring, so two steps are in flight
+//    while one is computed and no registers are spent on prefetching.
 //  * B (weights): each lane dequantises the 8 k-values its MFMA B fragment
 //    needs from the staged 2-bit words into registers: one and-or makes their
 //    e2m1 image, four FP4 -> bf16 conversions give the levels, and a packed
@@ -31,6 +34,9 @@
 //    a second instantiation that converts e2m1 -> f32, multiplies by the scale
 //    and rounds to bf16, exact as well (at most 5 significant bits).
 //    The per-tensor scale2 is applied in the epilogue.
+//  * The MFMAs take the dequantised B fragment as their first operand, so a
+//    lane's result holds four consecutive features of one row, stored with one
+//    8-byte (h) or 16-byte (y, pre-activations) access.
 //  * gate/up kernel: wave w owns 32 gate columns and the same 32 up columns,
 //    so SwiGLU is computed in registers and h = bf16(silu(g) * u) is written
 //    in sorted-pair order (the down kernel reads it contiguously).
@@ -43,10 +49,9 @@
 //    fp32 pre-activations of the flagged rows; FP4 kernels of their own then
 //    run only the flagged rows, 128 per tile, so no MFMA multiplies a row that
 //    takes no delta: gate/up adds the delta and applies SwiGLU, down adds its
-//    product to y.  One MFMA k-step is one FP4 block-16: a lane dequantises its
-//    8 values as e2m1 -> f32 -> * scale -> bf16, exact (e2m1 * e4m3 has at
-//    most 6 significant bits).  An NVFP4 shared expert's tiles run only in the
-//    FP4 kernels.
+//    product to y.  A lane dequantises each 8 FP4 values as e2m1 -> f32 ->
+//    * scale -> bf16, exact (e2m1 * e4m3 has at most 6 significant bits).  An
+//    NVFP4 shared expert's tiles run only in the FP4 kernels.
 #include <algorithm>
 
 #include "moet_common.h"
@@ -57,7 +62,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPM = 160;    // rows per M-tile
-constexpr int kPMB = 5;     // 32-row blocks per M-tile (A staging granularity)
 constexpr int kPB = kPM / 16;     // 16-row MFMA blocks per M-tile (2-bit kernels)
 constexpr int kASeg = kPM / 32;   // 8-row A segments each wavefront stages per step
 constexpr int kPK = 64;     // k per pipeline step

@@ -950,10 +950,16 @@ __global__ __launch_bounds__(256) void combine_prefill_kernel(PrefillParams p)
     // the y rows sit at fixed positions (pair t*k + j, shared P + t): their loads
     // go out before the ids and weights arrive, so the two round trips overlap
     float4 y[kCombineMaxK];
+    typedef float f4v __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int j = 0; j < kCombineMaxK; ++j)
-        y[j] = (j < p.k && in) ? *reinterpret_cast<const float4 *>(p.ypart + (size_t)(t * p.k + j) * p.H + n)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < kCombineMaxK; ++j) {
+        if (j < p.k && in) {
+            const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p.ypart + (size_t)(t * p.k + j) * p.H + n));
+            y[j] = make_float4(v.x, v.y, v.z, v.w);
+        } else {
+            y[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
     const float4 ysh = (p.has_shared && in) ? *reinterpret_cast<const float4 *>(p.ypart + (size_t)(P + t) * p.H + n)
                                             : make_float4(0.f, 0.f, 0.f, 0.f);
     const cu32 *idr = as_const(p.ids + (size_t)t * p.k);

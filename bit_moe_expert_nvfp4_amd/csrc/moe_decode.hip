@@ -71,6 +71,7 @@ struct DecodeParams {
 struct SlotInfo {
     int e, ws, pbeg, pend, dslot;   // expert, its slot in w13/w2, sorted pairs [pbeg, pend), delta slot
     bool shared;
+    bool sole;                      // no other entry of this call reads the same planes
 };
 
 // cache slot of expert e's 2-bit planes, or -1 when it is missing from the expert cache
@@ -108,6 +109,7 @@ __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotI
         si.pbeg = s;
         si.pend = s + 1;
         si.shared = true;
+        si.sole = p.T == 1;   // the T shared entries all read the shared planes
         si.dslot = -1;
         return true;
     }
@@ -145,6 +147,7 @@ __device__ __forceinline__ bool resolve_slot(const DecodeParams &p, int s, SlotI
     si.pbeg = q;
     si.pend = min(min(q + kTT, o1), P);
     si.shared = false;
+    si.sole = o1 - o0 <= kTT;
     int ds = -1;
     if (p.n_slots > 0 && p.gate != nullptr) {
         ds = p.slot_of_expert[e];
@@ -249,6 +252,10 @@ struct W2Buf {
     uint32_t sc;
 };
 
+// NT: the planes are read by this workgroup alone, so the loads are
+// non-temporal (streamed past the caches instead of displacing lines that
+// other workgroups still read)
+template <bool NT>
 __device__ __forceinline__ void w2_load(W2Buf &B, const LaneRow &L, int K, int g)
 {
     (void)K;
@@ -261,10 +268,18 @@ __device__ __forceinline__ void w2_load(W2Buf &B, const LaneRow &L, int K, int g
     gu8 *c = (gu8 *)(uintptr_t)(L.cb + (size_t)g * 2048);   // 64-k chunks 2g, 2g+1 of the row: 1 KiB apart
     gu8 *sc = (gu8 *)(uintptr_t)(L.sb + (size_t)g * 256);
     asm volatile("" : "+s"(c), "+s"(sc));
-    const v4u a = *(gv4 *)(c + L.co), b = *(gv4 *)(c + (L.co + 1024u));
+    v4u a, b;
+    if constexpr (NT) {
+        a = __builtin_nontemporal_load((gv4 *)(c + L.co));
+        b = __builtin_nontemporal_load((gv4 *)(c + (L.co + 1024u)));
+        B.sc = __builtin_nontemporal_load((gu32 *)(sc + L.so));
+    } else {
+        a = *(gv4 *)(c + L.co);
+        b = *(gv4 *)(c + (L.co + 1024u));
+        B.sc = *(gu32 *)(sc + L.so);
+    }
     B.c0 = make_uint4(a.x, a.y, a.z, a.w);
     B.c1 = make_uint4(b.x, b.y, b.z, b.w);
-    B.sc = *(gu32 *)(sc + L.so);
 }
 
 // activations of one 64-k chunk (32 bf16 pairs) of token rows xr[t] (scalar loads)
@@ -381,7 +396,7 @@ constexpr int kPF = MOET_DECODE_PF;   // weight groups loaded ahead of the one b
 // end it re-loads the final group) so that the outstanding-load count, and
 // with it the compiler's wait, is the same on every path.  xr[] must be
 // wave-uniform.
-template <int TT>
+template <int TT, bool NT>
 __device__ __forceinline__ void w2_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
 {
     if (g0 >= g1) return;
@@ -390,14 +405,14 @@ __device__ __forceinline__ void w2_gemv(const LaneRow &L, int K, int g0, int g1,
     W2Buf buf[kPF + 1];
     u32x8 xa[TT], xb[TT];
 #pragma unroll
-    for (int d = 0; d < kPF; ++d) w2_load(buf[d], L, K, min(g0 + d, g1 - 1));
+    for (int d = 0; d < kPF; ++d) w2_load<NT>(buf[d], L, K, min(g0 + d, g1 - 1));
 #pragma unroll
     for (int t = 0; t < TT; ++t) xload(xa[t], xr[t] + 8 * (8 * g0), acc[t]);
     for (int g = g0; g < g1; g += kPF + 1) {
 #pragma unroll
         for (int u = 0; u <= kPF; ++u) {
             if (g + u < g1) {
-                w2_load(buf[(u + kPF) % (kPF + 1)], L, K, min(g + u + kPF, g1 - 1));
+                w2_load<NT>(buf[(u + kPF) % (kPF + 1)], L, K, min(g + u + kPF, g1 - 1));
                 w2_group<TT>(buf[u], g + u, xr, wl, xa, xb, acc, kc);
             }
         }
@@ -415,12 +430,26 @@ struct FP4Buf {
     uint32_t sc;
 };
 
-// half group hg = 64-k chunk pair hg of the row
+// half group hg = 64-k chunk pair hg of the row (NT as for w2_load)
+template <bool NT>
 __device__ __forceinline__ void fp4_load(FP4Buf &B, const LaneRow &L, int K, int hg)
 {
-    B.c0 = L.dc4[fp4_chunk_idx(L.tile, 2 * hg, L.rt, K)];
-    B.c1 = L.dc4[fp4_chunk_idx(L.tile, 2 * hg + 1, L.rt, K)];
-    B.sc = reinterpret_cast<const uint32_t *>(L.ds8)[2 * fp4_scale_idx(L.tile, hg >> 1, L.rt, K) + (hg & 1)];
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u *c = reinterpret_cast<const v4u *>(L.dc4);
+    const uint32_t *sc = reinterpret_cast<const uint32_t *>(L.ds8) + 2 * fp4_scale_idx(L.tile, hg >> 1, L.rt, K) + (hg & 1);
+    const int i0 = fp4_chunk_idx(L.tile, 2 * hg, L.rt, K), i1 = fp4_chunk_idx(L.tile, 2 * hg + 1, L.rt, K);
+    v4u a, b;
+    if constexpr (NT) {
+        a = __builtin_nontemporal_load(c + i0);
+        b = __builtin_nontemporal_load(c + i1);
+        B.sc = __builtin_nontemporal_load(sc);
+    } else {
+        a = c[i0];
+        b = c[i1];
+        B.sc = *sc;
+    }
+    B.c0 = make_uint4(a.x, a.y, a.z, a.w);
+    B.c1 = make_uint4(b.x, b.y, b.z, b.w);
 }
 
 template <int TT>
@@ -462,7 +491,7 @@ __device__ __forceinline__ void fp4_half(const FP4Buf &B, int hg, const cu32 *co
 // acc[t] += sum over groups [g0, g1) of e2m1 * scale * x for this lane's FP4 row
 // (same prefetching as the 2-bit GEMV: weights one 64-k half group ahead,
 // activations one 16-k block ahead; xr[] wave-uniform)
-template <int TT>
+template <int TT, bool NT>
 __device__ __forceinline__ void fp4_gemv(const LaneRow &L, int K, int g0, int g1, const cu32 *const xr[TT], float acc[TT])
 {
     if (g0 >= g1) return;
@@ -470,13 +499,13 @@ __device__ __forceinline__ void fp4_gemv(const LaneRow &L, int K, int g0, int g1
     const int wl = 8 * g1 - 1;
     FP4Buf A, B;
     u32x8 xa[TT], xb[TT];
-    fp4_load(A, L, K, h0);
+    fp4_load<NT>(A, L, K, h0);
 #pragma unroll
     for (int t = 0; t < TT; ++t) xload(xa[t], xr[t] + 8 * (8 * g0), acc[t]);
     for (int hg = h0; hg < h1; hg += 2) {   // h1 - h0 is even
-        fp4_load(B, L, K, hg + 1);
+        fp4_load<NT>(B, L, K, hg + 1);
         fp4_half<TT>(A, hg, xr, wl, xa, xb, acc);
-        fp4_load(A, L, K, min(hg + 2, h1 - 1));
+        fp4_load<NT>(A, L, K, min(hg + 2, h1 - 1));
         fp4_half<TT>(B, hg + 1, xr, wl, xa, xb, acc);
     }
     xwait_acc<TT>(xa, acc);   // drain the last prefetch
@@ -487,6 +516,7 @@ constexpr int kW2 = 2;     // wavefronts per fc2 workgroup (K split)
 
 // One pass over up to kTT tokens: this lane's partial pre-activation per token
 // (2-bit part scaled by s2 plus the delta part scaled by ds2 for flagged tokens).
+template <bool NT>
 __device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2, int K, int g0, int g1,
                                           const cu32 *const xr[kTT], const bool flag[kTT], int n, float part[kTT])
 {
@@ -495,23 +525,24 @@ __device__ __forceinline__ void lane_pass(const LaneRow &L, float s2, float ds2,
     for (int t = 0; t < kTT; ++t) any_flag |= (t < n) && flag[t];
     float acc[kTT] = {0.f, 0.f}, dacc[kTT] = {0.f, 0.f};
     if (n == 1) {
-        w2_gemv<1>(L, K, g0, g1, xr, acc);
-        if (any_flag) fp4_gemv<1>(L, K, g0, g1, xr, dacc);
+        w2_gemv<1, NT>(L, K, g0, g1, xr, acc);
+        if (any_flag) fp4_gemv<1, NT>(L, K, g0, g1, xr, dacc);
     } else {
-        w2_gemv<2>(L, K, g0, g1, xr, acc);
-        if (any_flag) fp4_gemv<2>(L, K, g0, g1, xr, dacc);
+        w2_gemv<2, NT>(L, K, g0, g1, xr, acc);
+        if (any_flag) fp4_gemv<2, NT>(L, K, g0, g1, xr, dacc);
     }
 #pragma unroll
     for (int t = 0; t < kTT; ++t) part[t] = s2 * acc[t] + ((any_flag && flag[t]) ? ds2 * dacc[t] : 0.f);
 }
 
 // The same for an NVFP4 shared expert: FP4 planes only, scaled by their scale2.
+template <bool NT>
 __device__ __forceinline__ void lane_pass_fp4(const LaneRow &L, float s2, int K, int g0, int g1,
                                               const cu32 *const xr[kTT], int n, float part[kTT])
 {
     float acc[kTT] = {0.f, 0.f};
-    if (n == 1) fp4_gemv<1>(L, K, g0, g1, xr, acc);
-    else fp4_gemv<2>(L, K, g0, g1, xr, acc);
+    if (n == 1) fp4_gemv<1, NT>(L, K, g0, g1, xr, acc);
+    else fp4_gemv<2, NT>(L, K, g0, g1, xr, acc);
 #pragma unroll
     for (int t = 0; t < kTT; ++t) part[t] = s2 * acc[t];
 }
@@ -565,8 +596,14 @@ __global__ __launch_bounds__(64 * kW1) __attribute__((amdgpu_waves_per_eu(MOET_D
             xr[j] = as_const(p.x + (size_t)t * H);
         }
         float part[kTT];
-        if (fp4_shared) lane_pass_fp4(L, ds2, H, g0, g1, xr, n, part);
-        else lane_pass(L, s2, ds2, H, g0, g1, xr, flag, n, part);
+        if (fp4_shared) {
+            if (si.sole) lane_pass_fp4<true>(L, ds2, H, g0, g1, xr, n, part);
+            else lane_pass_fp4<false>(L, ds2, H, g0, g1, xr, n, part);
+        } else if (si.sole) {
+            lane_pass<true>(L, s2, ds2, H, g0, g1, xr, flag, n, part);
+        } else {
+            lane_pass<false>(L, s2, ds2, H, g0, g1, xr, flag, n, part);
+        }
 #pragma unroll
         for (int t = 0; t < kTT; ++t)
             if (t < n) red[wave][t][lane] = part[t];
@@ -635,8 +672,14 @@ __global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(MOET_D
             xr[j] = as_const(p.h + (size_t)hrow[j] * I);
         }
         float part[kTT];
-        if (fp4_shared) lane_pass_fp4(L, ds2, I, g0, g1, xr, n, part);
-        else lane_pass(L, s2, ds2, I, g0, g1, xr, flag, n, part);
+        if (fp4_shared) {
+            if (si.sole) lane_pass_fp4<true>(L, ds2, I, g0, g1, xr, n, part);
+            else lane_pass_fp4<false>(L, ds2, I, g0, g1, xr, n, part);
+        } else if (si.sole) {
+            lane_pass<true>(L, s2, ds2, I, g0, g1, xr, flag, n, part);
+        } else {
+            lane_pass<false>(L, s2, ds2, I, g0, g1, xr, flag, n, part);
+        }
 #pragma unroll
         for (int t = 0; t < kTT; ++t)
             if (t < n) red[wave][t][lane] = part[t];
@@ -725,7 +768,7 @@ __global__ __launch_bounds__(64 * kWd) void delta_gemv_kernel(moet_fp4 D, int n_
     L.rt = lane;
     const cu32 *xr[1] = {as_const(act + (size_t)r * K)};
     float a[1] = {0.f};
-    fp4_gemv<1>(L, K, g0, g1, xr, a);
+    fp4_gemv<1, false>(L, K, g0, g1, xr, a);
     red[wave][lane] = a[0];
     __syncthreads();
     if (wave == 0) {

@@ -202,55 +202,99 @@ static int launch_route_n(const float *logits, int T, int E, int k, int fn, int 
                           float *w, int32_t *offsets, int32_t *sorted, hipStream_t stream);
 
 // One workgroup per expert e: offset = #pairs with id < e, then its pairs in
-// pair order.  Thread t owns a contiguous range of pairs: one pass counts the
-// ids below e and equal to e, one block-wide exclusive scan of the equal counts
-// gives every thread its first output slot, and a second pass over its range
-// writes its pairs, so the order is stable with a single barrier phase.
-__global__ __launch_bounds__(256) void route_permute_kernel(const int32_t *__restrict__ ids, int P, int E,
-                                                            int32_t *__restrict__ offsets,
-                                                            int32_t *__restrict__ sorted)
+// pair order.  Wavefront w of 8 owns a contiguous eighth of the pairs and reads
+// it in 1 KiB steps (lane l takes ids 4l .. 4l + 3 of a step, one 16-byte load, 8
+// steps in flight), so every load is coalesced.  One pass counts the ids below
+// e and ranks the matches of e in pair order with one ballot per id of a lane
+// (earlier lanes, then the lane's own earlier ids), appending their positions
+// to the wave's list in LDS.  A block-wide sum gives the offset and every wave
+// its first output slot, and the lists are copied out, so the order is stable.
+// A wave with more matches than its list holds reads its range again.
+constexpr int kPermWaves = 8;
+constexpr int kPermList = 1024;   // positions per wave list (4 KiB)
+
+__global__ __launch_bounds__(64 * kPermWaves) void route_permute_kernel(const int32_t *__restrict__ ids, int P,
+                                                                       int E, int32_t *__restrict__ offsets,
+                                                                       int32_t *__restrict__ sorted)
 {
-    __shared__ int s_lt[4], s_eq[4];
+    __shared__ int s_lt[kPermWaves], s_eq[kPermWaves];
+    __shared__ int s_list[kPermWaves][kPermList];
     const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (((P + 255) / 256) + 3) & ~3;   // a multiple of 4: 16-byte loads (ids is 16-byte aligned)
-    const int p0 = min(tid * per, P), p1 = min(p0 + per, P);
-    int lt = 0, eq = 0;
-    int p = p0;
-    for (; p + 4 <= p1; p += 4) {
-        const int4 v = *reinterpret_cast<const int4 *>(ids + p);
-        lt += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
-        eq += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
-    }
-    for (; p < p1; ++p) {
-        const int v = ids[p];
-        lt += v < e;
-        eq += v == e;
-    }
-    // wave sums of lt; wave-inclusive scan of eq
-    int ltw = lt, inc = eq;
+    const int range = (((P + kPermWaves - 1) / kPermWaves) + 255) & ~255;   // whole 1 KiB steps
+    const int q0 = min(wave * range, P), q1 = min(q0 + range, P);
+    const uint64_t below = (1ull << lane) - 1ull;
+    // ids [p, p + 4) of this lane at step base b (beyond q1: INT_MAX, neither e nor below it)
+    auto load4 = [&](int b, int v[4]) {
+        const int p = b + 4 * lane;
+        if (p + 4 <= q1) {
+            const int4 x = *reinterpret_cast<const int4 *>(ids + p);   // ids is 16-byte aligned, p % 4 == 0
+            v[0] = x.x;
+            v[1] = x.y;
+            v[2] = x.z;
+            v[3] = x.w;
+        } else {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ltw += __shfl_xor(ltw, off, 64);
+            for (int i = 0; i < 4; ++i) v[i] = (p + i < q1) ? ids[p + i] : 0x7FFFFFFF;
+        }
+    };
+    // rank this step's matches after the wave's `cnt` earlier ones; emit(slot, position)
+    auto rank_step = [&](int b, const int v[4], int &cnt, auto emit) {
+        uint64_t m[4];
+        int tot = 0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(inc, off, 64);
-        if (lane >= off) inc += o;
+        for (int i = 0; i < 4; ++i) {
+            m[i] = __ballot(v[i] == e);
+            tot += __popcll(m[i]);
+        }
+        if (tot == 0) return;   // wave-uniform
+        int r = cnt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r += __popcll(m[i] & below);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (v[i] == e) emit(r++, b + 4 * lane + i);
+        cnt += tot;
+    };
+    int lt = 0, cnt = 0;
+    for (int b0 = q0; b0 < q1; b0 += 8 * 256) {
+        int v[8][4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) load4(b0 + 256 * u, v[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lt += (v[u][i] < e) ? 1 : 0;
+            rank_step(b0 + 256 * u, v[u], cnt, [&](int slot, int pos) {
+                if (slot < kPermList) s_list[wave][slot] = pos;
+            });
+        }
     }
-    if (lane == 63) {
-        s_lt[wave] = ltw;
-        s_eq[wave] = inc;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off, 64);
+    if (lane == 0) {
+        s_lt[wave] = lt;
+        s_eq[wave] = cnt;
     }
     __syncthreads();
-    const int off_e = s_lt[0] + s_lt[1] + s_lt[2] + s_lt[3];
-    int base = off_e + inc - eq;   // exclusive within the wave
+    int off_e = 0;
+    for (int i = 0; i < kPermWaves; ++i) off_e += s_lt[i];
+    int base = off_e;   // this wave's first output slot
     for (int i = 0; i < wave; ++i) base += s_eq[i];
     if (tid == 0) {
         offsets[e] = off_e;
         if (e == E - 1) offsets[E] = P;
     }
-    if (eq == 0) return;
-    for (p = p0; p < p1; ++p)
-        if (ids[p] == e) sorted[base++] = p;
+    if (cnt <= kPermList) {   // wave-uniform
+        for (int i = lane; i < cnt; i += 64) sorted[base + i] = s_list[wave][i];
+        return;
+    }
+    int c2 = 0;
+    for (int b = q0; b < q1; b += 256) {
+        int v[4];
+        load4(b, v);
+        rank_step(b, v, c2, [&](int slot, int pos) { sorted[base + slot] = pos; });
+    }
 }
 
 template <int NPL>
@@ -270,7 +314,7 @@ static int launch_route_n(const float *logits, int T, int E, int k, int fn, int 
                        rscale, ids, w);
     int rc = check_launch("route_topk_kernel");
     if (rc != MOET_OK) return rc;
-    hipLaunchKernelGGL(route_permute_kernel, dim3(E), dim3(256), 0, stream, (const int32_t *)ids, P, E, offsets, sorted);
+    hipLaunchKernelGGL(route_permute_kernel, dim3(E), dim3(64 * kPermWaves), 0, stream, (const int32_t *)ids, P, E, offsets, sorted);
     return check_launch("route_permute_kernel");
 }
 

@@ -127,6 +127,24 @@ def test_route_large_batch_path():
         assert np.allclose(np_(w), ow, rtol=2e-6, atol=1e-7)
 
 
+def test_route_skewed_large_run():
+    # one expert takes ~90% of 12,000 top-1 pairs: a permutation wave then holds
+    # more matches than its on-chip position list, and reads its range again
+    T, E, k = 12000, 8, 1
+    _print_case(f"route skewed T={T} E={E} k={k}")
+    g = torch.Generator().manual_seed(11)
+    lg = torch.randn((T, E), generator=g)
+    hot = torch.rand((T,), generator=g) < 0.9
+    lg[hot, 5] += 8.0
+    ids, w, offs, pairs = moet.route(lg.to(DEV), k, moet.SOFTMAX, True)
+    oids, ow, ooffs, opairs = oracle_route(lg, k, moet.SOFTMAX, True)
+    assert int(ooffs[6] - ooffs[5]) > 8 * 1024   # more than the eight lists hold: some wave overflows
+    assert (np_(ids) == oids).all()
+    assert (np_(offs) == ooffs).all()
+    assert (np_(pairs) == opairs).all()
+    assert np.allclose(np_(w), ow, rtol=2e-6, atol=1e-7)
+
+
 def _small_cfg(**kw):
     base = dict(name="tiny", T=4, H=256, I=128, E=8, k=2, score=synth.SOFTMAX)
     base.update(kw)

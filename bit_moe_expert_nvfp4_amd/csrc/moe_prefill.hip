@@ -84,6 +84,7 @@ struct PrefillParams {
     const int32_t *order;   // the pairs in expert order, a delta expert's flagged pairs first (= sorted without delta)
     const int32_t *nflag;   // per expert: its flagged pairs at the head of its run in `order` (null: none)
     int n_mslots;       // upper bound on 160-row M-tiles (grid of the 2-bit kernels)
+    int4 *tiles;        // [n_mslots] M-tile table: (expert, first row, rows, flagged end); rows 0 = no tile
     int n_ntiles;
     const int32_t *base_slot;   // expert -> cache slot of w13/w2 (null: expert e at e)
     int n_base_slots;
@@ -111,15 +112,15 @@ struct MTile {
     int fl_end;   // rows of `order` below this take the FP4 delta (the flagged head of a delta expert's run)
 };
 
-// M-tile number ms -> (expert, rows) of the 2-bit kernels.  Tiles of PM rows
-// are enumerated expert by expert over its run in `order` (ceil(count / PM)
-// each), then the 2-bit shared expert's tiles.  One wavefront computes it:
-// per-lane tile counts, inclusive scan, ballot search.
-template <int PM>
-__device__ bool locate_mtile(const PrefillParams &p, int ms, MTile &mt)
+// The M-tile table of the 2-bit kernels: slot ms -> (expert, first row in
+// `order`, rows, flagged end).  Tiles of kPM rows are enumerated expert by expert
+// over its run (ceil(count / kPM) each), then the 2-bit shared expert's tiles;
+// the slots after the last tile get rows = 0.  One wavefront writes it once per
+// forward (per-lane tile counts, inclusive scan), so each GEMM workgroup finds
+// its tile with one load and the slots beyond the last tile exit at once.
+__global__ __launch_bounds__(64) void mtile_table_kernel(PrefillParams p)
 {
-    constexpr int kPM = PM;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x;
     int base = 0;   // tiles before the current 64-expert chunk
     for (int c = 0; c < p.E; c += 64) {
         const int e = c + lane;
@@ -135,33 +136,30 @@ __device__ bool locate_mtile(const PrefillParams &p, int ms, MTile &mt)
             const int v = __shfl_up(incl, off, 64);
             if (lane >= off) incl += v;
         }
-        const int excl = base + incl - tiles;
-        const bool mine = (e < p.E) && ms >= excl && ms < excl + tiles;
-        const uint64_t b = __ballot(mine);
-        if (b) {
-            const int src = __builtin_ctzll(b);
-            const int ee = __shfl(e, src, 64), oo = __shfl(o0, src, 64), cc = __shfl(cnt, src, 64),
-                      ex = __shfl(excl, src, 64);
-            const int t = ms - ex;
-            mt.e = ee;
-            mt.row0 = oo + t * kPM;
-            mt.rows = min(kPM, cc - t * kPM);
-            mt.fl_end = oo + (p.nflag ? p.nflag[ee] : 0);
-            return true;
+        const int fl = o0 + ((p.nflag && e < p.E) ? p.nflag[e] : 0);
+        for (int t = 0; t < tiles; ++t) {
+            const int ms = base + incl - tiles + t;
+            if (ms < p.n_mslots) p.tiles[ms] = make_int4(e, o0 + t * kPM, min(kPM, cnt - t * kPM), fl);
         }
         base += __shfl(incl, 63, 64);
     }
     if (p.has_shared && !p.shared_fp4) {
-        const int t = ms - base;
-        if (t >= 0 && t * kPM < p.T) {
-            mt.e = -1;
-            mt.row0 = t * kPM;
-            mt.rows = min(kPM, p.T - t * kPM);
-            mt.fl_end = 0;
-            return true;
-        }
+        for (int t = lane; t * kPM < p.T; t += 64)
+            if (base + t < p.n_mslots) p.tiles[base + t] = make_int4(-1, t * kPM, min(kPM, p.T - t * kPM), 0);
+        base += (p.T + kPM - 1) / kPM;
     }
-    return false;
+    for (int ms = base + lane; ms < p.n_mslots; ms += 64) p.tiles[ms] = make_int4(0, 0, 0, 0);
+}
+
+// slot ms of the M-tile table (false: no tile)
+__device__ __forceinline__ bool lookup_mtile(const PrefillParams &p, int ms, MTile &mt)
+{
+    const int4 v = p.tiles[ms];
+    mt.e = __builtin_amdgcn_readfirstlane(v.x);
+    mt.row0 = __builtin_amdgcn_readfirstlane(v.y);
+    mt.rows = __builtin_amdgcn_readfirstlane(v.z);
+    mt.fl_end = __builtin_amdgcn_readfirstlane(v.w);
+    return mt.rows > 0;
 }
 
 // XCD-aware decode of the linear workgroup id into (M-tile slot, N-tile)
@@ -469,7 +467,7 @@ __device__ __forceinline__ void fc1_prefill_body(const PrefillParams &p, uint8_t
     decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
     if (ms >= p.n_mslots) return;
     MTile mt;
-    if (!locate_mtile<kPM>(p, ms, mt)) return;
+    if (!lookup_mtile(p, ms, mt)) return;
     const int nb16 = (mt.rows + 15) / 16;
     const int nmb = (nb16 + 1) / 2;   // staged 32-row blocks
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -561,7 +559,7 @@ __device__ __forceinline__ void fc2_prefill_body(const PrefillParams &p, uint8_t
     decode_wg(blockIdx.x, p.n_ntiles, ms, nt);
     if (ms >= p.n_mslots) return;
     MTile mt;
-    if (!locate_mtile<kPM>(p, ms, mt)) return;
+    if (!lookup_mtile(p, ms, mt)) return;
     const int nb16 = (mt.rows + 15) / 16;
     const int nmb = (nb16 + 1) / 2;   // staged 32-row blocks
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1011,7 +1009,10 @@ size_t prefill_workspace_bytes(int T, int k, int H, int I, int E)
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     // h rows, y rows (or the flagged rows' pre-activations before them), the reordered pairs, the
     // flagged count per expert
-    return al(rows * I * 2) + al(rows * (size_t)std::max(H, 2 * I) * 4) + al((size_t)T * k * 4) + al((size_t)E * 4);
+    // and the M-tile table
+    const size_t mslots = ((size_t)T * k + kPM - 1) / kPM + E + ((size_t)T + kPM - 1) / kPM;
+    return al(rows * I * 2) + al(rows * (size_t)std::max(H, 2 * I) * 4) + al((size_t)T * k * 4) + al((size_t)E * 4) +
+           al(mslots * 16);
 }
 
 int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const int32_t *ids, const float *w,
@@ -1063,6 +1064,7 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     int32_t *order = reinterpret_cast<int32_t *>(base + al(rows * L->I * 2) +
                                                  al(rows * (size_t)std::max(L->H, 2 * L->I) * 4));
     int32_t *nflag = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(order) + al((size_t)P * 4));
+    p.tiles = reinterpret_cast<int4 *>(reinterpret_cast<char *>(nflag) + al((size_t)L->E * 4));
     p.out = out;
     const bool delta = p.n_slots > 0;
     p.order = delta ? order : sorted;
@@ -1077,6 +1079,9 @@ int launch_prefill(const moet_layer *L, const uint16_t *x, int T, int k, const i
     const int mslots = (P + kPM - 1) / kPM + L->E + ((p.has_shared && !p.shared_fp4) ? (T + kPM - 1) / kPM : 0);
     p.n_mslots = mslots;
     const int ms8 = (mslots + 7) / 8 * 8;
+    hipLaunchKernelGGL(mtile_table_kernel, dim3(1), dim3(64), 0, stream, p);
+    rc = check_launch("mtile_table_kernel");
+    if (rc != MOET_OK) return rc;
     // FP4 delta tiles: (N-tile, delta slot, 2 workgroups splitting the slot's tiles); NVFP4 shared
     // expert: (N-tile, 128-token tile)
     const dim3 dgrid1(L->I / 128, L->n_slots, 2), dgrid2(L->H / 256, L->n_slots, 2);

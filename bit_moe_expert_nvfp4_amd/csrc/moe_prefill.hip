@@ -113,42 +113,85 @@ struct MTile {
 };
 
 // The M-tile table of the 2-bit kernels: slot ms -> (expert, first row in
-// `order`, rows, flagged end).  Tiles of kPM rows are enumerated expert by expert
-// over its run (ceil(count / kPM) each), then the 2-bit shared expert's tiles;
-// the slots after the last tile get rows = 0.  One wavefront writes it once per
-// forward (per-lane tile counts, inclusive scan), so each GEMM workgroup finds
-// its tile with one load and the slots beyond the last tile exit at once.
+// `order`, rows, flagged end).  Each expert's run (the 2-bit shared expert's
+// T tokens after the routed experts) is cut into tiles of kPM rows, the last
+// one partial.  The tiles are ordered by their 16-row block count, largest
+// first (within a count, by expert), so the grid's last workgroups are its
+// shortest and finish closer together; the slots after the last tile get
+// rows = 0.  One wavefront writes
+// the table once per forward (a pass counting the tiles of each block count,
+// then a pass placing them: scans for the full tiles, one ballot per count for
+// the partial ones), so each GEMM workgroup finds its tile with one load and the
+// slots beyond the last tile exit at once.
 __global__ __launch_bounds__(64) void mtile_table_kernel(PrefillParams p)
 {
+    constexpr int kCls = kPM / 16;   // classes 1 .. kCls (index = class - 1)
     const int lane = threadIdx.x;
-    int base = 0;   // tiles before the current 64-expert chunk
-    for (int c = 0; c < p.E; c += 64) {
-        const int e = c + lane;
-        int cnt = 0, o0 = 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const bool sh = p.has_shared && !p.shared_fp4;
+    // pass 1: tiles per class
+    int ncls[kCls];
+#pragma unroll
+    for (int c = 0; c < kCls; ++c) ncls[c] = 0;
+    for (int c0 = 0; c0 < p.E + 64; c0 += 64) {
+        const int e = c0 + lane;
+        int cnt = 0;
+        if (e < p.E) cnt = p.offsets[e + 1] - p.offsets[e];
+        else if (sh && e == p.E) cnt = p.T;   // the shared expert after the routed ones
+        const int full = cnt / kPM, rem = cnt - full * kPM;
+        const int rc = rem ? (rem + 15) / 16 : 0;
+        int fsum = full;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) fsum += __shfl_xor(fsum, off, 64);
+        ncls[kCls - 1] += fsum;
+#pragma unroll
+        for (int c = 0; c < kCls; ++c) ncls[c] += __popcll(__ballot(rc == c + 1));
+        if (c0 >= p.E) break;
+    }
+    int base[kCls];   // first slot of each class, largest class first
+    int acc = 0;
+#pragma unroll
+    for (int c = kCls - 1; c >= 0; --c) {
+        base[c] = acc;
+        acc += ncls[c];
+    }
+    // pass 2: write the tiles
+    for (int c0 = 0; c0 < p.E + 64; c0 += 64) {
+        const int e = c0 + lane;
+        int cnt = 0, o0 = 0, fl = 0, ee = e;
         if (e < p.E) {
             o0 = p.offsets[e];
             cnt = p.offsets[e + 1] - o0;
+            fl = o0 + (p.nflag ? p.nflag[e] : 0);
+        } else if (sh && e == p.E) {
+            cnt = p.T;
+            ee = -1;
         }
-        const int tiles = (cnt + kPM - 1) / kPM;
-        int incl = tiles;
+        const int full = cnt / kPM, rem = cnt - full * kPM;
+        const int rc = rem ? (rem + 15) / 16 : 0;
+        int incl = full;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int v = __shfl_up(incl, off, 64);
             if (lane >= off) incl += v;
         }
-        const int fl = o0 + ((p.nflag && e < p.E) ? p.nflag[e] : 0);
-        for (int t = 0; t < tiles; ++t) {
-            const int ms = base + incl - tiles + t;
-            if (ms < p.n_mslots) p.tiles[ms] = make_int4(e, o0 + t * kPM, min(kPM, cnt - t * kPM), fl);
+        for (int t = 0; t < full; ++t) {
+            const int ms = base[kCls - 1] + incl - full + t;
+            if (ms < p.n_mslots) p.tiles[ms] = make_int4(ee, o0 + t * kPM, kPM, fl);
         }
-        base += __shfl(incl, 63, 64);
+        base[kCls - 1] += __shfl(incl, 63, 64);
+#pragma unroll
+        for (int c = 0; c < kCls; ++c) {
+            const uint64_t m = __ballot(rc == c + 1);
+            if (rc == c + 1) {
+                const int ms = base[c] + __popcll(m & below);
+                if (ms < p.n_mslots) p.tiles[ms] = make_int4(ee, o0 + full * kPM, rem, fl);
+            }
+            base[c] += __popcll(m);
+        }
+        if (c0 >= p.E) break;
     }
-    if (p.has_shared && !p.shared_fp4) {
-        for (int t = lane; t * kPM < p.T; t += 64)
-            if (base + t < p.n_mslots) p.tiles[base + t] = make_int4(-1, t * kPM, min(kPM, p.T - t * kPM), 0);
-        base += (p.T + kPM - 1) / kPM;
-    }
-    for (int ms = base + lane; ms < p.n_mslots; ms += 64) p.tiles[ms] = make_int4(0, 0, 0, 0);
+    for (int ms = acc + lane; ms < p.n_mslots; ms += 64) p.tiles[ms] = make_int4(0, 0, 0, 0);
 }
 
 // slot ms of the M-tile table (false: no tile)

@@ -115,7 +115,9 @@ def test_route_small_and_ties():
 
 
 def test_route_large_batch_path():
-    for T, E, k in [(4096, 256, 8), (300, 384, 8), (1000, 8, 2)]:
+    # pair counts above the small-batch path, including ones that are not a multiple of 4 (the
+    # permutation's scalar tail) and expert counts that are not a multiple of 64
+    for T, E, k in [(4096, 256, 8), (300, 384, 8), (1000, 8, 2), (1025, 5, 1), (1031, 33, 3)]:
         _print_case(f"route large T={T} E={E} k={k}")
         g = torch.Generator().manual_seed(T)
         lg = torch.randn((T, E), generator=g)

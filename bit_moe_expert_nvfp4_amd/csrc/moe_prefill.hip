@@ -11,9 +11,10 @@
 //    N-tile).  160 rows hold a whole expert at the usual prefill load
 //    (T*k/E ~ 128 +- 11 rows), so the weights are staged and dequantised once
 //    per expert instead of twice for about half of them; MFMAs are issued per
-//    16-row block, so a tile pays for ceil(rows / 16) blocks.  M-tiles are
-//    numbered per expert from expert_offsets, so the routing never
-//    round-trips to the host.  Linear workgroup ids are mapped so that every
+//    16-row block, so a tile pays for ceil(rows / 16) blocks.  A one-wave
+//    kernel turns expert_offsets into the M-tile table on the device (largest
+//    tiles first), so the routing never round-trips to the host and each
+//    workgroup finds its tile with one load.  Linear workgroup ids are mapped so that every
 //    N-tile of one M-tile lands on the same XCD (workgroups are dispatched
 //    round-robin over the 8 XCDs): the gathered activation rows are then read
 //    from that XCD's L2 by all of them.

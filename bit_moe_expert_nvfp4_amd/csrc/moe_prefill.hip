@@ -113,6 +113,16 @@ struct MTile {
     int fl_end;   // rows of `order` below this take the FP4 delta (the flagged head of a delta expert's run)
 };
 
+// Expert e's run [o0, o1) of sorted pairs, clamped to [0, P]: the routing arrays
+// come from the route call, and the clamp keeps every index derived from them
+// in bounds if they do not.
+__device__ __forceinline__ void expert_run(const PrefillParams &p, int e, int &o0, int &o1)
+{
+    const int P = p.T * p.k;
+    o0 = min(max(p.offsets[e], 0), P);
+    o1 = min(max(p.offsets[e + 1], o0), P);
+}
+
 // The M-tile table of the 2-bit kernels: slot ms -> (expert, first row in
 // `order`, rows, flagged end).  Each expert's run (the 2-bit shared expert's
 // T tokens after the routed experts) is cut into tiles of kPM rows, the last
@@ -137,8 +147,13 @@ __global__ __launch_bounds__(64) void mtile_table_kernel(PrefillParams p)
     for (int c0 = 0; c0 < p.E + 64; c0 += 64) {
         const int e = c0 + lane;
         int cnt = 0;
-        if (e < p.E) cnt = p.offsets[e + 1] - p.offsets[e];
-        else if (sh && e == p.E) cnt = p.T;   // the shared expert after the routed ones
+        if (e < p.E) {
+            int o0, o1;
+            expert_run(p, e, o0, o1);
+            cnt = o1 - o0;
+        } else if (sh && e == p.E) {
+            cnt = p.T;   // the shared expert after the routed ones
+        }
         const int full = cnt / kPM, rem = cnt - full * kPM;
         const int rc = rem ? (rem + 15) / 16 : 0;
         int fsum = full;
@@ -161,8 +176,9 @@ __global__ __launch_bounds__(64) void mtile_table_kernel(PrefillParams p)
         const int e = c0 + lane;
         int cnt = 0, o0 = 0, fl = 0, ee = e;
         if (e < p.E) {
-            o0 = p.offsets[e];
-            cnt = p.offsets[e + 1] - o0;
+            int o1;
+            expert_run(p, e, o0, o1);
+            cnt = o1 - o0;
             fl = o0 + (p.nflag ? p.nflag[e] : 0);
         } else if (sh && e == p.E) {
             cnt = p.T;
@@ -476,7 +492,9 @@ __global__ __launch_bounds__(256) void partition_kernel(PrefillParams p, int32_t
     }
     __syncthreads();
     const bool delta = s_delta != 0;
-    const int o0 = p.offsets[e], o1 = p.offsets[e + 1], n = o1 - o0;
+    int o0, o1;
+    expert_run(p, e, o0, o1);
+    const int n = o1 - o0;
     const int per = (n + 255) / 256;
     const int b0 = o0 + min(tid * per, n), b1 = o0 + min(tid * per + per, n);
     int f = 0;
@@ -813,7 +831,8 @@ __device__ __forceinline__ bool delta_tiles(const PrefillParams &p, DeltaTiles &
         if (e < 0 || p.nflag[e] == 0) return false;   // nflag is 0 unless e takes the delta
         dt.e = e;
         dt.ds = s;
-        dt.row0 = p.offsets[e];
+        int o1;
+        expert_run(p, e, dt.row0, o1);
         dt.count = p.nflag[e];
         return true;
     }
